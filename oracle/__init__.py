@@ -1,0 +1,170 @@
+"""CPU oracle for ROSA retrieval -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path
+(``online_suffix_automaton_amd``) never imports it, and the two share no code.
+
+Source: "ROSA-Tuning: Enhancing Long-Context Modeling via Suffix Matching"
+(arXiv 2602.02499).  Each function cites the passage it follows; the
+arithmetic lives in ``rosa_oracle.c`` (plain C, built with gcc) apart from
+``brute_py``, an independent pure-Python statement of the definition used on
+tiny inputs.
+
+All functions take and return numpy arrays on the host:
+  * ``discretize_bf16(H_u16 [B,T,D], M) -> sym uint8 [S,T]``   (Sec. 3.2)
+  * ``match(sym uint8 [S,T], K) -> (E int32, SYM int16, L int32)``
+    (Sec. 2.2, Sec. 3.3 / App. B.3)
+  * ``brute(sym [S,T]) -> (E, L)``  O(T^2) definition, pins ``match``
+  * ``gather(V_u16 [B,T,D], E [S,T], M) -> out u16 [B,T,D]`` (App. C.4, Eq. 17)
+  * ``sam_stats(x [T], K) -> (states, transitions, clones, distinct)``
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "rosa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile rosa_oracle.c with gcc into oracle/liboracle.so."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-shared", "-fPIC",
+                               "-o", tmp, _SRC])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build(force=False)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    I = ctypes.c_int
+    lib.oracle_discretize_bf16.argtypes = [P, I64, I64, I64, I, P]
+    lib.oracle_match.argtypes = [P, I64, I, P, P, P]
+    lib.oracle_match_streams.argtypes = [P, I64, I64, I64, I, P, P, P]
+    lib.oracle_sam_stats.argtypes = [P, I64, I, P]
+    lib.oracle_brute.argtypes = [P, I64, P, P]
+    lib.oracle_gather.argtypes = [P, I64, I64, I64, I, P, P]
+    for f in (lib.oracle_discretize_bf16, lib.oracle_match,
+              lib.oracle_match_streams, lib.oracle_sam_stats,
+              lib.oracle_brute, lib.oracle_gather):
+        f.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc: int, what: str):
+    if rc == -2:
+        raise ValueError(f"{what}: symbol out of range [0, K)")
+    if rc != 0:
+        raise ValueError(f"{what}: error code {rc}")
+
+
+def discretize_bf16(H: np.ndarray, M: int) -> np.ndarray:
+    """Sec. 3.2, Eq. (10)-(15): bit = I[h > 0] per channel, route r packs
+    channels r*M .. r*M+M-1 with weight 2^j.  H: uint16 bf16 bits [B,T,D]."""
+    H = np.ascontiguousarray(H, dtype=np.uint16)
+    B, T, D = H.shape
+    S = B * (D // M)
+    sym = np.zeros((S, T), dtype=np.uint8)
+    _check(_load().oracle_discretize_bf16(_ptr(H), B, T, D, M, _ptr(sym)),
+           "discretize")
+    return sym
+
+
+def match(sym: np.ndarray, K: int):
+    """Sec. 2.2 + Sec. 3.3: per stream, longest recurring suffix, its most
+    recent earlier end E (-1 if none) and the next symbol x[E+1]."""
+    sym = np.ascontiguousarray(sym, dtype=np.uint8)
+    if sym.ndim == 1:
+        sym = sym[None, :]
+    S, T = sym.shape
+    E = np.empty((S, T), dtype=np.int32)
+    SYM = np.empty((S, T), dtype=np.int16)
+    L = np.empty((S, T), dtype=np.int32)
+    _check(_load().oracle_match_streams(_ptr(sym), S, T, T, K, _ptr(E),
+                                        _ptr(SYM), _ptr(L)), "match")
+    return E, SYM, L
+
+
+def match_one(x: np.ndarray, K: int, E: np.ndarray, SYM: np.ndarray,
+              L: np.ndarray) -> None:
+    """One stream into caller-provided rows (used by threaded baselines)."""
+    _check(_load().oracle_match(_ptr(x), x.shape[0], K, _ptr(E), _ptr(SYM),
+                                _ptr(L)), "match")
+
+
+def brute(sym: np.ndarray):
+    """The definition as an O(T^2) common-suffix table (pins ``match``)."""
+    sym = np.ascontiguousarray(sym, dtype=np.uint8)
+    if sym.ndim == 1:
+        sym = sym[None, :]
+    S, T = sym.shape
+    E = np.empty((S, T), dtype=np.int32)
+    L = np.empty((S, T), dtype=np.int32)
+    lib = _load()
+    for s in range(S):
+        row = np.ascontiguousarray(sym[s])
+        e = np.empty(T, dtype=np.int32)
+        l = np.empty(T, dtype=np.int32)
+        _check(lib.oracle_brute(_ptr(row), T, _ptr(e), _ptr(l)), "brute")
+        E[s], L[s] = e, l
+    return E, L
+
+
+def brute_py(x):
+    """Pure-Python restatement of the definition for tiny streams: for each
+    t, scan every earlier end e, count the common suffix length directly, keep
+    the longest and, among equals, the latest."""
+    x = [int(v) for v in x]
+    T = len(x)
+    E, L = [], []
+    for t in range(T):
+        best, arg = 0, -1
+        for e in range(t):
+            k = 0
+            while e - k >= 0 and x[e - k] == x[t - k]:
+                k += 1
+            if k > 0 and k >= best:
+                best, arg = k, e
+        E.append(arg)
+        L.append(best)
+    return E, L
+
+
+def gather(V: np.ndarray, E: np.ndarray, M: int) -> np.ndarray:
+    """App. C.4: read-out at tau = E+1 for the route's M channels; zero when
+    there is no hit (validity mask, Eq. (17))."""
+    V = np.ascontiguousarray(V, dtype=np.uint16)
+    B, T, D = V.shape
+    E = np.ascontiguousarray(E, dtype=np.int32)
+    out = np.empty_like(V)
+    _check(_load().oracle_gather(_ptr(V), B, T, D, M, _ptr(E), _ptr(out)),
+           "gather")
+    return out
+
+
+def sam_stats(x: np.ndarray, K: int):
+    """(states, transitions, clones, distinct substrings) of the automaton."""
+    x = np.ascontiguousarray(x, dtype=np.uint8)
+    out = np.zeros(4, dtype=np.int64)
+    _check(_load().oracle_sam_stats(_ptr(x), x.shape[0], K, _ptr(out)),
+           "sam_stats")
+    return tuple(int(v) for v in out)
