@@ -1,0 +1,171 @@
+/*
+ * rosa.h -- C-ABI of librosa: ROSA retrieval (online suffix-automaton
+ * longest-suffix matching over many independent symbol streams) on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Method: "ROSA-Tuning: Enhancing Long-Context Modeling via Suffix Matching"
+ * (Zheng, Wang, Ren, Chen; arXiv 2602.02499).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *    library never allocates device memory; scratch comes from a caller
+ *    workspace (rosa_match) or a caller state buffer (rosa_build/rosa_step).
+ *  - Every call only enqueues work on the caller's `stream` and returns; no
+ *    implicit device synchronisation, no internal streams.  The exceptions,
+ *    which synchronise `stream`, are rosa_match_status and rosa_state_status.
+ *  - On any return other than ROSA_OK nothing has been enqueued and no output
+ *    has been written.
+ *  - Streams: stream s = b*R + r with R = D/M routes per batch row (Sec. 4.1:
+ *    one symbol stream per (b, r) pair).  Time is 0-based.  Per-stream outputs
+ *    are laid out [S][T], contiguous in t.
+ *  - Outputs per position t of stream x (Sec. 3.3 and App. B.3; the body of
+ *    Eq. (16) is lost from the page text and is read as follows):
+ *        L(t)   length of the longest suffix of x[0..t] that also ends at
+ *               some earlier position e < t (0 if none);
+ *        E(t)   the largest such e, i.e. the most recent earlier occurrence
+ *               ("endpos" of the hit), or -1;
+ *        SYM(t) x[E+1], the symbol that followed that occurrence, or -1;
+ *        tau(t) = E+1, the retrieval destination read by the value gather
+ *               (App. C.4), or -1.
+ *    These values are unique, so results are bit-exact and independent of
+ *    launch geometry.
+ */
+#ifndef ROSA_H
+#define ROSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rosa_status {
+    ROSA_OK = 0,
+    ROSA_ERR_ARG = 1,      /* null pointer, bad size, shape or range        */
+    ROSA_ERR_CAPACITY = 2, /* workspace/state buffer too small, or a step
+                              past the capacity given to rosa_build         */
+    ROSA_ERR_SYMBOL = 3,   /* an input symbol >= K was seen (reported by
+                              rosa_match_status / rosa_state_status)        */
+    ROSA_ERR_HIP = 4,      /* a HIP runtime call failed                     */
+    ROSA_ERR_STATE = 5     /* null, freed or foreign state handle           */
+} rosa_status;
+
+/* Input kinds. */
+enum {
+    /* uint8 symbols [S][ld] (ld >= T, in bytes), values in [0, K). */
+    ROSA_IN_SYMBOLS = 0,
+    /* bf16 hidden states [B][T][ld] as raw 16-bit patterns (ld >= D, in
+     * elements).  Sec. 3.2, Eq. (10)-(15): channel c = r*M + j gives the
+     * bit I[h > 0] (+0, -0 and NaN give 0; +inf and positive subnormals
+     * give 1), route r packs its M bits with weight 2^j, K = 2^M. */
+    ROSA_IN_BF16 = 1
+};
+
+typedef struct rosa_input {
+    int32_t kind;      /* ROSA_IN_SYMBOLS or ROSA_IN_BF16                    */
+    int32_t M;         /* BF16: bits per symbol, 1..8, D % M == 0            */
+    int32_t K;         /* SYMBOLS: alphabet size 1..256; BF16: ignored (2^M) */
+    int32_t reserved;
+    const void *data;  /* device pointer                                      */
+    int64_t S;         /* SYMBOLS: number of streams; BF16: ignored (B*D/M)  */
+    int64_t T;         /* positions per stream                                */
+    int64_t B, D;      /* BF16 only: batch rows and channels                  */
+    int64_t ld;        /* row stride: bytes per stream (SYMBOLS) or elements
+                          per position (BF16)                                 */
+} rosa_input;
+
+typedef struct rosa_out {
+    int32_t *end;      /* [S][T] E, required                                  */
+    int16_t *sym;      /* [S][T] SYM, may be NULL                             */
+    int32_t *len;      /* [S][T] L, may be NULL                               */
+    uint8_t *symbols;  /* [S][T] the packed input symbols, may be NULL        */
+} rosa_out;
+
+/* ------------------------------------------------------------ batch match */
+
+/* Bytes of device workspace rosa_match needs for S streams of T positions
+ * over an alphabet of K symbols.  0 on bad arguments. */
+size_t rosa_match_workspace_bytes(int64_t S, int64_t T, int32_t K);
+
+/* Sec. 3.3 / Sec. 4.1: for every stream and every position t, L, E and SYM
+ * as defined above, for all S*T positions at once.  `in` gives the symbols
+ * (or the bf16 hidden states, discretised on the device first); `out->end`
+ * is required, the other outputs are optional.  `ws` is a device workspace
+ * of at least rosa_match_workspace_bytes(S, T, K) bytes, 256-byte aligned;
+ * it must not be shared by calls in flight at the same time.  Limits:
+ * 1 <= T < 2^26, S*T < 2^40.  A symbol >= K sets a sticky flag in `ws`
+ * (read it with rosa_match_status); the outputs of that call are then
+ * unspecified.  No device memory is read outside the given buffers. */
+rosa_status rosa_match(const rosa_input *in, const rosa_out *out, void *ws,
+                       size_t ws_bytes, hipStream_t stream);
+
+/* Synchronises `stream`, then returns ROSA_ERR_SYMBOL if the last rosa_match
+ * that used `ws` saw a symbol >= K, else ROSA_OK (or ROSA_ERR_HIP). */
+rosa_status rosa_match_status(const void *ws, hipStream_t stream);
+
+/* ------------------------------------------------------------ value gather */
+
+/* App. C.4 read-out with the validity mask of Eq. (17):
+ *   out[b][t][r*M+m] = V[b][E[s][t]+1][r*M+m]  if E[s][t] >= 0, else 0x0000,
+ * for s = b*R + r, m < M.  A bit copy of bf16 patterns (NaN payloads and -0
+ * kept).  V: [B][T][ldv], out: [B][T][ldo] (elements), E: [S][T] with every
+ * value in [-1, T-2] (as rosa_match produces; other values give ROSA-
+ * unspecified output but no out-of-bounds access: E is clamped on device). */
+rosa_status rosa_gather(const uint16_t *V, int64_t B, int64_t T, int64_t D,
+                        int64_t ldv, int32_t M, const int32_t *end,
+                        uint16_t *out, int64_t ldo, hipStream_t stream);
+
+/* ------------------------------------------------ online automaton (decode) */
+
+typedef struct rosa_state rosa_state;   /* opaque host handle */
+
+/* Bytes of device state for S streams, alphabet K, up to t_capacity
+ * positions per stream: one suffix automaton per stream with at most
+ * max(2, 2*t_capacity - 1) states (Sec. 2.2 bound), dense K-wide transition
+ * rows, and the symbol history.  0 on bad arguments. */
+size_t rosa_state_bytes(int64_t S, int32_t K, int64_t t_capacity);
+
+/* Sec. 2.2 / Sec. 4.1: builds, in the caller's device buffer `state_buf`,
+ * one online suffix automaton per stream over the prefix `in` (T may be 0),
+ * and returns a host handle in *handle.  If `out` is not NULL it receives
+ * L/E/SYM for the prefix positions, identical to rosa_match.  in->K (or
+ * 2^M) fixes the alphabet; t_capacity >= T bounds the total length.
+ * The handle must be released with rosa_free (which does not free
+ * state_buf).  A handle must not be used on two streams concurrently. */
+rosa_status rosa_build(const rosa_input *in, int64_t t_capacity,
+                       void *state_buf, size_t state_bytes,
+                       rosa_state **handle, const rosa_out *out,
+                       hipStream_t stream);
+
+/* One online step for every stream at position t = current length: extend
+ * each automaton by the new symbol (`row`: T == 1, same kind, S, B, D, M/K
+ * as at build), then write end[S] = E(t), sym[S] = SYM(t) (may be NULL) and,
+ * if out_row is not NULL, the gathered values
+ *   out_row[b*ldo_b + r*M + m] = V[b*ldv_b + (E+1)*ldv + r*M + m]  (0 if E<0)
+ * V must already hold position t (tau = E+1 can equal t).  Returns
+ * ROSA_ERR_CAPACITY (checked on the host) once t_capacity positions exist. */
+rosa_status rosa_step(rosa_state *h, const rosa_input *row, const uint16_t *V,
+                      int64_t ldv, int64_t ldv_b, int32_t *end, int16_t *sym,
+                      uint16_t *out_row, int64_t ldo_b, hipStream_t stream);
+
+/* Positions processed so far by the handle (host value, no sync). */
+int64_t rosa_state_length(const rosa_state *h);
+
+/* Synchronises `stream`; ROSA_ERR_SYMBOL if any build/step of this handle
+ * saw a symbol >= K, else ROSA_OK. */
+rosa_status rosa_state_status(rosa_state *h, hipStream_t stream);
+
+/* Frees the host handle only (the caller owns and frees state_buf).
+ * NULL is ignored. */
+void rosa_free(rosa_state *h);
+
+const char *rosa_error_string(rosa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROSA_H */

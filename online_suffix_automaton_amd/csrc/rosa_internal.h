@@ -1,0 +1,91 @@
+// rosa_internal.h -- layouts and launch parameters shared by librosa's HIP
+// sources.  Not part of the public ABI (that is include/rosa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rosa {
+
+// Symbol rows in the match workspace carry zero padding on both sides so
+// that 16-byte windows ending near position 0 or T-1 never leave the row.
+constexpr int kPadFront = 64;
+constexpr int kPadBack = 64;
+
+// d-gram bucketing limits (per stream, held in LDS by the stream kernel).
+constexpr int kMaxBuckets = 4096;    // K^d
+constexpr int kMaxFirstTab = 2048;   // sum_{l=1}^{d-1} K^l
+constexpr int kMaxD = 12;
+
+constexpr int kStreamThreads = 1024; // one workgroup per stream
+constexpr int kBigThreads = 64;      // one wave per large group
+
+// Flags word layout in the match workspace (first 256 bytes).
+constexpr int kFlagSymbol = 0;       // int32: nonzero if a symbol >= K was seen
+
+struct WsLayout {
+    size_t flags, sym, keys, pos, pos2, big, stack, total;
+    int64_t Tp;          // bytes per padded symbol row
+    int64_t big_cap;     // entries in the large-group list
+};
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline WsLayout ws_layout(int64_t S, int64_t T)
+{
+    WsLayout w;
+    w.Tp = (int64_t)align_up((size_t)T + kPadFront + kPadBack, 256);
+    w.big_cap = S * (T / 65 + 1);
+    size_t o = 0;
+    w.flags = o;  o += 256;
+    w.sym = o;    o = align_up(o + (size_t)S * w.Tp, 256);
+    w.keys = o;   o = align_up(o + (size_t)S * ((T + 7) & ~int64_t(7)) * 2, 256);
+    w.pos = o;    o = align_up(o + (size_t)S * T * 4, 256);
+    w.pos2 = o;   o = align_up(o + (size_t)S * T * 4, 256);
+    w.big = o;    o = align_up(o + 256 + (size_t)w.big_cap * 16, 256);
+    w.stack = o;  o = align_up(o + (size_t)S * (T / 16 + 4) * 16, 256);
+    w.total = o;
+    return w;
+}
+
+// Parameters of the bucketing/solve kernels (passed by value).
+struct MatchParams {
+    const uint8_t *sym;  // padded rows: stream s at sym + s*Tp + kPadFront
+    int64_t Tp;
+    int32_t T, K, d, NB, nbits, fl_total;
+    int32_t pw[kMaxD + 1];      // K^i
+    int32_t fl_off[kMaxD + 1];  // first-occurrence table offset of level l
+    uint16_t *keys;             // [S][T] d-gram key of position t (0xFFFF: none)
+    int32_t *pos;               // [S][T] bucket-ordered positions
+    int32_t *pos2;              // [S][T] second buffer for large groups
+    int32_t *big;               // [0]: count; entries from +64: {s, key, start, n}
+    int64_t big_cap;
+    int4 *stack;                // [S][T/16+4] group stacks of the large-group pass
+    int32_t *E;                 // [S][T]
+    int16_t *SYM;               // [S][T] or null
+    int32_t *L;                 // [S][T] or null
+};
+
+// Choice of the bucketing depth d for alphabet K and stream length T: the
+// largest d with K^d <= min(4096, T/8) (about 8+ positions per bucket on
+// i.i.d. streams, so buckets fit a 64-lane wave) and first-occurrence tables
+// for levels below d within kMaxFirstTab entries.
+inline int choose_d(int64_t K, int64_t T)
+{
+    int64_t cap = T / 8;
+    if (cap > kMaxBuckets) cap = kMaxBuckets;
+    if (cap < K) cap = K;
+    int d = 1;
+    int64_t pw = K, fl = 0;
+    while (d < kMaxD && d + 1 <= T) {
+        int64_t nb_next = pw * K;
+        int64_t fl_next = fl + pw;  // tables for levels 1..d
+        if (nb_next > cap || fl_next > kMaxFirstTab) break;
+        fl = fl_next;
+        pw = nb_next;
+        ++d;
+    }
+    return d;
+}
+
+}  // namespace rosa

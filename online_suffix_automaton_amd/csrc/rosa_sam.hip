@@ -1,0 +1,337 @@
+// rosa_sam.hip -- online suffix automaton per stream, for incremental
+// decoding: rosa_build over a prefix, then one rosa_step per new position.
+//
+// Method: "ROSA-Tuning: Enhancing Long-Context Modeling via Suffix Matching"
+// (arXiv 2602.02499), Sec. 2.2 (suffix automaton: at most 2n-1 states,
+// amortised O(1) transitions and suffix-link jumps, Blumer et al. 1985) and
+// Sec. 3.3 / App. B.3 (retrieval destination = end position of the longest
+// suffix seen before, plus one); Sec. 4.1: one automaton per (b, r) stream.
+//
+// Per step and stream: append the symbol (new state, missing transitions
+// set up the suffix-link path, attach to the target or split it with a clone
+// that inherits the target's transitions, link and last end position); the
+// new state's suffix link is the longest suffix that occurred before: its
+// length is L and its last end position (read before the update) is E; then
+// every state on the new state's suffix path gets last = t.
+//
+// Layout in the caller's state buffer (all per stream, stream-major):
+//   flags    [64]   int32 (flags[0]: symbol >= K seen)
+//   meta     [S]    int2 {tail state, number of states}
+//   nodes    [S][Ncap] int4 {len, link, last, 0}, Ncap = max(2, 2*Tcap-1)
+//   next     [S][Ncap][K] int32 dense transition rows (-1 = none)
+//   hist     [S][Hs] uint8 symbol history (SYM = hist[E+1])
+// One lane owns one stream, so every access to a stream's tables is ordered
+// by program order; lanes of a wave work on different streams.
+#include "rosa_internal.h"
+
+namespace rosa {
+
+struct SamLayout {
+    size_t flags, meta, nodes, next, hist, total;
+    int64_t Ncap, Hs;
+};
+
+SamLayout sam_layout(int64_t S, int64_t K, int64_t Tcap)
+{
+    SamLayout l;
+    l.Ncap = Tcap <= 1 ? 2 : 2 * Tcap - 1;
+    l.Hs = (int64_t)align_up((size_t)Tcap + 16, 16);
+    size_t o = 0;
+    l.flags = o;  o += 256;
+    l.meta = o;   o = align_up(o + (size_t)S * 8, 256);
+    l.nodes = o;  o = align_up(o + (size_t)S * l.Ncap * 16, 256);
+    l.next = o;   o = align_up(o + (size_t)S * l.Ncap * K * 4, 256);
+    l.hist = o;   o = align_up(o + (size_t)S * l.Hs, 256);
+    l.total = o;
+    return l;
+}
+
+struct SamView {
+    int32_t *flags;
+    int2 *meta;
+    int4 *nodes;
+    int32_t *next;
+    uint8_t *hist;
+    int64_t Ncap, Hs;
+    int32_t K;
+};
+
+struct SamStream {
+    int4 *nd;
+    int32_t *nx;
+    int K;
+    int tail, nst;
+};
+
+__device__ __forceinline__ int sam_new_state(SamStream &a, int len)
+{
+    const int v = a.nst++;
+    a.nd[v] = make_int4(len, -1, -1, 0);
+    int32_t *row = a.nx + (int64_t)v * a.K;
+    if ((a.K & 3) == 0) {
+        int4 *r4 = reinterpret_cast<int4 *>(row);
+        for (int c = 0; c < (a.K >> 2); ++c)
+            r4[c] = make_int4(-1, -1, -1, -1);
+    } else {
+        for (int c = 0; c < a.K; ++c)
+            row[c] = -1;
+    }
+    return v;
+}
+
+// Append symbol c; returns the new state.
+__device__ int sam_extend(SamStream &a, int c)
+{
+    const int K = a.K;
+    const int cur = sam_new_state(a, a.nd[a.tail].x + 1);
+    int p = a.tail;
+    while (p != -1 && a.nx[(int64_t)p * K + c] == -1) {
+        a.nx[(int64_t)p * K + c] = cur;
+        p = a.nd[p].y;
+    }
+    if (p == -1) {
+        a.nd[cur].y = 0;
+    } else {
+        const int q = a.nx[(int64_t)p * K + c];
+        const int4 nq = a.nd[q];
+        const int lp = a.nd[p].x;
+        if (lp + 1 == nq.x) {
+            a.nd[cur].y = q;
+        } else {
+            const int clone = a.nst++;
+            a.nd[clone] = make_int4(lp + 1, nq.y, nq.z, 0);
+            const int32_t *src = a.nx + (int64_t)q * K;
+            int32_t *dst = a.nx + (int64_t)clone * K;
+            if ((K & 3) == 0) {
+                const int4 *s4 = reinterpret_cast<const int4 *>(src);
+                int4 *d4 = reinterpret_cast<int4 *>(dst);
+                for (int k = 0; k < (K >> 2); ++k)
+                    d4[k] = s4[k];
+            } else {
+                for (int k = 0; k < K; ++k)
+                    dst[k] = src[k];
+            }
+            while (p != -1 && a.nx[(int64_t)p * K + c] == q) {
+                a.nx[(int64_t)p * K + c] = clone;
+                p = a.nd[p].y;
+            }
+            a.nd[q].y = clone;
+            a.nd[cur].y = clone;
+        }
+    }
+    a.tail = cur;
+    return cur;
+}
+
+// Match for position t after the extension, then the last-end update.
+__device__ __forceinline__ void sam_match(SamStream &a, int cur, int t,
+                                          int &E, int &L)
+{
+    const int v = a.nd[cur].y;
+    E = -1;
+    L = 0;
+    if (v > 0) {
+        const int4 nv = a.nd[v];
+        L = nv.x;
+        E = nv.z;
+    }
+    for (int u = cur; u != -1; u = a.nd[u].y)
+        a.nd[u].z = t;
+}
+
+__device__ __forceinline__ SamStream sam_open(const SamView &v, int64_t s)
+{
+    SamStream a;
+    a.nd = v.nodes + s * v.Ncap;
+    a.nx = v.next + s * v.Ncap * v.K;
+    a.K = v.K;
+    const int2 m = v.meta[s];
+    a.tail = m.x;
+    a.nst = m.y;
+    return a;
+}
+
+// Build over hist[s][0..T): one lane per stream, `spw` streams per wave.
+__global__ __launch_bounds__(64) void sam_build_kernel(
+    SamView v, int64_t S, int64_t T, int spw, int32_t *__restrict__ E,
+    int16_t *__restrict__ SYM, int32_t *__restrict__ L)
+{
+    const int lane = threadIdx.x;
+    if (lane >= spw)
+        return;
+    const int64_t s = (int64_t)blockIdx.x * spw + lane;
+    if (s >= S)
+        return;
+    SamStream a;
+    a.nd = v.nodes + s * v.Ncap;
+    a.nx = v.next + s * v.Ncap * v.K;
+    a.K = v.K;
+    a.tail = 0;
+    a.nst = 0;
+    sam_new_state(a, 0);   // root: len 0, no link
+    const uint8_t *h = v.hist + s * v.Hs;
+    for (int64_t t = 0; t < T; ++t) {
+        const int c = h[t];
+        const int cur = sam_extend(a, c);
+        int e, l;
+        sam_match(a, cur, (int)t, e, l);
+        if (E) {
+            E[s * T + t] = e;
+            if (L)
+                L[s * T + t] = l;
+            if (SYM)
+                SYM[s * T + t] = e >= 0 ? (int16_t)h[e + 1] : (int16_t)-1;
+        }
+    }
+    v.meta[s] = make_int2(a.tail, a.nst);
+}
+
+// Validate/clamp symbols of a SYMBOLS prefix into the history rows.
+__global__ void sam_hist_kernel(const uint8_t *__restrict__ in, int64_t ld,
+                                int64_t T, int32_t K, uint8_t *__restrict__ hist,
+                                int64_t Hs, uint8_t *__restrict__ copy_out,
+                                int32_t *__restrict__ flags)
+{
+    const int64_t s = blockIdx.y;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= T)
+        return;
+    uint8_t c = in[s * ld + t];
+    if (c >= K) {
+        atomicOr(&flags[0], 1);
+        c = (uint8_t)(K - 1);
+    }
+    hist[s * Hs + t] = c;
+    if (copy_out)
+        copy_out[s * T + t] = c;
+}
+
+__device__ __forceinline__ uint32_t bf16_pos_s(uint32_t h)
+{
+    return (h - 1u) < 0x7F80u ? 1u : 0u;
+}
+
+// One position for every stream.  kind 0: symbols row[s*ld]; kind 1: bf16
+// row [B][ld], stream s = b*R + r reads channels r*M .. r*M+M-1.
+__global__ __launch_bounds__(64) void sam_step_kernel(
+    SamView v, int64_t S, int64_t t, int spw, int kind, const void *row,
+    int64_t ld, int64_t R, int M, const uint16_t *__restrict__ V, int64_t ldv,
+    int64_t ldv_b, int32_t *__restrict__ end, int16_t *__restrict__ sym,
+    uint16_t *__restrict__ out_row, int64_t ldo_b)
+{
+    const int lane = threadIdx.x;
+    if (lane >= spw)
+        return;
+    const int64_t s = (int64_t)blockIdx.x * spw + lane;
+    if (s >= S)
+        return;
+    int c;
+    const int64_t b = s / R, r = s % R;
+    if (kind == 0) {
+        c = reinterpret_cast<const uint8_t *>(row)[s * ld];
+        if (c >= v.K) {
+            atomicOr(&v.flags[0], 1);
+            c = v.K - 1;
+        }
+    } else {
+        const uint16_t *hrow = reinterpret_cast<const uint16_t *>(row) + b * ld + r * M;
+        c = 0;
+        for (int j = 0; j < M; ++j)
+            c |= (int)bf16_pos_s(hrow[j]) << j;
+    }
+    uint8_t *h = v.hist + s * v.Hs;
+    h[t] = (uint8_t)c;
+    SamStream a = sam_open(v, s);
+    const int cur = sam_extend(a, c);
+    int e, l;
+    sam_match(a, cur, (int)t, e, l);
+    v.meta[s] = make_int2(a.tail, a.nst);
+    end[s] = e;
+    if (sym)
+        sym[s] = e >= 0 ? (int16_t)h[e + 1] : (int16_t)-1;
+    if (out_row) {
+        uint16_t *o = out_row + b * ldo_b + r * M;
+        const uint16_t *src = V + b * ldv_b + (int64_t)(e + 1) * ldv + r * M;
+        for (int m = 0; m < M; ++m)
+            o[m] = e >= 0 ? src[m] : (uint16_t)0;
+    }
+}
+
+// --------------------------------------------------------------- launchers
+
+SamView sam_view(void *buf, int64_t S, int64_t K, int64_t Tcap)
+{
+    const SamLayout l = sam_layout(S, K, Tcap);
+    char *base = reinterpret_cast<char *>(buf);
+    SamView v;
+    v.flags = reinterpret_cast<int32_t *>(base + l.flags);
+    v.meta = reinterpret_cast<int2 *>(base + l.meta);
+    v.nodes = reinterpret_cast<int4 *>(base + l.nodes);
+    v.next = reinterpret_cast<int32_t *>(base + l.next);
+    v.hist = base ? reinterpret_cast<uint8_t *>(base + l.hist) : nullptr;
+    v.Ncap = l.Ncap;
+    v.Hs = l.Hs;
+    v.K = (int32_t)K;
+    return v;
+}
+
+size_t sam_total_bytes(int64_t S, int64_t K, int64_t Tcap)
+{
+    return sam_layout(S, K, Tcap).total;
+}
+
+uint8_t *sam_hist_base(void *buf, int64_t S, int64_t K, int64_t Tcap,
+                       int64_t *Hs)
+{
+    const SamLayout l = sam_layout(S, K, Tcap);
+    *Hs = l.Hs;
+    return reinterpret_cast<uint8_t *>(buf) + l.hist;
+}
+
+int32_t *sam_flags(void *buf) { return reinterpret_cast<int32_t *>(buf); }
+
+constexpr int kSamStreamsPerWave = 8;
+
+hipError_t launch_sam_hist(const uint8_t *in, int64_t ld, int64_t S, int64_t T,
+                           int32_t K, void *buf, int64_t Tcap,
+                           uint8_t *copy_out, hipStream_t st)
+{
+    if (T == 0)
+        return hipSuccess;
+    SamView v = sam_view(buf, S, K, Tcap);
+    dim3 grid((unsigned)((T + 255) / 256), (unsigned)S);
+    hipLaunchKernelGGL(sam_hist_kernel, grid, dim3(256), 0, st, in, ld, T, K,
+                       v.hist, v.Hs, copy_out, v.flags);
+    return hipGetLastError();
+}
+
+hipError_t launch_clear_flags(int32_t *flags, hipStream_t st);
+
+hipError_t launch_sam_build(void *buf, int64_t S, int64_t K, int64_t Tcap,
+                            int64_t T, int32_t *E, int16_t *SYM, int32_t *L,
+                            hipStream_t st)
+{
+    SamView v = sam_view(buf, S, K, Tcap);
+    const int spw = kSamStreamsPerWave;
+    dim3 grid((unsigned)((S + spw - 1) / spw));
+    hipLaunchKernelGGL(sam_build_kernel, grid, dim3(64), 0, st, v, S, T, spw,
+                       E, SYM, L);
+    return hipGetLastError();
+}
+
+hipError_t launch_sam_step(void *buf, int64_t S, int64_t K, int64_t Tcap,
+                           int64_t t, int kind, const void *row, int64_t ld,
+                           int64_t R, int M, const uint16_t *V, int64_t ldv,
+                           int64_t ldv_b, int32_t *end, int16_t *sym,
+                           uint16_t *out_row, int64_t ldo_b, hipStream_t st)
+{
+    SamView v = sam_view(buf, S, K, Tcap);
+    const int spw = kSamStreamsPerWave;
+    dim3 grid((unsigned)((S + spw - 1) / spw));
+    hipLaunchKernelGGL(sam_step_kernel, grid, dim3(64), 0, st, v, S, t, spw,
+                       kind, row, ld, R, M, V, ldv, ldv_b, end, sym, out_row,
+                       ldo_b);
+    return hipGetLastError();
+}
+
+}  // namespace rosa

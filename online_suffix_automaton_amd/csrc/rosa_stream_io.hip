@@ -1,0 +1,259 @@
+// rosa_stream_io.hip -- streaming kernels of librosa: symbol preparation,
+// bf16 discretisation and value gather.  All HBM-bound; each is laid out so
+// that global reads and writes are coalesced and the [B][T][D] <-> [S][T]
+// transposes happen in LDS.
+//
+// Method: "ROSA-Tuning: Enhancing Long-Context Modeling via Suffix Matching"
+// (arXiv 2602.02499), Sec. 3.2 (Eq. 10-15: sign bits packed M per route) and
+// App. C.4 with Eq. (17) (read-out at tau = E+1, zero without a hit).
+#include "rosa_internal.h"
+
+namespace rosa {
+
+// I[h > 0] on a bf16 bit pattern, as an integer range test: the positive
+// non-NaN patterns are exactly 0x0001 (smallest subnormal) .. 0x7F80 (+inf).
+__device__ __forceinline__ uint32_t bf16_pos(uint32_t h)
+{
+    return (h - 1u) < 0x7F80u ? 1u : 0u;
+}
+
+// ------------------------------------------------------------ symbol prep
+
+// Copies caller symbols [S][ld] into padded workspace rows (zero padding on
+// both sides), clamps values >= K to K-1 and raises the sticky flag for them.
+__global__ void prep_symbols_kernel(const uint8_t *__restrict__ in, int64_t ld,
+                                    int64_t T, int32_t K,
+                                    uint8_t *__restrict__ rows, int64_t Tp,
+                                    uint8_t *__restrict__ copy_out,
+                                    int32_t *__restrict__ flags)
+{
+    const int64_t s = blockIdx.y;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // 0..Tp-1
+    if (i >= Tp)
+        return;
+    const int64_t t = i - kPadFront;
+    uint8_t v = 0;
+    if (t >= 0 && t < T) {
+        v = in[s * ld + t];
+        if (v >= K) {
+            atomicOr(&flags[kFlagSymbol], 1);
+            v = (uint8_t)(K - 1);
+        }
+        if (copy_out)
+            copy_out[s * T + t] = v;
+    }
+    rows[s * Tp + i] = v;
+}
+
+// Zero the padding of the padded rows (used after discretisation, which only
+// writes positions 0..T-1).
+__global__ void pad_rows_kernel(uint8_t *__restrict__ rows, int64_t Tp,
+                                int64_t T)
+{
+    const int64_t s = blockIdx.y;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t nfront = kPadFront, nback = Tp - kPadFront - T;
+    if (i < nfront)
+        rows[s * Tp + i] = 0;
+    else if (i - nfront < nback)
+        rows[s * Tp + kPadFront + T + (i - nfront)] = 0;
+}
+
+__global__ void clear_flags_kernel(int32_t *flags)
+{
+    if (threadIdx.x < 64)
+        flags[threadIdx.x] = 0;
+}
+
+// --------------------------------------------------------- discretisation
+
+// Tile: 64 positions x 64 routes of one batch row.  256 threads = 4 waves;
+// wave w discretises positions t0+16w .. t0+16w+15, lane = route, reading the
+// route's M channels (coalesced along the row), into an LDS tile [route][t];
+// then the tile is written out as 64-byte runs of each stream's row.
+template <int MC>
+__global__ __launch_bounds__(256) void discretize_kernel(
+    const uint16_t *__restrict__ H, int64_t T, int64_t D, int64_t ld, int M,
+    uint8_t *__restrict__ rows, int64_t row_stride, int64_t row_off,
+    uint8_t *__restrict__ copy_out)
+{
+    __shared__ uint8_t tile[64][64 + 4];
+    const int64_t R = D / M;
+    const int64_t b = blockIdx.z;
+    const int64_t t0 = (int64_t)blockIdx.x * 64;
+    const int64_t r0 = (int64_t)blockIdx.y * 64;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int64_t r = r0 + lane;
+    for (int k = 0; k < 16; ++k) {
+        const int tl = w * 16 + k;
+        const int64_t t = t0 + tl;
+        uint32_t a = 0;
+        if (t < T && r < R) {
+            const uint16_t *h = H + (b * T + t) * ld + r * M;
+            if (MC == 4) {
+                // four channels in one 8-byte load (alignment checked on host)
+                uint2 v = *reinterpret_cast<const uint2 *>(h);
+                a = bf16_pos(v.x & 0xFFFFu) | (bf16_pos(v.x >> 16) << 1) |
+                    (bf16_pos(v.y & 0xFFFFu) << 2) | (bf16_pos(v.y >> 16) << 3);
+            } else {
+                for (int j = 0; j < M; ++j)
+                    a |= bf16_pos(h[j]) << j;
+            }
+        }
+        tile[lane][tl] = (uint8_t)a;
+    }
+    __syncthreads();
+    // write: thread i -> route i/4, 16 positions starting at (i%4)*16
+    const int rr = threadIdx.x >> 2;
+    const int tc = (threadIdx.x & 3) * 16;
+    const int64_t rg = r0 + rr;
+    if (rg >= R)
+        return;
+    const int64_t s = b * R + rg;
+    uint8_t *dst = rows + s * row_stride + row_off + t0 + tc;
+    if (t0 + tc + 16 <= T && (((uintptr_t)dst) & 15) == 0) {
+        uint4 v;
+        uint32_t *vv = reinterpret_cast<uint32_t *>(&v);
+        for (int q = 0; q < 4; ++q)
+            vv[q] = (uint32_t)tile[rr][tc + 4 * q] |
+                    ((uint32_t)tile[rr][tc + 4 * q + 1] << 8) |
+                    ((uint32_t)tile[rr][tc + 4 * q + 2] << 16) |
+                    ((uint32_t)tile[rr][tc + 4 * q + 3] << 24);
+        *reinterpret_cast<uint4 *>(dst) = v;
+    } else {
+        for (int q = 0; q < 16; ++q)
+            if (t0 + tc + q < T)
+                dst[q] = tile[rr][tc + q];
+    }
+    if (copy_out) {
+        uint8_t *c = copy_out + s * T + t0 + tc;
+        for (int q = 0; q < 16; ++q)
+            if (t0 + tc + q < T)
+                c[q] = tile[rr][tc + q];
+    }
+}
+
+// ----------------------------------------------------------------- gather
+
+// Tile: 64 positions x 64 routes of one batch row, 256 threads.  E for the
+// tile is read as 64 contiguous 256-byte runs (one per stream) into LDS;
+// then wave w handles positions t0+16w..+15 with lane = route: one M-wide
+// value slice read from row tau = E+1 (random rows, inherent to the method)
+// and one coalesced write of the output row segment.
+template <int MC>
+__global__ __launch_bounds__(256) void gather_kernel(
+    const uint16_t *__restrict__ V, int64_t T, int64_t D, int64_t ldv, int M,
+    const int32_t *__restrict__ E, uint16_t *__restrict__ out, int64_t ldo)
+{
+    __shared__ int32_t et[64][64 + 1];
+    const int64_t R = D / M;
+    const int64_t b = blockIdx.z;
+    const int64_t t0 = (int64_t)blockIdx.x * 64;
+    const int64_t r0 = (int64_t)blockIdx.y * 64;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    // load E tile: 16 streams per wave-iteration, lane = position
+    for (int k = 0; k < 16; ++k) {
+        const int rl = w * 16 + k;
+        const int64_t rg = r0 + rl;
+        const int64_t t = t0 + lane;
+        int32_t e = -1;
+        if (rg < R && t < T) {
+            e = E[(b * R + rg) * T + t];
+            if (e < -1) e = -1;
+            if (e > T - 2) e = (int32_t)(T - 2);
+        }
+        et[rl][lane] = e;
+    }
+    __syncthreads();
+    const int64_t r = r0 + lane;
+    if (r >= R)
+        return;
+    for (int k = 0; k < 16; ++k) {
+        const int tl = w * 16 + k;
+        const int64_t t = t0 + tl;
+        if (t >= T)
+            break;
+        const int32_t e = et[lane][tl];
+        uint16_t *o = out + (b * T + t) * ldo + r * M;
+        if (MC == 4) {
+            uint2 v = make_uint2(0u, 0u);
+            if (e >= 0)
+                v = *reinterpret_cast<const uint2 *>(
+                    V + (b * T + (e + 1)) * ldv + r * M);
+            *reinterpret_cast<uint2 *>(o) = v;
+        } else {
+            const uint16_t *src = V + (b * T + (e + 1)) * ldv + r * M;
+            for (int m = 0; m < M; ++m)
+                o[m] = e >= 0 ? src[m] : (uint16_t)0;
+        }
+    }
+}
+
+// --------------------------------------------------------------- launchers
+
+hipError_t launch_prep_symbols(const uint8_t *in, int64_t ld, int64_t S,
+                               int64_t T, int32_t K, uint8_t *rows, int64_t Tp,
+                               uint8_t *copy_out, int32_t *flags,
+                               hipStream_t st)
+{
+    dim3 grid((unsigned)((Tp + 255) / 256), (unsigned)S);
+    hipLaunchKernelGGL(prep_symbols_kernel, grid, dim3(256), 0, st, in, ld, T,
+                       K, rows, Tp, copy_out, flags);
+    return hipGetLastError();
+}
+
+hipError_t launch_pad_rows(uint8_t *rows, int64_t S, int64_t Tp, int64_t T,
+                           hipStream_t st)
+{
+    int64_t n = Tp - T;
+    dim3 grid((unsigned)((n + 255) / 256), (unsigned)S);
+    hipLaunchKernelGGL(pad_rows_kernel, grid, dim3(256), 0, st, rows, Tp, T);
+    return hipGetLastError();
+}
+
+hipError_t launch_clear_flags(int32_t *flags, hipStream_t st)
+{
+    hipLaunchKernelGGL(clear_flags_kernel, dim3(1), dim3(64), 0, st, flags);
+    return hipGetLastError();
+}
+
+hipError_t launch_discretize(const uint16_t *H, int64_t B, int64_t T,
+                             int64_t D, int64_t ld, int M, uint8_t *rows,
+                             int64_t row_stride, int64_t row_off,
+                             uint8_t *copy_out, hipStream_t st)
+{
+    const int64_t R = D / M;
+    dim3 grid((unsigned)((T + 63) / 64), (unsigned)((R + 63) / 64),
+              (unsigned)B);
+    const bool vec4 = M == 4 && (ld % 4) == 0 &&
+                      (((uintptr_t)H) & 7) == 0;
+    if (vec4)
+        hipLaunchKernelGGL(discretize_kernel<4>, grid, dim3(256), 0, st, H, T,
+                           D, ld, M, rows, row_stride, row_off, copy_out);
+    else
+        hipLaunchKernelGGL(discretize_kernel<0>, grid, dim3(256), 0, st, H, T,
+                           D, ld, M, rows, row_stride, row_off, copy_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather(const uint16_t *V, int64_t B, int64_t T, int64_t D,
+                         int64_t ldv, int M, const int32_t *E, uint16_t *out,
+                         int64_t ldo, hipStream_t st)
+{
+    const int64_t R = D / M;
+    dim3 grid((unsigned)((T + 63) / 64), (unsigned)((R + 63) / 64),
+              (unsigned)B);
+    const bool vec4 = M == 4 && (ldv % 4) == 0 && (ldo % 4) == 0 &&
+                      (((uintptr_t)V) & 7) == 0 && (((uintptr_t)out) & 7) == 0;
+    if (vec4)
+        hipLaunchKernelGGL(gather_kernel<4>, grid, dim3(256), 0, st, V, T, D,
+                           ldv, M, E, out, ldo);
+    else
+        hipLaunchKernelGGL(gather_kernel<0>, grid, dim3(256), 0, st, V, T, D,
+                           ldv, M, E, out, ldo);
+    return hipGetLastError();
+}
+
+}  // namespace rosa

@@ -1,0 +1,130 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/rosa.h declares, sizes its buffers, and rejects bad arguments on the
+host before anything is launched (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from online_suffix_automaton_amd import rosa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "rosa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rosa_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_header_symbols():
+    lib = rosa.load_library()
+    names = _declared()
+    assert "rosa_match" in names and "rosa_step" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(rosa._SYMBOLS)
+
+
+def test_error_strings():
+    for st in range(6):
+        assert rosa.rosa_error_string(st)
+    assert "unknown" in rosa.rosa_error_string(99)
+
+
+def test_workspace_and_state_sizes():
+    assert rosa.rosa_match_workspace_bytes(0, 10, 2) == 0
+    assert rosa.rosa_match_workspace_bytes(1, 10, 0) == 0
+    assert rosa.rosa_match_workspace_bytes(1, 10, 257) == 0
+    assert rosa.rosa_match_workspace_bytes(1, 1 << 26, 2) == 0
+    a = rosa.rosa_match_workspace_bytes(512, 65536, 16)
+    b = rosa.rosa_match_workspace_bytes(512, 65537, 16)
+    assert 0 < a < b
+    assert rosa.rosa_state_bytes(4, 2, 0) == 0
+    s1 = rosa.rosa_state_bytes(512, 16, 66560)
+    # dense rows: (2*Tcap-1) states x (16 B node + 4K B row) per stream
+    assert s1 >= 512 * (2 * 66560 - 1) * (16 + 64)
+    assert rosa.rosa_state_bytes(1, 16, 1) > 0
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def _inp(**kw):
+    i = rosa.rosa_input()
+    i.kind, i.K, i.S, i.T, i.ld = 0, 16, 4, 100, 100
+    i.data = FAKE.value
+    for k, v in kw.items():
+        setattr(i, k, v)
+    return i
+
+
+@pytest.mark.parametrize("bad", [
+    dict(kind=7), dict(K=0), dict(K=300), dict(S=0), dict(T=-1),
+    dict(T=1 << 26, ld=1 << 26), dict(ld=50), dict(data=None),
+    dict(kind=1, M=0, B=1, D=8), dict(kind=1, M=9, B=1, D=9),
+    dict(kind=1, M=3, B=1, D=8, ld=8), dict(kind=1, M=4, B=1, D=8, ld=4),
+])
+def test_match_rejects_bad_input(bad):
+    lib = rosa.load_library()
+    inp = _inp(**bad)
+    out = rosa.rosa_out()
+    out.end = FAKE.value
+    st = lib.rosa_match(ctypes.byref(inp), ctypes.byref(out), 0x100000, 1 << 30,
+                        None)
+    assert st == rosa.ROSA_ERR_ARG
+
+
+def test_match_rejects_bad_buffers():
+    lib = rosa.load_library()
+    inp = _inp()
+    out = rosa.rosa_out()
+    out.end = FAKE.value
+    # null / misaligned workspace, missing end, too small workspace
+    assert lib.rosa_match(ctypes.byref(inp), ctypes.byref(out), None, 1 << 30,
+                          None) == rosa.ROSA_ERR_ARG
+    assert lib.rosa_match(ctypes.byref(inp), ctypes.byref(out), 0x100010,
+                          1 << 30, None) == rosa.ROSA_ERR_ARG
+    assert lib.rosa_match(ctypes.byref(inp), None, 0x100000, 1 << 30,
+                          None) == rosa.ROSA_ERR_ARG
+    out2 = rosa.rosa_out()
+    assert lib.rosa_match(ctypes.byref(inp), ctypes.byref(out2), 0x100000,
+                          1 << 30, None) == rosa.ROSA_ERR_ARG
+    assert lib.rosa_match(ctypes.byref(inp), ctypes.byref(out), 0x100000, 16,
+                          None) == rosa.ROSA_ERR_CAPACITY
+
+
+def test_gather_rejects_bad_arguments():
+    lib = rosa.load_library()
+    f = lib.rosa_gather
+    P = FAKE.value
+    assert f(P, 0, 10, 8, 8, 4, P, P, 8, None) == rosa.ROSA_ERR_ARG   # B
+    assert f(P, 1, 10, 8, 8, 3, P, P, 8, None) == rosa.ROSA_ERR_ARG   # D % M
+    assert f(P, 1, 10, 8, 4, 4, P, P, 8, None) == rosa.ROSA_ERR_ARG   # ldv
+    assert f(P, 1, 10, 8, 8, 4, P, P, 4, None) == rosa.ROSA_ERR_ARG   # ldo
+    assert f(None, 1, 10, 8, 8, 4, P, P, 8, None) == rosa.ROSA_ERR_ARG
+    assert f(P, 1, 10, 8, 8, 9, P, P, 8, None) == rosa.ROSA_ERR_ARG   # M
+
+
+def test_state_api_rejects_bad_handles_and_args():
+    lib = rosa.load_library()
+    assert lib.rosa_state_length(None) == -1
+    assert lib.rosa_state_status(None, None) == rosa.ROSA_ERR_STATE
+    lib.rosa_free(None)   # ignored
+    inp = _inp(T=1, ld=1)
+    end = FAKE.value
+    assert lib.rosa_step(None, ctypes.byref(inp), None, 0, 0, end, None, None,
+                         0, None) == rosa.ROSA_ERR_STATE
+    h = ctypes.c_void_p()
+    # capacity below T, misaligned or null buffer, too small buffer
+    inp2 = _inp()
+    assert lib.rosa_build(ctypes.byref(inp2), 50, 0x100000, 1 << 30,
+                          ctypes.byref(h), None, None) == rosa.ROSA_ERR_ARG
+    assert lib.rosa_build(ctypes.byref(inp2), 200, 0x100010, 1 << 30,
+                          ctypes.byref(h), None, None) == rosa.ROSA_ERR_ARG
+    assert lib.rosa_build(ctypes.byref(inp2), 200, None, 1 << 30,
+                          ctypes.byref(h), None, None) == rosa.ROSA_ERR_ARG
+    assert lib.rosa_build(ctypes.byref(inp2), 200, 0x100000, 64,
+                          ctypes.byref(h), None, None) == rosa.ROSA_ERR_CAPACITY
+    assert not h.value

@@ -1,0 +1,205 @@
+"""GPU parity: the HIP path through the C-ABI against the CPU oracle.
+
+Every integer output (E, SYM, L, packed symbols) must be bit-exact, and the
+gathered bf16 values byte-identical.  Cases span several tiles and ragged
+tails, every alphabet size class, structured streams that defeat the bucket
+fast path, and the full-size workloads.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from online_suffix_automaton_amd import rosa, synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _dev(a):
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _check(E, SYM, L, Eo, SYMo, Lo, what):
+    E, SYM, L = E.cpu().numpy(), SYM.cpu().numpy(), L.cpu().numpy()
+    for name, a, b in (("E", E, Eo), ("SYM", SYM, SYMo), ("L", L, Lo)):
+        if not np.array_equal(a, b):
+            bad = np.argwhere(a != b)
+            s, t = bad[0]
+            raise AssertionError(
+                f"{what}: {name} differs at {len(bad)} places, first (s={s}, "
+                f"t={t}): gpu {a[s, t]} oracle {b[s, t]}")
+
+
+def _run_symbols(sym, K, what):
+    x = _dev(sym)
+    E, SYM, L, syms = rosa.match(x, K=K, want_symbols=True)
+    torch.cuda.synchronize()
+    Eo, SYMo, Lo = oracle.match(sym, K)
+    _check(E, SYM, L, Eo, SYMo, Lo, what)
+    assert np.array_equal(syms.cpu().numpy(), sym)
+    return E
+
+
+def test_tiny_workload():
+    w = synth.tiny()
+    _run_symbols(w["sym"], w["K"], "tiny")
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 4, 16, 17, 256])
+def test_random_streams_all_alphabets(K):
+    rng = np.random.default_rng(100 + K)
+    for T in (1, 2, 3, 5, 17, 64, 65, 100, 257, 1000, 4099):
+        S = int(rng.integers(1, 9))
+        sym = rng.integers(0, K, size=(S, T), dtype=np.uint8)
+        _say(f"K={K} S={S} T={T}")
+        _run_symbols(sym, K, f"random K={K} T={T}")
+
+
+def test_structured_streams():
+    T = 3000
+    rows = [synth.constant(T), synth.periodic(T, [0, 1]),
+            synth.periodic(T, [0, 1, 2]), synth.periodic(T, [0, 0, 1]),
+            synth.fibonacci_word(T), np.resize(synth.de_bruijn(2, 10), T),
+            synth.planted_copies(T, 4, 11, gap_mean=40, len_lo=20, len_hi=200),
+            synth.planted_copies(T, 16, 12, gap_mean=100, len_lo=32, len_hi=512)]
+    sym = np.stack([r.astype(np.uint8) for r in rows])
+    for K in (3, 16):
+        _say(f"structured K={K}")
+        _run_symbols(sym, K, f"structured K={K}")
+
+
+def test_constant_and_periodic_long():
+    # one bucket holds (nearly) the whole stream: large-group path only
+    T = 8192
+    sym = np.stack([synth.constant(T, 1), synth.periodic(T, [2, 5]),
+                    synth.periodic(T, [0, 1, 2, 3, 4, 5, 6])])
+    _run_symbols(sym, 8, "constant/periodic 8192")
+
+
+def test_mixed_bucket_sizes():
+    # some streams random, some low-entropy, in one call
+    rng = np.random.default_rng(7)
+    T = 20000
+    rows = [rng.integers(0, 16, T), rng.integers(0, 2, T),
+            synth.periodic(T, list(range(16))), rng.integers(0, 3, T) * 5,
+            synth.planted_copies(T, 16, 3)]
+    sym = np.stack([np.asarray(r, dtype=np.uint8) for r in rows])
+    _run_symbols(sym, 16, "mixed")
+
+
+def test_strided_symbol_rows():
+    rng = np.random.default_rng(8)
+    base = rng.integers(0, 16, size=(6, 1500), dtype=np.uint8)
+    x = _dev(base)[:, :1333]          # rows with stride 1500 > T
+    E, SYM, L, _ = rosa.match(x, K=16)
+    Eo, SYMo, Lo = oracle.match(np.ascontiguousarray(base[:, :1333]), 16)
+    _check(E, SYM, L, Eo, SYMo, Lo, "strided rows")
+
+
+def test_symbol_out_of_range_flag():
+    sym = np.array([[0, 1, 2, 9, 1]], dtype=np.uint8)
+    x = _dev(sym)
+    ws = torch.empty(rosa.rosa_match_workspace_bytes(1, 5, 4), dtype=torch.uint8,
+                     device=DEV)
+    rosa.match(x, K=4, ws=ws)
+    assert rosa.rosa_match_status(ws) == rosa.ROSA_ERR_SYMBOL
+    x2 = _dev(np.array([[0, 1, 2, 3, 1]], dtype=np.uint8))
+    rosa.match(x2, K=4, ws=ws)
+    assert rosa.rosa_match_status(ws) == rosa.ROSA_OK
+
+
+def test_bf16_threshold_all_patterns():
+    # one position, 65536 channels, M = 1: symbol = I[h > 0]
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(1, 1, -1)
+    E, SYM, L, syms = rosa.match(_dev(bits), M=1, want_symbols=True)
+    want = oracle.discretize_bf16(bits, 1)
+    assert np.array_equal(syms.cpu().numpy(), want)
+    assert (E.cpu().numpy() == -1).all()
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8])
+def test_bf16_small_all_widths(M):
+    B, T, D = 3, 333, 24 if M != 8 else 32
+    H = synth.bf16_normal((B, T, D), 20 + M)
+    E, SYM, L, syms = rosa.match(_dev(H), M=M, want_symbols=True)
+    so = oracle.discretize_bf16(H, M)
+    assert np.array_equal(syms.cpu().numpy(), so)
+    Eo, SYMo, Lo = oracle.match(so, 1 << M)
+    _check(E, SYM, L, Eo, SYMo, Lo, f"bf16 M={M}")
+
+
+def test_batched_workload():
+    w = synth.batched()
+    H = w["H"]
+    E, SYM, L, syms = rosa.match(_dev(H), M=4, want_symbols=True)
+    torch.cuda.synchronize()
+    so = oracle.discretize_bf16(H, 4)
+    assert np.array_equal(syms.cpu().numpy(), so)
+    Eo, SYMo, Lo = oracle.match(so, 16)
+    _check(E, SYM, L, Eo, SYMo, Lo, "batched")
+
+
+def test_repeat_workload():
+    _say("generating repeat workload")
+    w = synth.repeat()
+    _say("gpu")
+    x = _dev(w["sym"])
+    E, SYM, L, _ = rosa.match(x, K=16)
+    torch.cuda.synchronize()
+    _say("oracle")
+    Eo, SYMo, Lo = oracle.match(w["sym"], 16)
+    _check(E, SYM, L, Eo, SYMo, Lo, "repeat")
+    assert Lo.max() >= 256
+
+
+def test_long_workload_with_gather():
+    _say("generating long workload")
+    w = synth.long()
+    H, V = w["H"], w["V"]
+    Hd, Vd = _dev(H), _dev(V)
+    _say("gpu")
+    E, SYM, L, syms = rosa.match(Hd, M=4, want_symbols=True)
+    out = torch.empty_like(Vd)
+    rosa.rosa_gather(Vd, 4, E, out)
+    torch.cuda.synchronize()
+    _say("oracle")
+    so = oracle.discretize_bf16(H, 4)
+    assert np.array_equal(syms.cpu().numpy(), so)
+    Eo, SYMo, Lo = oracle.match(so, 16)
+    _check(E, SYM, L, Eo, SYMo, Lo, "long")
+    oo = oracle.gather(V, Eo, 4)
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), oo)
+
+
+def test_gather_random_destinations():
+    rng = np.random.default_rng(9)
+    for (B, T, D, M) in ((2, 700, 48, 4), (1, 130, 30, 3), (3, 64, 16, 8)):
+        V = rng.integers(0, 65536, size=(B, T, D), dtype=np.uint16)
+        S = B * D // M
+        E = np.empty((S, T), dtype=np.int32)
+        for t in range(T):
+            E[:, t] = rng.integers(-1, t, size=S) if t > 0 else -1
+        out = torch.empty((B, T, D), dtype=torch.int16, device=DEV)
+        rosa.rosa_gather(_dev(V), M, _dev(E), out)
+        assert np.array_equal(out.cpu().numpy().view(np.uint16),
+                              oracle.gather(V, E, M))
+
+
+def test_launch_geometry_independence():
+    # the same streams inside different batches give the same rows
+    rng = np.random.default_rng(10)
+    sym = rng.integers(0, 16, size=(9, 5000), dtype=np.uint8)
+    E_all = rosa.match(_dev(sym), K=16)[0].cpu().numpy()
+    perm = rng.permutation(9)
+    E_perm = rosa.match(_dev(sym[perm]), K=16)[0].cpu().numpy()
+    assert np.array_equal(E_perm, E_all[perm])
+    E_one = rosa.match(_dev(sym[3:4]), K=16)[0].cpu().numpy()
+    assert np.array_equal(E_one[0], E_all[3])
