@@ -71,7 +71,7 @@ def test_structured_streams():
             synth.planted_copies(T, 4, 11, gap_mean=40, len_lo=20, len_hi=200),
             synth.planted_copies(T, 16, 12, gap_mean=100, len_lo=32, len_hi=512)]
     sym = np.stack([r.astype(np.uint8) for r in rows])
-    for K in (3, 16):
+    for K in (16, 256):
         _say(f"structured K={K}")
         _run_symbols(sym, K, f"structured K={K}")
 
