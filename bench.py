@@ -1,0 +1,277 @@
+"""Benchmark of the ROSA retrieval hot path on one MI355X.
+
+One step = the whole path over one batch: bf16 hidden states -> sign bits ->
+4-bit route symbols (512 streams) -> longest-recurring-suffix match for all
+65,536 positions of every stream (E and next symbol) -> gather of the matched
+value slices from V.  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line: throughput in matched positions/s, the roofline of the
+dominant kernel (the retrieval kernel, timed with HIP events on its own
+stream), and the CPU oracle timed on the host as a reported baseline.  Every
+output of the timed run is compared with the oracle before the line is
+printed.
+
+    python bench.py [--steps K] [--warmup W] [--workload long|batched|repeat]
+                    [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "matched positions/sec (streams×T) at T=64K, 512 streams"
+HBM_PEAK = 8.0e12     # MI355X HBM3E, bytes/s
+# Algorithmic bytes per stream-position of the retrieval kernel: the symbol
+# read (1 B) plus E (int32) and SYM (int16) written.
+KERNEL_BYTES_PER_POS = 1 + 4 + 2
+PMC_FILE = os.path.join(ROOT, "profiles", "stream_kernel_long_pmc.txt")
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("rosa_match.hip", "rosa_internal.h"):
+        with open(os.path.join(ROOT, "online_suffix_automaton_amd", "csrc",
+                               name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the retrieval kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current source."""
+    try:
+        txt = open(PMC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"^source_sha\s*=\s*(\w+)", txt, re.M)
+    b = re.search(r"^traffic_bytes_per_launch\s*=\s*([0-9.eE+]+)", txt, re.M)
+    if not m or not b or m.group(1) != kernel_source_hash():
+        return None
+    return float(b.group(1))
+
+
+# ------------------------------------------------------------- workloads
+
+def make_workload(name):
+    from online_suffix_automaton_amd import synth
+    if name == "long":
+        w = synth.long()
+        return dict(kind="bf16", H=w["H"], V=w["V"], M=4, S=512, T=65536,
+                    desc="long: hidden [1,65536,2048] bf16 N(0,1), M=4 -> 512 "
+                         "streams x 65536 positions, K=16; match + gather of "
+                         "V [65536,2048] bf16 slices")
+    if name == "batched":
+        w = synth.batched()
+        return dict(kind="bf16", H=w["H"], V=None, M=4, S=512, T=4096,
+                    desc="batched: hidden [8,4096,256] bf16 N(0,1), M=4 -> 512 "
+                         "streams x 4096, K=16; match")
+    if name == "repeat":
+        w = synth.repeat()
+        return dict(kind="symbols", sym=w["sym"], K=16, S=1024, T=32768,
+                    desc="repeat: 1024 streams x 32768, K=16, planted copies "
+                         "(U{32..512}) over ~30% of positions; match")
+    raise ValueError(name)
+
+
+# ------------------------------------------------------------ CPU oracle
+
+def oracle_run(w, threads):
+    """The oracle over the whole workload, streams split across threads
+    (each thread runs the unchanged single-threaded oracle).  Returns
+    (wall seconds, E, SYM, gathered or None)."""
+    import oracle
+    S, T = w["S"], w["T"]
+    chunks = np.array_split(np.arange(S), threads)
+    jobs = []
+    for c in chunks:
+        if len(c) == 0:
+            continue
+        s0, s1 = int(c[0]), int(c[-1]) + 1
+        if w["kind"] == "bf16":
+            H = w["H"]
+            B, _, D = H.shape
+            R = D // w["M"]
+            # streams of one batch row, as contiguous channel slices
+            b0, b1 = s0 // R, (s1 - 1) // R
+            assert b0 == b1, "thread chunk crosses a batch row"
+            M = w["M"]
+            h = np.ascontiguousarray(H[b0:b0 + 1, :, (s0 % R) * M:((s1 - 1) % R + 1) * M])
+            v = None
+            if w["V"] is not None:
+                v = np.ascontiguousarray(w["V"][b0:b0 + 1, :, (s0 % R) * M:((s1 - 1) % R + 1) * M])
+            jobs.append((s0, s1, h, v))
+        else:
+            jobs.append((s0, s1, np.ascontiguousarray(w["sym"][s0:s1]), None))
+
+    def work(job):
+        s0, s1, a, v = job
+        if w["kind"] == "bf16":
+            sym = oracle.discretize_bf16(a, w["M"])
+            E, SYM, _ = oracle.match(sym, 1 << w["M"])
+            g = oracle.gather(v, E, w["M"]) if v is not None else None
+        else:
+            E, SYM, _ = oracle.match(a, w["K"])
+            g = None
+        return s0, s1, E, SYM, g
+
+    oracle._load()
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        res = list(ex.map(work, jobs))
+    wall = time.perf_counter() - t0
+    E = np.empty((S, T), np.int32)
+    SYM = np.empty((S, T), np.int16)
+    G = None
+    if w["kind"] == "bf16" and w["V"] is not None:
+        G = np.empty_like(w["V"])
+    for (s0, s1, e, sy, g) in res:
+        E[s0:s1], SYM[s0:s1] = e, sy
+        if g is not None:
+            R = w["H"].shape[2] // w["M"]
+            b = s0 // R
+            M = w["M"]
+            G[b, :, (s0 % R) * M:((s1 - 1) % R + 1) * M] = g[0]
+    return wall, E, SYM, G
+
+
+# -------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long",
+                    choices=["long", "batched", "repeat"])
+    ap.add_argument("--no-cpu", action="store_true",
+                    help="skip the oracle baseline and parity check")
+    ap.add_argument("--cpu-threads", type=int, default=16)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the retrieval path has no "
+              "cross-GPU step and this build runs on a single MI355X; "
+              "use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from online_suffix_automaton_amd import rosa
+
+    dev = torch.device("cuda:0")
+    _log(f"workload {args.workload}: generating")
+    w = make_workload(args.workload)
+    S, T = w["S"], w["T"]
+
+    if w["kind"] == "bf16":
+        Hd = torch.from_numpy(w["H"].view(np.int16)).to(dev)
+        Vd = (torch.from_numpy(w["V"].view(np.int16)).to(dev)
+              if w["V"] is not None else None)
+        inp = rosa.bf16_input(Hd, w["M"])
+        K = 1 << w["M"]
+    else:
+        Xd = torch.from_numpy(w["sym"]).to(dev)
+        inp = rosa.symbols_input(Xd, w["K"])
+        Vd = None
+        K = w["K"]
+    E = torch.empty((S, T), dtype=torch.int32, device=dev)
+    SYM = torch.empty((S, T), dtype=torch.int16, device=dev)
+    out = torch.empty_like(Vd) if Vd is not None else None
+    ws = torch.empty(rosa.rosa_match_workspace_bytes(S, T, K), dtype=torch.uint8,
+                     device=dev)
+    outs = rosa.make_out(E, SYM)
+    stream = torch.cuda.current_stream()
+
+    n_ev = args.steps
+    kb = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ke = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+
+    def step(i=None):
+        if i is None:
+            rosa.rosa_match(inp, outs, ws, stream)
+        else:
+            rosa.rosa_match_timed(inp, outs, ws, kb[i], ke[i], stream)
+        if Vd is not None:
+            rosa.rosa_gather(Vd, w["M"], E, out, stream)
+
+    _log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    _log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    k_ms = [kb[i].elapsed_time(ke[i]) for i in range(n_ev)]
+    k_avg = float(np.mean(k_ms))
+    if rosa.rosa_match_status(ws) != rosa.ROSA_OK:
+        raise SystemExit("symbol range flag raised")
+    value = S * T / (ms_step / 1e3)
+    _log(f"ms/step {ms_step:.4f}  retrieval kernel {k_avg:.4f} ms")
+
+    kbytes = KERNEL_BYTES_PER_POS * S * T
+    achieved = kbytes / (k_avg / 1e3)
+    roof = {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK,
+            "traffic": measured_traffic() if args.workload == "long" else None}
+
+    cpu = None
+    if not args.no_cpu:
+        threads = max(1, min(args.cpu_threads, os.cpu_count() or 1))
+        _log(f"oracle on {threads} threads (parity check + baseline)")
+        walls = []
+        for _ in range(3):
+            wall, Eo, SYMo, Go = oracle_run(w, threads)
+            walls.append(wall)
+        wall = float(np.median(walls))
+        if not np.array_equal(E.cpu().numpy(), Eo):
+            raise SystemExit("parity failure: E differs from the oracle")
+        if not np.array_equal(SYM.cpu().numpy(), SYMo):
+            raise SystemExit("parity failure: SYM differs from the oracle")
+        if Go is not None and not np.array_equal(
+                out.cpu().numpy().view(np.uint16), Go):
+            raise SystemExit("parity failure: gathered values differ")
+        _log(f"parity ok; oracle {wall:.3f} s")
+        cpu = {"value": S * T / wall, "unit": "positions/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"whole workload ({S} streams x {T}), "
+                         + ("discretize + match + gather" if w["kind"] == "bf16"
+                            and w["V"] is not None else "match")
+                         + f", streams split over {threads} threads, median of 3"}
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "positions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u8", "data": "synthetic",
+        "config": {"workload": w["desc"], "streams": S, "T": T, "K": K,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "kernel_ms": k_avg,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

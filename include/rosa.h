@@ -102,6 +102,14 @@ size_t rosa_match_workspace_bytes(int64_t S, int64_t T, int32_t K);
 rosa_status rosa_match(const rosa_input *in, const rosa_out *out, void *ws,
                        size_t ws_bytes, hipStream_t stream);
 
+/* Same as rosa_match, and also records `ev_begin` on `stream` just before
+ * the retrieval kernel (per-stream bucketing and group refinement) and
+ * `ev_end` just after it, so a caller can time that kernel alone with
+ * hipEventElapsedTime.  Both events must be valid (ROSA_ERR_ARG otherwise). */
+rosa_status rosa_match_timed(const rosa_input *in, const rosa_out *out,
+                             void *ws, size_t ws_bytes, hipStream_t stream,
+                             hipEvent_t ev_begin, hipEvent_t ev_end);
+
 /* Synchronises `stream`, then returns ROSA_ERR_SYMBOL if the last rosa_match
  * that used `ws` saw a symbol >= K, else ROSA_OK (or ROSA_ERR_HIP). */
 rosa_status rosa_match_status(const void *ws, hipStream_t stream);

@@ -186,8 +186,9 @@ size_t rosa_match_workspace_bytes(int64_t S, int64_t T, int32_t K)
     return ws_layout(S, T).total;
 }
 
-rosa_status rosa_match(const rosa_input *in, const rosa_out *out, void *ws,
-                       size_t ws_bytes, hipStream_t stream)
+static rosa_status match_impl(const rosa_input *in, const rosa_out *out,
+                              void *ws, size_t ws_bytes, hipStream_t stream,
+                              hipEvent_t ev_begin, hipEvent_t ev_end)
 {
     Shape sh;
     rosa_status st = resolve(in, &sh, true);
@@ -217,12 +218,31 @@ rosa_status rosa_match(const rosa_input *in, const rosa_out *out, void *ws,
     }
     MatchParams p = match_params(sh, base, w, out);
     ROSA_TRY(launch_clear_flags(p.big, stream));
+    if (ev_begin)
+        ROSA_TRY(hipEventRecord(ev_begin, stream));
     ROSA_TRY(launch_stream(p, sh.S, stream));
+    if (ev_end)
+        ROSA_TRY(hipEventRecord(ev_end, stream));
     int grid = (int)(w.big_cap < 1024 ? w.big_cap : 1024);
     if (grid < 1)
         grid = 1;
     ROSA_TRY(launch_big(p, grid, stream));
     return ROSA_OK;
+}
+
+rosa_status rosa_match(const rosa_input *in, const rosa_out *out, void *ws,
+                       size_t ws_bytes, hipStream_t stream)
+{
+    return match_impl(in, out, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+rosa_status rosa_match_timed(const rosa_input *in, const rosa_out *out,
+                             void *ws, size_t ws_bytes, hipStream_t stream,
+                             hipEvent_t ev_begin, hipEvent_t ev_end)
+{
+    if (!ev_begin || !ev_end)
+        return ROSA_ERR_ARG;
+    return match_impl(in, out, ws, ws_bytes, stream, ev_begin, ev_end);
 }
 
 rosa_status rosa_match_status(const void *ws, hipStream_t stream)

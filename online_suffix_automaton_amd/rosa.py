@@ -41,7 +41,8 @@ class rosa_out(ctypes.Structure):
 
 
 _lib = None
-_SYMBOLS = ["rosa_match_workspace_bytes", "rosa_match", "rosa_match_status",
+_SYMBOLS = ["rosa_match_workspace_bytes", "rosa_match", "rosa_match_timed",
+            "rosa_match_status",
             "rosa_gather", "rosa_state_bytes", "rosa_build", "rosa_step",
             "rosa_state_length", "rosa_state_status", "rosa_free",
             "rosa_error_string"]
@@ -61,6 +62,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     sig = {
         "rosa_match_workspace_bytes": ([I64, I64, I32], SZ),
         "rosa_match": ([P, P, P, SZ, P], ctypes.c_int),
+        "rosa_match_timed": ([P, P, P, SZ, P, P, P], ctypes.c_int),
         "rosa_match_status": ([P, P], ctypes.c_int),
         "rosa_gather": ([P, I64, I64, I64, I64, I32, P, P, I64, P], ctypes.c_int),
         "rosa_state_bytes": ([I64, I32, I64], SZ),
@@ -157,6 +159,19 @@ def rosa_match(inp: rosa_input, out: rosa_out, ws: torch.Tensor,
     _check(load_library().rosa_match(ctypes.byref(inp), ctypes.byref(out),
                                      ws.data_ptr(), ws.numel() * ws.element_size(),
                                      _stream(stream)), "rosa_match")
+
+
+def rosa_match_timed(inp: rosa_input, out: rosa_out, ws: torch.Tensor,
+                     ev_begin: torch.cuda.Event, ev_end: torch.cuda.Event,
+                     stream=None) -> None:
+    """rosa_match that also records two torch (HIP) events around the
+    retrieval kernel on the same stream."""
+    _require_device(ws)
+    _check(load_library().rosa_match_timed(
+        ctypes.byref(inp), ctypes.byref(out), ws.data_ptr(),
+        ws.numel() * ws.element_size(), _stream(stream),
+        ctypes.c_void_p(ev_begin.cuda_event), ctypes.c_void_p(ev_end.cuda_event)),
+        "rosa_match_timed")
 
 
 def rosa_match_status(ws: torch.Tensor, stream=None) -> int:
