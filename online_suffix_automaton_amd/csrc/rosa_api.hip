@@ -149,7 +149,6 @@ MatchParams match_params(const Shape &sh, char *ws, const WsLayout &w,
             fl += p.pw[l];
     }
     p.fl_total = fl;
-    p.keys = reinterpret_cast<uint16_t *>(ws + w.keys);
     p.pos = reinterpret_cast<int32_t *>(ws + w.pos);
     p.pos2 = reinterpret_cast<int32_t *>(ws + w.pos2);
     p.big = reinterpret_cast<int32_t *>(ws + w.big);

@@ -24,7 +24,7 @@ constexpr int kBigThreads = 64;      // one wave per large group
 constexpr int kFlagSymbol = 0;       // int32: nonzero if a symbol >= K was seen
 
 struct WsLayout {
-    size_t flags, sym, keys, pos, pos2, big, stack, total;
+    size_t flags, sym, pos, pos2, big, stack, total;
     int64_t Tp;          // bytes per padded symbol row
     int64_t big_cap;     // entries in the large-group list
 };
@@ -39,7 +39,6 @@ inline WsLayout ws_layout(int64_t S, int64_t T)
     size_t o = 0;
     w.flags = o;  o += 256;
     w.sym = o;    o = align_up(o + (size_t)S * w.Tp, 256);
-    w.keys = o;   o = align_up(o + (size_t)S * ((T + 7) & ~int64_t(7)) * 2, 256);
     w.pos = o;    o = align_up(o + (size_t)S * T * 4, 256);
     w.pos2 = o;   o = align_up(o + (size_t)S * T * 4, 256);
     w.big = o;    o = align_up(o + 256 + (size_t)w.big_cap * 16, 256);
@@ -55,7 +54,6 @@ struct MatchParams {
     int32_t T, K, d, NB, nbits, fl_total;
     int32_t pw[kMaxD + 1];      // K^i
     int32_t fl_off[kMaxD + 1];  // first-occurrence table offset of level l
-    uint16_t *keys;             // [S][T] d-gram key of position t (0xFFFF: none)
     int32_t *pos;               // [S][T] bucket-ordered positions
     int32_t *pos2;              // [S][T] second buffer for large groups
     int32_t *big;               // [0]: count; entries from +64: {s, key, start, n}

@@ -21,16 +21,19 @@
 //
 // Kernels.
 //   stream_kernel (one 1024-thread workgroup per stream):
+//     0  the stream's symbols are staged in LDS (T <= 65536);
 //     A  histogram of d-gram keys in LDS, first occurrence of every l-gram
-//        (l <= d) by LDS atomicMin, keys written for later passes;
+//        (l <= d) by LDS atomicMin;
 //     B  scan -> bucket offsets; buckets packed into <=64-element tasks;
 //        buckets larger than 64 go to a global list;
 //     C  positions scattered into buckets (LDS atomics);
 //     D  positions whose d-gram is new (L < d) and the first d-1 positions
-//        are answered from the first-occurrence tables plus a backward scan
-//        of the keys for the most recent equal l-gram;
-//     E  each wave takes tasks: sorts each bucket by time (bitonic over the
-//        64 lanes), then refines groups with lane masks (solve_wave).
+//        are answered from the first-occurrence tables plus a time-ordered
+//        scan per segment (ballot match inside 64-position chunks, LDS
+//        last-end tables across chunks and segments);
+//     E  each wave takes tasks: sorts the task's positions by time
+//        (bitonic over the 64 lanes), then refines groups with lane masks
+//        (solve_wave).
 //   big_kernel (one wave per bucket of more than 64 positions): rebuilds the
 //     bucket in time order, then refines it with stable partitions by the
 //     next symbol until groups fit a wave, then solve_wave.
@@ -64,14 +67,15 @@ __device__ __forceinline__ int wave_incl_scan(int v)
 }
 
 // Symbols x[p .. p+15] as two little-endian 64-bit halves: byte i of
-// (lo, hi) is x[p+i].  The row has zero padding, so p may be slightly
-// negative or run past the end.
+// (lo, hi) is x[p+i].  `row` is 4-byte aligned and zero padded, so p may be
+// slightly negative or run past the end.  Five aligned dword reads and a
+// byte funnel shift (pointer arithmetic keeps the row's address space, so
+// an LDS row is read with ds_read).
 __device__ __forceinline__ void load_window(const uint8_t *row, int p,
                                             uint64_t &lo, uint64_t &hi)
 {
-    const uintptr_t u = reinterpret_cast<uintptr_t>(row + p);
-    const uint32_t *q = reinterpret_cast<const uint32_t *>(u & ~uintptr_t(3));
-    const uint32_t sh = (uint32_t)(u & 3);
+    const uint32_t *q = reinterpret_cast<const uint32_t *>(row) + (p >> 2);
+    const uint32_t sh = (uint32_t)(p & 3);
     const uint32_t d0 = q[0], d1 = q[1], d2 = q[2], d3 = q[3], d4 = q[4];
     const uint32_t w0 = __builtin_amdgcn_alignbyte(d1, d0, sh);
     const uint32_t w1 = __builtin_amdgcn_alignbyte(d2, d1, sh);
@@ -233,87 +237,44 @@ __device__ int block_excl_scan(int v, int *ws, int *total)
     return r;
 }
 
-// ----------------------------------------------------------- short solve
+// ---------------------------------------------------------- stream kernel
 //
-// Answers a position t whose d-gram never occurred before t (so L < d), or
-// one of the first d-1 positions (L <= t).  L is the longest l with an
-// l-gram occurrence before t, read from the first-occurrence tables; E is
-// the most recent earlier end of that l-gram, found by scanning the keys
-// backwards (a position e >= d-1 ends the l-gram iff the top l digits of its
-// d-gram key match).
-__device__ void short_solve(const StreamOut &o, const MatchParams &p,
-                            const uint16_t *keys, const int32_t *firstl, int t)
+// LDS: the stream's padded symbol row (when T <= 65536; otherwise symbols
+// are read from the workspace row in HBM), plus an arena reused across
+// phases (byte offsets):
+//   [0, 32832)       A-C: cnt[4096] + off[4112]     D: segment tables
+//   [32832, 49216)   A-D: firstd[4096]
+//   [49216, 57408)   A-D: firstl[2048]
+//   [57408, 73856)   D:   pending queries[4112]
+//   [73856, 90240)   B-E: tasks[4096]
+//   [90240, 90368)   misc
+constexpr int kArenaBytes = 90368;
+constexpr int kSegTabInts = 8192;
+constexpr int kSymLds = 65792;     // padded row bytes for T <= 65536
+
+// Key of the reversed d-gram ending at t (t >= d-1): x[t] is the most
+// significant digit.  Its top l digits form the key of the l-gram.
+__device__ __forceinline__ int dgram_key(const uint8_t *x, int t, int d, int K)
 {
-    const int d = p.d, K = p.K;
-    const uint8_t *x = o.x;
-    const int lmax = min(d - 1, t);
-    int Lq = 0, kl = 0;
-    for (int l = lmax; l >= 1; --l) {
-        int k = 0;
-        for (int i = 0; i < l; ++i)
-            k = k * K + x[t - i];
-        if (firstl[p.fl_off[l] + k] < t) {
-            Lq = l;
-            kl = k;
-            break;
-        }
-    }
-    int Eq = -1;
-    if (Lq > 0) {
-        const uint32_t span = (uint32_t)p.pw[d - Lq];
-        const uint32_t lo = (uint32_t)kl * span, hi = lo + span;
-        int e = t - 1;
-        while (e >= d - 1) {
-            if ((e & 7) == 7 && e - 7 >= d - 1) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(keys + e - 7);
-                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-                int hit = -1;
-                for (int q = 7; q >= 0; --q) {
-                    const uint32_t k = (w[q >> 1] >> (16 * (q & 1))) & 0xFFFFu;
-                    if (k >= lo && k < hi) {
-                        hit = q;
-                        break;
-                    }
-                }
-                if (hit >= 0) {
-                    Eq = e - 7 + hit;
-                    break;
-                }
-                e -= 8;
-                continue;
-            }
-            const uint32_t k = keys[e];
-            if (k >= lo && k < hi) {
-                Eq = e;
-                break;
-            }
-            --e;
-        }
-        if (Eq < 0) {
-            for (e = min(t - 1, d - 2); e >= Lq - 1; --e) {
-                int k = 0;
-                for (int i = 0; i < Lq; ++i)
-                    k = k * K + x[e - i];
-                if (k == kl) {
-                    Eq = e;
-                    break;
-                }
-            }
-        }
-    }
-    emit(o, t, Eq, Lq);
+    int k = 0;
+    for (int i = 0; i < d; ++i)
+        k = k * K + x[t - i];
+    return k;
 }
 
-// ---------------------------------------------------------- stream kernel
-
+template <bool kLds>
 __global__ __launch_bounds__(kStreamThreads) void stream_kernel(MatchParams p)
 {
-    __shared__ int32_t cnt[kMaxBuckets];
-    __shared__ int32_t off[kMaxBuckets + 16];
-    __shared__ int32_t firstd[kMaxBuckets];
-    __shared__ int32_t firstl[kMaxFirstTab];
-    __shared__ uint32_t tasks[kMaxBuckets];
-    __shared__ int32_t misc[32];
+    __shared__ __align__(16) unsigned char arena[kArenaBytes];
+    __shared__ __align__(16) unsigned char symrow[kLds ? kSymLds : 16];
+    int32_t *cnt = reinterpret_cast<int32_t *>(arena);
+    int32_t *off = reinterpret_cast<int32_t *>(arena + 16384);
+    int32_t *segtab = reinterpret_cast<int32_t *>(arena);
+    int32_t *firstd = reinterpret_cast<int32_t *>(arena + 32832);
+    int32_t *firstl = reinterpret_cast<int32_t *>(arena + 49216);
+    int32_t *pend = reinterpret_cast<int32_t *>(arena + 57408);
+    uint32_t *tasks = reinterpret_cast<uint32_t *>(arena + 73856);
+    int32_t *misc = reinterpret_cast<int32_t *>(arena + 90240);
 
     const int s = blockIdx.x;
     const int tid = threadIdx.x;
@@ -321,23 +282,32 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(MatchParams p)
     const int lane = tid & 63;
     const int wid = tid >> 6;
     const int nw = nt >> 6;
-    const int T = p.T, K = p.K, d = p.d, NB = p.NB;
-    const uint8_t *x = p.sym + (int64_t)s * p.Tp + kPadFront;
-    const int64_t Tk = (T + 7) & ~7;
-    uint16_t *keys = p.keys + (int64_t)s * Tk;
+    const uint64_t self = 1ull << lane;
+    const uint64_t below = self - 1;
+    const uint64_t above = ~(below | self);
+    const int T = p.T, K = p.K, d = p.d, NB = p.NB, FL = p.fl_total;
+    const uint8_t *xg = p.sym + (int64_t)s * p.Tp + kPadFront;
     int32_t *pos = p.pos + (int64_t)s * T;
+
+    if (kLds) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(p.sym + (int64_t)s * p.Tp);
+        uint4 *dst = reinterpret_cast<uint4 *>(symrow);
+        for (int i = tid; i < (int)(p.Tp >> 4); i += nt)
+            dst[i] = src[i];
+    }
+    const uint8_t *x = kLds ? symrow + kPadFront : xg;
     StreamOut o;
     o.x = x;
     o.E = p.E + (int64_t)s * T;
     o.SYM = p.SYM ? p.SYM + (int64_t)s * T : nullptr;
     o.L = p.L ? p.L + (int64_t)s * T : nullptr;
 
-    // ---- A: histogram, first occurrences, keys
+    // ---- A: histogram, first occurrences
     for (int i = tid; i < NB; i += nt) {
         cnt[i] = 0;
         firstd[i] = 0x7FFFFFFF;
     }
-    for (int i = tid; i < p.fl_total; i += nt)
+    for (int i = tid; i < FL; i += nt)
         firstl[i] = 0x7FFFFFFF;
     if (tid < 32)
         misc[tid] = 0;
@@ -347,15 +317,16 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(MatchParams p)
         const int dm = min(d, t + 1);
         for (int i = 0; i < dm; ++i) {
             k = k * K + x[t - i];
-            if (i + 1 < d)
-                atomicMin(&firstl[p.fl_off[i + 1] + k], t);
+            if (i + 1 < d) {
+                int32_t *f = &firstl[p.fl_off[i + 1] + k];
+                if (t < *f)
+                    atomicMin(f, t);
+            }
         }
         if (t >= d - 1) {
             atomicAdd(&cnt[k], 1);
-            atomicMin(&firstd[k], t);
-            keys[t] = (uint16_t)k;
-        } else {
-            keys[t] = 0xFFFFu;
+            if (t < firstd[k])
+                atomicMin(&firstd[k], t);
         }
     }
     __syncthreads();
@@ -449,7 +420,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(MatchParams p)
     for (int t = tid; t < T; t += nt) {
         if (t < d - 1)
             continue;
-        const int k = keys[t];
+        const int k = dgram_key(x, t, d, K);
         const int c = off[k + 1] - off[k];
         if (c >= 2 && c <= 64) {
             const int slot = atomicAdd(&cnt[k], 1);
@@ -458,21 +429,89 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(MatchParams p)
     }
     __syncthreads();
 
-    // ---- D: positions with L < d (first occurrence of their d-gram, or
-    //         one of the first d-1 positions)
-    for (int t = tid; t < T; t += nt) {
-        const bool q = (t < d - 1) || (firstd[keys[t]] == t);
-        if (q) {
-            const int qi = atomicAdd(&misc[25], 1);
-            off[qi] = t;
+    // ---- D: positions with L < d: the first d-1 positions and the first
+    // occurrence of every d-gram.  L is the longest l < d whose l-gram
+    // occurred before t (first-occurrence tables); E is the latest earlier
+    // end of that l-gram.  Wave w scans time segment w in chunks of 64 in
+    // order, keeping the last end of every l-gram seen so far in segment w
+    // (segtab[w]); inside a chunk, the latest earlier lane with the same
+    // l-gram comes from a ballot match.  Queries with no earlier end inside
+    // their segment are resolved after the scan from the tables of earlier
+    // segments.
+    const int nseg = FL > 0 ? min(nw, kSegTabInts / FL) : nw;
+    const int Ts = (((T + nseg - 1) / nseg) + 63) & ~63;
+    for (int i = tid; i < nseg * FL; i += nt)
+        segtab[i] = -1;
+    __syncthreads();
+    if (wid < nseg) {
+        int32_t *tab = segtab + wid * FL;
+        const int lo = wid * Ts, hi = min(T, lo + Ts);
+        for (int c0 = lo; c0 < hi; c0 += 64) {
+            const int t = c0 + lane;
+            const bool inr = t < hi;
+            const bool q = inr && (t < d - 1 || firstd[dgram_key(x, t, d, K)] == t);
+            int Lq = 0, Eq = -1;
+            bool miss = false;
+            int gk = 0;
+            uint64_t eq = ~0ull;
+            for (int l = 1; l < d; ++l) {
+                const bool v = inr && t >= l - 1;
+                const int dig = v ? x[t - l + 1] : 0;
+                gk = gk * K + dig;
+                uint64_t m = ballot(v);
+                for (int b = 0; b < p.nbits; ++b) {
+                    const bool bit = (dig >> b) & 1;
+                    const uint64_t B = ballot(v && bit);
+                    m &= bit ? B : ~B;
+                }
+                eq &= m;
+                const int slot = p.fl_off[l] + gk;
+                if (q && v && firstl[slot] < t) {
+                    Lq = l;
+                    const uint64_t pm = eq & below;
+                    if (pm) {
+                        Eq = c0 + 63 - __clzll((long long)pm);
+                        miss = false;
+                    } else {
+                        Eq = tab[slot];
+                        miss = Eq < 0;
+                    }
+                }
+                if (v && !(eq & above))
+                    tab[slot] = t;
+            }
+            if (q) {
+                if (miss)
+                    pend[atomicAdd(&misc[25], 1)] = t;
+                else
+                    emit(o, t, Lq > 0 ? Eq : -1, Lq);
+            }
         }
     }
     __syncthreads();
-    const int nq = misc[25];
-    for (int qi = tid; qi < nq; qi += nt)
-        short_solve(o, p, keys, firstl, off[qi]);
+    {
+        const int npend = misc[25];
+        for (int i = tid; i < npend; i += nt) {
+            const int t = pend[i];
+            int Lq = 0, gq = 0, gk = 0;
+            for (int l = 1; l < d && l <= t + 1; ++l) {
+                gk = gk * K + x[t - l + 1];
+                if (firstl[p.fl_off[l] + gk] < t) {
+                    Lq = l;
+                    gq = gk;
+                }
+            }
+            int e = -1;
+            for (int w = t / Ts - 1; w >= 0 && e < 0; --w)
+                e = segtab[w * FL + p.fl_off[Lq] + gq];
+            emit(o, t, e, Lq);
+        }
+    }
 
-    // ---- E: tasks of buckets with 2..64 members, one wave per task
+    // ---- E: tasks of buckets with 2..64 members, one wave per task.  The
+    // task's members are sorted by time across the whole wave (bitonic on
+    // t<<6 | bucket); a group is the set of lanes with the same bucket
+    // index, so lane order is time order inside every group.
     const int ntasks = misc[24];
     for (int ti = wid; ti < ntasks; ti += nw) {
         const uint32_t tk = tasks[ti];
@@ -480,28 +519,28 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(MatchParams p)
         const int n = (int)(tk & 63u) + 1;
         const bool has = lane < n;
         const uint32_t v = has ? (uint32_t)pos[start + lane] : 0u;
-        const int t = (int)(v & ~kFirstFlag);
         const uint64_t F = ballot(has && (v & kFirstFlag));
-        const uint64_t self = 1ull << lane;
         const uint64_t upto = (self << 1) - 1;   // lanes 0..lane (lane 63: all)
-        const int seg0 = 63 - __clzll((long long)(F & upto));
-        const uint64_t after = F & ~upto;
-        const int seg1 = after ? __ffsll((long long)after) - 1 : n;
-        uint64_t g = (seg1 >= 64 ? ~0ull : ((1ull << seg1) - 1)) &
-                     ~((1ull << seg0) - 1);
-        if (!has)
-            g = self;
-        // time order inside each bucket: bitonic sort of (segment, t)
-        uint64_t key = has ? (((uint64_t)seg0 << 32) | (uint32_t)t) : ~0ull;
+        const uint32_t seg = (uint32_t)__popcll(F & upto) - 1u;
+        uint32_t key = has ? (((v & ~kFirstFlag) << 6) | seg) : 0xFFFFFFFFu;
         for (int kk = 2; kk <= 64; kk <<= 1)
             for (int j = kk >> 1; j > 0; j >>= 1) {
-                const uint64_t other = shfl64(key, lane ^ j);
+                const uint32_t other = (uint32_t)__shfl_xor((int)key, j);
                 const bool up = (lane & kk) == 0;
                 const bool lower = (lane & j) == 0;
                 key = (lower == up) ? min(key, other) : max(key, other);
             }
-        const int ts = (int)(uint32_t)key;
-        solve_wave(o, p.nbits, ts, g, d, has);
+        const int nbk = 64 - __clzll((long long)__popcll(F));   // bits for bucket ids
+        const uint32_t sg = key & 63u;
+        uint64_t g = ballot(has);
+        for (int b = 0; b < nbk; ++b) {
+            const bool bit = (sg >> b) & 1u;
+            const uint64_t B = ballot(has && bit);
+            g &= bit ? B : ~B;
+        }
+        if (!has)
+            g = self;
+        solve_wave(o, p.nbits, (int)(key >> 6), g, d, has);
     }
 }
 
@@ -532,14 +571,12 @@ __global__ __launch_bounds__(kBigThreads) void big_kernel(MatchParams p)
     const uint64_t self = 1ull << lane;
     const uint64_t below = self - 1;
     const int T = p.T, d = p.d;
-    const int64_t Tk = (T + 7) & ~7;
     const int count = min((int64_t)p.big[0], p.big_cap);
 
     for (int item = blockIdx.x; item < count; item += gridDim.x) {
         const int32_t *ent = p.big + 64 + 4 * (int64_t)item;
         const int s = ent[0], key = ent[1], start = ent[2], n0 = ent[3];
         const uint8_t *x = p.sym + (int64_t)s * p.Tp + kPadFront;
-        const uint16_t *keys = p.keys + (int64_t)s * Tk;
         int32_t *buf[2] = {p.pos + (int64_t)s * T, p.pos2 + (int64_t)s * T};
         StreamOut o;
         o.x = x;
@@ -554,7 +591,7 @@ __global__ __launch_bounds__(kBigThreads) void big_kernel(MatchParams p)
             int w = 0;
             for (int t0 = d - 1; t0 < T; t0 += 64) {
                 const int t = t0 + lane;
-                const bool m = t < T && keys[t] == key;
+                const bool m = t < T && dgram_key(x, t, d, K) == key;
                 const uint64_t bm = ballot(m);
                 if (m)
                     buf[0][start + w + __popcll(bm & below)] = t;
@@ -701,8 +738,12 @@ __global__ __launch_bounds__(kBigThreads) void big_kernel(MatchParams p)
 
 hipError_t launch_stream(const MatchParams &p, int64_t S, hipStream_t st)
 {
-    hipLaunchKernelGGL(stream_kernel, dim3((unsigned)S), dim3(kStreamThreads),
-                       0, st, p);
+    if (p.Tp <= kSymLds)
+        hipLaunchKernelGGL(stream_kernel<true>, dim3((unsigned)S),
+                           dim3(kStreamThreads), 0, st, p);
+    else
+        hipLaunchKernelGGL(stream_kernel<false>, dim3((unsigned)S),
+                           dim3(kStreamThreads), 0, st, p);
     return hipGetLastError();
 }
 

@@ -170,20 +170,32 @@ __global__ __launch_bounds__(256) void gather_kernel(
     const int64_t r = r0 + lane;
     if (r >= R)
         return;
-    for (int k = 0; k < 16; ++k) {
-        const int tl = w * 16 + k;
-        const int64_t t = t0 + tl;
-        if (t >= T)
-            break;
-        const int32_t e = et[lane][tl];
-        uint16_t *o = out + (b * T + t) * ldo + r * M;
-        if (MC == 4) {
-            uint2 v = make_uint2(0u, 0u);
-            if (e >= 0)
-                v = *reinterpret_cast<const uint2 *>(
+    if (MC == 4) {
+        // all 16 value loads in flight before the stores
+        uint2 v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int tl = w * 16 + k;
+            const int32_t e = et[lane][tl];
+            v[k] = make_uint2(0u, 0u);
+            if (t0 + tl < T && e >= 0)
+                v[k] = *reinterpret_cast<const uint2 *>(
                     V + (b * T + (e + 1)) * ldv + r * M);
-            *reinterpret_cast<uint2 *>(o) = v;
-        } else {
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int64_t t = t0 + w * 16 + k;
+            if (t < T)
+                *reinterpret_cast<uint2 *>(out + (b * T + t) * ldo + r * M) = v[k];
+        }
+    } else {
+        for (int k = 0; k < 16; ++k) {
+            const int tl = w * 16 + k;
+            const int64_t t = t0 + tl;
+            if (t >= T)
+                break;
+            const int32_t e = et[lane][tl];
+            uint16_t *o = out + (b * T + t) * ldo + r * M;
             const uint16_t *src = V + (b * T + (e + 1)) * ldv + r * M;
             for (int m = 0; m < M; ++m)
                 o[m] = e >= 0 ? src[m] : (uint16_t)0;

@@ -167,6 +167,9 @@ def rosa_match_timed(inp: rosa_input, out: rosa_out, ws: torch.Tensor,
     """rosa_match that also records two torch (HIP) events around the
     retrieval kernel on the same stream."""
     _require_device(ws)
+    for ev in (ev_begin, ev_end):
+        if not ev.cuda_event:      # torch creates the HIP event on first record
+            ev.record(stream if stream is not None else torch.cuda.current_stream())
     _check(load_library().rosa_match_timed(
         ctypes.byref(inp), ctypes.byref(out), ws.data_ptr(),
         ws.numel() * ws.element_size(), _stream(stream),
