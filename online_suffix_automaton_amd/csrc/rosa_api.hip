@@ -26,6 +26,7 @@ hipError_t launch_gather(const uint16_t *V, int64_t B, int64_t T, int64_t D,
 // rosa_match.hip
 hipError_t launch_stream(const MatchParams &p, int64_t S, hipStream_t st);
 hipError_t launch_big(const MatchParams &p, int grid, hipStream_t st);
+hipError_t launch_unpermute(const MatchParams &p, int64_t S, hipStream_t st);
 // rosa_sam.hip
 size_t sam_total_bytes(int64_t S, int64_t K, int64_t Tcap);
 uint8_t *sam_hist_base(void *buf, int64_t S, int64_t K, int64_t Tcap,
@@ -154,6 +155,7 @@ MatchParams match_params(const Shape &sh, char *ws, const WsLayout &w,
     p.big = reinterpret_cast<int32_t *>(ws + w.big);
     p.big_cap = w.big_cap;
     p.stack = reinterpret_cast<int4 *>(ws + w.stack);
+    p.rec = sh.T <= 65536 ? reinterpret_cast<uint32_t *>(ws + w.rec) : nullptr;
     p.E = out->end;
     p.SYM = out->sym;
     p.L = out->len;
@@ -226,6 +228,7 @@ static rosa_status match_impl(const rosa_input *in, const rosa_out *out,
     if (grid < 1)
         grid = 1;
     ROSA_TRY(launch_big(p, grid, stream));
+    ROSA_TRY(launch_unpermute(p, sh.S, stream));
     return ROSA_OK;
 }
 

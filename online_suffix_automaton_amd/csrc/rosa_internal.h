@@ -24,7 +24,7 @@ constexpr int kBigThreads = 64;      // one wave per large group
 constexpr int kFlagSymbol = 0;       // int32: nonzero if a symbol >= K was seen
 
 struct WsLayout {
-    size_t flags, sym, pos, pos2, big, stack, total;
+    size_t flags, sym, pos, pos2, rec, big, stack, total;
     int64_t Tp;          // bytes per padded symbol row
     int64_t big_cap;     // entries in the large-group list
 };
@@ -41,6 +41,7 @@ inline WsLayout ws_layout(int64_t S, int64_t T)
     w.sym = o;    o = align_up(o + (size_t)S * w.Tp, 256);
     w.pos = o;    o = align_up(o + (size_t)S * T * 4, 256);
     w.pos2 = o;   o = align_up(o + (size_t)S * T * 4, 256);
+    w.rec = o;    o = align_up(o + (size_t)S * T * 4, 256);
     w.big = o;    o = align_up(o + 256 + (size_t)w.big_cap * 16, 256);
     w.stack = o;  o = align_up(o + (size_t)S * (T / 16 + 4) * 16, 256);
     w.total = o;
@@ -59,6 +60,7 @@ struct MatchParams {
     int32_t *big;               // [0]: count; entries from +64: {s, key, start, n}
     int64_t big_cap;
     int4 *stack;                // [S][T/16+4] group stacks of the large-group pass
+    uint32_t *rec;              // [S][T] result records (streams of <= 65536)
     int32_t *E;                 // [S][T]
     int16_t *SYM;               // [S][T] or null
     int32_t *L;                 // [S][T] or null

@@ -42,7 +42,8 @@
 namespace rosa {
 
 constexpr uint32_t kFirstFlag = 0x80000000u;
-constexpr int kWordThresh = 4;
+constexpr int kWordThresh = 4;       // level steps only for groups larger than this
+constexpr int kWordThreshDeep = 32;  // ... and past the first levels, larger than this
 
 // ----------------------------------------------------------- wave helpers
 
@@ -92,11 +93,17 @@ __device__ __forceinline__ uint64_t shfl64(uint64_t v, int src)
     return (uint64_t)a | ((uint64_t)b << 32);
 }
 
+// Where results go.  Direct mode writes E / SYM / L of the stream at t.
+// Record mode (streams of <= 65536 positions) writes one 32-bit record
+// (t << 16 | E+1) per bucket slot, coalesced; a later kernel scatters the
+// records into time order in LDS and writes E and SYM.  L, if requested,
+// is always written directly.
 struct StreamOut {
-    const uint8_t *x;  // padded symbol row of the stream
+    const uint8_t *x;  // padded symbol row of the stream (LDS or HBM)
     int32_t *E;
     int16_t *SYM;
     int32_t *L;
+    uint32_t *rec;     // record row (record mode) or null
 };
 
 __device__ __forceinline__ void emit(const StreamOut &o, int t, int e, int l)
@@ -108,105 +115,122 @@ __device__ __forceinline__ void emit(const StreamOut &o, int t, int e, int l)
         o.SYM[t] = e >= 0 ? (int16_t)o.x[e + 1] : (int16_t)-1;
 }
 
+__device__ __forceinline__ void emit_record(const StreamOut &o, int slot,
+                                            int t, int e, int l)
+{
+    o.rec[slot] = ((uint32_t)t << 16) | (uint32_t)(e + 1);
+    if (o.L)
+        o.L[t] = l;
+}
+
+struct Found {
+    int e, l;
+    bool ok;
+};
+
 // ------------------------------------------------------------ solve_wave
 //
 // Each lane holds one element t (or none).  g is the lane mask of its group:
-// all members share the reversed `ell`-gram ending at their position, lanes
-// of a group are contiguous and in increasing time order, and every member
-// except the first already has L >= ell.  Refines until every group is a
-// singleton, emitting (L, E) for each element when it leaves its last
-// group with an earlier member.
+// all members share the reversed `ell`-gram ending at their position, lane
+// order is time order inside every group, and every member except the first
+// already has L >= ell.  Returns (E, L) for every member that has an earlier
+// member (ok); the first member of each group gets nothing.
 //
-// Two step kinds, chosen per iteration for the whole wave:
-//  level step (large groups): split by the symbol x[t-ell]; an element that
-//    is first in its new group but was not first before gets L = ell and
-//    E = its previous group member.
-//  word step (groups of <= kWordThresh): compare the next 16 symbols with
-//    every group member at once; the common run c with the latest earlier
-//    member that maximises it gives L = ell + c (c < 16); members equal on
-//    all 16 symbols stay grouped at level ell + 16.
-__device__ void solve_wave(const StreamOut &o, int nbits, int t, uint64_t g,
-                           int ell, bool has)
+//  level steps (while groups are large and still splitting: the first
+//    levels after bucketing, or very large groups): split by the symbol
+//    x[t-ell]; an element that is first in its new group but was not first
+//    before gets L = ell and E = its previous group member.
+//  direct resolution (then): each element compares its history with each
+//    earlier member's, 16 symbols per step, up to the first mismatch or the
+//    start of that member's history; the longest common extension c (the
+//    latest member among equals) gives L = ell + c and E = that member.
+__device__ Found solve_wave(const uint8_t *x, int nbits, int t, uint64_t g,
+                            int ell, bool has)
 {
     const int lane = __lane_id();
     const uint64_t self = 1ull << lane;
     const uint64_t below = self - 1;
+    Found r = {-1, 0, false};
     if (!has)
         g = self;
     uint64_t lo = 0, hi = 0;
     int wl = -(1 << 30);
+    const int ell0 = ell;
     for (;;) {
         const bool live = has && __popcll(g) >= 2;
         if (ballot(live) == 0)
-            break;
+            return r;
         const int gmax = wave_max(live ? __popcll(g) : 0);
-        if (gmax > kWordThresh) {
-            // ---------------------------------------------- level step
-            if (ell - wl >= 16) {
-                if (live && t - ell >= 0)
-                    load_window(o.x, t - ell - 15, lo, hi);
-                wl = ell;
-            }
-            const int bi = 15 - (ell - wl);
-            const uint32_t dig =
-                (uint32_t)((bi >= 8 ? (hi >> (8 * (bi - 8))) : (lo >> (8 * bi))) &
-                           0xFFu);
-            const bool valid = live && (t - ell >= 0);
-            uint64_t eq = ballot(valid);
-            for (int b = 0; b < nbits; ++b) {
-                const bool bit = (dig >> b) & 1u;
-                const uint64_t B = ballot(valid && bit);
-                eq &= bit ? B : ~B;
-            }
-            const uint64_t ng = valid ? (g & eq) : self;
-            const uint64_t prev = g & below;
-            const int p = prev ? 63 - __clzll((long long)prev) : lane;
-            const int e_prev = __shfl(t, p);
-            if (live && prev && !(ng & below))
-                emit(o, t, e_prev, ell);
-            if (live)
-                g = ng;
-            ++ell;
-        } else {
-            // ----------------------------------------------- word step
-            const bool valid = live && (t - ell >= 0);
-            if (valid)
-                load_window(o.x, t - ell - 15, lo, hi);
+        if (!(gmax > kWordThresh && (ell <= ell0 + 1 || gmax > kWordThreshDeep)))
+            break;
+        // ---------------------------------------------------- level step
+        if (ell - wl >= 16) {
+            if (live && t - ell >= 0)
+                load_window(x, t - ell - 15, lo, hi);
             wl = ell;
-            const int avail = valid ? (t - ell + 1) : 0;
-            int best_c = -1, best_e = -1;
-            uint64_t gnew = self;
-            uint64_t rem = valid ? g : 0;
-            while (ballot(rem != 0)) {
-                const bool have = rem != 0;
-                const int j = have ? __ffsll((long long)rem) - 1 : lane;
-                rem &= rem - 1;
-                const uint64_t lo_j = shfl64(lo, j);
-                const uint64_t hi_j = shfl64(hi, j);
-                const int t_j = __shfl(t, j);
-                const int a_j = __shfl(avail, j);
-                if (have && j != lane) {
-                    const uint64_t xh = hi ^ hi_j, xl = lo ^ lo_j;
-                    const int c = xh ? (__clzll((long long)xh) >> 3)
-                                     : (xl ? 8 + (__clzll((long long)xl) >> 3) : 16);
-                    if (j < lane) {
-                        const int cc = min(c, a_j);
-                        if (cc >= best_c) {
-                            best_c = cc;
-                            best_e = t_j;
-                        }
-                    }
-                    if (c == 16 && avail >= 16 && a_j >= 16)
-                        gnew |= 1ull << j;
+        }
+        const int bi = 15 - (ell - wl);
+        const uint32_t dig =
+            (uint32_t)((bi >= 8 ? (hi >> (8 * (bi - 8))) : (lo >> (8 * bi))) & 0xFFu);
+        const bool valid = live && (t - ell >= 0);
+        uint64_t eq = ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (dig >> b) & 1u;
+            const uint64_t B = ballot(valid && bit);
+            eq &= bit ? B : ~B;
+        }
+        const uint64_t ng = valid ? (g & eq) : self;
+        const uint64_t prev = g & below;
+        const int p = prev ? 63 - __clzll((long long)prev) : lane;
+        const int e_prev = __shfl(t, p);
+        if (live && prev && !(ng & below)) {
+            r.e = e_prev;
+            r.l = ell;
+            r.ok = true;
+        }
+        if (live)
+            g = ng;
+        ++ell;
+    }
+    // ------------------------------------------------- direct resolution
+    uint64_t rem = (has && __popcll(g) >= 2) ? (g & below) : 0;
+    int best_c = -1, best_e = -1;
+    while (ballot(rem != 0)) {
+        const bool have = rem != 0;
+        const int j = have ? __ffsll((long long)rem) - 1 : lane;
+        rem &= rem - 1;
+        const int tj = __shfl(t, j);
+        if (have) {
+            const int aj = tj - ell + 1;   // history of member j from x[tj-ell]
+            int c = 0;
+            while (c < aj) {
+                uint64_t alo, ahi, blo, bhi;
+                load_window(x, t - ell - c - 15, alo, ahi);
+                load_window(x, tj - ell - c - 15, blo, bhi);
+                const uint64_t xh = ahi ^ bhi, xl = alo ^ blo;
+                if (xh) {
+                    c += __clzll((long long)xh) >> 3;
+                    break;
                 }
+                if (xl) {
+                    c += 8 + (__clzll((long long)xl) >> 3);
+                    break;
+                }
+                c += 16;
             }
-            if (valid && best_c >= 0 && best_c < 16)
-                emit(o, t, best_e, ell + best_c);
-            if (live)
-                g = avail >= 16 ? gnew : self;
-            ell += 16;
+            c = min(c, aj);
+            if (c >= best_c) {
+                best_c = c;
+                best_e = tj;
+            }
         }
     }
+    if (best_c >= 0) {
+        r.e = best_e;
+        r.l = ell + best_c;
+        r.ok = true;
+    }
+    return r;
 }
 
 // ------------------------------------------------------------ block scan
@@ -237,20 +261,9 @@ __device__ int block_excl_scan(int v, int *ws, int *total)
     return r;
 }
 
-// ---------------------------------------------------------- stream kernel
-//
-// LDS: the stream's padded symbol row (when T <= 65536; otherwise symbols
-// are read from the workspace row in HBM), plus an arena reused across
-// phases (byte offsets):
-//   [0, 32832)       A-C: cnt[4096] + off[4112]     D: segment tables
-//   [32832, 49216)   A-D: firstd[4096]
-//   [49216, 57408)   A-D: firstl[2048]
-//   [57408, 73856)   D:   pending queries[4112]
-//   [73856, 90240)   B-E: tasks[4096]
-//   [90240, 90368)   misc
-constexpr int kArenaBytes = 90368;
+// ---------------------------------------------------------- shared phases
+
 constexpr int kSegTabInts = 8192;
-constexpr int kSymLds = 65792;     // padded row bytes for T <= 65536
 
 // Key of the reversed d-gram ending at t (t >= d-1): x[t] is the most
 // significant digit.  Its top l digits form the key of the l-gram.
@@ -262,55 +275,18 @@ __device__ __forceinline__ int dgram_key(const uint8_t *x, int t, int d, int K)
     return k;
 }
 
-template <bool kLds>
-__global__ __launch_bounds__(kStreamThreads) void stream_kernel(MatchParams p)
+// Phase A: d-gram histogram and first occurrence of every l-gram, l <= d.
+__device__ void phase_hist(const MatchParams &p, const uint8_t *x, int32_t *cnt,
+                           int32_t *firstd, int32_t *firstl)
 {
-    __shared__ __align__(16) unsigned char arena[kArenaBytes];
-    __shared__ __align__(16) unsigned char symrow[kLds ? kSymLds : 16];
-    int32_t *cnt = reinterpret_cast<int32_t *>(arena);
-    int32_t *off = reinterpret_cast<int32_t *>(arena + 16384);
-    int32_t *segtab = reinterpret_cast<int32_t *>(arena);
-    int32_t *firstd = reinterpret_cast<int32_t *>(arena + 32832);
-    int32_t *firstl = reinterpret_cast<int32_t *>(arena + 49216);
-    int32_t *pend = reinterpret_cast<int32_t *>(arena + 57408);
-    uint32_t *tasks = reinterpret_cast<uint32_t *>(arena + 73856);
-    int32_t *misc = reinterpret_cast<int32_t *>(arena + 90240);
-
-    const int s = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int nt = blockDim.x;
-    const int lane = tid & 63;
-    const int wid = tid >> 6;
-    const int nw = nt >> 6;
-    const uint64_t self = 1ull << lane;
-    const uint64_t below = self - 1;
-    const uint64_t above = ~(below | self);
-    const int T = p.T, K = p.K, d = p.d, NB = p.NB, FL = p.fl_total;
-    const uint8_t *xg = p.sym + (int64_t)s * p.Tp + kPadFront;
-    int32_t *pos = p.pos + (int64_t)s * T;
-
-    if (kLds) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(p.sym + (int64_t)s * p.Tp);
-        uint4 *dst = reinterpret_cast<uint4 *>(symrow);
-        for (int i = tid; i < (int)(p.Tp >> 4); i += nt)
-            dst[i] = src[i];
-    }
-    const uint8_t *x = kLds ? symrow + kPadFront : xg;
-    StreamOut o;
-    o.x = x;
-    o.E = p.E + (int64_t)s * T;
-    o.SYM = p.SYM ? p.SYM + (int64_t)s * T : nullptr;
-    o.L = p.L ? p.L + (int64_t)s * T : nullptr;
-
-    // ---- A: histogram, first occurrences
-    for (int i = tid; i < NB; i += nt) {
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int T = p.T, K = p.K, d = p.d;
+    for (int i = tid; i < p.NB; i += nt) {
         cnt[i] = 0;
         firstd[i] = 0x7FFFFFFF;
     }
-    for (int i = tid; i < FL; i += nt)
+    for (int i = tid; i < p.fl_total; i += nt)
         firstl[i] = 0x7FFFFFFF;
-    if (tid < 32)
-        misc[tid] = 0;
     __syncthreads();
     for (int t = tid; t < T; t += nt) {
         int k = 0;
@@ -330,8 +306,20 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(MatchParams p)
         }
     }
     __syncthreads();
+}
 
-    // ---- B: bucket offsets, task packing, large buckets
+// Phase B: bucket offsets, then wave 0 packs buckets of 2..64 members into
+// tasks of at most 64 positions (a task never spans a singleton or large
+// bucket, nor a boundary between position ranges of `pcap` slots) and
+// lists buckets of more than 64 members for the large-group kernel.
+// Returns the number of tasks (in misc[24]).
+__device__ void phase_tasks(const MatchParams &p, int s, const int32_t *cnt,
+                            int32_t *off, uint32_t *tasks, int32_t *misc,
+                            int pcap)
+{
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int lane = tid & 63, wid = tid >> 6;
+    const int NB = p.NB;
     {
         const int per = (NB + nt - 1) / nt;
         const int b0 = tid * per;
@@ -353,7 +341,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(MatchParams p)
     if (wid == 0) {
         const int b0 = (int)((int64_t)lane * NB / 64);
         const int b1 = (int)((int64_t)(lane + 1) * NB / 64);
-        int ntask = 0, cur = 0;
+        int ntask = 0, cur = 0, crange = -1;
         for (int b = b0; b < b1; ++b) {
             const int c = cnt[b];
             if (c == 0)
@@ -365,10 +353,12 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(MatchParams p)
                 }
                 continue;
             }
-            if (cur + c > 64) {
+            const int rg = off[b] / pcap;
+            if (cur + c > 64 || (cur && rg != crange)) {
                 ++ntask;
                 cur = 0;
             }
+            crange = rg;
             cur += c;
         }
         if (cur)
@@ -377,6 +367,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(MatchParams p)
         int k = incl - ntask;
         int start = 0;
         cur = 0;
+        crange = -1;
         for (int b = b0; b < b1; ++b) {
             const int c = cnt[b];
             if (c == 0)
@@ -398,10 +389,12 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(MatchParams p)
                 }
                 continue;
             }
-            if (cur + c > 64) {
+            const int rg = off[b] / pcap;
+            if (cur + c > 64 || (cur && rg != crange)) {
                 tasks[k++] = ((uint32_t)start << 6) | (uint32_t)(cur - 1);
                 cur = 0;
             }
+            crange = rg;
             if (cur == 0)
                 start = off[b];
             cur += c;
@@ -412,36 +405,35 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(MatchParams p)
             misc[24] = incl;
     }
     __syncthreads();
-    for (int i = tid; i < NB; i += nt)
-        cnt[i] = off[i];   // cursors
-    __syncthreads();
+}
 
-    // ---- C: scatter positions of buckets with 2..64 members
-    for (int t = tid; t < T; t += nt) {
-        if (t < d - 1)
-            continue;
-        const int k = dgram_key(x, t, d, K);
-        const int c = off[k + 1] - off[k];
-        if (c >= 2 && c <= 64) {
-            const int slot = atomicAdd(&cnt[k], 1);
-            pos[slot] = t | (slot == off[k] ? (int)kFirstFlag : 0);
-        }
-    }
-    __syncthreads();
-
-    // ---- D: positions with L < d: the first d-1 positions and the first
-    // occurrence of every d-gram.  L is the longest l < d whose l-gram
-    // occurred before t (first-occurrence tables); E is the latest earlier
-    // end of that l-gram.  Wave w scans time segment w in chunks of 64 in
-    // order, keeping the last end of every l-gram seen so far in segment w
-    // (segtab[w]); inside a chunk, the latest earlier lane with the same
-    // l-gram comes from a ballot match.  Queries with no earlier end inside
-    // their segment are resolved after the scan from the tables of earlier
-    // segments.
-    const int nseg = FL > 0 ? min(nw, kSegTabInts / FL) : nw;
+// Phase D: positions with L < d: the first d-1 positions and the first
+// occurrence of every d-gram.  L is the longest l < d whose l-gram occurred
+// before t (first-occurrence tables); E is the latest earlier end of that
+// l-gram.  Wave w scans time segment w in chunks of 64 in order, keeping the
+// last end of every l-gram seen so far in segment w (segtab[w]); inside a
+// chunk, the latest earlier lane with the same l-gram comes from a ballot
+// match.  Queries with no earlier end inside their segment are resolved
+// after the scan from the tables of earlier segments.  `put(t, e, l)`
+// receives every answer.
+template <class Put, class PendT>
+__device__ void phase_short(const MatchParams &p, const uint8_t *x,
+                            const int32_t *firstd, const int32_t *firstl,
+                            int32_t *segtab, int segcap, PendT *pend,
+                            int32_t *misc, Put put)
+{
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int lane = tid & 63, wid = tid >> 6, nw = nt >> 6;
+    const uint64_t self = 1ull << lane;
+    const uint64_t below = self - 1;
+    const uint64_t above = ~(below | self);
+    const int T = p.T, K = p.K, d = p.d, FL = p.fl_total;
+    const int nseg = FL > 0 ? max(1, min(nw, segcap / FL)) : nw;
     const int Ts = (((T + nseg - 1) / nseg) + 63) & ~63;
     for (int i = tid; i < nseg * FL; i += nt)
         segtab[i] = -1;
+    if (tid == 0)
+        misc[25] = 0;
     __syncthreads();
     if (wid < nseg) {
         int32_t *tab = segtab + wid * FL;
@@ -482,65 +474,250 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(MatchParams p)
             }
             if (q) {
                 if (miss)
-                    pend[atomicAdd(&misc[25], 1)] = t;
+                    pend[atomicAdd(&misc[25], 1)] = (PendT)t;
                 else
-                    emit(o, t, Lq > 0 ? Eq : -1, Lq);
+                    put(t, Lq > 0 ? Eq : -1, Lq);
             }
         }
     }
     __syncthreads();
-    {
-        const int npend = misc[25];
-        for (int i = tid; i < npend; i += nt) {
-            const int t = pend[i];
-            int Lq = 0, gq = 0, gk = 0;
-            for (int l = 1; l < d && l <= t + 1; ++l) {
-                gk = gk * K + x[t - l + 1];
-                if (firstl[p.fl_off[l] + gk] < t) {
-                    Lq = l;
-                    gq = gk;
-                }
+    const int npend = misc[25];
+    for (int i = tid; i < npend; i += nt) {
+        const int t = (int)pend[i];
+        int Lq = 0, gq = 0, gk = 0;
+        for (int l = 1; l < d && l <= t + 1; ++l) {
+            gk = gk * K + x[t - l + 1];
+            if (firstl[p.fl_off[l] + gk] < t) {
+                Lq = l;
+                gq = gk;
             }
-            int e = -1;
-            for (int w = t / Ts - 1; w >= 0 && e < 0; --w)
-                e = segtab[w * FL + p.fl_off[Lq] + gq];
-            emit(o, t, e, Lq);
         }
+        int e = -1;
+        for (int w = t / Ts - 1; w >= 0 && e < 0; --w)
+            e = segtab[w * FL + p.fl_off[Lq] + gq];
+        put(t, e, Lq);
     }
+    __syncthreads();
+}
 
-    // ---- E: tasks of buckets with 2..64 members, one wave per task.  The
-    // task's members are sorted by time across the whole wave (bitonic on
-    // t<<6 | bucket); a group is the set of lanes with the same bucket
-    // index, so lane order is time order inside every group.
+// One task: `n` positions of consecutive buckets read from `src`.  Bucket
+// boundaries are where the d-gram key changes; the positions are sorted by
+// time across the wave (bitonic on t<<6 | bucket) and a group is the set of
+// lanes with the same bucket index.  Returns solve_wave's answer for the
+// lane and the lane's (sorted) position in t_out.
+template <class Src>
+__device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
+                          int n, int &t_out)
+{
+    const int lane = __lane_id();
+    const uint64_t self = 1ull << lane;
+    const bool has = lane < n;
+    const int t0 = has ? src(lane) : 0;
+    const int k0 = has ? dgram_key(x, t0, p.d, p.K) : -1;
+    const int kprev = __shfl_up(k0, 1);
+    const uint64_t B = ballot(has && (lane == 0 || kprev != k0));
+    const uint64_t upto = (self << 1) - 1;   // lanes 0..lane (lane 63: all)
+    const uint32_t seg = (uint32_t)__popcll(B & upto) - 1u;
+    uint32_t key = has ? (((uint32_t)t0 << 6) | seg) : 0xFFFFFFFFu;
+    for (int kk = 2; kk <= 64; kk <<= 1)
+        for (int j = kk >> 1; j > 0; j >>= 1) {
+            const uint32_t other = (uint32_t)__shfl_xor((int)key, j);
+            const bool up = (lane & kk) == 0;
+            const bool lower = (lane & j) == 0;
+            key = (lower == up) ? min(key, other) : max(key, other);
+        }
+    const int nbk = 64 - __clzll((long long)__popcll(B));
+    const uint32_t sg = key & 63u;
+    uint64_t g = ballot(has);
+    for (int b = 0; b < nbk; ++b) {
+        const bool bit = (sg >> b) & 1u;
+        const uint64_t Bb = ballot(has && bit);
+        g &= bit ? Bb : ~Bb;
+    }
+    if (!has)
+        g = self;
+    t_out = (int)(key >> 6);
+    return solve_wave(x, p.nbits, t_out, g, p.d, has);
+}
+
+// ------------------------------------------------- stream kernel (LDS)
+//
+// Streams of up to 65536 positions.  LDS: the padded symbol row, bucket
+// offsets, tasks, the short-match answers of first bucket members, and a
+// union reused across phases:
+//   A-B  cnt[4096] | firstd[4096] | firstl[2048]
+//   D    pending u16[4112] | firstd | firstl | segment tables
+//   E    cursors[4096] | positions u16[kLposCap]
+// Phase E runs in passes over ranges of bucket slots that fit kLposCap:
+// each pass scatters the range's positions into LDS (LDS atomics on the
+// cursors), then the waves solve the range's tasks from LDS.  All results
+// are staged as records (coalesced) and put into time order by
+// unpermute_kernel.
+constexpr int kLdsSymBytes = 65792;
+constexpr int kTaskCap = 4128;
+constexpr int kUnionBytes = 163840 - kLdsSymBytes - (kMaxBuckets + 16) * 4 -
+                            kTaskCap * 4 - kMaxBuckets * 2 - 128;
+constexpr int kUSegTab = 40960;
+constexpr int kSegTabLds = (kUnionBytes - kUSegTab) / 4;
+constexpr int kLposCap = (kUnionBytes - 16384) / 2;
+constexpr int kPassCap = kLposCap - 64;
+
+__global__ __launch_bounds__(kStreamThreads) void stream_kernel_lds(MatchParams p)
+{
+    __shared__ __align__(16) unsigned char symrow[kLdsSymBytes];
+    __shared__ int32_t off[kMaxBuckets + 16];
+    __shared__ uint32_t tasks[kTaskCap];
+    __shared__ uint16_t qres[kMaxBuckets];
+    __shared__ int32_t misc[32];
+    __shared__ __align__(16) unsigned char U[kUnionBytes];
+    int32_t *cnt = reinterpret_cast<int32_t *>(U);
+    int32_t *firstd = reinterpret_cast<int32_t *>(U + 16384);
+    int32_t *firstl = reinterpret_cast<int32_t *>(U + 32768);
+    uint16_t *pend = reinterpret_cast<uint16_t *>(U);
+    int32_t *segtab = reinterpret_cast<int32_t *>(U + kUSegTab);
+    int32_t *cursor = reinterpret_cast<int32_t *>(U);
+    uint16_t *lpos = reinterpret_cast<uint16_t *>(U + 16384);
+
+    const int s = blockIdx.x;
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int lane = tid & 63, wid = tid >> 6, nw = nt >> 6;
+    const int T = p.T, K = p.K, d = p.d, NB = p.NB;
+    {
+        const uint4 *src = reinterpret_cast<const uint4 *>(p.sym + (int64_t)s * p.Tp);
+        uint4 *dst = reinterpret_cast<uint4 *>(symrow);
+        for (int i = tid; i < (int)(p.Tp >> 4); i += nt)
+            dst[i] = src[i];
+    }
+    if (tid < 32)
+        misc[tid] = 0;
+    const uint8_t *x = symrow + kPadFront;
+    StreamOut o;
+    o.x = x;
+    o.E = nullptr;
+    o.SYM = nullptr;
+    o.L = p.L ? p.L + (int64_t)s * T : nullptr;
+    o.rec = p.rec + (int64_t)s * T;
+
+    phase_hist(p, x, cnt, firstd, firstl);
+    phase_tasks(p, s, cnt, off, tasks, misc, kPassCap);
+
+    // D: records of the first d-1 positions go to the slots T-d+1.. (no
+    // bucket holds them); a first occurrence in a singleton or large bucket
+    // takes the bucket's first slot; for buckets of 2..64 members the answer
+    // waits in qres until the bucket's task writes it.
+    phase_short(p, x, firstd, firstl, segtab, kSegTabLds, pend, misc,
+                [&](int t, int e, int l) {
+                    if (t < d - 1) {
+                        emit_record(o, T - d + 1 + t, t, e, l);
+                        return;
+                    }
+                    const int k = dgram_key(x, t, d, K);
+                    const int c = off[k + 1] - off[k];
+                    if (c == 1 || c > 64)
+                        emit_record(o, off[k], t, e, l);
+                    else {
+                        qres[k] = (uint16_t)(e + 1);
+                        if (o.L)
+                            o.L[t] = l;
+                    }
+                });
+
+    // E: passes over slot ranges
+    for (int i = tid; i < NB; i += nt)
+        cursor[i] = off[i];
+    const int ntasks = misc[24];
+    const int nslots = off[NB];
+    __syncthreads();
+    for (int base = 0; base < nslots; base += kPassCap) {
+        const int rg = base / kPassCap;
+        for (int t = d - 1 + tid; t < T; t += nt) {
+            const int k = dgram_key(x, t, d, K);
+            const int ok = off[k];
+            const int c = off[k + 1] - ok;
+            if (c >= 2 && c <= 64 && ok / kPassCap == rg) {
+                const int slot = atomicAdd(&cursor[k], 1);
+                lpos[slot - base] = (uint16_t)t;
+            }
+        }
+        __syncthreads();
+        for (int ti = wid; ti < ntasks; ti += nw) {
+            const uint32_t tk = tasks[ti];
+            const int start = (int)(tk >> 6);
+            if (start / kPassCap != rg)
+                continue;
+            const int n = (int)(tk & 63u) + 1;
+            int t;
+            const Found f = run_task(
+                p, x, [&](int i) { return (int)lpos[start - base + i]; }, n, t);
+            if (lane < n) {
+                if (f.ok)
+                    emit_record(o, start + lane, t, f.e, f.l);
+                else
+                    o.rec[start + lane] =
+                        ((uint32_t)t << 16) | (uint32_t)qres[dgram_key(x, t, d, K)];
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------- stream kernel (HBM rows)
+//
+// Streams of more than 65536 positions: the same phases with symbols and
+// bucket positions in HBM and results written directly.
+constexpr int kArenaBytes = 90368;
+
+__global__ __launch_bounds__(kStreamThreads) void stream_kernel_hbm(MatchParams p)
+{
+    __shared__ __align__(16) unsigned char arena[kArenaBytes];
+    int32_t *cnt = reinterpret_cast<int32_t *>(arena);
+    int32_t *off = reinterpret_cast<int32_t *>(arena + 16384);
+    int32_t *segtab = reinterpret_cast<int32_t *>(arena);
+    int32_t *firstd = reinterpret_cast<int32_t *>(arena + 32832);
+    int32_t *firstl = reinterpret_cast<int32_t *>(arena + 49216);
+    int32_t *pend = reinterpret_cast<int32_t *>(arena + 57408);
+    uint32_t *tasks = reinterpret_cast<uint32_t *>(arena + 73856);
+    int32_t *misc = reinterpret_cast<int32_t *>(arena + 90240);
+
+    const int s = blockIdx.x;
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int lane = tid & 63, wid = tid >> 6, nw = nt >> 6;
+    const int T = p.T, K = p.K, d = p.d;
+    const uint8_t *x = p.sym + (int64_t)s * p.Tp + kPadFront;
+    int32_t *pos = p.pos + (int64_t)s * T;
+    if (tid < 32)
+        misc[tid] = 0;
+    StreamOut o;
+    o.x = x;
+    o.E = p.E + (int64_t)s * T;
+    o.SYM = p.SYM ? p.SYM + (int64_t)s * T : nullptr;
+    o.L = p.L ? p.L + (int64_t)s * T : nullptr;
+    o.rec = nullptr;
+
+    phase_hist(p, x, cnt, firstd, firstl);
+    phase_tasks(p, s, cnt, off, tasks, misc, 0x7FFFFFFF);
+    for (int i = tid; i < p.NB; i += nt)
+        cnt[i] = off[i];   // cursors
+    __syncthreads();
+    // scatter positions of buckets with 2..64 members
+    for (int t = d - 1 + tid; t < T; t += nt) {
+        const int k = dgram_key(x, t, d, K);
+        const int c = off[k + 1] - off[k];
+        if (c >= 2 && c <= 64)
+            pos[atomicAdd(&cnt[k], 1)] = t;
+    }
+    __syncthreads();
+    phase_short(p, x, firstd, firstl, segtab, kSegTabInts, pend, misc,
+                [&](int t, int e, int l) { emit(o, t, e, l); });
     const int ntasks = misc[24];
     for (int ti = wid; ti < ntasks; ti += nw) {
         const uint32_t tk = tasks[ti];
         const int start = (int)(tk >> 6);
         const int n = (int)(tk & 63u) + 1;
-        const bool has = lane < n;
-        const uint32_t v = has ? (uint32_t)pos[start + lane] : 0u;
-        const uint64_t F = ballot(has && (v & kFirstFlag));
-        const uint64_t upto = (self << 1) - 1;   // lanes 0..lane (lane 63: all)
-        const uint32_t seg = (uint32_t)__popcll(F & upto) - 1u;
-        uint32_t key = has ? (((v & ~kFirstFlag) << 6) | seg) : 0xFFFFFFFFu;
-        for (int kk = 2; kk <= 64; kk <<= 1)
-            for (int j = kk >> 1; j > 0; j >>= 1) {
-                const uint32_t other = (uint32_t)__shfl_xor((int)key, j);
-                const bool up = (lane & kk) == 0;
-                const bool lower = (lane & j) == 0;
-                key = (lower == up) ? min(key, other) : max(key, other);
-            }
-        const int nbk = 64 - __clzll((long long)__popcll(F));   // bits for bucket ids
-        const uint32_t sg = key & 63u;
-        uint64_t g = ballot(has);
-        for (int b = 0; b < nbk; ++b) {
-            const bool bit = (sg >> b) & 1u;
-            const uint64_t B = ballot(has && bit);
-            g &= bit ? B : ~B;
-        }
-        if (!has)
-            g = self;
-        solve_wave(o, p.nbits, (int)(key >> 6), g, d, has);
+        int t;
+        const Found f = run_task(p, x, [&](int i) { return pos[start + i]; }, n, t);
+        if (lane < n && f.ok)
+            emit(o, t, f.e, f.l);
     }
 }
 
@@ -555,7 +732,9 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(MatchParams p)
 // stack region from entry start/16 on (n/16 >= n/65 + 2 entries for
 // n >= 65, and ranges of different buckets do not overlap).  A level where
 // every member has the same next symbol only drops the first member if its
-// history ends (t = level-1).
+// history ends (t = level-1).  In record mode the bucket's members other
+// than the first (answered by the stream kernel in slot `start`) fill slots
+// start+1 .. start+n-1 in completion order.
 
 struct GroupRef {
     int start, n, ell, buf;
@@ -577,14 +756,28 @@ __global__ __launch_bounds__(kBigThreads) void big_kernel(MatchParams p)
         const int32_t *ent = p.big + 64 + 4 * (int64_t)item;
         const int s = ent[0], key = ent[1], start = ent[2], n0 = ent[3];
         const uint8_t *x = p.sym + (int64_t)s * p.Tp + kPadFront;
-        int32_t *buf[2] = {p.pos + (int64_t)s * T, p.pos2 + (int64_t)s * T};
+        int32_t *buf0 = p.pos + (int64_t)s * T;
+        int32_t *buf1 = p.pos2 + (int64_t)s * T;
         StreamOut o;
         o.x = x;
-        o.E = p.E + (int64_t)s * T;
+        o.E = p.E ? p.E + (int64_t)s * T : nullptr;
         o.SYM = p.SYM ? p.SYM + (int64_t)s * T : nullptr;
         o.L = p.L ? p.L + (int64_t)s * T : nullptr;
+        o.rec = p.rec ? p.rec + (int64_t)s * T : nullptr;
         int4 *stk = p.stack + (int64_t)s * (T / 16 + 4) + start / 16;
         const int stack_cap = n0 / 16;
+        int nrec = 0;   // records written so far (uniform)
+        // emits the answers of the lanes with `want`, compacting record slots
+        auto put = [&](bool want, int t, int e, int l) {
+            if (o.rec) {
+                const uint64_t m = ballot(want);
+                if (want)
+                    emit_record(o, start + 1 + nrec + __popcll(m & below), t, e, l);
+                nrec += __popcll(m);
+            } else if (want) {
+                emit(o, t, e, l);
+            }
+        };
 
         // the bucket's positions in time order
         {
@@ -594,7 +787,7 @@ __global__ __launch_bounds__(kBigThreads) void big_kernel(MatchParams p)
                 const bool m = t < T && dgram_key(x, t, d, K) == key;
                 const uint64_t bm = ballot(m);
                 if (m)
-                    buf[0][start + w + __popcll(bm & below)] = t;
+                    buf0[start + w + __popcll(bm & below)] = t;
                 w += __popcll(bm);
             }
         }
@@ -602,14 +795,15 @@ __global__ __launch_bounds__(kBigThreads) void big_kernel(MatchParams p)
         GroupRef cur = {start, n0, d, 0};
         bool have = true;
         while (have) {
+            const int32_t *X = cur.buf ? buf1 : buf0;
+            int32_t *Y = cur.buf ? buf0 : buf1;
             if (cur.n <= 64) {
                 const bool hs = lane < cur.n;
-                const int t = hs ? buf[cur.buf][cur.start + lane] : 0;
+                const int t = hs ? X[cur.start + lane] : 0;
                 const uint64_t g = cur.n >= 64 ? ~0ull : ((1ull << cur.n) - 1);
-                solve_wave(o, p.nbits, t, hs ? g : self, cur.ell, hs);
+                const Found f = solve_wave(x, p.nbits, t, hs ? g : self, cur.ell, hs);
+                put(hs && f.ok, t, f.e, f.l);
             } else {
-                const int32_t *X = buf[cur.buf];
-                int32_t *Y = buf[cur.buf ^ 1];
                 const int a = cur.start, n = cur.n, ell = cur.ell;
                 // uniform level?  reference symbol from the last member
                 const int tl = X[a + n - 1];
@@ -632,8 +826,7 @@ __global__ __launch_bounds__(kBigThreads) void big_kernel(MatchParams p)
                     if (t0 - ell < 0) {
                         // the first member's history ends: the next member
                         // loses its only predecessor at this level
-                        if (lane == 0)
-                            emit(o, X[a + 1], t0, ell);
+                        put(lane == 0, X[a + 1], t0, ell);
                         cur.start = a + 1;
                         cur.n = n - 1;
                     }
@@ -671,8 +864,8 @@ __global__ __launch_bounds__(kBigThreads) void big_kernel(MatchParams p)
                         uint64_t eq = ballot(hs);
                         for (int b = 0; b < 9; ++b) {
                             const bool bit = (dg >> b) & 1;
-                            const uint64_t B = ballot(hs && bit);
-                            eq &= bit ? B : ~B;
+                            const uint64_t Bb = ballot(hs && bit);
+                            eq &= bit ? Bb : ~Bb;
                         }
                         const int rank = __popcll(eq & below);
                         int dest = 0;
@@ -682,11 +875,11 @@ __global__ __launch_bounds__(kBigThreads) void big_kernel(MatchParams p)
                         if (hs && !(eq & ~(below | self)))   // last of its class
                             bbase[dg] = dest + 1;
                         __syncthreads();
-                        if (hs && dg < K) {
+                        const bool moved = hs && dg < K;
+                        if (moved)
                             Y[a + dest] = t;
-                            if (dest == bbase0[dg] && i > 0)
-                                emit(o, t, X[a + i - 1], ell);
-                        }
+                        const bool fin = moved && dest == bbase0[dg] && i > 0;
+                        put(fin, t, fin ? X[a + i - 1] : 0, ell);
                     }
                     __syncthreads();
                     // children: small ones solved now, large ones stacked;
@@ -701,7 +894,9 @@ __global__ __launch_bounds__(kBigThreads) void big_kernel(MatchParams p)
                             const bool hs = lane < c;
                             const int t = hs ? Y[cs + lane] : 0;
                             const uint64_t g = c >= 64 ? ~0ull : ((1ull << c) - 1);
-                            solve_wave(o, p.nbits, t, hs ? g : self, ell + 1, hs);
+                            const Found f =
+                                solve_wave(x, p.nbits, t, hs ? g : self, ell + 1, hs);
+                            put(hs && f.ok, t, f.e, f.l);
                         } else if (c < bestn) {
                             if (best >= 0 && sp < stack_cap && lane == 0)
                                 stk[sp] = make_int4(a + bbase0[best], bcnt[best],
@@ -734,15 +929,62 @@ __global__ __launch_bounds__(kBigThreads) void big_kernel(MatchParams p)
     }
 }
 
+// ------------------------------------------------------ unpermute kernel
+//
+// Record mode: one workgroup per stream.  With the stream's symbol row in
+// LDS, the records are scattered into tau[t] = E+1 for one half of the time
+// axis at a time (LDS holds tau for 32768 positions), then E and
+// SYM = x[E+1] of that half are written in time order with coalesced
+// stores.
+constexpr int kTauHalf = 32768;
+
+__global__ __launch_bounds__(kStreamThreads) void unpermute_kernel(MatchParams p)
+{
+    __shared__ __align__(16) unsigned char symrow[kLdsSymBytes];
+    __shared__ uint16_t tau[kTauHalf];
+    const int s = blockIdx.x;
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int T = p.T;
+    const uint32_t *rec = p.rec + (int64_t)s * T;
+    int32_t *E = p.E + (int64_t)s * T;
+    int16_t *SYM = p.SYM ? p.SYM + (int64_t)s * T : nullptr;
+    if (SYM) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(p.sym + (int64_t)s * p.Tp);
+        uint4 *dst = reinterpret_cast<uint4 *>(symrow);
+        for (int i = tid; i < (int)(p.Tp >> 4); i += nt)
+            dst[i] = src[i];
+    }
+    const uint8_t *x = symrow + kPadFront;
+    for (int h0 = 0; h0 < T; h0 += kTauHalf) {
+        const int h1 = min(T, h0 + kTauHalf);
+        for (int i = tid; i < T; i += nt) {
+            const uint32_t r = rec[i];
+            const int t = (int)(r >> 16);
+            if (t >= h0 && t < h1)
+                tau[t - h0] = (uint16_t)(r & 0xFFFFu);
+        }
+        __syncthreads();
+        for (int t = h0 + tid; t < h1; t += nt) {
+            const int e1 = tau[t - h0];
+            E[t] = e1 - 1;
+            if (SYM)
+                SYM[t] = e1 ? (int16_t)x[e1] : (int16_t)-1;
+        }
+        __syncthreads();
+    }
+}
+
 // --------------------------------------------------------------- launchers
+
+bool stream_uses_records(int64_t T) { return T <= 65536; }
 
 hipError_t launch_stream(const MatchParams &p, int64_t S, hipStream_t st)
 {
-    if (p.Tp <= kSymLds)
-        hipLaunchKernelGGL(stream_kernel<true>, dim3((unsigned)S),
+    if (stream_uses_records(p.T))
+        hipLaunchKernelGGL(stream_kernel_lds, dim3((unsigned)S),
                            dim3(kStreamThreads), 0, st, p);
     else
-        hipLaunchKernelGGL(stream_kernel<false>, dim3((unsigned)S),
+        hipLaunchKernelGGL(stream_kernel_hbm, dim3((unsigned)S),
                            dim3(kStreamThreads), 0, st, p);
     return hipGetLastError();
 }
@@ -751,6 +993,15 @@ hipError_t launch_big(const MatchParams &p, int grid, hipStream_t st)
 {
     hipLaunchKernelGGL(big_kernel, dim3((unsigned)grid), dim3(kBigThreads), 0,
                        st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpermute(const MatchParams &p, int64_t S, hipStream_t st)
+{
+    if (!stream_uses_records(p.T))
+        return hipSuccess;
+    hipLaunchKernelGGL(unpermute_kernel, dim3((unsigned)S), dim3(kStreamThreads),
+                       0, st, p);
     return hipGetLastError();
 }
 

@@ -85,23 +85,35 @@ __global__ __launch_bounds__(256) void discretize_kernel(
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int64_t r = r0 + lane;
-    for (int k = 0; k < 16; ++k) {
-        const int tl = w * 16 + k;
-        const int64_t t = t0 + tl;
-        uint32_t a = 0;
-        if (t < T && r < R) {
-            const uint16_t *h = H + (b * T + t) * ld + r * M;
-            if (MC == 4) {
-                // four channels in one 8-byte load (alignment checked on host)
-                uint2 v = *reinterpret_cast<const uint2 *>(h);
-                a = bf16_pos(v.x & 0xFFFFu) | (bf16_pos(v.x >> 16) << 1) |
-                    (bf16_pos(v.y & 0xFFFFu) << 2) | (bf16_pos(v.y >> 16) << 3);
-            } else {
+    if (MC == 4) {
+        // four channels in one 8-byte load (alignment checked on host); all
+        // 16 loads of the thread in flight before they are used
+        uint2 v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int64_t t = t0 + w * 16 + k;
+            v[k] = make_uint2(0u, 0u);
+            if (t < T && r < R)
+                v[k] = *reinterpret_cast<const uint2 *>(H + (b * T + t) * ld + r * M);
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            tile[lane][w * 16 + k] =
+                (uint8_t)(bf16_pos(v[k].x & 0xFFFFu) | (bf16_pos(v[k].x >> 16) << 1) |
+                          (bf16_pos(v[k].y & 0xFFFFu) << 2) |
+                          (bf16_pos(v[k].y >> 16) << 3));
+    } else {
+        for (int k = 0; k < 16; ++k) {
+            const int tl = w * 16 + k;
+            const int64_t t = t0 + tl;
+            uint32_t a = 0;
+            if (t < T && r < R) {
+                const uint16_t *h = H + (b * T + t) * ld + r * M;
                 for (int j = 0; j < M; ++j)
                     a |= bf16_pos(h[j]) << j;
             }
+            tile[lane][tl] = (uint8_t)a;
         }
-        tile[lane][tl] = (uint8_t)a;
     }
     __syncthreads();
     // write: thread i -> route i/4, 16 positions starting at (i%4)*16
@@ -140,7 +152,11 @@ __global__ __launch_bounds__(256) void discretize_kernel(
 // tile is read as 64 contiguous 256-byte runs (one per stream) into LDS;
 // then wave w handles positions t0+16w..+15 with lane = route: one M-wide
 // value slice read from row tau = E+1 (random rows, inherent to the method)
-// and one coalesced write of the output row segment.
+// and one coalesced write of the output row segment.  Route tiles are the
+// fast grid dimension, so the blocks in flight cover a narrow band of
+// positions: destinations cluster a few thousand rows behind t, and the
+// band of V rows they read stays cache resident, each line serving the
+// eight or more streams that share it.
 template <int MC>
 __global__ __launch_bounds__(256) void gather_kernel(
     const uint16_t *__restrict__ V, int64_t T, int64_t D, int64_t ldv, int M,
@@ -149,8 +165,8 @@ __global__ __launch_bounds__(256) void gather_kernel(
     __shared__ int32_t et[64][64 + 1];
     const int64_t R = D / M;
     const int64_t b = blockIdx.z;
-    const int64_t t0 = (int64_t)blockIdx.x * 64;
-    const int64_t r0 = (int64_t)blockIdx.y * 64;
+    const int64_t t0 = (int64_t)blockIdx.y * 64;
+    const int64_t r0 = (int64_t)blockIdx.x * 64;
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     // load E tile: 16 streams per wave-iteration, lane = position
@@ -255,7 +271,7 @@ hipError_t launch_gather(const uint16_t *V, int64_t B, int64_t T, int64_t D,
                          int64_t ldo, hipStream_t st)
 {
     const int64_t R = D / M;
-    dim3 grid((unsigned)((T + 63) / 64), (unsigned)((R + 63) / 64),
+    dim3 grid((unsigned)((R + 63) / 64), (unsigned)((T + 63) / 64),
               (unsigned)B);
     const bool vec4 = M == 4 && (ldv % 4) == 0 && (ldo % 4) == 0 &&
                       (((uintptr_t)V) & 7) == 0 && (((uintptr_t)out) & 7) == 0;
