@@ -32,9 +32,10 @@ import numpy as np  # noqa: E402
 
 METRIC = "matched positions/sec (streams×T) at T=64K, 512 streams"
 HBM_PEAK = 8.0e12     # MI355X HBM3E, bytes/s
-# Algorithmic bytes per stream-position of the retrieval kernel: the symbol
-# read (1 B) plus E (int32) and SYM (int16) written.
-KERNEL_BYTES_PER_POS = 1 + 4 + 2
+# Algorithmic bytes per stream-position of the retrieval kernel (streams of
+# up to 65536 positions): the symbol read (1 B) and one 4-byte result record
+# (position, E+1) written; a separate kernel puts the records in time order.
+KERNEL_BYTES_PER_POS = 1 + 4
 PMC_FILE = os.path.join(ROOT, "profiles", "stream_kernel_long_pmc.txt")
 
 
@@ -161,6 +162,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the oracle baseline and parity check")
     ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--copy-reference", type=int, default=0, metavar="BYTES",
+                    help="after timing, run one plain device-to-device copy of "
+                         "BYTES (the reference for scaling HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -226,6 +230,12 @@ def main():
     k_avg = float(np.mean(k_ms))
     if rosa.rosa_match_status(ws) != rosa.ROSA_OK:
         raise SystemExit("symbol range flag raised")
+    if args.copy_reference > 0:
+        src = torch.empty(args.copy_reference, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     value = S * T / (ms_step / 1e3)
     _log(f"ms/step {ms_step:.4f}  retrieval kernel {k_avg:.4f} ms")
 
