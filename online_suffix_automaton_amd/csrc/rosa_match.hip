@@ -98,6 +98,53 @@ __device__ __forceinline__ uint64_t shfl64(uint64_t v, int src)
 // (t << 16 | E+1) per bucket slot, coalesced; a later kernel scatters the
 // records into time order in LDS and writes E and SYM.  L, if requested,
 // is always written directly.
+// Exchange with lane ^ J for the bitonic network.  J < 16 stays inside a
+// 16-lane row: quad permutes for 1 and 2, row shifts for 4 and 8 (lane i
+// reads i+J or i-J), no LDS round trip; 16 uses a swizzle, 32 a permute.
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v)
+{
+    if (J == 1)
+        return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false);
+    if (J == 2)
+        return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false);
+    if (J == 4 || J == 8) {
+        const uint32_t up = __builtin_amdgcn_update_dpp(0u, v, 0x100 | J, 0xF, 0xF, false);
+        const uint32_t dn = __builtin_amdgcn_update_dpp(0u, v, 0x110 | J, 0xF, 0xF, false);
+        return (__lane_id() & J) ? dn : up;
+    }
+    if (J == 16)
+        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+    return (uint32_t)__shfl_xor((int)v, 32);
+}
+
+template <int KK, int J>
+__device__ __forceinline__ uint32_t bitonic_step(uint32_t key, int lane)
+{
+    const uint32_t o = xor_lane<J>(key);
+    const bool take_min = ((lane & KK) == 0) == ((lane & J) == 0);
+    return take_min ? min(key, o) : max(key, o);
+}
+
+// Ascending sort of one 32-bit key per lane across the wave.
+__device__ __forceinline__ uint32_t bitonic64(uint32_t k)
+{
+    const int l = __lane_id();
+    k = bitonic_step<2, 1>(k, l);
+    k = bitonic_step<4, 2>(k, l);   k = bitonic_step<4, 1>(k, l);
+    k = bitonic_step<8, 4>(k, l);   k = bitonic_step<8, 2>(k, l);
+    k = bitonic_step<8, 1>(k, l);
+    k = bitonic_step<16, 8>(k, l);  k = bitonic_step<16, 4>(k, l);
+    k = bitonic_step<16, 2>(k, l);  k = bitonic_step<16, 1>(k, l);
+    k = bitonic_step<32, 16>(k, l); k = bitonic_step<32, 8>(k, l);
+    k = bitonic_step<32, 4>(k, l);  k = bitonic_step<32, 2>(k, l);
+    k = bitonic_step<32, 1>(k, l);
+    k = bitonic_step<64, 32>(k, l); k = bitonic_step<64, 16>(k, l);
+    k = bitonic_step<64, 8>(k, l);  k = bitonic_step<64, 4>(k, l);
+    k = bitonic_step<64, 2>(k, l);  k = bitonic_step<64, 1>(k, l);
+    return k;
+}
+
 struct StreamOut {
     const uint8_t *x;  // padded symbol row of the stream (LDS or HBM)
     int32_t *E;
@@ -160,9 +207,15 @@ __device__ Found solve_wave(const uint8_t *x, int nbits, int t, uint64_t g,
         const bool live = has && __popcll(g) >= 2;
         if (ballot(live) == 0)
             return r;
-        const int gmax = wave_max(live ? __popcll(g) : 0);
-        if (!(gmax > kWordThresh && (ell <= ell0 + 1 || gmax > kWordThreshDeep)))
+        // level steps while some group is larger than kWordThresh during the
+        // first two levels after bucketing (groups still split fast there),
+        // later only while some group is larger than kWordThreshDeep
+        if (ell <= ell0 + 1) {
+            if (ballot(live && __popcll(g) > kWordThresh) == 0)
+                break;
+        } else if (wave_max(live ? __popcll(g) : 0) <= kWordThreshDeep) {
             break;
+        }
         // ---------------------------------------------------- level step
         if (ell - wl >= 16) {
             if (live && t - ell >= 0)
@@ -195,28 +248,39 @@ __device__ Found solve_wave(const uint8_t *x, int nbits, int t, uint64_t g,
     // ------------------------------------------------- direct resolution
     uint64_t rem = (has && __popcll(g) >= 2) ? (g & below) : 0;
     int best_c = -1, best_e = -1;
+    // every element's first 16 symbols past level ell, shared by shuffle
+    uint64_t w0lo = 0, w0hi = 0;
+    if (has && t - ell >= 0)
+        load_window(x, t - ell - 15, w0lo, w0hi);
     while (ballot(rem != 0)) {
         const bool have = rem != 0;
         const int j = have ? __ffsll((long long)rem) - 1 : lane;
         rem &= rem - 1;
         const int tj = __shfl(t, j);
+        const uint64_t jlo = shfl64(w0lo, j), jhi = shfl64(w0hi, j);
         if (have) {
             const int aj = tj - ell + 1;   // history of member j from x[tj-ell]
-            int c = 0;
-            while (c < aj) {
-                uint64_t alo, ahi, blo, bhi;
-                load_window(x, t - ell - c - 15, alo, ahi);
-                load_window(x, tj - ell - c - 15, blo, bhi);
-                const uint64_t xh = ahi ^ bhi, xl = alo ^ blo;
-                if (xh) {
-                    c += __clzll((long long)xh) >> 3;
-                    break;
+            // first 16 symbols from the shared windows, further ones from
+            // memory while they keep matching
+            const uint64_t fh = w0hi ^ jhi, fl = w0lo ^ jlo;
+            int c = fh ? (__clzll((long long)fh) >> 3)
+                       : (fl ? 8 + (__clzll((long long)fl) >> 3) : 16);
+            if (!(fh | fl)) {
+                while (c < aj) {
+                    uint64_t alo, ahi, blo, bhi;
+                    load_window(x, t - ell - c - 15, alo, ahi);
+                    load_window(x, tj - ell - c - 15, blo, bhi);
+                    const uint64_t xh = ahi ^ bhi, xl = alo ^ blo;
+                    if (xh) {
+                        c += __clzll((long long)xh) >> 3;
+                        break;
+                    }
+                    if (xl) {
+                        c += 8 + (__clzll((long long)xl) >> 3);
+                        break;
+                    }
+                    c += 16;
                 }
-                if (xl) {
-                    c += 8 + (__clzll((long long)xl) >> 3);
-                    break;
-                }
-                c += 16;
             }
             c = min(c, aj);
             if (c >= best_c) {
@@ -308,7 +372,7 @@ __device__ void phase_hist(const MatchParams &p, const uint8_t *x, int32_t *cnt,
     __syncthreads();
 }
 
-// Phase B: bucket offsets, then wave 0 packs buckets of 2..64 members into
+// Phase B: bucket offsets, then buckets of 2..64 members are packed into
 // tasks of at most 64 positions (a task never spans a singleton or large
 // bucket, nor a boundary between position ranges of `pcap` slots) and
 // lists buckets of more than 64 members for the large-group kernel.
@@ -318,7 +382,6 @@ __device__ void phase_tasks(const MatchParams &p, int s, const int32_t *cnt,
                             int pcap)
 {
     const int tid = threadIdx.x, nt = blockDim.x;
-    const int lane = tid & 63, wid = tid >> 6;
     const int NB = p.NB;
     {
         const int per = (NB + nt - 1) / nt;
@@ -338,72 +401,74 @@ __device__ void phase_tasks(const MatchParams &p, int s, const int32_t *cnt,
             off[NB] = total;
     }
     __syncthreads();
-    if (wid == 0) {
-        const int b0 = (int)((int64_t)lane * NB / 64);
-        const int b1 = (int)((int64_t)(lane + 1) * NB / 64);
-        int ntask = 0, cur = 0, crange = -1;
-        for (int b = b0; b < b1; ++b) {
-            const int c = cnt[b];
-            if (c == 0)
-                continue;
-            if (c == 1 || c > 64) {
-                if (cur) {
-                    ++ntask;
-                    cur = 0;
-                }
-                continue;
-            }
-            const int rg = off[b] / pcap;
-            if (cur + c > 64 || (cur && rg != crange)) {
+    // Each thread packs a run of `bpl` consecutive buckets (about 256
+    // positions' worth, at least NB/nt so every bucket is covered); tasks
+    // do not span runs, so longer runs pack tasks fuller.
+    const int avg = max(1, off[NB] / NB);
+    const int bpl = max((NB + nt - 1) / nt, min(64, max(1, 256 / avg)));
+    const int b0 = min(NB, tid * bpl), b1 = min(NB, b0 + bpl);
+    int ntask = 0, cur = 0, crange = -1;
+    for (int b = b0; b < b1; ++b) {
+        const int c = cnt[b];
+        if (c == 0)
+            continue;
+        if (c == 1 || c > 64) {
+            if (cur) {
                 ++ntask;
                 cur = 0;
             }
-            crange = rg;
-            cur += c;
+            continue;
         }
-        if (cur)
+        const int rg = off[b] / pcap;
+        if (cur + c > 64 || (cur && rg != crange)) {
             ++ntask;
-        const int incl = wave_incl_scan(ntask);
-        int k = incl - ntask;
-        int start = 0;
-        cur = 0;
-        crange = -1;
-        for (int b = b0; b < b1; ++b) {
-            const int c = cnt[b];
-            if (c == 0)
-                continue;
-            if (c == 1 || c > 64) {
-                if (cur) {
-                    tasks[k++] = ((uint32_t)start << 6) | (uint32_t)(cur - 1);
-                    cur = 0;
-                }
-                if (c > 64) {
-                    const int idx = atomicAdd(&p.big[0], 1);
-                    if (idx < p.big_cap) {
-                        int32_t *ent = p.big + 64 + 4 * (int64_t)idx;
-                        ent[0] = s;
-                        ent[1] = b;
-                        ent[2] = off[b];
-                        ent[3] = c;
-                    }
-                }
-                continue;
-            }
-            const int rg = off[b] / pcap;
-            if (cur + c > 64 || (cur && rg != crange)) {
+            cur = 0;
+        }
+        crange = rg;
+        cur += c;
+    }
+    if (cur)
+        ++ntask;
+    int total;
+    int k = block_excl_scan(ntask, misc, &total);
+    int start = 0;
+    cur = 0;
+    crange = -1;
+    for (int b = b0; b < b1; ++b) {
+        const int c = cnt[b];
+        if (c == 0)
+            continue;
+        if (c == 1 || c > 64) {
+            if (cur) {
                 tasks[k++] = ((uint32_t)start << 6) | (uint32_t)(cur - 1);
                 cur = 0;
             }
-            crange = rg;
-            if (cur == 0)
-                start = off[b];
-            cur += c;
+            if (c > 64) {
+                const int idx = atomicAdd(&p.big[0], 1);
+                if (idx < p.big_cap) {
+                    int32_t *ent = p.big + 64 + 4 * (int64_t)idx;
+                    ent[0] = s;
+                    ent[1] = b;
+                    ent[2] = off[b];
+                    ent[3] = c;
+                }
+            }
+            continue;
         }
-        if (cur)
+        const int rg = off[b] / pcap;
+        if (cur + c > 64 || (cur && rg != crange)) {
             tasks[k++] = ((uint32_t)start << 6) | (uint32_t)(cur - 1);
-        if (lane == 63)
-            misc[24] = incl;
+            cur = 0;
+        }
+        crange = rg;
+        if (cur == 0)
+            start = off[b];
+        cur += c;
     }
+    if (cur)
+        tasks[k++] = ((uint32_t)start << 6) | (uint32_t)(cur - 1);
+    if (tid == 0)
+        misc[24] = total;
     __syncthreads();
 }
 
@@ -518,14 +583,7 @@ __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
     const uint64_t B = ballot(has && (lane == 0 || kprev != k0));
     const uint64_t upto = (self << 1) - 1;   // lanes 0..lane (lane 63: all)
     const uint32_t seg = (uint32_t)__popcll(B & upto) - 1u;
-    uint32_t key = has ? (((uint32_t)t0 << 6) | seg) : 0xFFFFFFFFu;
-    for (int kk = 2; kk <= 64; kk <<= 1)
-        for (int j = kk >> 1; j > 0; j >>= 1) {
-            const uint32_t other = (uint32_t)__shfl_xor((int)key, j);
-            const bool up = (lane & kk) == 0;
-            const bool lower = (lane & j) == 0;
-            key = (lower == up) ? min(key, other) : max(key, other);
-        }
+    const uint32_t key = bitonic64(has ? (((uint32_t)t0 << 6) | seg) : 0xFFFFFFFFu);
     const int nbk = 64 - __clzll((long long)__popcll(B));
     const uint32_t sg = key & 63u;
     uint64_t g = ballot(has);
@@ -547,7 +605,7 @@ __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
 // union reused across phases:
 //   A-B  cnt[4096] | firstd[4096] | firstl[2048]
 //   D    pending u16[4112] | firstd | firstl | segment tables
-//   E    cursors[4096] | positions u16[kLposCap]
+//   E    cursors[4096] | pass id u8[4096] | positions u16[kLposCap]
 // Phase E runs in passes over ranges of bucket slots that fit kLposCap:
 // each pass scatters the range's positions into LDS (LDS atomics on the
 // cursors), then the waves solve the range's tasks from LDS.  All results
@@ -559,7 +617,7 @@ constexpr int kUnionBytes = 163840 - kLdsSymBytes - (kMaxBuckets + 16) * 4 -
                             kTaskCap * 4 - kMaxBuckets * 2 - 128;
 constexpr int kUSegTab = 40960;
 constexpr int kSegTabLds = (kUnionBytes - kUSegTab) / 4;
-constexpr int kLposCap = (kUnionBytes - 16384) / 2;
+constexpr int kLposCap = (kUnionBytes - 16384 - 4096) / 2;
 constexpr int kPassCap = kLposCap - 64;
 
 __global__ __launch_bounds__(kStreamThreads) void stream_kernel_lds(MatchParams p)
@@ -576,7 +634,8 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_lds(MatchParams 
     uint16_t *pend = reinterpret_cast<uint16_t *>(U);
     int32_t *segtab = reinterpret_cast<int32_t *>(U + kUSegTab);
     int32_t *cursor = reinterpret_cast<int32_t *>(U);
-    uint16_t *lpos = reinterpret_cast<uint16_t *>(U + 16384);
+    uint8_t *passid = U + 16384;
+    uint16_t *lpos = reinterpret_cast<uint16_t *>(U + 16384 + 4096);
 
     const int s = blockIdx.x;
     const int tid = threadIdx.x, nt = blockDim.x;
@@ -622,22 +681,32 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_lds(MatchParams 
                     }
                 });
 
-    // E: passes over slot ranges
-    for (int i = tid; i < NB; i += nt)
+    // E: passes over slot ranges.  passid[k] is the pass that scatters
+    // bucket k (255: not scattered, a singleton or large bucket).
+    for (int i = tid; i < NB; i += nt) {
+        const int c = off[i + 1] - off[i];
         cursor[i] = off[i];
+        passid[i] = (c >= 2 && c <= 64) ? (uint8_t)(off[i] / kPassCap) : (uint8_t)255;
+    }
     const int ntasks = misc[24];
     const int nslots = off[NB];
     __syncthreads();
     for (int base = 0; base < nslots; base += kPassCap) {
         const int rg = base / kPassCap;
-        for (int t = d - 1 + tid; t < T; t += nt) {
-            const int k = dgram_key(x, t, d, K);
-            const int ok = off[k];
-            const int c = off[k + 1] - ok;
-            if (c >= 2 && c <= 64 && ok / kPassCap == rg) {
-                const int slot = atomicAdd(&cursor[k], 1);
-                lpos[slot - base] = (uint16_t)t;
+        // four positions per thread per iteration, independent chains
+        for (int t0 = d - 1 + 4 * tid; t0 < T; t0 += 4 * nt) {
+            int kk[4];
+            bool in[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int t = t0 + u;
+                kk[u] = t < T ? dgram_key(x, t, d, K) : 0;
+                in[u] = t < T && passid[kk[u]] == rg;
             }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (in[u])
+                    lpos[atomicAdd(&cursor[kk[u]], 1) - base] = (uint16_t)(t0 + u);
         }
         __syncthreads();
         for (int ti = wid; ti < ntasks; ti += nw) {
