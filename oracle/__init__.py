@@ -17,6 +17,11 @@ All functions take and return numpy arrays on the host:
   * ``brute(sym [S,T]) -> (E, L)``  O(T^2) definition, pins ``match``
   * ``gather(V_u16 [B,T,D], E [S,T], M) -> out u16 [B,T,D]`` (App. C.4, Eq. 17)
   * ``sam_stats(x [T], K) -> (states, transitions, clones, distinct)``
+  * ``match_qk(q [S,T], k [S,T], K, M, rle) -> dict``  query/key retrieval,
+    optional run-length folding and per-bit counterfactual destinations
+    (Sec. 3.3; App. C.5, C.6; Sec. 4.2 step 3)
+  * ``brute_qk_py(q [T], k [T], K, M, rle) -> dict``  the same definition by
+    direct search, for tiny streams (pins ``match_qk``)
 """
 from __future__ import annotations
 
@@ -58,9 +63,10 @@ def _load():
     lib.oracle_sam_stats.argtypes = [P, I64, I, P]
     lib.oracle_brute.argtypes = [P, I64, P, P]
     lib.oracle_gather.argtypes = [P, I64, I64, I64, I, P, P]
+    lib.oracle_match_qk.argtypes = [P, P, I64, I, I, I] + [P] * 8
     for f in (lib.oracle_discretize_bf16, lib.oracle_match,
               lib.oracle_match_streams, lib.oracle_sam_stats,
-              lib.oracle_brute, lib.oracle_gather):
+              lib.oracle_brute, lib.oracle_gather, lib.oracle_match_qk):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -168,3 +174,99 @@ def sam_stats(x: np.ndarray, K: int):
     _check(_load().oracle_sam_stats(_ptr(x), x.shape[0], K, _ptr(out)),
            "sam_stats")
     return tuple(int(v) for v in out)
+
+
+QK_FIELDS = ("tau", "end", "len", "run_of", "run_start", "ridx")
+
+
+def match_qk(q: np.ndarray, k: np.ndarray, K: int, M: int = 0,
+             rle: bool = False, cf: bool = False):
+    """Query/key retrieval (Sec. 3.3): per time t the destination tau of the
+    longest suffix of the query units that occurs in the earlier key units,
+    its most recent end unit ``end`` and length ``len``; with ``rle`` the
+    key stream is folded into runs (``run_of``, ``run_start``, ``ridx``);
+    with ``cf`` the per-bit counterfactual tables ``cf_tau``/``cf_ridx``
+    [S,T,M,2] (App. C.5, C.6).  q, k: uint8 [S,T] (or [T])."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    k = np.ascontiguousarray(k, dtype=np.uint8)
+    if q.ndim == 1:
+        q, k = q[None, :], k[None, :]
+    S, T = q.shape
+    out = {f: np.empty((S, T), np.int32) for f in QK_FIELDS}
+    if cf:
+        out["cf_tau"] = np.empty((S, T, M, 2), np.int32)
+        out["cf_ridx"] = np.empty((S, T, M, 2), np.int32)
+    lib = _load()
+    for s_ in range(S):
+        rows = {f: np.empty(T, np.int32) for f in QK_FIELDS}
+        cft = np.empty((T, M, 2), np.int32) if cf else None
+        cfr = np.empty((T, M, 2), np.int32) if cf else None
+        qs, ks = np.ascontiguousarray(q[s_]), np.ascontiguousarray(k[s_])
+        _check(lib.oracle_match_qk(_ptr(qs), _ptr(ks), T, K, M, int(rle),
+                                   *[_ptr(rows[f]) for f in QK_FIELDS],
+                                   _ptr(cft) if cf else None,
+                                   _ptr(cfr) if cf else None), "match_qk")
+        for f in QK_FIELDS:
+            out[f][s_] = rows[f]
+        if cf:
+            out["cf_tau"][s_], out["cf_ridx"][s_] = cft, cfr
+    return out
+
+
+def brute_qk_py(q, k, K: int, M: int = 0, rle: bool = False):
+    """The query/key definition by direct search, pure Python, tiny streams.
+    Units as in ``match_qk``; at unit u every earlier key unit e is scanned,
+    the common suffix of Q[..u] and C[..e] counted symbol by symbol, the
+    longest kept and among equals the latest; the destination time is the
+    start of unit e+1 when it exists and is before t.  Counterfactuals
+    replace Q[u] by the symbol with bit j forced to v."""
+    q = [int(v) for v in q]
+    k = [int(v) for v in k]
+    T = len(q)
+    start, unit = [], []
+    for t in range(T):
+        if not rle or t == 0 or k[t] != k[t - 1]:
+            start.append(t)
+        unit.append(len(start) - 1)
+    N = len(start)
+    C = [k[s] for s in start]
+    Q = [q[s] for s in start]
+
+    def best(u, qu):
+        b, arg = 0, -1
+        for e in range(u):
+            n = 0
+            while e - n >= 0 and u - n >= 0:
+                a = qu if n == 0 else Q[u - n]
+                if a != C[e - n]:
+                    break
+                n += 1
+            if n > 0 and n >= b:
+                b, arg = n, e
+        return b, arg
+
+    def dest(e, t):
+        if e < 0 or e + 1 >= N:
+            return -1
+        return start[e + 1] if start[e + 1] < t else -1
+
+    res = {f: [] for f in QK_FIELDS}
+    res["cf_tau"], res["cf_ridx"] = [], []
+    per_unit = [best(u, Q[u]) for u in range(N)]
+    cfu = [[[best(u, (Q[u] & ~(1 << j)) | (v << j))[1] for v in (0, 1)]
+            for j in range(M)] for u in range(N)]
+    for t in range(T):
+        u = unit[t]
+        ln, e = per_unit[u]
+        tt = dest(e, t)
+        res["tau"].append(tt)
+        res["end"].append(e)
+        res["len"].append(ln)
+        res["run_of"].append(u)
+        res["run_start"].append(start[t] if t < N else -1)
+        res["ridx"].append(e + 1 if tt >= 0 else -1)
+        res["cf_tau"].append([[dest(cfu[u][j][v], t) for v in (0, 1)]
+                              for j in range(M)])
+        res["cf_ridx"].append([[cfu[u][j][v] + 1 if dest(cfu[u][j][v], t) >= 0
+                                else -1 for v in (0, 1)] for j in range(M)])
+    return res

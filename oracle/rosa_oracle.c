@@ -303,3 +303,152 @@ int oracle_gather(const uint16_t *V, int64_t B, int64_t T, int64_t D, int M,
             }
     return 0;
 }
+
+/* ---------------------------------------------- query / key retrieval */
+
+/*
+ * oracle_match_qk -- Sec. 3.3 with a query stream q and a key stream k
+ * (k_{1:t} = a^(k), q_{1:t} = a^(q)), optionally with run-length folding of
+ * the key stream (Sec. 3.3, RLE paragraph; App. C.6) and with per-bit
+ * counterfactual destinations (App. C.5 and C.6; Sec. 4.2 step 3).
+ *
+ * Units.  Without folding, unit u is time u.  With folding, unit u is the
+ * u-th maximal run of equal adjacent key symbols; start[u] is its first
+ * time, its key symbol C[u] is the run's symbol and its query symbol Q[u]
+ * is q[start[u]] (the automaton and the matching state move only at run
+ * boundaries).  N = number of units.
+ *
+ * Retrieval at unit u.  The automaton holds C[0..u-1] (strictly earlier
+ * units); the matching state is advanced by Q[u].  The match is the longest
+ * suffix of Q[0..u] that occurs in C[0..u-1] (length L, in units, 0 if
+ * none) and e is the last unit at which it ends (the state's last end
+ * position).  Destination unit d = e + 1.  For every time t of unit u:
+ *   tau(t) = start[d]  if L >= 1, d < N and start[d] < t  (strictly from
+ *            the past, the range of Eq. (16)), else -1.
+ * Computed the textbook way (matching statistics on a suffix automaton):
+ * from (state s, length l), follow suffix links until a transition on the
+ * symbol exists, take it and add one, or fall to the root with l = 0; after
+ * the key symbol of unit u is appended, move s up the suffix links while
+ * the link's length is still >= l (a clone may have taken the matched
+ * string).
+ *
+ * Counterfactual (bit j < M, value v): the query symbol of unit u with bit j
+ * forced to v, one matching update from the same state; tau^(v) as above.
+ *
+ * Outputs, all [T] (per time step) unless noted, NULL to skip:
+ *   tau, end (e, in units; -1), len (L, in units);
+ *   run_of (unit of t), run_start ([T]: start[u] for u < N, then -1),
+ *   ridx (d where tau(t) >= 0, else -1);
+ *   cf_tau, cf_ridx ([T][M][2]: entry [t][j][v]).
+ * K must be 2^M when counterfactual outputs are asked for.
+ * Returns 0, -1 on bad arguments, -2 on a symbol >= K, -3 on allocation
+ * failure.
+ */
+static void qk_advance(const sam_t *a, int32_t *s, int32_t *l, int c)
+{
+    int K = a->K;
+    while (*s != 0 && a->next[(int64_t)*s * K + c] == -1) {
+        *s = a->link[*s];
+        *l = a->len[*s];
+    }
+    int32_t nx = a->next[(int64_t)*s * K + c];
+    if (nx != -1) {
+        *s = nx;
+        *l += 1;
+    } else {
+        *s = 0;
+        *l = 0;
+    }
+}
+
+static int32_t qk_dest_time(int32_t e, int64_t t, int64_t N,
+                            const int32_t *start)
+{
+    if (e < 0 || e + 1 >= N)
+        return -1;
+    return start[e + 1] < t ? start[e + 1] : -1;
+}
+
+int oracle_match_qk(const uint8_t *q, const uint8_t *k, int64_t T, int K,
+                    int M, int rle, int32_t *tau, int32_t *end, int32_t *len,
+                    int32_t *run_of, int32_t *run_start, int32_t *ridx,
+                    int32_t *cf_tau, int32_t *cf_ridx)
+{
+    if (T < 0 || K < 1 || K > 256 || M < 0 || M > 8)
+        return -1;
+    if ((cf_tau || cf_ridx) && (M < 1 || K != (1 << M)))
+        return -1;
+    for (int64_t t = 0; t < T; ++t)
+        if (q[t] >= K || k[t] >= K)
+            return -2;
+    if (T == 0)
+        return 0;
+    int32_t *start = (int32_t *)malloc(sizeof(int32_t) * T);
+    int32_t *unit = (int32_t *)malloc(sizeof(int32_t) * T);
+    int32_t *ue = (int32_t *)malloc(sizeof(int32_t) * T);
+    int32_t *ul = (int32_t *)malloc(sizeof(int32_t) * T);
+    int32_t *ucf = (int32_t *)malloc(sizeof(int32_t) * T * (M > 0 ? 2 * M : 1));
+    sam_t a;
+    if (!start || !unit || !ue || !ul || !ucf || sam_init(&a, T, K) != 0) {
+        free(start); free(unit); free(ue); free(ul); free(ucf);
+        return -3;
+    }
+    /* units */
+    int64_t N = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        if (!rle || t == 0 || k[t] != k[t - 1])
+            start[N++] = (int32_t)t;
+        unit[t] = (int32_t)(N - 1);
+    }
+    int want_cf = (cf_tau || cf_ridx) ? 1 : 0;
+    int32_t s = 0, l = 0;
+    for (int64_t u = 0; u < N; ++u) {
+        int Qu = q[start[u]];
+        if (want_cf)
+            for (int j = 0; j < M; ++j)
+                for (int v = 0; v < 2; ++v) {
+                    int c = (Qu & ~(1 << j)) | (v << j);
+                    int32_t s2 = s, l2 = l;
+                    qk_advance(&a, &s2, &l2, c);
+                    ucf[(u * M + j) * 2 + v] = l2 > 0 ? a.last[s2] : -1;
+                }
+        qk_advance(&a, &s, &l, Qu);
+        ul[u] = l;
+        ue[u] = l > 0 ? a.last[s] : -1;
+        int32_t cur = sam_extend(&a, k[start[u]]);
+        for (int32_t w = cur; w != -1; w = a.link[w])
+            a.last[w] = (int32_t)u;
+        while (s != 0 && a.len[a.link[s]] >= l)
+            s = a.link[s];
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        int32_t u = unit[t];
+        int32_t tt = qk_dest_time(ue[u], t, N, start);
+        if (tau)
+            tau[t] = tt;
+        if (end)
+            end[t] = ue[u];
+        if (len)
+            len[t] = ul[u];
+        if (run_of)
+            run_of[t] = u;
+        if (run_start)
+            run_start[t] = t < N ? start[t] : -1;
+        if (ridx)
+            ridx[t] = tt >= 0 ? ue[u] + 1 : -1;
+        if (want_cf)
+            for (int j = 0; j < M; ++j)
+                for (int v = 0; v < 2; ++v) {
+                    int32_t e = ucf[(u * M + j) * 2 + v];
+                    int32_t ct = qk_dest_time(e, t, N, start);
+                    int64_t o = (t * M + j) * 2 + v;
+                    if (cf_tau)
+                        cf_tau[o] = ct;
+                    if (cf_ridx)
+                        cf_ridx[o] = ct >= 0 ? e + 1 : -1;
+                }
+    }
+    sam_free(&a);
+    free(start); free(unit); free(ue); free(ul); free(ucf);
+    return 0;
+}
