@@ -11,8 +11,14 @@ stream), and the CPU oracle timed on the host as a reported baseline.  Every
 output of the timed run is compared with the oracle before the line is
 printed.
 
-    python bench.py [--steps K] [--warmup W] [--workload long|batched|repeat]
-                    [--no-cpu]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload long|batched|repeat|decode] [--no-cpu]
+
+The decode workload builds one automaton per stream over the long
+workload's 65,536-position prefix, then appends 1024 positions with one
+rosa_step each (extend + match + gather of the value row); it reports the
+per-step latency (HIP events around every step) and positions/s over the
+appended positions.
 """
 from __future__ import annotations
 
@@ -150,6 +156,127 @@ def oracle_run(w, threads):
     return wall, E, SYM, G
 
 
+# ------------------------------------------------------------------ decode
+
+DECODE_METRIC = ("decode positions/sec (512 streams, 65,536-position prefix, "
+                 "1024 appended positions, one rosa_step each)")
+# Compulsory bytes of one step for all 512 streams: the new hidden row
+# (2048 bf16), E and SYM out (6 B per stream), the gathered value slices
+# (8 B per stream read, 8 B written).
+DECODE_BYTES_PER_STEP = 2048 * 2 + 512 * (4 + 2) + 512 * (8 + 8)
+
+
+def run_decode(args):
+    import torch
+    from online_suffix_automaton_amd import rosa, synth
+    dev = torch.device("cuda:0")
+    _log("workload decode: generating")
+    pre = synth.long()
+    n = 1024
+    tail = synth.decode_tail(n)
+    H = np.concatenate([pre["H"], tail["H"]], axis=1)
+    V = np.concatenate([pre["V"], tail["V"]], axis=1)
+    T0 = pre["H"].shape[1]
+    Tc = T0 + n
+    S, M = 512, 4
+    Hd = torch.from_numpy(H.view(np.int16)).to(dev)
+    Vd = torch.from_numpy(V.view(np.int16)).to(dev)
+    buf = torch.empty(rosa.rosa_state_bytes(S, 1 << M, Tc), dtype=torch.uint8,
+                      device=dev)
+    # warm-up on a separate short automaton (same kernels, other buffer)
+    wbuf = torch.empty(rosa.rosa_state_bytes(S, 1 << M, 64), dtype=torch.uint8,
+                       device=dev)
+    we = torch.empty(S, dtype=torch.int32, device=dev)
+    wst = rosa.rosa_build(rosa.bf16_input(Hd[:, :32], M), 64, wbuf)
+    for i in range(min(args.warmup, 32)):
+        rosa.rosa_step(wst, rosa.bf16_input(Hd[:, 32 + i:33 + i], M), Vd, we)
+    torch.cuda.synchronize()
+    del wst, wbuf
+    _log("build over the prefix")
+    b0 = torch.cuda.Event(enable_timing=True)
+    b1 = torch.cuda.Event(enable_timing=True)
+    b0.record()
+    st = rosa.rosa_build(rosa.bf16_input(Hd[:, :T0], M), Tc, buf)
+    b1.record()
+    torch.cuda.synchronize()
+    build_ms = b0.elapsed_time(b1)
+    ends = torch.empty((n, S), dtype=torch.int32, device=dev)
+    syms = torch.empty((n, S), dtype=torch.int16, device=dev)
+    orows = torch.empty((n, 2048), dtype=torch.int16, device=dev)
+    rows = [rosa.bf16_input(Hd[:, T0 + i:T0 + i + 1], M) for i in range(n)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    _log(f"timing {n} steps")
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev[0].record()
+    for i in range(n):
+        rosa.rosa_step(st, rows[i], Vd, ends[i], syms[i], orows[i:i + 1])
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    step_ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
+    total_ms = ev[0].elapsed_time(ev[n])
+    if rosa.rosa_state_status(st) != rosa.ROSA_OK:
+        raise SystemExit("symbol range flag raised")
+    med = float(np.median(step_ms))
+    achieved = DECODE_BYTES_PER_STEP / (med / 1e3)
+    roof = {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK, "traffic": None}
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        _log("oracle over prefix + appended positions (parity + baseline)")
+        oracle._load()
+        threads = max(1, min(args.cpu_threads, os.cpu_count() or 1))
+        chunks = [c for c in np.array_split(np.arange(S), threads) if len(c)]
+
+        def work(c):
+            s0, s1 = int(c[0]), int(c[-1]) + 1
+            h = np.ascontiguousarray(H[:, :, s0 * M:s1 * M])
+            sym = oracle.discretize_bf16(h, M)
+            E, SYM, _ = oracle.match(sym, 1 << M)
+            return s0, s1, E, SYM
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+            res = list(ex.map(work, chunks))
+        cwall = time.perf_counter() - t0
+        Eo = np.empty((S, Tc), np.int32)
+        So = np.empty((S, Tc), np.int16)
+        for s0, s1, e, sy in res:
+            Eo[s0:s1], So[s0:s1] = e, sy
+        if not np.array_equal(ends.cpu().numpy(), Eo[:, T0:].T):
+            raise SystemExit("parity failure: decode E differs from the oracle")
+        if not np.array_equal(syms.cpu().numpy(), So[:, T0:].T):
+            raise SystemExit("parity failure: decode SYM differs from the oracle")
+        go = oracle.gather(V, Eo, M)[0, T0:]
+        if not np.array_equal(orows.cpu().numpy().view(np.uint16), go):
+            raise SystemExit("parity failure: decode gather differs")
+        _log(f"parity ok; oracle {cwall:.3f} s")
+        cpu = {"value": S * Tc / cwall, "unit": "positions/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{S} streams x {Tc} positions (prefix + appended), "
+                         f"discretize + automaton match, streams split over "
+                         f"{threads} threads"}
+    return {
+        "metric": DECODE_METRIC, "value": S * n / (total_ms / 1e3),
+        "unit": "positions/s", "n_gpus": 1, "steps": n, "warmup": args.warmup,
+        "ms_per_step": total_ms / n, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u8",
+        "data": "synthetic",
+        "config": {"workload": "decode: 512 streams (hidden [1,T,2048] bf16, "
+                               "M=4, K=16), prefix 65536, 1024 appended "
+                               "positions, step = extend + match + gather",
+                   "streams": S, "T": Tc, "K": 1 << M,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "step_latency_us": {"median": med * 1e3,
+                            "p99": float(np.percentile(step_ms, 99)) * 1e3,
+                            "host_wall_per_step": wall / n * 1e6},
+        "build_ms": build_ms,
+        "cpu_baseline": cpu,
+    }
+
+
 # -------------------------------------------------------------------- main
 
 def main():
@@ -158,7 +285,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long",
-                    choices=["long", "batched", "repeat"])
+                    choices=["long", "batched", "repeat", "decode"])
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the oracle baseline and parity check")
     ap.add_argument("--cpu-threads", type=int, default=16)
@@ -172,6 +299,10 @@ def main():
               "cross-GPU step and this build runs on a single MI355X; "
               "use --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "decode":
+        print(json.dumps(run_decode(args)), flush=True)
+        return
 
     import torch
     from online_suffix_automaton_amd import rosa
