@@ -114,6 +114,60 @@ rosa_status rosa_match_timed(const rosa_input *in, const rosa_out *out,
  * that used `ws` saw a symbol >= K, else ROSA_OK (or ROSA_ERR_HIP). */
 rosa_status rosa_match_status(const void *ws, hipStream_t stream);
 
+/* --------------------------------------------------- query / key retrieval */
+
+/* Flags of rosa_match_qk. */
+enum {
+    /* Fold the key stream into runs of equal adjacent symbols (Sec. 3.3, the
+     * run-length paragraph; App. C.6): the automaton and the matching state
+     * move once per run, at its first time step. */
+    ROSA_QK_RLE = 1
+};
+
+typedef struct rosa_qk_out {
+    int32_t *tau;       /* [S][T] destination time, -1 if none; required      */
+    int32_t *end;       /* [S][T] end unit e of the match, -1; may be NULL      */
+    int32_t *len;       /* [S][T] match length in units; may be NULL            */
+    int32_t *run_of;    /* [S][T] unit of each time step; may be NULL           */
+    int32_t *run_start; /* [S][T] first time of unit u (u < number of units),
+                           -1 for the remaining entries; may be NULL            */
+    int32_t *ridx;      /* [S][T] destination unit e+1 where tau >= 0, else -1;
+                           may be NULL                                          */
+    int32_t *cf_tau;    /* [S][T][M][2] counterfactual destinations; may be NULL */
+    int32_t *cf_ridx;   /* [S][T][M][2] their destination units; may be NULL    */
+} rosa_qk_out;
+
+/* Bytes of device workspace rosa_match_qk needs (0 on bad arguments). */
+size_t rosa_match_qk_workspace_bytes(int64_t S, int64_t T, int32_t K);
+
+/* Sec. 3.3 with a query stream q and a key stream k (k_{1:t} = a^(k),
+ * q_{1:t} = a^(q)), one suffix automaton per stream over the key units and
+ * one matching state advanced by the query units.
+ *   Units: time steps; with ROSA_QK_RLE the maximal runs of equal adjacent
+ *   key symbols, whose key symbol is the run's symbol and whose query
+ *   symbol is q at the run's first time step.
+ *   At unit u the match is the longest suffix of the query units 0..u that
+ *   occurs in the key units 0..u-1 (strictly earlier); e is the most recent
+ *   unit at which it ends.  For every time t of unit u,
+ *     tau(t) = first time of unit e+1  if a match exists and that time is
+ *              < t (the read position is strictly from the past, Eq. (16)),
+ *     tau(t) = -1 otherwise.
+ *   With q = k and no folding, end/len equal rosa_match's E/L.
+ *   Counterfactual tables (App. C.5, C.6; Sec. 4.2 step 3): entry [t][j][v]
+ *   is tau (or the destination unit) when bit j of the unit's query symbol
+ *   is forced to v and one matching update is made from the same state;
+ *   they need K = 2^M (bf16 inputs: M; symbols: K a power of two >= 2),
+ *   else ROSA_ERR_ARG.
+ * q and k: same kind and shape (S, T, K; B, D, M for bf16), each laid out
+ * as for rosa_match.  `ws`: at least rosa_match_qk_workspace_bytes(S, T, K)
+ * bytes, 256-byte aligned, not shared by calls in flight; its first 256
+ * bytes hold the symbol flag, so rosa_match_status(ws, stream) reports a
+ * symbol >= K in q or k.  The work is sequential per stream (one lane per
+ * stream walks its automaton in device memory). */
+rosa_status rosa_match_qk(const rosa_input *q, const rosa_input *k,
+                          int32_t flags, const rosa_qk_out *out, void *ws,
+                          size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------ value gather */
 
 /* App. C.4 read-out with the validity mask of Eq. (17):

@@ -43,6 +43,7 @@ hipError_t launch_sam_step(void *buf, int64_t S, int64_t K, int64_t Tcap,
                            int64_t R, int M, const uint16_t *V, int64_t ldv,
                            int64_t ldv_b, int32_t *end, int16_t *sym,
                            uint16_t *out_row, int64_t ldo_b, hipStream_t st);
+hipError_t launch_qk(QkParams p, hipStream_t st);
 }  // namespace rosa
 
 using namespace rosa;
@@ -245,6 +246,108 @@ rosa_status rosa_match_timed(const rosa_input *in, const rosa_out *out,
     if (!ev_begin || !ev_end)
         return ROSA_ERR_ARG;
     return match_impl(in, out, ws, ws_bytes, stream, ev_begin, ev_end);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Symbols of one input into padded rows (stride Tp, data at kPadFront).
+rosa_status prep_rows(const Shape &sh, const rosa_input *in, uint8_t *rows,
+                      int64_t Tp, int32_t *flags, hipStream_t stream)
+{
+    if (sh.kind == ROSA_IN_SYMBOLS) {
+        ROSA_TRY(launch_prep_symbols(reinterpret_cast<const uint8_t *>(in->data),
+                                     sh.ld, sh.S, sh.T, sh.K, rows, Tp, nullptr,
+                                     flags, stream));
+    } else {
+        ROSA_TRY(launch_discretize(reinterpret_cast<const uint16_t *>(in->data),
+                                   sh.B, sh.T, sh.D, sh.ld, sh.M, rows, Tp,
+                                   kPadFront, nullptr, stream));
+        ROSA_TRY(launch_pad_rows(rows, sh.S, Tp, sh.T, stream));
+    }
+    return ROSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t rosa_match_qk_workspace_bytes(int64_t S, int64_t T, int32_t K)
+{
+    if (S < 1 || T < 0 || T >= kMaxT || K < 1 || K > 256 ||
+        S * (T > 0 ? T : 1) >= kMaxST)
+        return 0;
+    return qk_layout(S, T, K).total;
+}
+
+rosa_status rosa_match_qk(const rosa_input *q, const rosa_input *k,
+                          int32_t flags, const rosa_qk_out *out, void *ws,
+                          size_t ws_bytes, hipStream_t stream)
+{
+    Shape sq, sk;
+    rosa_status st = resolve(q, &sq, true);
+    if (st != ROSA_OK)
+        return st;
+    st = resolve(k, &sk, true);
+    if (st != ROSA_OK)
+        return st;
+    if (sq.kind != sk.kind || sq.S != sk.S || sq.T != sk.T || sq.K != sk.K ||
+        sq.B != sk.B || sq.D != sk.D || sq.M != sk.M)
+        return ROSA_ERR_ARG;
+    if ((flags & ~ROSA_QK_RLE) != 0 || !out || (!out->tau && sq.T > 0) || !ws ||
+        (reinterpret_cast<uintptr_t>(ws) & 255) != 0)
+        return ROSA_ERR_ARG;
+    int M = sq.M;
+    if (sq.kind == ROSA_IN_SYMBOLS) {
+        M = 0;
+        while ((1 << M) < sq.K)
+            ++M;
+        if ((1 << M) != sq.K)
+            M = 0;
+    }
+    if ((out->cf_tau || out->cf_ridx) && M < 1)
+        return ROSA_ERR_ARG;
+    const QkLayout l = qk_layout(sq.S, sq.T, sq.K);
+    if (ws_bytes < l.total)
+        return ROSA_ERR_CAPACITY;
+    char *base = reinterpret_cast<char *>(ws);
+    int32_t *fl = reinterpret_cast<int32_t *>(base + l.flags);
+    ROSA_TRY(launch_clear_flags(fl, stream));
+    if (sq.T == 0)
+        return ROSA_OK;
+    uint8_t *qrows = reinterpret_cast<uint8_t *>(base + l.qrows);
+    uint8_t *krows = reinterpret_cast<uint8_t *>(base + l.krows);
+    st = prep_rows(sq, q, qrows, l.Tp, fl, stream);
+    if (st != ROSA_OK)
+        return st;
+    st = prep_rows(sk, k, krows, l.Tp, fl, stream);
+    if (st != ROSA_OK)
+        return st;
+    QkParams p;
+    memset(&p, 0, sizeof p);
+    p.q = qrows;
+    p.k = krows;
+    p.Tp = l.Tp;
+    p.S = sq.S;
+    p.T = sq.T;
+    p.Ncap = l.Ncap;
+    p.K = sq.K;
+    p.M = M;
+    p.rle = (flags & ROSA_QK_RLE) ? 1 : 0;
+    p.nodes = reinterpret_cast<int4 *>(base + l.nodes);
+    p.next = reinterpret_cast<int32_t *>(base + l.next);
+    p.start = reinterpret_cast<int32_t *>(base + l.start);
+    p.tau = out->tau;
+    p.end = out->end;
+    p.len = out->len;
+    p.run_of = out->run_of;
+    p.run_start = out->run_start;
+    p.ridx = out->ridx;
+    p.cf_tau = out->cf_tau;
+    p.cf_ridx = out->cf_ridx;
+    ROSA_TRY(launch_qk(p, stream));
+    return ROSA_OK;
 }
 
 rosa_status rosa_match_status(const void *ws, hipStream_t stream)

@@ -88,4 +88,39 @@ inline int choose_d(int64_t K, int64_t T)
     return d;
 }
 
+// Parameters of the query/key automaton kernel (rosa_sam.hip).
+struct QkParams {
+    const uint8_t *q, *k;   // padded rows: stream s at + s*Tp + kPadFront
+    int64_t Tp, S, T, Ncap;
+    int32_t K, M, rle, spw;
+    int4 *nodes;            // [S][Ncap] {len, link, last unit, 0}
+    int32_t *next;          // [S][Ncap][K]
+    int32_t *start;         // [S][T] start time of each unit
+    int32_t *tau, *end, *len, *run_of, *run_start, *ridx, *cf_tau, *cf_ridx;
+};
+
+
+// Workspace of rosa_match_qk: flags, padded query and key rows, unit starts,
+// the automaton nodes and dense transition rows.
+struct QkLayout {
+    size_t flags, qrows, krows, start, nodes, next, total;
+    int64_t Tp, Ncap;
+};
+
+inline QkLayout qk_layout(int64_t S, int64_t T, int64_t K)
+{
+    QkLayout l;
+    l.Tp = (int64_t)align_up((size_t)T + kPadFront + kPadBack, 256);
+    l.Ncap = T <= 1 ? 2 : 2 * T - 1;
+    size_t o = 0;
+    l.flags = o;  o += 256;
+    l.qrows = o;  o = align_up(o + (size_t)S * l.Tp, 256);
+    l.krows = o;  o = align_up(o + (size_t)S * l.Tp, 256);
+    l.start = o;  o = align_up(o + (size_t)S * T * 4, 256);
+    l.nodes = o;  o = align_up(o + (size_t)S * l.Ncap * 16, 256);
+    l.next = o;   o = align_up(o + (size_t)S * l.Ncap * K * 4, 256);
+    l.total = o;
+    return l;
+}
+
 }  // namespace rosa

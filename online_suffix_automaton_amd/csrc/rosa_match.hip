@@ -1000,46 +1000,96 @@ __global__ __launch_bounds__(kBigThreads) void big_kernel(MatchParams p)
 
 // ------------------------------------------------------ unpermute kernel
 //
-// Record mode: one workgroup per stream.  With the stream's symbol row in
-// LDS, the records are scattered into tau[t] = E+1 for one half of the time
-// axis at a time (LDS holds tau for 32768 positions), then E and
-// SYM = x[E+1] of that half are written in time order with coalesced
-// stores.
-constexpr int kTauHalf = 32768;
+// Record mode: one workgroup per stream.  The stream's records are read
+// once (coalesced) and scattered into tau[t] = E+1 in LDS (u16 for all of
+// the up to 65536 positions, 128 KiB); then E and SYM = x[E+1] are written
+// in time order with coalesced stores, the symbol read from the stream's
+// padded row (64 KiB per stream, served from cache).  Vec: T % 4 == 0 and
+// 16-byte aligned E / 8-byte aligned SYM rows, four positions per thread.
+constexpr int kTauMax = 65536;
 
+template <bool Vec>
 __global__ __launch_bounds__(kStreamThreads) void unpermute_kernel(MatchParams p)
 {
-    __shared__ __align__(16) unsigned char symrow[kLdsSymBytes];
-    __shared__ uint16_t tau[kTauHalf];
+    __shared__ __align__(16) uint16_t tau[kTauMax];
     const int s = blockIdx.x;
     const int tid = threadIdx.x, nt = blockDim.x;
     const int T = p.T;
     const uint32_t *rec = p.rec + (int64_t)s * T;
     int32_t *E = p.E + (int64_t)s * T;
     int16_t *SYM = p.SYM ? p.SYM + (int64_t)s * T : nullptr;
-    if (SYM) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(p.sym + (int64_t)s * p.Tp);
-        uint4 *dst = reinterpret_cast<uint4 *>(symrow);
-        for (int i = tid; i < (int)(p.Tp >> 4); i += nt)
-            dst[i] = src[i];
-    }
-    const uint8_t *x = symrow + kPadFront;
-    for (int h0 = 0; h0 < T; h0 += kTauHalf) {
-        const int h1 = min(T, h0 + kTauHalf);
+    // every record names a position t < T <= 65536 (16-bit field), so the
+    // scatter stays inside tau; tau <= T-1 for every record, the clamp
+    // below only keeps the symbol read inside the row
+    const uint8_t *x = p.sym + (int64_t)s * p.Tp + kPadFront;
+    if (Vec) {
+        // four 16-byte loads in flight per thread before the LDS scatter
+        const uint4 *r4 = reinterpret_cast<const uint4 *>(rec);
+        const int n4 = T >> 2;
+        for (int i0 = tid; i0 < n4; i0 += 4 * nt) {
+            uint4 r[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (i0 + u * nt < n4)
+                    r[u] = r4[i0 + u * nt];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (i0 + u * nt < n4) {
+                    tau[r[u].x >> 16] = (uint16_t)r[u].x;
+                    tau[r[u].y >> 16] = (uint16_t)r[u].y;
+                    tau[r[u].z >> 16] = (uint16_t)r[u].z;
+                    tau[r[u].w >> 16] = (uint16_t)r[u].w;
+                }
+        }
+    } else {
         for (int i = tid; i < T; i += nt) {
             const uint32_t r = rec[i];
-            const int t = (int)(r >> 16);
-            if (t >= h0 && t < h1)
-                tau[t - h0] = (uint16_t)(r & 0xFFFFu);
+            tau[r >> 16] = (uint16_t)r;
         }
-        __syncthreads();
-        for (int t = h0 + tid; t < h1; t += nt) {
-            const int e1 = tau[t - h0];
+    }
+    __syncthreads();
+    if (Vec) {
+        const uint2 *t4 = reinterpret_cast<const uint2 *>(tau);
+        int4 *E4 = reinterpret_cast<int4 *>(E);
+        uint2 *S4 = reinterpret_cast<uint2 *>(SYM);
+        // two groups of four positions per thread: eight symbol reads in
+        // flight
+        const int n4 = T >> 2;
+        for (int i0 = tid; i0 < n4; i0 += 2 * nt) {
+            uint32_t sv[2][4];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int i = i0 + u * nt;
+                if (i < n4) {
+                    const uint2 w = t4[i];
+                    const int a = (int)(w.x & 0xFFFFu), b = (int)(w.x >> 16);
+                    const int c = (int)(w.y & 0xFFFFu), d = (int)(w.y >> 16);
+                    E4[i] = make_int4(a - 1, b - 1, c - 1, d - 1);
+                    if (SYM) {
+                        sv[u][0] = a ? x[min(a, T - 1)] : 0xFFFFu;
+                        sv[u][1] = b ? x[min(b, T - 1)] : 0xFFFFu;
+                        sv[u][2] = c ? x[min(c, T - 1)] : 0xFFFFu;
+                        sv[u][3] = d ? x[min(d, T - 1)] : 0xFFFFu;
+                    }
+                }
+            }
+            if (SYM) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int i = i0 + u * nt;
+                    if (i < n4)
+                        S4[i] = make_uint2(sv[u][0] | (sv[u][1] << 16),
+                                           sv[u][2] | (sv[u][3] << 16));
+                }
+            }
+        }
+    } else {
+        for (int t = tid; t < T; t += nt) {
+            const int e1 = tau[t];
             E[t] = e1 - 1;
             if (SYM)
-                SYM[t] = e1 ? (int16_t)x[e1] : (int16_t)-1;
+                SYM[t] = e1 ? (int16_t)x[min(e1, T - 1)] : (int16_t)-1;
         }
-        __syncthreads();
     }
 }
 
@@ -1069,8 +1119,14 @@ hipError_t launch_unpermute(const MatchParams &p, int64_t S, hipStream_t st)
 {
     if (!stream_uses_records(p.T))
         return hipSuccess;
-    hipLaunchKernelGGL(unpermute_kernel, dim3((unsigned)S), dim3(kStreamThreads),
-                       0, st, p);
+    const bool vec = (p.T & 3) == 0 && ((uintptr_t)p.E & 15) == 0 &&
+                     ((uintptr_t)p.SYM & 7) == 0;
+    if (vec)
+        hipLaunchKernelGGL(unpermute_kernel<true>, dim3((unsigned)S),
+                           dim3(kStreamThreads), 0, st, p);
+    else
+        hipLaunchKernelGGL(unpermute_kernel<false>, dim3((unsigned)S),
+                           dim3(kStreamThreads), 0, st, p);
     return hipGetLastError();
 }
 

@@ -257,6 +257,128 @@ __global__ __launch_bounds__(64) void sam_step_kernel(
     }
 }
 
+// ------------------------------------------------- query / key retrieval
+//
+// Sec. 3.3 with separate streams: one automaton per stream over the key
+// units, one matching state (state, length) advanced by the query units.
+// Units are time steps, or with run folding the maximal runs of equal key
+// symbols (Sec. 3.3 RLE paragraph): the automaton and the matching state
+// move once per run, at its first time step, with the run's key symbol and
+// the query symbol at that time.  At unit u the automaton holds the key
+// units 0..u-1 (the query is matched before the key symbol of u is
+// appended), so the match is strictly earlier; its end unit e is the
+// matched state's last end position and the destination is the start time
+// of unit e+1, kept when it is before t (the range of Eq. (16)).  App. C.5:
+// for each query bit the branch with the bit flipped is one more matching
+// update from the same state (the branch with the bit as it is equals the
+// forward pass).
+//
+// The matching state is not re-normalised after an append that splits the
+// state it sits in: until the next append the split state and its clone
+// have identical transition rows, and the next query update leaves the
+// state through a transition or a suffix link, so both give the same
+// result.
+constexpr int kQkMaxM = 8;
+
+// One matching update by symbol c: follow suffix links until a transition
+// on c exists, take it (length + 1), or fall to the root (length 0).
+__device__ __forceinline__ void qk_advance(const SamStream &a, int &s, int &l,
+                                           int c)
+{
+    const int K = a.K;
+    for (;;) {
+        const int nx = a.nx[(int64_t)s * K + c];
+        if (nx != -1) {
+            s = nx;
+            ++l;
+            return;
+        }
+        if (s == 0) {
+            l = 0;
+            return;
+        }
+        s = a.nd[s].y;
+        l = a.nd[s].x;
+    }
+}
+
+__global__ __launch_bounds__(64) void qk_kernel(QkParams p)
+{
+    const int lane = threadIdx.x;
+    if (lane >= p.spw)
+        return;
+    const int64_t s = (int64_t)blockIdx.x * p.spw + lane;
+    if (s >= p.S)
+        return;
+    const int64_t T = p.T;
+    SamStream a;
+    a.nd = p.nodes + s * p.Ncap;
+    a.nx = p.next + s * p.Ncap * p.K;
+    a.K = p.K;
+    a.tail = 0;
+    a.nst = 0;
+    sam_new_state(a, 0);
+    const uint8_t *qr = p.q + s * p.Tp + kPadFront;
+    const uint8_t *kr = p.k + s * p.Tp + kPadFront;
+    int32_t *st = p.start + s * T;
+    const bool want_cf = p.cf_tau || p.cf_ridx;
+    int u = -1, ms = 0, ml = 0, ue = -1, ul = 0, dstart = -1, kprev = -1, qc = 0;
+    int cfe[kQkMaxM], cfs[kQkMaxM];
+    for (int64_t t = 0; t < T; ++t) {
+        const int kc = kr[t];
+        if (!p.rle || kc != kprev) {
+            ++u;
+            st[u] = (int32_t)t;
+            qc = qr[t];
+            if (want_cf) {
+                for (int j = 0; j < p.M; ++j) {
+                    int s2 = ms, l2 = ml;
+                    qk_advance(a, s2, l2, qc ^ (1 << j));
+                    cfe[j] = l2 > 0 ? a.nd[s2].z : -1;
+                    cfs[j] = cfe[j] >= 0 ? st[cfe[j] + 1] : -1;
+                }
+            }
+            qk_advance(a, ms, ml, qc);
+            ul = ml;
+            ue = ml > 0 ? a.nd[ms].z : -1;
+            dstart = ue >= 0 ? st[ue + 1] : -1;
+            const int cur = sam_extend(a, kc);
+            for (int w = cur; w != -1; w = a.nd[w].y)
+                a.nd[w].z = u;
+            kprev = kc;
+        }
+        const int64_t o = s * T + t;
+        const int tt = (ue >= 0 && dstart < t) ? dstart : -1;
+        p.tau[o] = tt;
+        if (p.end)
+            p.end[o] = ue;
+        if (p.len)
+            p.len[o] = ul;
+        if (p.run_of)
+            p.run_of[o] = u;
+        if (p.ridx)
+            p.ridx[o] = tt >= 0 ? ue + 1 : -1;
+        if (want_cf) {
+            for (int j = 0; j < p.M; ++j) {
+                const int b = (qc >> j) & 1;
+                const int ct = (cfe[j] >= 0 && cfs[j] < t) ? cfs[j] : -1;
+                const int64_t c0 = (o * p.M + j) * 2;
+                if (p.cf_tau) {
+                    p.cf_tau[c0 + b] = tt;
+                    p.cf_tau[c0 + 1 - b] = ct;
+                }
+                if (p.cf_ridx) {
+                    p.cf_ridx[c0 + b] = tt >= 0 ? ue + 1 : -1;
+                    p.cf_ridx[c0 + 1 - b] = ct >= 0 ? cfe[j] + 1 : -1;
+                }
+            }
+        }
+    }
+    if (p.run_start)
+        for (int64_t v = 0; v < T; ++v)
+            p.run_start[s * T + v] = v <= u ? st[v] : -1;
+}
+
 // --------------------------------------------------------------- launchers
 
 SamView sam_view(void *buf, int64_t S, int64_t K, int64_t Tcap)
@@ -331,6 +453,16 @@ hipError_t launch_sam_step(void *buf, int64_t S, int64_t K, int64_t Tcap,
     hipLaunchKernelGGL(sam_step_kernel, grid, dim3(64), 0, st, v, S, t, spw,
                        kind, row, ld, R, M, V, ldv, ldv_b, end, sym, out_row,
                        ldo_b);
+    return hipGetLastError();
+}
+
+constexpr int kQkStreamsPerWave = 1;
+
+hipError_t launch_qk(QkParams p, hipStream_t st)
+{
+    p.spw = kQkStreamsPerWave;
+    dim3 grid((unsigned)((p.S + p.spw - 1) / p.spw));
+    hipLaunchKernelGGL(qk_kernel, grid, dim3(64), 0, st, p);
     return hipGetLastError();
 }
 

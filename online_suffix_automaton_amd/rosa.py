@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "librosa.so")
 ROSA_OK, ROSA_ERR_ARG, ROSA_ERR_CAPACITY, ROSA_ERR_SYMBOL, ROSA_ERR_HIP, \
     ROSA_ERR_STATE = range(6)
 ROSA_IN_SYMBOLS, ROSA_IN_BF16 = 0, 1
+ROSA_QK_RLE = 1
 
 
 class RosaError(RuntimeError):
@@ -40,9 +41,16 @@ class rosa_out(ctypes.Structure):
                 ("len", ctypes.c_void_p), ("symbols", ctypes.c_void_p)]
 
 
+class rosa_qk_out(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("tau", "end", "len", "run_of", "run_start", "ridx", "cf_tau",
+                 "cf_ridx")]
+
+
 _lib = None
 _SYMBOLS = ["rosa_match_workspace_bytes", "rosa_match", "rosa_match_timed",
-            "rosa_match_status",
+            "rosa_match_status", "rosa_match_qk_workspace_bytes",
+            "rosa_match_qk",
             "rosa_gather", "rosa_state_bytes", "rosa_build", "rosa_step",
             "rosa_state_length", "rosa_state_status", "rosa_free",
             "rosa_error_string"]
@@ -64,6 +72,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "rosa_match": ([P, P, P, SZ, P], ctypes.c_int),
         "rosa_match_timed": ([P, P, P, SZ, P, P, P], ctypes.c_int),
         "rosa_match_status": ([P, P], ctypes.c_int),
+        "rosa_match_qk_workspace_bytes": ([I64, I64, I32], SZ),
+        "rosa_match_qk": ([P, P, I32, P, P, SZ, P], ctypes.c_int),
         "rosa_gather": ([P, I64, I64, I64, I64, I32, P, P, I64, P], ctypes.c_int),
         "rosa_state_bytes": ([I64, I32, I64], SZ),
         "rosa_build": ([P, I64, P, SZ, ctypes.POINTER(P), P, P], ctypes.c_int),
@@ -177,6 +187,32 @@ def rosa_match_timed(inp: rosa_input, out: rosa_out, ws: torch.Tensor,
         "rosa_match_timed")
 
 
+def rosa_match_qk_workspace_bytes(S: int, T: int, K: int) -> int:
+    return int(load_library().rosa_match_qk_workspace_bytes(S, T, K))
+
+
+def make_qk_out(tau, **opt) -> rosa_qk_out:
+    """tau: int32 [S, T]; optional end, len, run_of, run_start, ridx (int32
+    [S, T]) and cf_tau, cf_ridx (int32 [S, T, M, 2])."""
+    _require_device(tau, *opt.values())
+    o = rosa_qk_out()
+    o.tau = _ptr(tau)
+    for name, t in opt.items():
+        if name not in dict(rosa_qk_out._fields_):
+            raise ValueError(f"unknown output {name}")
+        setattr(o, name, _ptr(t))
+    return o
+
+
+def rosa_match_qk(q: rosa_input, k: rosa_input, flags: int, out: rosa_qk_out,
+                  ws: torch.Tensor, stream=None) -> None:
+    _require_device(ws)
+    _check(load_library().rosa_match_qk(
+        ctypes.byref(q), ctypes.byref(k), flags, ctypes.byref(out),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)),
+        "rosa_match_qk")
+
+
 def rosa_match_status(ws: torch.Tensor, stream=None) -> int:
     return int(load_library().rosa_match_status(ws.data_ptr(), _stream(stream)))
 
@@ -279,3 +315,32 @@ def match(x: torch.Tensor, *, K: int | None = None, M: int | None = None,
                          device=dev)
     rosa_match(inp, make_out(E, SYM, L, syms), ws, stream)
     return E, SYM, L, syms
+
+
+def match_qk(q: torch.Tensor, k: torch.Tensor, *, K: int | None = None,
+             M: int | None = None, rle: bool = False, cf: bool = False,
+             ws=None, stream=None):
+    """Allocate outputs (and workspace unless given) and run rosa_match_qk.
+    q, k: uint8 symbols [S, T] with K, or bf16 [B, T, D] with M.  Returns a
+    dict of int32 tensors: tau, end, len, run_of, run_start, ridx [S, T] and,
+    with cf, cf_tau and cf_ridx [S, T, M, 2]."""
+    if q.dtype == torch.uint8:
+        qi, ki = symbols_input(q, K), symbols_input(k, K)
+        S, T, Kk = q.shape[0], q.shape[1], K
+        Mm = max(1, (K - 1).bit_length())
+    else:
+        qi, ki = bf16_input(q, M), bf16_input(k, M)
+        B, T, D = q.shape
+        S, Kk, Mm = B * (D // M), 1 << M, M
+    dev = q.device
+    res = {n: torch.empty((S, T), dtype=torch.int32, device=dev)
+           for n in ("tau", "end", "len", "run_of", "run_start", "ridx")}
+    if cf:
+        res["cf_tau"] = torch.empty((S, T, Mm, 2), dtype=torch.int32, device=dev)
+        res["cf_ridx"] = torch.empty((S, T, Mm, 2), dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = torch.empty(rosa_match_qk_workspace_bytes(S, T, Kk),
+                         dtype=torch.uint8, device=dev)
+    out = make_qk_out(res["tau"], **{n: v for n, v in res.items() if n != "tau"})
+    rosa_match_qk(qi, ki, ROSA_QK_RLE if rle else 0, out, ws, stream)
+    return res

@@ -128,3 +128,32 @@ def test_state_api_rejects_bad_handles_and_args():
     assert lib.rosa_build(ctypes.byref(inp2), 200, 0x100000, 64,
                           ctypes.byref(h), None, None) == rosa.ROSA_ERR_CAPACITY
     assert not h.value
+
+
+def test_match_qk_rejects_bad_arguments():
+    lib = rosa.load_library()
+    f = lib.rosa_match_qk
+    assert rosa.rosa_match_qk_workspace_bytes(0, 10, 2) == 0
+    assert rosa.rosa_match_qk_workspace_bytes(4, 100, 16) > 0
+    q, k = _inp(), _inp()
+    out = rosa.rosa_qk_out()
+    out.tau = FAKE.value
+    big = 1 << 40
+    ws = 0x100000
+
+    def call(q_, k_, flags=0, o=out, w=ws, nb=big):
+        return f(ctypes.byref(q_), ctypes.byref(k_), flags,
+                 ctypes.byref(o) if o is not None else None, w, nb, None)
+    assert call(q, _inp(T=99)) == rosa.ROSA_ERR_ARG          # T differs
+    assert call(q, _inp(S=3)) == rosa.ROSA_ERR_ARG           # S differs
+    assert call(q, _inp(K=8)) == rosa.ROSA_ERR_ARG           # K differs
+    assert call(q, k, flags=2) == rosa.ROSA_ERR_ARG          # unknown flag
+    assert call(q, k, o=None) == rosa.ROSA_ERR_ARG
+    assert call(q, k, o=rosa.rosa_qk_out()) == rosa.ROSA_ERR_ARG   # no tau
+    assert call(q, k, w=0x100010) == rosa.ROSA_ERR_ARG       # misaligned
+    assert call(q, k, nb=64) == rosa.ROSA_ERR_CAPACITY
+    # counterfactual tables need K = 2^M
+    o2 = rosa.rosa_qk_out()
+    o2.tau, o2.cf_tau = FAKE.value, FAKE.value
+    assert call(_inp(K=3), _inp(K=3), o=o2) == rosa.ROSA_ERR_ARG
+    assert call(_inp(K=1), _inp(K=1), o=o2) == rosa.ROSA_ERR_ARG
