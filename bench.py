@@ -277,6 +277,96 @@ def run_decode(args):
     }
 
 
+# ---------------------------------------------------------------------- qk
+
+def run_qk(args):
+    """Query/key retrieval on the batched shape: separate query and key
+    hidden states [8, 4096, 256] bf16, M = 4 (512 streams, K = 16)."""
+    import torch
+    from online_suffix_automaton_amd import rosa, synth
+    dev = torch.device("cuda:0")
+    B, T, D, M = 8, 4096, 256, 4
+    S, K = B * (D // M), 1 << M
+    _log("workload qk: generating")
+    Hq = synth.bf16_normal((B, T, D), 31)
+    Hk = synth.bf16_normal((B, T, D), 32)
+    dq = torch.from_numpy(Hq.view(np.int16)).to(dev)
+    dk = torch.from_numpy(Hk.view(np.int16)).to(dev)
+    qi, ki = rosa.bf16_input(dq, M), rosa.bf16_input(dk, M)
+    res = {n: torch.empty((S, T), dtype=torch.int32, device=dev)
+           for n in ("tau", "end", "len", "run_of", "run_start", "ridx")}
+    if args.cf:
+        res["cf_tau"] = torch.empty((S, T, M, 2), dtype=torch.int32, device=dev)
+        res["cf_ridx"] = torch.empty((S, T, M, 2), dtype=torch.int32, device=dev)
+    out = rosa.make_qk_out(res["tau"], **{n: v for n, v in res.items()
+                                          if n != "tau"})
+    ws = torch.empty(rosa.rosa_match_qk_workspace_bytes(S, T, K),
+                     dtype=torch.uint8, device=dev)
+    flags = rosa.ROSA_QK_RLE if args.rle else 0
+    for _ in range(args.warmup):
+        rosa.rosa_match_qk(qi, ki, flags, out, ws)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    steps = max(1, min(args.steps, 5))
+    _log(f"timing {steps} steps")
+    e0.record()
+    for _ in range(steps):
+        rosa.rosa_match_qk(qi, ki, flags, out, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # compulsory bytes per stream-position: query and key rows (4 bf16
+    # each), the six int32 outputs, and 2M int32 x 2 tables with --cf
+    bpp = 8 + 8 + 6 * 4 + (2 * M * 2 * 4 if args.cf else 0)
+    achieved = bpp * S * T / (ms / 1e3)
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        oracle._load()
+        _log("oracle (parity + baseline)")
+        q = oracle.discretize_bf16(Hq, M)
+        k = oracle.discretize_bf16(Hk, M)
+        threads = max(1, min(args.cpu_threads, os.cpu_count() or 1))
+        chunks = [c for c in np.array_split(np.arange(S), threads) if len(c)]
+
+        def work(c):
+            return int(c[0]), oracle.match_qk(q[c[0]:c[-1] + 1],
+                                               k[c[0]:c[-1] + 1], K, M,
+                                               args.rle, cf=args.cf)
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+            parts = list(ex.map(work, chunks))
+        wall = time.perf_counter() - t0
+        for name, g in res.items():
+            want = np.concatenate([pt[name] for _, pt in sorted(parts, key=lambda z: z[0])])
+            if not np.array_equal(g.cpu().numpy(), want):
+                raise SystemExit(f"parity failure: qk {name} differs")
+        _log(f"parity ok; oracle {wall:.3f} s")
+        cpu = {"value": S * T / wall, "unit": "positions/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"whole workload ({S} streams x {T}), query/key "
+                         f"match{' with folding' if args.rle else ''}"
+                         f"{' and counterfactual tables' if args.cf else ''}, "
+                         f"streams split over {threads} threads"}
+    return {
+        "metric": "query/key matched positions/sec (512 streams x 4096)",
+        "value": S * T / (ms / 1e3), "unit": "positions/s", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u8", "data": "synthetic",
+        "config": {"workload": "qk: query and key hidden states [8,4096,256] "
+                               "bf16 N(0,1) (seeds 31, 32), M=4 -> 512 streams, "
+                               "K=16" + (", key runs folded" if args.rle else "")
+                               + (", counterfactual tables" if args.cf else ""),
+                   "streams": S, "T": T, "K": K, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved / 1e9,
+                     "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK, "traffic": None},
+        "cpu_baseline": cpu,
+    }
+
+
 # -------------------------------------------------------------------- main
 
 def main():
@@ -285,7 +375,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long",
-                    choices=["long", "batched", "repeat", "decode"])
+                    choices=["long", "batched", "repeat", "decode", "qk"])
+    ap.add_argument("--rle", action="store_true",
+                    help="qk workload: fold the key stream into runs")
+    ap.add_argument("--cf", action="store_true",
+                    help="qk workload: also the per-bit counterfactual tables")
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the oracle baseline and parity check")
     ap.add_argument("--cpu-threads", type=int, default=16)
@@ -302,6 +396,9 @@ def main():
 
     if args.workload == "decode":
         print(json.dumps(run_decode(args)), flush=True)
+        return
+    if args.workload == "qk":
+        print(json.dumps(run_qk(args)), flush=True)
         return
 
     import torch
