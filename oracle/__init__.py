@@ -22,6 +22,9 @@ All functions take and return numpy arrays on the host:
     (Sec. 3.3; App. C.5, C.6; Sec. 4.2 step 3)
   * ``brute_qk_py(q [T], k [T], K, M, rle) -> dict``  the same definition by
     direct search, for tiny streams (pins ``match_qk``)
+  * ``scatter_grad(theta f32 [B,T,D], E [S,T], M) -> G f32 [B,T,D]``  the
+    transpose of ``gather`` (App. C.4), summed over t in increasing order in
+    double precision
 """
 from __future__ import annotations
 
@@ -64,9 +67,11 @@ def _load():
     lib.oracle_brute.argtypes = [P, I64, P, P]
     lib.oracle_gather.argtypes = [P, I64, I64, I64, I, P, P]
     lib.oracle_match_qk.argtypes = [P, P, I64, I, I, I] + [P] * 8
+    lib.oracle_scatter_grad.argtypes = [P, I64, I64, I64, I, P, P]
     for f in (lib.oracle_discretize_bf16, lib.oracle_match,
               lib.oracle_match_streams, lib.oracle_sam_stats,
-              lib.oracle_brute, lib.oracle_gather, lib.oracle_match_qk):
+              lib.oracle_brute, lib.oracle_gather, lib.oracle_match_qk,
+              lib.oracle_scatter_grad):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -270,3 +275,16 @@ def brute_qk_py(q, k, K: int, M: int = 0, rle: bool = False):
         res["cf_ridx"].append([[cfu[u][j][v] + 1 if dest(cfu[u][j][v], t) >= 0
                                 else -1 for v in (0, 1)] for j in range(M)])
     return res
+
+
+def scatter_grad(theta: np.ndarray, E: np.ndarray, M: int) -> np.ndarray:
+    """App. C.4: G[b, tau, c] = sum_t theta[b, t, c] * [E[s, t] + 1 == tau]
+    (s = b*R + c // M; E < 0 adds nothing), the transpose of ``gather``.
+    theta: float32 [B, T, D]."""
+    theta = np.ascontiguousarray(theta, dtype=np.float32)
+    B, T, D = theta.shape
+    E = np.ascontiguousarray(E, dtype=np.int32)
+    G = np.empty_like(theta)
+    _check(_load().oracle_scatter_grad(_ptr(theta), B, T, D, M, _ptr(E),
+                                       _ptr(G)), "scatter_grad")
+    return G

@@ -452,3 +452,40 @@ int oracle_match_qk(const uint8_t *q, const uint8_t *k, int64_t T, int K,
     free(start); free(unit); free(ue); free(ul); free(ucf);
     return 0;
 }
+
+/* ---------------------------------------------- destination scatter (grad) */
+
+/* App. C.4 (destination-scatter aggregation) and the gradient of the values
+ * in Sec. 3: the value read at destination tau collects the upstream
+ * gradient of every time step that read it,
+ *   G[b][tau][c] = sum over t = 0..T-1 of theta[b][t][c] * I[tau(b,r(c),t) = tau],
+ * the transpose of oracle_gather.  Here tau(s,t) = E[s][t] + 1 for
+ * E[s][t] >= 0 (and E+1 < T); other entries read nothing and add nothing.
+ * theta, G: float [B][T][D]; E: [S][T], S = B*D/M, s = b*R + r, channel
+ * c = r*M + m.  The sum runs over t in increasing order in double precision
+ * and is rounded to float once. */
+int oracle_scatter_grad(const float *theta, int64_t B, int64_t T, int64_t D,
+                        int M, const int32_t *E, float *G)
+{
+    if (M < 1 || M > 8 || D % M != 0 || B < 0 || T < 0)
+        return -1;
+    int64_t R = D / M;
+    double *acc = (double *)calloc((size_t)(B * T * D > 0 ? B * T * D : 1),
+                                   sizeof(double));
+    if (!acc)
+        return -3;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t r = 0; r < R; ++r)
+            for (int64_t t = 0; t < T; ++t) {
+                int64_t e = E[(b * R + r) * T + t];
+                if (e < 0 || e + 1 >= T)
+                    continue;
+                for (int m = 0; m < M; ++m)
+                    acc[(b * T + (e + 1)) * D + r * M + m] +=
+                        (double)theta[(b * T + t) * D + r * M + m];
+            }
+    for (int64_t i = 0; i < B * T * D; ++i)
+        G[i] = (float)acc[i];
+    free(acc);
+    return 0;
+}
