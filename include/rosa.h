@@ -180,6 +180,30 @@ rosa_status rosa_gather(const uint16_t *V, int64_t B, int64_t T, int64_t D,
                         int64_t ldv, int32_t M, const int32_t *end,
                         uint16_t *out, int64_t ldo, hipStream_t stream);
 
+/* ---------------------------------------- destination scatter (gradient) */
+
+/* Bytes of device workspace rosa_scatter_grad needs for S = B*D/M streams of
+ * T positions (0 on bad arguments). */
+size_t rosa_scatter_grad_workspace_bytes(int64_t S, int64_t T);
+
+/* App. C.4 (destination-scatter aggregation), the transpose of rosa_gather:
+ *   G[b][tau][r*M+m] = sum over t of theta[b][t][r*M+m] * I[E[s][t]+1 == tau]
+ * for s = b*R + r, m < M; rows no time step points at get 0.  Entries with
+ * E < 0 or E+1 >= T add nothing.  theta, G: float [B][T][ldt] / [B][T][ldg]
+ * (ld >= D, in elements); E: int32 [S][T] (rosa_match's `end`; for
+ * rosa_match_qk pass tau - 1).  The sum over t runs in increasing t in
+ * double precision and is rounded to float once: the result is
+ * deterministic and independent of launch geometry.  Cost: a counting sort
+ * of the time steps by destination per stream, then one thread per
+ * (row, route) walking its few time steps in order; a destination with more
+ * than 64 time steps is summed by one wave scanning the stream's E row.
+ * `ws`: rosa_scatter_grad_workspace_bytes(B*D/M, T) bytes, 256-byte aligned,
+ * not shared by calls in flight.  G must not overlap theta. */
+rosa_status rosa_scatter_grad(const float *theta, int64_t B, int64_t T,
+                              int64_t D, int64_t ldt, int32_t M,
+                              const int32_t *end, float *G, int64_t ldg,
+                              void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------ online automaton (decode) */
 
 typedef struct rosa_state rosa_state;   /* opaque host handle */

@@ -44,6 +44,8 @@ hipError_t launch_sam_step(void *buf, int64_t S, int64_t K, int64_t Tcap,
                            int64_t ldv_b, int32_t *end, int16_t *sym,
                            uint16_t *out_row, int64_t ldo_b, hipStream_t st);
 hipError_t launch_qk(QkParams p, hipStream_t st);
+// rosa_scatter.hip
+hipError_t launch_scatter(const ScatterParams &p, hipStream_t st);
 }  // namespace rosa
 
 using namespace rosa;
@@ -347,6 +349,52 @@ rosa_status rosa_match_qk(const rosa_input *q, const rosa_input *k,
     p.cf_tau = out->cf_tau;
     p.cf_ridx = out->cf_ridx;
     ROSA_TRY(launch_qk(p, stream));
+    return ROSA_OK;
+}
+
+size_t rosa_scatter_grad_workspace_bytes(int64_t S, int64_t T)
+{
+    if (S < 1 || T < 0 || T >= kMaxT || S * (T > 0 ? T : 1) >= kMaxST)
+        return 0;
+    return scatter_layout(S, T).total;
+}
+
+rosa_status rosa_scatter_grad(const float *theta, int64_t B, int64_t T,
+                              int64_t D, int64_t ldt, int32_t M,
+                              const int32_t *end, float *G, int64_t ldg,
+                              void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (B < 1 || T < 0 || T >= kMaxT || M < 1 || M > 8 || D < M || D % M != 0 ||
+        ldt < D || ldg < D || B * (D / M) * (T > 0 ? T : 1) >= kMaxST)
+        return ROSA_ERR_ARG;
+    if (T == 0)
+        return ROSA_OK;
+    if (!theta || !end || !G || !ws || (reinterpret_cast<uintptr_t>(ws) & 255) != 0)
+        return ROSA_ERR_ARG;
+    const int64_t S = B * (D / M);
+    const ScatterLayout l = scatter_layout(S, T);
+    if (ws_bytes < l.total)
+        return ROSA_ERR_CAPACITY;
+    char *base = reinterpret_cast<char *>(ws);
+    ScatterParams p;
+    memset(&p, 0, sizeof p);
+    p.theta = theta;
+    p.G = G;
+    p.end = end;
+    p.ldt = ldt;
+    p.ldg = ldg;
+    p.B = B;
+    p.T = T;
+    p.D = D;
+    p.R = D / M;
+    p.Tq = l.Tq;
+    p.big_cap = l.big_cap;
+    p.M = M;
+    p.cnt = reinterpret_cast<int32_t *>(base + l.cnt);
+    p.off = reinterpret_cast<int32_t *>(base + l.off);
+    p.list = reinterpret_cast<int32_t *>(base + l.list);
+    p.big = reinterpret_cast<int32_t *>(base + l.big);
+    ROSA_TRY(launch_scatter(p, stream));
     return ROSA_OK;
 }
 

@@ -123,4 +123,36 @@ inline QkLayout qk_layout(int64_t S, int64_t T, int64_t K)
     return l;
 }
 
+// Parameters of the destination-scatter kernels (rosa_scatter.hip).
+struct ScatterParams {
+    const float *theta;     // [B][T][ldt]
+    float *G;               // [B][T][ldg]
+    const int32_t *end;     // [S][T], destination E+1 where E >= 0
+    int64_t ldt, ldg, B, T, D, R, Tq, big_cap;
+    int32_t M;
+    int32_t *cnt;           // [S][T] counts, then fill cursors
+    int32_t *off;           // [S][Tq] exclusive prefix, Tq = T + 1
+    int32_t *list;          // [S][T] time steps grouped by destination
+    int32_t *big;           // [0]: count; entries from +64: {s, tau}
+};
+
+struct ScatterLayout {
+    size_t cnt, off, list, big, total;
+    int64_t Tq, big_cap;
+};
+
+inline ScatterLayout scatter_layout(int64_t S, int64_t T)
+{
+    ScatterLayout l;
+    l.Tq = T + 1;
+    l.big_cap = S * (T / 65 + 1);
+    size_t o = 0;
+    l.cnt = o;   o = align_up(o + (size_t)S * T * 4, 256);
+    l.off = o;   o = align_up(o + (size_t)S * l.Tq * 4, 256);
+    l.list = o;  o = align_up(o + (size_t)S * T * 4, 256);
+    l.big = o;   o = align_up(o + 256 + (size_t)l.big_cap * 8, 256);
+    l.total = o;
+    return l;
+}
+
 }  // namespace rosa

@@ -1,0 +1,233 @@
+// rosa_scatter.hip -- destination-scatter gradient: the transpose of the
+// value gather.
+//
+// Method: "ROSA-Tuning: Enhancing Long-Context Modeling via Suffix Matching"
+// (arXiv 2602.02499), App. C.4 (destination-scatter aggregation) and the
+// value gradient of Sec. 3: the value read at destination tau receives the
+// sum of the upstream gradient theta of every time step t whose destination
+// is tau, channel by channel within the route:
+//   G[b][tau][r*M+m] = sum_t theta[b][t][r*M+m] * I[E[s][t] + 1 == tau],
+// s = b*R + r.  The sum runs over t in increasing order in double precision
+// and is rounded to float once, so the result is deterministic and does not
+// depend on the launch geometry.
+//
+// Per stream, a counting sort groups the time steps by destination:
+//   count   cnt[s][tau]        (integer atomics: order-free)
+//   scan    off[s][tau]        (exclusive prefix, one workgroup per stream)
+//   fill    list[s][off + i]   (unordered inside a destination)
+//   sum     one thread per (b, tau, route): walks its time steps in
+//           increasing order (selection over the few entries a destination
+//           has) and writes the route's M values of row tau; rows are
+//           written route-contiguous, so the stores are coalesced.
+// A destination with more than kSelectMax time steps is handed to a wave
+// that visits the stream's time steps in order (ballot over 64 at a time).
+#include "rosa_internal.h"
+
+namespace rosa {
+
+constexpr int kSelectMax = 64;
+
+__global__ void scatter_zero_kernel(int32_t *__restrict__ p, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+__global__ void scatter_count_kernel(ScatterParams p)
+{
+    const int64_t s = blockIdx.y;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= p.T)
+        return;
+    const int64_t e = p.end[s * p.T + t];
+    if (e >= 0 && e + 1 < p.T)
+        atomicAdd(&p.cnt[s * p.T + e + 1], 1);
+}
+
+__device__ __forceinline__ int sc_wave_incl_scan(int v)
+{
+    const int lane = __lane_id();
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(v, d);
+        if (lane >= d)
+            v += o;
+    }
+    return v;
+}
+
+// Exclusive prefix of cnt[s][0..T) into off[s][0..T]; cnt is cleared for
+// its second use as the fill cursor.
+__global__ __launch_bounds__(1024) void scatter_scan_kernel(ScatterParams p)
+{
+    __shared__ int wsum[16];
+    __shared__ int carry_s;
+    const int64_t s = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    int32_t *cnt = p.cnt + s * p.T;
+    int32_t *off = p.off + s * p.Tq;
+    if (tid == 0)
+        carry_s = 0;
+    __syncthreads();
+    for (int64_t c0 = 0; c0 < p.T; c0 += 4096) {
+        int v[4], sum = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t i = c0 + 4 * tid + u;
+            v[u] = i < p.T ? cnt[i] : 0;
+            sum += v[u];
+        }
+        const int incl = sc_wave_incl_scan(sum);
+        if (lane == 63)
+            wsum[wid] = incl;
+        __syncthreads();
+        if (wid == 0) {
+            const int w = lane < 16 ? wsum[lane] : 0;
+            const int wi = sc_wave_incl_scan(w);
+            if (lane < 16)
+                wsum[lane] = wi - w;
+        }
+        __syncthreads();
+        int run = carry_s + wsum[wid] + incl - sum;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t i = c0 + 4 * tid + u;
+            if (i < p.T) {
+                off[i] = run;
+                cnt[i] = 0;
+            }
+            run += v[u];
+        }
+        __syncthreads();
+        if (tid == 1023)
+            carry_s = run;
+        __syncthreads();
+    }
+    if (tid == 0)
+        off[p.T] = carry_s;
+}
+
+__global__ void scatter_fill_kernel(ScatterParams p)
+{
+    const int64_t s = blockIdx.y;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= p.T)
+        return;
+    const int64_t e = p.end[s * p.T + t];
+    if (e >= 0 && e + 1 < p.T) {
+        const int slot = p.off[s * p.Tq + e + 1] + atomicAdd(&p.cnt[s * p.T + e + 1], 1);
+        p.list[s * p.T + slot] = (int32_t)t;
+    }
+}
+
+// 256 threads: 4 destination rows x 64 routes; grid (rows/4, routes/64, B).
+template <int MC>
+__global__ __launch_bounds__(256) void scatter_sum_kernel(ScatterParams p)
+{
+    const int tid = threadIdx.x;
+    const int64_t r = (int64_t)blockIdx.y * 64 + (tid & 63);
+    const int64_t tau = (int64_t)blockIdx.x * 4 + (tid >> 6);
+    const int64_t b = blockIdx.z;
+    if (r >= p.R || tau >= p.T)
+        return;
+    const int64_t s = b * p.R + r;
+    const int o0 = p.off[s * p.Tq + tau], o1 = p.off[s * p.Tq + tau + 1];
+    const int n = o1 - o0;
+    float *g = p.G + (b * p.T + tau) * p.ldg + r * MC;
+    if (n > kSelectMax) {
+        const int idx = atomicAdd(&p.big[0], 1);
+        if (idx < p.big_cap) {
+            p.big[64 + 2 * (int64_t)idx] = (int32_t)s;
+            p.big[64 + 2 * (int64_t)idx + 1] = (int32_t)tau;
+        }
+        return;
+    }
+    double acc[MC];
+#pragma unroll
+    for (int m = 0; m < MC; ++m)
+        acc[m] = 0.0;
+    const int32_t *lst = p.list + s * p.T;
+    int prev = -1;
+    for (int k = 0; k < n; ++k) {
+        int tmin = 0x7FFFFFFF;
+        for (int i = o0; i < o1; ++i) {
+            const int t = lst[i];
+            if (t > prev && t < tmin)
+                tmin = t;
+        }
+        prev = tmin;
+        const float *th = p.theta + (b * p.T + tmin) * p.ldt + r * MC;
+#pragma unroll
+        for (int m = 0; m < MC; ++m)
+            acc[m] += (double)th[m];
+    }
+#pragma unroll
+    for (int m = 0; m < MC; ++m)
+        g[m] = (float)acc[m];
+}
+
+// One wave per destination with many time steps: the stream's time steps
+// are visited in order, 64 at a time; lanes m < M hold channel m's sum.
+template <int MC>
+__global__ __launch_bounds__(64) void scatter_big_kernel(ScatterParams p)
+{
+    const int lane = threadIdx.x;
+    const int64_t nbig = min((int64_t)p.big[0], p.big_cap);
+    for (int64_t w = blockIdx.x; w < nbig; w += gridDim.x) {
+        const int64_t s = p.big[64 + 2 * w], tau = p.big[64 + 2 * w + 1];
+        const int64_t b = s / p.R, r = s % p.R;
+        const int32_t *E = p.end + s * p.T;
+        double acc = 0.0;
+        for (int64_t c0 = 0; c0 < p.T; c0 += 64) {
+            const int64_t t = c0 + lane;
+            const bool hit = t < p.T && (int64_t)E[t] + 1 == tau;
+            uint64_t mask = __ballot(hit);
+            while (mask) {
+                const int j = __ffsll((long long)mask) - 1;
+                mask &= mask - 1;
+                if (lane < MC)
+                    acc += (double)p.theta[(b * p.T + c0 + j) * p.ldt + r * MC + lane];
+            }
+        }
+        if (lane < MC)
+            p.G[(b * p.T + tau) * p.ldg + r * MC + lane] = (float)acc;
+    }
+}
+
+hipError_t launch_scatter(const ScatterParams &p, hipStream_t st)
+{
+    const int64_t S = p.B * p.R;
+    hipLaunchKernelGGL(scatter_zero_kernel, dim3(1024), dim3(256), 0, st, p.cnt,
+                       S * p.T);
+    hipLaunchKernelGGL(scatter_zero_kernel, dim3(1), dim3(64), 0, st, p.big,
+                       (int64_t)64);
+    const dim3 gt((unsigned)((p.T + 255) / 256), (unsigned)S);
+    hipLaunchKernelGGL(scatter_count_kernel, gt, dim3(256), 0, st, p);
+    hipLaunchKernelGGL(scatter_scan_kernel, dim3((unsigned)S), dim3(1024), 0, st, p);
+    hipLaunchKernelGGL(scatter_fill_kernel, gt, dim3(256), 0, st, p);
+    const dim3 gs((unsigned)((p.T + 3) / 4), (unsigned)((p.R + 63) / 64),
+                  (unsigned)p.B);
+    const unsigned gb = 1024;
+    switch (p.M) {
+#define ROSA_SCATTER_M(MM)                                                        \
+    case MM:                                                                      \
+        hipLaunchKernelGGL(scatter_sum_kernel<MM>, gs, dim3(256), 0, st, p);      \
+        hipLaunchKernelGGL(scatter_big_kernel<MM>, dim3(gb), dim3(64), 0, st, p); \
+        break;
+        ROSA_SCATTER_M(1)
+        ROSA_SCATTER_M(2)
+        ROSA_SCATTER_M(3)
+        ROSA_SCATTER_M(4)
+        ROSA_SCATTER_M(5)
+        ROSA_SCATTER_M(6)
+        ROSA_SCATTER_M(7)
+        ROSA_SCATTER_M(8)
+#undef ROSA_SCATTER_M
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace rosa

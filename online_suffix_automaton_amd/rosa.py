@@ -50,7 +50,8 @@ class rosa_qk_out(ctypes.Structure):
 _lib = None
 _SYMBOLS = ["rosa_match_workspace_bytes", "rosa_match", "rosa_match_timed",
             "rosa_match_status", "rosa_match_qk_workspace_bytes",
-            "rosa_match_qk",
+            "rosa_match_qk", "rosa_scatter_grad_workspace_bytes",
+            "rosa_scatter_grad",
             "rosa_gather", "rosa_state_bytes", "rosa_build", "rosa_step",
             "rosa_state_length", "rosa_state_status", "rosa_free",
             "rosa_error_string"]
@@ -74,6 +75,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "rosa_match_status": ([P, P], ctypes.c_int),
         "rosa_match_qk_workspace_bytes": ([I64, I64, I32], SZ),
         "rosa_match_qk": ([P, P, I32, P, P, SZ, P], ctypes.c_int),
+        "rosa_scatter_grad_workspace_bytes": ([I64, I64], SZ),
+        "rosa_scatter_grad": ([P, I64, I64, I64, I64, I32, P, P, I64, P, SZ, P],
+                              ctypes.c_int),
         "rosa_gather": ([P, I64, I64, I64, I64, I32, P, P, I64, P], ctypes.c_int),
         "rosa_state_bytes": ([I64, I32, I64], SZ),
         "rosa_build": ([P, I64, P, SZ, ctypes.POINTER(P), P, P], ctypes.c_int),
@@ -227,6 +231,29 @@ def rosa_gather(V: torch.Tensor, M: int, end: torch.Tensor, out: torch.Tensor,
                                       end.data_ptr(), out.data_ptr(),
                                       out.stride(1) if T > 1 else D,
                                       _stream(stream)), "rosa_gather")
+
+
+def rosa_scatter_grad_workspace_bytes(S: int, T: int) -> int:
+    return int(load_library().rosa_scatter_grad_workspace_bytes(S, T))
+
+
+def rosa_scatter_grad(theta: torch.Tensor, M: int, end: torch.Tensor,
+                      G: torch.Tensor, ws: torch.Tensor | None = None,
+                      stream=None) -> None:
+    """theta, G: float32 [B, T, D] (unit channel stride); end: int32 [S, T].
+    Allocates the workspace with torch when none is given."""
+    _require_device(theta, end, G, ws)
+    if theta.dtype != torch.float32 or G.dtype != torch.float32:
+        raise ValueError("theta and G must be float32")
+    B, T, D = theta.shape
+    if ws is None:
+        ws = torch.empty(rosa_scatter_grad_workspace_bytes(B * (D // M), T),
+                         dtype=torch.uint8, device=theta.device)
+    _check(load_library().rosa_scatter_grad(
+        theta.data_ptr(), B, T, D, theta.stride(1) if T > 1 else D, M,
+        end.data_ptr(), G.data_ptr(), G.stride(1) if T > 1 else D,
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)),
+        "rosa_scatter_grad")
 
 
 def rosa_state_bytes(S: int, K: int, t_capacity: int) -> int:

@@ -157,3 +157,20 @@ def test_match_qk_rejects_bad_arguments():
     o2.tau, o2.cf_tau = FAKE.value, FAKE.value
     assert call(_inp(K=3), _inp(K=3), o=o2) == rosa.ROSA_ERR_ARG
     assert call(_inp(K=1), _inp(K=1), o=o2) == rosa.ROSA_ERR_ARG
+
+
+def test_scatter_grad_rejects_bad_arguments():
+    lib = rosa.load_library()
+    f = lib.rosa_scatter_grad
+    P = FAKE.value
+    assert rosa.rosa_scatter_grad_workspace_bytes(0, 10) == 0
+    assert rosa.rosa_scatter_grad_workspace_bytes(4, 10) > 0
+    ws, big = 0x100000, 1 << 40
+    assert f(P, 0, 10, 8, 8, 4, P, P, 8, ws, big, None) == rosa.ROSA_ERR_ARG  # B
+    assert f(P, 1, 10, 8, 8, 3, P, P, 8, ws, big, None) == rosa.ROSA_ERR_ARG  # D % M
+    assert f(P, 1, 10, 8, 8, 9, P, P, 8, ws, big, None) == rosa.ROSA_ERR_ARG  # M
+    assert f(P, 1, 10, 8, 4, 4, P, P, 8, ws, big, None) == rosa.ROSA_ERR_ARG  # ldt
+    assert f(P, 1, 10, 8, 8, 4, P, P, 4, ws, big, None) == rosa.ROSA_ERR_ARG  # ldg
+    assert f(None, 1, 10, 8, 8, 4, P, P, 8, ws, big, None) == rosa.ROSA_ERR_ARG
+    assert f(P, 1, 10, 8, 8, 4, P, P, 8, 0x100010, big, None) == rosa.ROSA_ERR_ARG
+    assert f(P, 1, 10, 8, 8, 4, P, P, 8, ws, 16, None) == rosa.ROSA_ERR_CAPACITY
