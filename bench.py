@@ -367,6 +367,76 @@ def run_qk(args):
     }
 
 
+# ----------------------------------------------------------------- scatter
+
+def run_scatter(args):
+    """Destination-scatter gradient on the long workload: destinations from
+    rosa_match on the long workload's hidden states, upstream gradient theta
+    [1, 65536, 2048] float32 N(0,1) (seed 45)."""
+    import torch
+    from online_suffix_automaton_amd import rosa, synth
+    dev = torch.device("cuda:0")
+    B, T, D, M = 1, 65536, 2048, 4
+    S = B * D // M
+    _log("workload scatter: generating")
+    w = synth.long(with_v=False)
+    Hd = torch.from_numpy(w["H"].view(np.int16)).to(dev)
+    E, _, _, _ = rosa.match(Hd, M=M, want_len=False)
+    del Hd
+    theta = np.random.default_rng(45).standard_normal((B, T, D), dtype=np.float32)
+    th = torch.from_numpy(theta).to(dev)
+    G = torch.empty_like(th)
+    ws = torch.empty(rosa.rosa_scatter_grad_workspace_bytes(S, T),
+                     dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        rosa.rosa_scatter_grad(th, M, E, G, ws)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    _log(f"timing {args.steps} steps")
+    e0.record()
+    for _ in range(args.steps):
+        rosa.rosa_scatter_grad(th, M, E, G, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    # compulsory bytes per stream-position: E in (4), theta's M floats in
+    # (16), G's M floats out (16)
+    bpp = 4 + 4 * M + 4 * M
+    achieved = bpp * S * T / (ms / 1e3)
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        oracle._load()
+        _log("oracle (parity + baseline)")
+        Eh = E.cpu().numpy()
+        t0 = time.perf_counter()
+        want = oracle.scatter_grad(theta, Eh, M)
+        wall = time.perf_counter() - t0
+        if not np.array_equal(G.cpu().numpy().view(np.uint32), want.view(np.uint32)):
+            raise SystemExit("parity failure: scatter gradient differs")
+        _log(f"parity ok; oracle {wall:.3f} s")
+        cpu = {"value": S * T / wall, "unit": "positions/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"whole workload ({S} streams x {T}), single thread "
+                         "(the oracle sums every stream into one array)"}
+    return {
+        "metric": "scatter-gradient positions/sec (512 streams x 65536)",
+        "value": S * T / (ms / 1e3), "unit": "positions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f64 accumulate, f32 in/out", "data": "synthetic",
+        "config": {"workload": "scatter: destinations of the long workload "
+                               "(512 streams x 65536, K=16), theta "
+                               "[1,65536,2048] f32 N(0,1)",
+                   "streams": S, "T": T, "K": 16, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved / 1e9,
+                     "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK, "traffic": None},
+        "cpu_baseline": cpu,
+    }
+
+
 # -------------------------------------------------------------------- main
 
 def main():
@@ -375,7 +445,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long",
-                    choices=["long", "batched", "repeat", "decode", "qk"])
+                    choices=["long", "batched", "repeat", "decode", "qk",
+                             "scatter"])
     ap.add_argument("--rle", action="store_true",
                     help="qk workload: fold the key stream into runs")
     ap.add_argument("--cf", action="store_true",
@@ -399,6 +470,9 @@ def main():
         return
     if args.workload == "qk":
         print(json.dumps(run_qk(args)), flush=True)
+        return
+    if args.workload == "scatter":
+        print(json.dumps(run_scatter(args)), flush=True)
         return
 
     import torch
