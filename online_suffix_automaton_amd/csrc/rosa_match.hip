@@ -26,14 +26,14 @@
 //        (l <= d) by LDS atomicMin;
 //     B  scan -> bucket offsets; buckets packed into <=64-element tasks;
 //        buckets larger than 64 go to a global list;
-//     C  positions scattered into buckets (LDS atomics);
 //     D  positions whose d-gram is new (L < d) and the first d-1 positions
 //        are answered from the first-occurrence tables plus a time-ordered
 //        scan per segment (ballot match inside 64-position chunks, LDS
 //        last-end tables across chunks and segments);
-//     E  each wave takes tasks: sorts the task's positions by time
-//        (bitonic over the 64 lanes), then refines groups with lane masks
-//        (solve_wave).
+//     E  positions scattered into buckets (LDS atomics), each bucket put in
+//        time order (insertion sort, one bucket per thread); each wave then
+//        takes tasks: a group is the lane range of one bucket, refined with
+//        lane masks (solve_wave).
 //   big_kernel (one wave per bucket of more than 64 positions): rebuilds the
 //     bucket in time order, then refines it with stable partitions by the
 //     next symbol until groups fit a wave, then solve_wave.
@@ -48,13 +48,6 @@ constexpr int kWordThreshDeep = 32;  // ... and past the first levels, larger th
 // ----------------------------------------------------------- wave helpers
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
-
-__device__ __forceinline__ int wave_max(int v)
-{
-    for (int o = 32; o > 0; o >>= 1)
-        v = max(v, __shfl_xor(v, o));
-    return v;
-}
 
 __device__ __forceinline__ int wave_incl_scan(int v)
 {
@@ -98,53 +91,6 @@ __device__ __forceinline__ uint64_t shfl64(uint64_t v, int src)
 // (t << 16 | E+1) per bucket slot, coalesced; a later kernel scatters the
 // records into time order in LDS and writes E and SYM.  L, if requested,
 // is always written directly.
-// Exchange with lane ^ J for the bitonic network.  J < 16 stays inside a
-// 16-lane row: quad permutes for 1 and 2, row shifts for 4 and 8 (lane i
-// reads i+J or i-J), no LDS round trip; 16 uses a swizzle, 32 a permute.
-template <int J>
-__device__ __forceinline__ uint32_t xor_lane(uint32_t v)
-{
-    if (J == 1)
-        return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false);
-    if (J == 2)
-        return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false);
-    if (J == 4 || J == 8) {
-        const uint32_t up = __builtin_amdgcn_update_dpp(0u, v, 0x100 | J, 0xF, 0xF, false);
-        const uint32_t dn = __builtin_amdgcn_update_dpp(0u, v, 0x110 | J, 0xF, 0xF, false);
-        return (__lane_id() & J) ? dn : up;
-    }
-    if (J == 16)
-        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
-    return (uint32_t)__shfl_xor((int)v, 32);
-}
-
-template <int KK, int J>
-__device__ __forceinline__ uint32_t bitonic_step(uint32_t key, int lane)
-{
-    const uint32_t o = xor_lane<J>(key);
-    const bool take_min = ((lane & KK) == 0) == ((lane & J) == 0);
-    return take_min ? min(key, o) : max(key, o);
-}
-
-// Ascending sort of one 32-bit key per lane across the wave.
-__device__ __forceinline__ uint32_t bitonic64(uint32_t k)
-{
-    const int l = __lane_id();
-    k = bitonic_step<2, 1>(k, l);
-    k = bitonic_step<4, 2>(k, l);   k = bitonic_step<4, 1>(k, l);
-    k = bitonic_step<8, 4>(k, l);   k = bitonic_step<8, 2>(k, l);
-    k = bitonic_step<8, 1>(k, l);
-    k = bitonic_step<16, 8>(k, l);  k = bitonic_step<16, 4>(k, l);
-    k = bitonic_step<16, 2>(k, l);  k = bitonic_step<16, 1>(k, l);
-    k = bitonic_step<32, 16>(k, l); k = bitonic_step<32, 8>(k, l);
-    k = bitonic_step<32, 4>(k, l);  k = bitonic_step<32, 2>(k, l);
-    k = bitonic_step<32, 1>(k, l);
-    k = bitonic_step<64, 32>(k, l); k = bitonic_step<64, 16>(k, l);
-    k = bitonic_step<64, 8>(k, l);  k = bitonic_step<64, 4>(k, l);
-    k = bitonic_step<64, 2>(k, l);  k = bitonic_step<64, 1>(k, l);
-    return k;
-}
-
 struct StreamOut {
     const uint8_t *x;  // padded symbol row of the stream (LDS or HBM)
     int32_t *E;
@@ -213,7 +159,7 @@ __device__ Found solve_wave(const uint8_t *x, int nbits, int t, uint64_t g,
         if (ell <= ell0 + 1) {
             if (ballot(live && __popcll(g) > kWordThresh) == 0)
                 break;
-        } else if (wave_max(live ? __popcll(g) : 0) <= kWordThreshDeep) {
+        } else if (ballot(live && __popcll(g) > kWordThreshDeep) == 0) {
             break;
         }
         // ---------------------------------------------------- level step
@@ -565,11 +511,39 @@ __device__ void phase_short(const MatchParams &p, const uint8_t *x,
     __syncthreads();
 }
 
-// One task: `n` positions of consecutive buckets read from `src`.  Bucket
-// boundaries are where the d-gram key changes; the positions are sorted by
-// time across the wave (bitonic on t<<6 | bucket) and a group is the set of
-// lanes with the same bucket index.  Returns solve_wave's answer for the
-// lane and the lane's (sorted) position in t_out.
+// Puts every selected bucket's positions in time order, one bucket per
+// thread (insertion sort in place).  The scatter that filled the buckets
+// appends in nearly increasing time, so each insertion moves an element a
+// few places at most.  `list` + off[k] - base holds bucket k's positions.
+template <class Ptr, class Sel>
+__device__ void sort_buckets(Ptr list, const int32_t *off, int NB, int base,
+                             Sel selected)
+{
+    for (int k = threadIdx.x; k < NB; k += blockDim.x) {
+        if (!selected(k))
+            continue;
+        const int b0 = off[k] - base, c = off[k + 1] - off[k];
+        for (int i = 1; i < c; ++i) {
+            const auto v = list[b0 + i];
+            int j = i - 1;
+            while (j >= 0) {
+                const auto u = list[b0 + j];
+                if (u <= v)
+                    break;
+                list[b0 + j + 1] = u;
+                --j;
+            }
+            list[b0 + j + 1] = v;
+        }
+    }
+}
+
+// One task: `n` positions of consecutive buckets read from `src`, each
+// bucket in time order.  Bucket boundaries are where the d-gram key
+// changes; a group is the lane range of one bucket, so inside a group lane
+// order is time order.  Returns solve_wave's answer for the lane (not ok for
+// the first member of each bucket: its answer has L < d) and the lane's
+// position in t_out.
 template <class Src>
 __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
                           int n, int &t_out)
@@ -582,39 +556,33 @@ __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
     const int kprev = __shfl_up(k0, 1);
     const uint64_t B = ballot(has && (lane == 0 || kprev != k0));
     const uint64_t upto = (self << 1) - 1;   // lanes 0..lane (lane 63: all)
-    const uint32_t seg = (uint32_t)__popcll(B & upto) - 1u;
-    const uint32_t key = bitonic64(has ? (((uint32_t)t0 << 6) | seg) : 0xFFFFFFFFu);
-    const int nbk = 64 - __clzll((long long)__popcll(B));
-    const uint32_t sg = key & 63u;
-    uint64_t g = ballot(has);
-    for (int b = 0; b < nbk; ++b) {
-        const bool bit = (sg >> b) & 1u;
-        const uint64_t Bb = ballot(has && bit);
-        g &= bit ? Bb : ~Bb;
-    }
-    if (!has)
-        g = self;
-    t_out = (int)(key >> 6);
-    return solve_wave(x, p.nbits, t_out, g, p.d, has);
+    const uint64_t nxt = B & ~upto;          // bucket starts above this lane
+    const int ss = 63 - __clzll((long long)(B & upto | 1ull));
+    const int se = nxt ? __ffsll((long long)nxt) - 1 : n;   // exclusive
+    const uint64_t hi = se >= 64 ? ~0ull : ((1ull << se) - 1);
+    const uint64_t g = has ? (hi & ~((1ull << ss) - 1)) : self;
+    t_out = t0;
+    return solve_wave(x, p.nbits, t0, g, p.d, has);
 }
 
 // ------------------------------------------------- stream kernel (LDS)
 //
 // Streams of up to 65536 positions.  LDS: the padded symbol row, bucket
-// offsets, tasks, the short-match answers of first bucket members, and a
-// union reused across phases:
+// offsets, tasks, and a union reused across phases:
 //   A-B  cnt[4096] | firstd[4096] | firstl[2048]
 //   D    pending u16[4112] | firstd | firstl | segment tables
 //   E    cursors[4096] | pass id u8[4096] | positions u16[kLposCap]
 // Phase E runs in passes over ranges of bucket slots that fit kLposCap:
 // each pass scatters the range's positions into LDS (LDS atomics on the
-// cursors), then the waves solve the range's tasks from LDS.  All results
-// are staged as records (coalesced) and put into time order by
-// unpermute_kernel.
+// cursors), puts each bucket in time order, then the waves solve the
+// range's tasks from LDS.  All results are staged as records (coalesced)
+// and put into time order by unpermute_kernel: the first member of every
+// bucket (L < d) gets its record in the bucket's first slot from phase D,
+// every other position from its task.
 constexpr int kLdsSymBytes = 65792;
 constexpr int kTaskCap = 4128;
 constexpr int kUnionBytes = 163840 - kLdsSymBytes - (kMaxBuckets + 16) * 4 -
-                            kTaskCap * 4 - kMaxBuckets * 2 - 128;
+                            kTaskCap * 4 - 128;
 constexpr int kUSegTab = 40960;
 constexpr int kSegTabLds = (kUnionBytes - kUSegTab) / 4;
 constexpr int kLposCap = (kUnionBytes - 16384 - 4096) / 2;
@@ -625,7 +593,6 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_lds(MatchParams 
     __shared__ __align__(16) unsigned char symrow[kLdsSymBytes];
     __shared__ int32_t off[kMaxBuckets + 16];
     __shared__ uint32_t tasks[kTaskCap];
-    __shared__ uint16_t qres[kMaxBuckets];
     __shared__ int32_t misc[32];
     __shared__ __align__(16) unsigned char U[kUnionBytes];
     int32_t *cnt = reinterpret_cast<int32_t *>(U);
@@ -661,24 +628,15 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_lds(MatchParams 
     phase_tasks(p, s, cnt, off, tasks, misc, kPassCap);
 
     // D: records of the first d-1 positions go to the slots T-d+1.. (no
-    // bucket holds them); a first occurrence in a singleton or large bucket
-    // takes the bucket's first slot; for buckets of 2..64 members the answer
-    // waits in qres until the bucket's task writes it.
+    // bucket holds them); the first occurrence of a d-gram takes its
+    // bucket's first slot (after the bucket sort it is the bucket's first
+    // member, which its task leaves unwritten).
     phase_short(p, x, firstd, firstl, segtab, kSegTabLds, pend, misc,
                 [&](int t, int e, int l) {
-                    if (t < d - 1) {
+                    if (t < d - 1)
                         emit_record(o, T - d + 1 + t, t, e, l);
-                        return;
-                    }
-                    const int k = dgram_key(x, t, d, K);
-                    const int c = off[k + 1] - off[k];
-                    if (c == 1 || c > 64)
-                        emit_record(o, off[k], t, e, l);
-                    else {
-                        qres[k] = (uint16_t)(e + 1);
-                        if (o.L)
-                            o.L[t] = l;
-                    }
+                    else
+                        emit_record(o, off[dgram_key(x, t, d, K)], t, e, l);
                 });
 
     // E: passes over slot ranges.  passid[k] is the pass that scatters
@@ -709,6 +667,8 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_lds(MatchParams 
                     lpos[atomicAdd(&cursor[kk[u]], 1) - base] = (uint16_t)(t0 + u);
         }
         __syncthreads();
+        sort_buckets(lpos, off, NB, base, [&](int k) { return passid[k] == rg; });
+        __syncthreads();
         for (int ti = wid; ti < ntasks; ti += nw) {
             const uint32_t tk = tasks[ti];
             const int start = (int)(tk >> 6);
@@ -718,13 +678,8 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_lds(MatchParams 
             int t;
             const Found f = run_task(
                 p, x, [&](int i) { return (int)lpos[start - base + i]; }, n, t);
-            if (lane < n) {
-                if (f.ok)
-                    emit_record(o, start + lane, t, f.e, f.l);
-                else
-                    o.rec[start + lane] =
-                        ((uint32_t)t << 16) | (uint32_t)qres[dgram_key(x, t, d, K)];
-            }
+            if (lane < n && f.ok)
+                emit_record(o, start + lane, t, f.e, f.l);
         }
         __syncthreads();
     }
@@ -775,6 +730,11 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_hbm(MatchParams 
         if (c >= 2 && c <= 64)
             pos[atomicAdd(&cnt[k], 1)] = t;
     }
+    __syncthreads();
+    sort_buckets(pos, off, p.NB, 0, [&](int k) {
+        const int c = off[k + 1] - off[k];
+        return c >= 2 && c <= 64;
+    });
     __syncthreads();
     phase_short(p, x, firstd, firstl, segtab, kSegTabInts, pend, misc,
                 [&](int t, int e, int l) { emit(o, t, e, l); });
