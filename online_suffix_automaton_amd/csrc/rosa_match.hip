@@ -275,22 +275,66 @@ __device__ int block_excl_scan(int v, int *ws, int *total)
 
 constexpr int kSegTabInts = 8192;
 
+// The four symbols x[t-3..t] as one word, x[t] in the top byte (one LDS or
+// cache round trip instead of one per symbol; rows carry zero padding in
+// front, so t-3 >= -3 stays inside).
+__device__ __forceinline__ uint32_t load4_end(const uint8_t *row, int t)
+{
+    const int p = t - 3;
+    const uint32_t *q = reinterpret_cast<const uint32_t *>(row) + (p >> 2);
+    return __builtin_amdgcn_alignbyte(q[1], q[0], (uint32_t)(p & 3));
+}
+
+// The eight symbols x[t-7..t] (x[t] in the top byte); t-7 >= -7 stays in
+// the front padding.
+__device__ __forceinline__ uint64_t load8_end(const uint8_t *row, int t)
+{
+    const int p = t - 7;
+    const uint32_t *q = reinterpret_cast<const uint32_t *>(row) + (p >> 2);
+    const uint32_t sh = (uint32_t)(p & 3);
+    const uint32_t d0 = q[0], d1 = q[1], d2 = q[2];
+    return (uint64_t)__builtin_amdgcn_alignbyte(d1, d0, sh) |
+           ((uint64_t)__builtin_amdgcn_alignbyte(d2, d1, sh) << 32);
+}
+
+// Key of the d-gram (d <= 4) whose last symbol is the top byte of w.
+__device__ __forceinline__ int key_of_word(uint32_t w, int d, int K)
+{
+    int k = (int)(w >> 24);
+    if (d > 1)
+        k = (int)__umul24((uint32_t)k, (uint32_t)K) + (int)((w >> 16) & 0xFFu);
+    if (d > 2)
+        k = (int)__umul24((uint32_t)k, (uint32_t)K) + (int)((w >> 8) & 0xFFu);
+    if (d > 3)
+        k = (int)__umul24((uint32_t)k, (uint32_t)K) + (int)(w & 0xFFu);
+    return k;
+}
+
+// Symbol x[t-i] (i < 4) out of load4_end's word.
+__device__ __forceinline__ int sym_of(uint32_t w, int i)
+{
+    return (int)((w >> (24 - 8 * i)) & 0xFFu);
+}
+
 // Key of the reversed d-gram ending at t (t >= d-1): x[t] is the most
 // significant digit.  Its top l digits form the key of the l-gram.
 __device__ __forceinline__ int dgram_key(const uint8_t *x, int t, int d, int K)
 {
+    if (d <= 4)
+        return key_of_word(load4_end(x, t), d, K);
     int k = 0;
     for (int i = 0; i < d; ++i)
-        k = k * K + x[t - i];
+        k = (int)__umul24((uint32_t)k, (uint32_t)K) + x[t - i];
     return k;
 }
 
 // Phase A: d-gram histogram and first occurrence of every l-gram, l <= d.
+template <int DC>
 __device__ void phase_hist(const MatchParams &p, const uint8_t *x, int32_t *cnt,
                            int32_t *firstd, int32_t *firstl)
 {
     const int tid = threadIdx.x, nt = blockDim.x;
-    const int T = p.T, K = p.K, d = p.d;
+    const int T = p.T, K = p.K, d = DC > 0 ? DC : p.d;
     for (int i = tid; i < p.NB; i += nt) {
         cnt[i] = 0;
         firstd[i] = 0x7FFFFFFF;
@@ -301,8 +345,9 @@ __device__ void phase_hist(const MatchParams &p, const uint8_t *x, int32_t *cnt,
     for (int t = tid; t < T; t += nt) {
         int k = 0;
         const int dm = min(d, t + 1);
+        const uint32_t w = d <= 4 ? load4_end(x, t) : 0u;
         for (int i = 0; i < dm; ++i) {
-            k = k * K + x[t - i];
+            k = (int)__umul24((uint32_t)k, (uint32_t)K) + (d <= 4 ? sym_of(w, i) : (int)x[t - i]);
             if (i + 1 < d) {
                 int32_t *f = &firstl[p.fl_off[i + 1] + k];
                 if (t < *f)
@@ -427,7 +472,7 @@ __device__ void phase_tasks(const MatchParams &p, int s, const int32_t *cnt,
 // match.  Queries with no earlier end inside their segment are resolved
 // after the scan from the tables of earlier segments.  `put(t, e, l)`
 // receives every answer.
-template <class Put, class PendT>
+template <int DC, class Put, class PendT>
 __device__ void phase_short(const MatchParams &p, const uint8_t *x,
                             const int32_t *firstd, const int32_t *firstl,
                             int32_t *segtab, int segcap, PendT *pend,
@@ -438,7 +483,7 @@ __device__ void phase_short(const MatchParams &p, const uint8_t *x,
     const uint64_t self = 1ull << lane;
     const uint64_t below = self - 1;
     const uint64_t above = ~(below | self);
-    const int T = p.T, K = p.K, d = p.d, FL = p.fl_total;
+    const int T = p.T, K = p.K, d = DC > 0 ? DC : p.d, FL = p.fl_total;
     const int nseg = FL > 0 ? max(1, min(nw, segcap / FL)) : nw;
     const int Ts = (((T + nseg - 1) / nseg) + 63) & ~63;
     for (int i = tid; i < nseg * FL; i += nt)
@@ -452,6 +497,7 @@ __device__ void phase_short(const MatchParams &p, const uint8_t *x,
         for (int c0 = lo; c0 < hi; c0 += 64) {
             const int t = c0 + lane;
             const bool inr = t < hi;
+            const uint32_t w = d <= 4 ? load4_end(x, t) : 0u;
             const bool q = inr && (t < d - 1 || firstd[dgram_key(x, t, d, K)] == t);
             int Lq = 0, Eq = -1;
             bool miss = false;
@@ -459,8 +505,8 @@ __device__ void phase_short(const MatchParams &p, const uint8_t *x,
             uint64_t eq = ~0ull;
             for (int l = 1; l < d; ++l) {
                 const bool v = inr && t >= l - 1;
-                const int dig = v ? x[t - l + 1] : 0;
-                gk = gk * K + dig;
+                const int dig = v ? (d <= 4 ? sym_of(w, l - 1) : (int)x[t - l + 1]) : 0;
+                gk = (int)__umul24((uint32_t)gk, (uint32_t)K) + dig;
                 uint64_t m = ballot(v);
                 for (int b = 0; b < p.nbits; ++b) {
                     const bool bit = (dig >> b) & 1;
@@ -544,7 +590,7 @@ __device__ void sort_buckets(Ptr list, const int32_t *off, int NB, int base,
 // order is time order.  Returns solve_wave's answer for the lane (not ok for
 // the first member of each bucket: its answer has L < d) and the lane's
 // position in t_out.
-template <class Src>
+template <int DC, class Src>
 __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
                           int n, int &t_out)
 {
@@ -552,7 +598,8 @@ __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
     const uint64_t self = 1ull << lane;
     const bool has = lane < n;
     const int t0 = has ? src(lane) : 0;
-    const int k0 = has ? dgram_key(x, t0, p.d, p.K) : -1;
+    const int d = DC > 0 ? DC : p.d;
+    const int k0 = has ? dgram_key(x, t0, d, p.K) : -1;
     const int kprev = __shfl_up(k0, 1);
     const uint64_t B = ballot(has && (lane == 0 || kprev != k0));
     const uint64_t upto = (self << 1) - 1;   // lanes 0..lane (lane 63: all)
@@ -562,7 +609,7 @@ __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
     const uint64_t hi = se >= 64 ? ~0ull : ((1ull << se) - 1);
     const uint64_t g = has ? (hi & ~((1ull << ss) - 1)) : self;
     t_out = t0;
-    return solve_wave(x, p.nbits, t0, g, p.d, has);
+    return solve_wave(x, p.nbits, t0, g, d, has);
 }
 
 // ------------------------------------------------- stream kernel (LDS)
@@ -588,6 +635,9 @@ constexpr int kSegTabLds = (kUnionBytes - kUSegTab) / 4;
 constexpr int kLposCap = (kUnionBytes - 16384 - 4096) / 2;
 constexpr int kPassCap = kLposCap - 64;
 
+// DC: the bucketing depth d as a compile-time constant (1..4), or 0 to read
+// it from p.
+template <int DC>
 __global__ __launch_bounds__(kStreamThreads) void stream_kernel_lds(MatchParams p)
 {
     __shared__ __align__(16) unsigned char symrow[kLdsSymBytes];
@@ -607,7 +657,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_lds(MatchParams 
     const int s = blockIdx.x;
     const int tid = threadIdx.x, nt = blockDim.x;
     const int lane = tid & 63, wid = tid >> 6, nw = nt >> 6;
-    const int T = p.T, K = p.K, d = p.d, NB = p.NB;
+    const int T = p.T, K = p.K, d = DC > 0 ? DC : p.d, NB = p.NB;
     {
         const uint4 *src = reinterpret_cast<const uint4 *>(p.sym + (int64_t)s * p.Tp);
         uint4 *dst = reinterpret_cast<uint4 *>(symrow);
@@ -624,14 +674,14 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_lds(MatchParams 
     o.L = p.L ? p.L + (int64_t)s * T : nullptr;
     o.rec = p.rec + (int64_t)s * T;
 
-    phase_hist(p, x, cnt, firstd, firstl);
+    phase_hist<DC>(p, x, cnt, firstd, firstl);
     phase_tasks(p, s, cnt, off, tasks, misc, kPassCap);
 
     // D: records of the first d-1 positions go to the slots T-d+1.. (no
     // bucket holds them); the first occurrence of a d-gram takes its
     // bucket's first slot (after the bucket sort it is the bucket's first
     // member, which its task leaves unwritten).
-    phase_short(p, x, firstd, firstl, segtab, kSegTabLds, pend, misc,
+    phase_short<DC>(p, x, firstd, firstl, segtab, kSegTabLds, pend, misc,
                 [&](int t, int e, int l) {
                     if (t < d - 1)
                         emit_record(o, T - d + 1 + t, t, e, l);
@@ -655,10 +705,14 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_lds(MatchParams 
         for (int t0 = d - 1 + 4 * tid; t0 < T; t0 += 4 * nt) {
             int kk[4];
             bool in[4];
+            // one 8-symbol read covers the four d-grams when d <= 4
+            const uint64_t v8 = d <= 4 ? load8_end(x, t0 + 3) : 0ull;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int t = t0 + u;
-                kk[u] = t < T ? dgram_key(x, t, d, K) : 0;
+                kk[u] = t >= T ? 0
+                        : d <= 4 ? key_of_word((uint32_t)(v8 >> (8 * (u + 1))), d, K)
+                                 : dgram_key(x, t, d, K);
                 in[u] = t < T && passid[kk[u]] == rg;
             }
 #pragma unroll
@@ -676,7 +730,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_lds(MatchParams 
                 continue;
             const int n = (int)(tk & 63u) + 1;
             int t;
-            const Found f = run_task(
+            const Found f = run_task<DC>(
                 p, x, [&](int i) { return (int)lpos[start - base + i]; }, n, t);
             if (lane < n && f.ok)
                 emit_record(o, start + lane, t, f.e, f.l);
@@ -718,7 +772,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_hbm(MatchParams 
     o.L = p.L ? p.L + (int64_t)s * T : nullptr;
     o.rec = nullptr;
 
-    phase_hist(p, x, cnt, firstd, firstl);
+    phase_hist<0>(p, x, cnt, firstd, firstl);
     phase_tasks(p, s, cnt, off, tasks, misc, 0x7FFFFFFF);
     for (int i = tid; i < p.NB; i += nt)
         cnt[i] = off[i];   // cursors
@@ -736,7 +790,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_hbm(MatchParams 
         return c >= 2 && c <= 64;
     });
     __syncthreads();
-    phase_short(p, x, firstd, firstl, segtab, kSegTabInts, pend, misc,
+    phase_short<0>(p, x, firstd, firstl, segtab, kSegTabInts, pend, misc,
                 [&](int t, int e, int l) { emit(o, t, e, l); });
     const int ntasks = misc[24];
     for (int ti = wid; ti < ntasks; ti += nw) {
@@ -744,7 +798,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_hbm(MatchParams 
         const int start = (int)(tk >> 6);
         const int n = (int)(tk & 63u) + 1;
         int t;
-        const Found f = run_task(p, x, [&](int i) { return pos[start + i]; }, n, t);
+        const Found f = run_task<0>(p, x, [&](int i) { return pos[start + i]; }, n, t);
         if (lane < n && f.ok)
             emit(o, t, f.e, f.l);
     }
@@ -1059,10 +1113,29 @@ bool stream_uses_records(int64_t T) { return T <= 65536; }
 
 hipError_t launch_stream(const MatchParams &p, int64_t S, hipStream_t st)
 {
-    if (stream_uses_records(p.T))
-        hipLaunchKernelGGL(stream_kernel_lds, dim3((unsigned)S),
-                           dim3(kStreamThreads), 0, st, p);
-    else
+    if (stream_uses_records(p.T)) {
+        switch (p.d) {
+        case 1:
+            hipLaunchKernelGGL(stream_kernel_lds<1>, dim3((unsigned)S),
+                               dim3(kStreamThreads), 0, st, p);
+            break;
+        case 2:
+            hipLaunchKernelGGL(stream_kernel_lds<2>, dim3((unsigned)S),
+                               dim3(kStreamThreads), 0, st, p);
+            break;
+        case 3:
+            hipLaunchKernelGGL(stream_kernel_lds<3>, dim3((unsigned)S),
+                               dim3(kStreamThreads), 0, st, p);
+            break;
+        case 4:
+            hipLaunchKernelGGL(stream_kernel_lds<4>, dim3((unsigned)S),
+                               dim3(kStreamThreads), 0, st, p);
+            break;
+        default:
+            hipLaunchKernelGGL(stream_kernel_lds<0>, dim3((unsigned)S),
+                               dim3(kStreamThreads), 0, st, p);
+        }
+    } else
         hipLaunchKernelGGL(stream_kernel_hbm, dim3((unsigned)S),
                            dim3(kStreamThreads), 0, st, p);
     return hipGetLastError();
