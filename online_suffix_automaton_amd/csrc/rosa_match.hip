@@ -47,7 +47,10 @@ constexpr int kWordThreshDeep = 32;  // ... and past the first levels, larger th
 
 // ----------------------------------------------------------- wave helpers
 
-__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+__device__ __forceinline__ uint64_t ballot(bool p)
+{
+    return __builtin_amdgcn_ballot_w64(p);
+}
 
 __device__ __forceinline__ int wave_incl_scan(int v)
 {
@@ -146,8 +149,6 @@ __device__ Found solve_wave(const uint8_t *x, int nbits, int t, uint64_t g,
     Found r = {-1, 0, false};
     if (!has)
         g = self;
-    uint64_t lo = 0, hi = 0;
-    int wl = -(1 << 30);
     const int ell0 = ell;
     for (;;) {
         const bool live = has && __popcll(g) >= 2;
@@ -163,20 +164,18 @@ __device__ Found solve_wave(const uint8_t *x, int nbits, int t, uint64_t g,
             break;
         }
         // ---------------------------------------------------- level step
-        if (ell - wl >= 16) {
-            if (live && t - ell >= 0)
-                load_window(x, t - ell - 15, lo, hi);
-            wl = ell;
-        }
-        const int bi = 15 - (ell - wl);
-        const uint32_t dig =
-            (uint32_t)((bi >= 8 ? (hi >> (8 * (bi - 8))) : (lo >> (8 * bi))) & 0xFFu);
+        // split every group by the symbol x[t-ell]: lanes agree on it iff
+        // they agree on each of its nbits bits (one ballot per bit)
         const bool valid = live && (t - ell >= 0);
+        const uint32_t dig = valid ? (uint32_t)x[t - ell] : 0u;
         uint64_t eq = ballot(valid);
-        for (int b = 0; b < nbits; ++b) {
-            const bool bit = (dig >> b) & 1u;
-            const uint64_t B = ballot(valid && bit);
-            eq &= bit ? B : ~B;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            if (b < nbits) {
+                const uint32_t bit = (dig >> b) & 1u;
+                const uint64_t B = ballot(bit != 0);
+                eq &= ~(B ^ (0ull - (uint64_t)bit));
+            }
         }
         const uint64_t ng = valid ? (g & eq) : self;
         const uint64_t prev = g & below;
