@@ -159,6 +159,7 @@ MatchParams match_params(const Shape &sh, char *ws, const WsLayout &w,
     p.big_cap = w.big_cap;
     p.stack = reinterpret_cast<int4 *>(ws + w.stack);
     p.rec = sh.T <= 65536 ? reinterpret_cast<uint32_t *>(ws + w.rec) : nullptr;
+    p.tasks = reinterpret_cast<uint32_t *>(ws + w.tasks);
     p.E = out->end;
     p.SYM = out->sym;
     p.L = out->len;

@@ -18,13 +18,14 @@ constexpr int kMaxFirstTab = 2048;   // sum_{l=1}^{d-1} K^l
 constexpr int kMaxD = 12;
 
 constexpr int kStreamThreads = 1024; // one workgroup per stream
+constexpr int kTaskCap = 4128;       // tasks per stream (<= kMaxBuckets)
 constexpr int kBigThreads = 64;      // one wave per large group
 
 // Flags word layout in the match workspace (first 256 bytes).
 constexpr int kFlagSymbol = 0;       // int32: nonzero if a symbol >= K was seen
 
 struct WsLayout {
-    size_t flags, sym, pos, pos2, rec, big, stack, total;
+    size_t flags, sym, pos, pos2, rec, big, stack, tasks, total;
     int64_t Tp;          // bytes per padded symbol row
     int64_t big_cap;     // entries in the large-group list
 };
@@ -44,6 +45,7 @@ inline WsLayout ws_layout(int64_t S, int64_t T)
     w.rec = o;    o = align_up(o + (size_t)S * T * 4, 256);
     w.big = o;    o = align_up(o + 256 + (size_t)w.big_cap * 16, 256);
     w.stack = o;  o = align_up(o + (size_t)S * (T / 16 + 4) * 16, 256);
+    w.tasks = o;  o = align_up(o + (size_t)S * kTaskCap * 4, 256);
     w.total = o;
     return w;
 }
@@ -61,6 +63,7 @@ struct MatchParams {
     int64_t big_cap;
     int4 *stack;                // [S][T/16+4] group stacks of the large-group pass
     uint32_t *rec;              // [S][T] result records (streams of <= 65536)
+    uint32_t *tasks;            // [S][kTaskCap] task lists (LDS kernel)
     int32_t *E;                 // [S][T]
     int16_t *SYM;               // [S][T] or null
     int32_t *L;                 // [S][T] or null

@@ -43,6 +43,7 @@ namespace rosa {
 
 constexpr uint32_t kFirstFlag = 0x80000000u;
 constexpr int kWordThresh = 4;       // level steps only for groups larger than this
+constexpr int kMiscPass = 26;        // misc[26..31]: tasks per slot range
 constexpr int kWordThreshDeep = 32;  // ... and past the first levels, larger than this
 
 // ----------------------------------------------------------- wave helpers
@@ -366,7 +367,9 @@ __device__ void phase_hist(const MatchParams &p, const uint8_t *x, int32_t *cnt,
 // tasks of at most 64 positions (a task never spans a singleton or large
 // bucket, nor a boundary between position ranges of `pcap` slots) and
 // lists buckets of more than 64 members for the large-group kernel.
-// Returns the number of tasks (in misc[24]).
+// Returns the number of tasks in misc[24] and the number of tasks of each
+// slot range in misc[kMiscPass + range] (tasks are in slot order, so the
+// tasks of one range are consecutive).
 __device__ void phase_tasks(const MatchParams &p, int s, const int32_t *cnt,
                             int32_t *off, uint32_t *tasks, int32_t *misc,
                             int pcap)
@@ -421,6 +424,10 @@ __device__ void phase_tasks(const MatchParams &p, int s, const int32_t *cnt,
         ++ntask;
     int total;
     int k = block_excl_scan(ntask, misc, &total);
+    auto put_task = [&](int i, int st, int n) {
+        tasks[i] = ((uint32_t)st << 6) | (uint32_t)(n - 1);
+        atomicAdd(&misc[kMiscPass + st / pcap], 1);
+    };
     int start = 0;
     cur = 0;
     crange = -1;
@@ -430,7 +437,7 @@ __device__ void phase_tasks(const MatchParams &p, int s, const int32_t *cnt,
             continue;
         if (c == 1 || c > 64) {
             if (cur) {
-                tasks[k++] = ((uint32_t)start << 6) | (uint32_t)(cur - 1);
+                put_task(k++, start, cur);
                 cur = 0;
             }
             if (c > 64) {
@@ -447,7 +454,7 @@ __device__ void phase_tasks(const MatchParams &p, int s, const int32_t *cnt,
         }
         const int rg = off[b] / pcap;
         if (cur + c > 64 || (cur && rg != crange)) {
-            tasks[k++] = ((uint32_t)start << 6) | (uint32_t)(cur - 1);
+            put_task(k++, start, cur);
             cur = 0;
         }
         crange = rg;
@@ -456,7 +463,7 @@ __device__ void phase_tasks(const MatchParams &p, int s, const int32_t *cnt,
         cur += c;
     }
     if (cur)
-        tasks[k++] = ((uint32_t)start << 6) | (uint32_t)(cur - 1);
+        put_task(k++, start, cur);
     if (tid == 0)
         misc[24] = total;
     __syncthreads();
@@ -614,10 +621,12 @@ __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
 // ------------------------------------------------- stream kernel (LDS)
 //
 // Streams of up to 65536 positions.  LDS: the padded symbol row, bucket
-// offsets, tasks, and a union reused across phases:
+// offsets and a union reused across phases:
 //   A-B  cnt[4096] | firstd[4096] | firstl[2048]
 //   D    pending u16[4112] | firstd | firstl | segment tables
-//   E    cursors[4096] | pass id u8[4096] | positions u16[kLposCap]
+//   E    cursors u16[4096] | pass id u8[4096] | positions u16[kLposCap]
+// The task list lives in the workspace (written once in phase B, read once
+// per task), which leaves room for two passes over a 65536-position stream.
 // Phase E runs in passes over ranges of bucket slots that fit kLposCap:
 // each pass scatters the range's positions into LDS (LDS atomics on the
 // cursors), puts each bucket in time order, then the waves solve the
@@ -626,12 +635,10 @@ __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
 // bucket (L < d) gets its record in the bucket's first slot from phase D,
 // every other position from its task.
 constexpr int kLdsSymBytes = 65792;
-constexpr int kTaskCap = 4128;
-constexpr int kUnionBytes = 163840 - kLdsSymBytes - (kMaxBuckets + 16) * 4 -
-                            kTaskCap * 4 - 128;
+constexpr int kUnionBytes = 163840 - kLdsSymBytes - (kMaxBuckets + 16) * 4 - 128;
 constexpr int kUSegTab = 40960;
 constexpr int kSegTabLds = (kUnionBytes - kUSegTab) / 4;
-constexpr int kLposCap = (kUnionBytes - 16384 - 4096) / 2;
+constexpr int kLposCap = (kUnionBytes - 8192 - 4096) / 2;
 constexpr int kPassCap = kLposCap - 64;
 
 // DC: the bucketing depth d as a compile-time constant (1..4), or 0 to read
@@ -641,7 +648,6 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_lds(MatchParams 
 {
     __shared__ __align__(16) unsigned char symrow[kLdsSymBytes];
     __shared__ int32_t off[kMaxBuckets + 16];
-    __shared__ uint32_t tasks[kTaskCap];
     __shared__ int32_t misc[32];
     __shared__ __align__(16) unsigned char U[kUnionBytes];
     int32_t *cnt = reinterpret_cast<int32_t *>(U);
@@ -649,9 +655,12 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_lds(MatchParams 
     int32_t *firstl = reinterpret_cast<int32_t *>(U + 32768);
     uint16_t *pend = reinterpret_cast<uint16_t *>(U);
     int32_t *segtab = reinterpret_cast<int32_t *>(U + kUSegTab);
-    int32_t *cursor = reinterpret_cast<int32_t *>(U);
-    uint8_t *passid = U + 16384;
-    uint16_t *lpos = reinterpret_cast<uint16_t *>(U + 16384 + 4096);
+    // bucket k's cursor is half k & 1 of word k >> 1 (slot relative to the
+    // pass, < 65536, so an increment never carries into the other half)
+    uint32_t *cur2 = reinterpret_cast<uint32_t *>(U);
+    uint8_t *passid = U + 8192;
+    uint16_t *lpos = reinterpret_cast<uint16_t *>(U + 8192 + 4096);
+    uint32_t *tasks = p.tasks + (int64_t)blockIdx.x * kTaskCap;
 
     const int s = blockIdx.x;
     const int tid = threadIdx.x, nt = blockDim.x;
@@ -692,14 +701,20 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_lds(MatchParams 
     // bucket k (255: not scattered, a singleton or large bucket).
     for (int i = tid; i < NB; i += nt) {
         const int c = off[i + 1] - off[i];
-        cursor[i] = off[i];
         passid[i] = (c >= 2 && c <= 64) ? (uint8_t)(off[i] / kPassCap) : (uint8_t)255;
     }
-    const int ntasks = misc[24];
     const int nslots = off[NB];
+    int tfirst = 0;
     __syncthreads();
     for (int base = 0; base < nslots; base += kPassCap) {
         const int rg = base / kPassCap;
+        for (int i = tid; i < (NB + 1) / 2; i += nt) {
+            const int k0 = 2 * i, k1 = 2 * i + 1;
+            const uint32_t c0 = passid[k0] == rg ? (uint32_t)(off[k0] - base) : 0u;
+            const uint32_t c1 = (k1 < NB && passid[k1] == rg) ? (uint32_t)(off[k1] - base) : 0u;
+            cur2[i] = c0 | (c1 << 16);
+        }
+        __syncthreads();
         // four positions per thread per iteration, independent chains
         for (int t0 = d - 1 + 4 * tid; t0 < T; t0 += 4 * nt) {
             int kk[4];
@@ -716,17 +731,25 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_lds(MatchParams 
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                if (in[u])
-                    lpos[atomicAdd(&cursor[kk[u]], 1) - base] = (uint16_t)(t0 + u);
+                if (in[u]) {
+                    const uint32_t sh = 16u * (uint32_t)(kk[u] & 1);
+                    const uint32_t old = atomicAdd(&cur2[kk[u] >> 1], 1u << sh);
+                    lpos[(old >> sh) & 0xFFFFu] = (uint16_t)(t0 + u);
+                }
         }
         __syncthreads();
         sort_buckets(lpos, off, NB, base, [&](int k) { return passid[k] == rg; });
         __syncthreads();
-        for (int ti = wid; ti < ntasks; ti += nw) {
-            const uint32_t tk = tasks[ti];
+        // this range's tasks: [tlo, thi); the next task's descriptor is
+        // loaded while this one is solved
+        const int tlo = tfirst, thi = tfirst + misc[kMiscPass + rg];
+        tfirst = thi;
+        uint32_t tk_next = tlo + wid < thi ? __builtin_nontemporal_load(&tasks[tlo + wid]) : 0u;
+        for (int ti = tlo + wid; ti < thi; ti += nw) {
+            const uint32_t tk = tk_next;
+            if (ti + nw < thi)
+                tk_next = __builtin_nontemporal_load(&tasks[ti + nw]);
             const int start = (int)(tk >> 6);
-            if (start / kPassCap != rg)
-                continue;
             const int n = (int)(tk & 63u) + 1;
             int t;
             const Found f = run_task<DC>(
