@@ -42,7 +42,7 @@
 namespace rosa {
 
 constexpr uint32_t kFirstFlag = 0x80000000u;
-constexpr int kWordThresh = 4;       // level steps only for groups larger than this
+constexpr int kWordThresh = 3;       // level steps only for groups larger than this
 constexpr int kMiscPass = 26;        // misc[26..31]: tasks per slot range
 constexpr int kWordThreshDeep = 32;  // ... and past the first levels, larger than this
 
@@ -590,13 +590,13 @@ __device__ void sort_buckets(Ptr list, const int32_t *off, int NB, int base,
     }
 }
 
-// One task: `n` positions of consecutive buckets read from `src`, each
-// bucket in time order.  Bucket boundaries are where the d-gram key
-// changes; a group is the lane range of one bucket, so inside a group lane
-// order is time order.  Returns solve_wave's answer for the lane (not ok for
+// One task: `n` positions of consecutive buckets read from `src` (SORT:
+// put each bucket in time order here; otherwise the buckets come sorted).
+// Bucket boundaries are where the d-gram key changes; a group is the lane
+// range of one bucket, so inside a group lane order is time order.  Returns solve_wave's answer for the lane (not ok for
 // the first member of each bucket: its answer has L < d) and the lane's
 // position in t_out.
-template <int DC, class Src>
+template <int DC, bool SORT, class Src>
 __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
                           int n, int &t_out)
 {
@@ -614,8 +614,37 @@ __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
     const int se = nxt ? __ffsll((long long)nxt) - 1 : n;   // exclusive
     const uint64_t hi = se >= 64 ? ~0ull : ((1ull << se) - 1);
     const uint64_t g = has ? (hi & ~((1ull << ss) - 1)) : self;
-    t_out = t0;
-    return solve_wave(x, p.nbits, t0, g, d, has);
+    // time order inside each bucket: odd-even transposition over the wave
+    // on (bucket, t); buckets are already in lane order, so no element
+    // crosses a bucket boundary.  The scatter leaves each bucket nearly in
+    // time order, so the sort usually stops after a few rounds (64 rounds
+    // always suffice).
+    if (!SORT) {
+        t_out = t0;
+        return solve_wave(x, p.nbits, t0, g, d, has);
+    }
+    uint32_t key = has ? (((uint32_t)__popcll(B & upto) << 16) | (uint32_t)t0)
+                       : 0xFFFFFFFFu;
+    for (int r = 0; r < 64; r += 2) {
+        bool swapped = false;
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+            // wave_shl:1 / wave_shr:1: the keys of lanes i+1 and i-1
+            const uint32_t nx = (uint32_t)__builtin_amdgcn_update_dpp(
+                (int)0xFFFFFFFF, (int)key, 0x130, 0xF, 0xF, false);
+            const uint32_t pv = (uint32_t)__builtin_amdgcn_update_dpp(
+                0, (int)key, 0x138, 0xF, 0xF, false);
+            const bool left = (lane & 1) == par;
+            const uint32_t nk = left ? min(key, nx) : max(key, pv);
+            swapped |= nk != key;
+            key = nk;
+        }
+        if (ballot(swapped) == 0)
+            break;
+    }
+    const int t1 = has ? (int)(key & 0xFFFFu) : 0;
+    t_out = t1;
+    return solve_wave(x, p.nbits, t1, g, d, has);
 }
 
 // ------------------------------------------------- stream kernel (LDS)
@@ -738,8 +767,6 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_lds(MatchParams 
                 }
         }
         __syncthreads();
-        sort_buckets(lpos, off, NB, base, [&](int k) { return passid[k] == rg; });
-        __syncthreads();
         // this range's tasks: [tlo, thi); the next task's descriptor is
         // loaded while this one is solved
         const int tlo = tfirst, thi = tfirst + misc[kMiscPass + rg];
@@ -752,7 +779,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_lds(MatchParams 
             const int start = (int)(tk >> 6);
             const int n = (int)(tk & 63u) + 1;
             int t;
-            const Found f = run_task<DC>(
+            const Found f = run_task<DC, true>(
                 p, x, [&](int i) { return (int)lpos[start - base + i]; }, n, t);
             if (lane < n && f.ok)
                 emit_record(o, start + lane, t, f.e, f.l);
@@ -820,7 +847,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_hbm(MatchParams 
         const int start = (int)(tk >> 6);
         const int n = (int)(tk & 63u) + 1;
         int t;
-        const Found f = run_task<0>(p, x, [&](int i) { return pos[start + i]; }, n, t);
+        const Found f = run_task<0, false>(p, x, [&](int i) { return pos[start + i]; }, n, t);
         if (lane < n && f.ok)
             emit(o, t, f.e, f.l);
     }
