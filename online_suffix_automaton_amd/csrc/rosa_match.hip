@@ -329,6 +329,12 @@ __device__ __forceinline__ int dgram_key(const uint8_t *x, int t, int d, int K)
 }
 
 // Phase A: d-gram histogram and first occurrence of every l-gram, l <= d.
+// Positions are counted four per thread (one 8-symbol read covers their
+// d-grams when d <= 4).  The first occurrence of a shorter l-gram is the
+// minimum over its K one-symbol-longer extensions (the l-gram ending at t
+// is the top l digits of the d-gram ending at t), taken level by level
+// down from d-1; the few positions t < d-1 that end l-grams but no d-gram
+// enter the l-gram tables directly.
 template <int DC>
 __device__ void phase_hist(const MatchParams &p, const uint8_t *x, int32_t *cnt,
                            int32_t *firstd, int32_t *firstl)
@@ -342,25 +348,40 @@ __device__ void phase_hist(const MatchParams &p, const uint8_t *x, int32_t *cnt,
     for (int i = tid; i < p.fl_total; i += nt)
         firstl[i] = 0x7FFFFFFF;
     __syncthreads();
-    for (int t = tid; t < T; t += nt) {
-        int k = 0;
-        const int dm = min(d, t + 1);
-        const uint32_t w = d <= 4 ? load4_end(x, t) : 0u;
-        for (int i = 0; i < dm; ++i) {
-            k = (int)__umul24((uint32_t)k, (uint32_t)K) + (d <= 4 ? sym_of(w, i) : (int)x[t - i]);
-            if (i + 1 < d) {
-                int32_t *f = &firstl[p.fl_off[i + 1] + k];
-                if (t < *f)
-                    atomicMin(f, t);
+    for (int t0 = d - 1 + 4 * tid; t0 < T; t0 += 4 * nt) {
+        const uint64_t v8 = d <= 4 ? load8_end(x, t0 + 3) : 0ull;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int t = t0 + u;
+            if (t < T) {
+                const int k = d <= 4 ? key_of_word((uint32_t)(v8 >> (8 * (u + 1))), d, K)
+                                     : dgram_key(x, t, d, K);
+                atomicAdd(&cnt[k], 1);
+                if (t < firstd[k])
+                    atomicMin(&firstd[k], t);
             }
         }
-        if (t >= d - 1) {
-            atomicAdd(&cnt[k], 1);
-            if (t < firstd[k])
-                atomicMin(&firstd[k], t);
+    }
+    if (tid < d - 1 && tid < T) {
+        const int t = tid;
+        int k = 0;
+        for (int i = 0; i <= t; ++i) {
+            k = (int)__umul24((uint32_t)k, (uint32_t)K) + x[t - i];
+            atomicMin(&firstl[p.fl_off[i + 1] + k], t);
         }
     }
     __syncthreads();
+    for (int l = d - 1; l >= 1; --l) {
+        const int n = p.pw[l];
+        const int32_t *up = l + 1 == d ? firstd : firstl + p.fl_off[l + 1];
+        for (int g = tid; g < n; g += nt) {
+            int m = firstl[p.fl_off[l] + g];
+            for (int c = 0; c < K; ++c)
+                m = min(m, up[g * K + c]);
+            firstl[p.fl_off[l] + g] = m;
+        }
+        __syncthreads();
+    }
 }
 
 // Phase B: bucket offsets, then buckets of 2..64 members are packed into
@@ -514,10 +535,13 @@ __device__ void phase_short(const MatchParams &p, const uint8_t *x,
                 const int dig = v ? (d <= 4 ? sym_of(w, l - 1) : (int)x[t - l + 1]) : 0;
                 gk = (int)__umul24((uint32_t)gk, (uint32_t)K) + dig;
                 uint64_t m = ballot(v);
-                for (int b = 0; b < p.nbits; ++b) {
-                    const bool bit = (dig >> b) & 1;
-                    const uint64_t B = ballot(v && bit);
-                    m &= bit ? B : ~B;
+#pragma unroll
+                for (int b = 0; b < 8; ++b) {
+                    if (b < p.nbits) {
+                        const uint32_t bit = ((uint32_t)dig >> b) & 1u;
+                        const uint64_t B = ballot(bit != 0);
+                        m &= ~(B ^ (0ull - (uint64_t)bit));
+                    }
                 }
                 eq &= m;
                 const int slot = p.fl_off[l] + gk;
