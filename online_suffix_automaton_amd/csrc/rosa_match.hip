@@ -212,20 +212,27 @@ __device__ Found solve_wave(const uint8_t *x, int nbits, int t, uint64_t g,
             int c = fh ? (__clzll((long long)fh) >> 3)
                        : (fl ? 8 + (__clzll((long long)fl) >> 3) : 16);
             if (!(fh | fl)) {
+                // 64 symbols per step (long recurrences); every read stays
+                // at or after position -63 because c < aj <= t - ell and
+                // tj - ell - c >= 0, inside the rows' front padding
                 while (c < aj) {
-                    uint64_t alo, ahi, blo, bhi;
-                    load_window(x, t - ell - c - 15, alo, ahi);
-                    load_window(x, tj - ell - c - 15, blo, bhi);
-                    const uint64_t xh = ahi ^ bhi, xl = alo ^ blo;
-                    if (xh) {
-                        c += __clzll((long long)xh) >> 3;
+                    uint64_t xs[8];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        uint64_t alo, ahi, blo, bhi;
+                        load_window(x, t - ell - c - 15 - 16 * q, alo, ahi);
+                        load_window(x, tj - ell - c - 15 - 16 * q, blo, bhi);
+                        xs[2 * q] = ahi ^ bhi;
+                        xs[2 * q + 1] = alo ^ blo;
+                    }
+                    int k = 0;
+                    while (k < 8 && !xs[k])
+                        ++k;
+                    if (k < 8) {
+                        c += 8 * k + (__clzll((long long)xs[k]) >> 3);
                         break;
                     }
-                    if (xl) {
-                        c += 8 + (__clzll((long long)xl) >> 3);
-                        break;
-                    }
-                    c += 16;
+                    c += 64;
                 }
             }
             c = min(c, aj);
