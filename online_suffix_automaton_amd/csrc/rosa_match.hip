@@ -398,8 +398,9 @@ __device__ void phase_hist(const MatchParams &p, const uint8_t *x, int32_t *cnt,
 // Returns the number of tasks in misc[24] and the number of tasks of each
 // slot range in misc[kMiscPass + range] (tasks are in slot order, so the
 // tasks of one range are consecutive).
+template <class OffT>
 __device__ void phase_tasks(const MatchParams &p, int s, const int32_t *cnt,
-                            int32_t *off, uint32_t *tasks, int32_t *misc,
+                            OffT *off, uint32_t *tasks, int32_t *misc,
                             int pcap)
 {
     const int tid = threadIdx.x, nt = blockDim.x;
@@ -415,17 +416,17 @@ __device__ void phase_tasks(const MatchParams &p, int s, const int32_t *cnt,
         int ex = block_excl_scan(local, misc, &total);
         for (int q = 0; q < per; ++q)
             if (b0 + q < NB) {
-                off[b0 + q] = ex;
+                off[b0 + q] = (OffT)ex;
                 ex += cnt[b0 + q];
             }
         if (tid == 0)
-            off[NB] = total;
+            off[NB] = (OffT)total;
     }
     __syncthreads();
     // Each thread packs a run of `bpl` consecutive buckets (about 256
     // positions' worth, at least NB/nt so every bucket is covered); tasks
     // do not span runs, so longer runs pack tasks fuller.
-    const int avg = max(1, off[NB] / NB);
+    const int avg = max(1, (int)off[NB] / NB);
     const int bpl = max((NB + nt - 1) / nt, min(64, max(1, 256 / avg)));
     const int b0 = min(NB, tid * bpl), b1 = min(NB, b0 + bpl);
     int ntask = 0, cur = 0, crange = -1;
@@ -440,7 +441,7 @@ __device__ void phase_tasks(const MatchParams &p, int s, const int32_t *cnt,
             }
             continue;
         }
-        const int rg = off[b] / pcap;
+        const int rg = (int)off[b] / pcap;
         if (cur + c > 64 || (cur && rg != crange)) {
             ++ntask;
             cur = 0;
@@ -474,20 +475,20 @@ __device__ void phase_tasks(const MatchParams &p, int s, const int32_t *cnt,
                     int32_t *ent = p.big + 64 + 4 * (int64_t)idx;
                     ent[0] = s;
                     ent[1] = b;
-                    ent[2] = off[b];
+                    ent[2] = (int32_t)off[b];
                     ent[3] = c;
                 }
             }
             continue;
         }
-        const int rg = off[b] / pcap;
+        const int rg = (int)off[b] / pcap;
         if (cur + c > 64 || (cur && rg != crange)) {
             put_task(k++, start, cur);
             cur = 0;
         }
         crange = rg;
         if (cur == 0)
-            start = off[b];
+            start = (int)off[b];
         cur += c;
     }
     if (cur)
@@ -598,14 +599,14 @@ __device__ void phase_short(const MatchParams &p, const uint8_t *x,
 // thread (insertion sort in place).  The scatter that filled the buckets
 // appends in nearly increasing time, so each insertion moves an element a
 // few places at most.  `list` + off[k] - base holds bucket k's positions.
-template <class Ptr, class Sel>
-__device__ void sort_buckets(Ptr list, const int32_t *off, int NB, int base,
+template <class Ptr, class OffT, class Sel>
+__device__ void sort_buckets(Ptr list, const OffT *off, int NB, int base,
                              Sel selected)
 {
     for (int k = threadIdx.x; k < NB; k += blockDim.x) {
         if (!selected(k))
             continue;
-        const int b0 = off[k] - base, c = off[k + 1] - off[k];
+        const int b0 = (int)off[k] - base, c = (int)off[k + 1] - (int)off[k];
         for (int i = 1; i < c; ++i) {
             const auto v = list[b0 + i];
             int j = i - 1;
@@ -629,7 +630,7 @@ __device__ void sort_buckets(Ptr list, const int32_t *off, int NB, int base,
 // position in t_out.
 template <int DC, bool SORT, class Src>
 __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
-                          int n, int &t_out)
+                          int n, int &t_out, int &key_out)
 {
     const int lane = __lane_id();
     const uint64_t self = 1ull << lane;
@@ -637,6 +638,7 @@ __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
     const int t0 = has ? src(lane) : 0;
     const int d = DC > 0 ? DC : p.d;
     const int k0 = has ? dgram_key(x, t0, d, p.K) : -1;
+    key_out = k0;   // the lane's bucket (sorting stays inside buckets)
     const int kprev = __shfl_up(k0, 1);
     const uint64_t B = ballot(has && (lane == 0 || kprev != k0));
     const uint64_t upto = (self << 1) - 1;   // lanes 0..lane (lane 63: all)
@@ -681,7 +683,8 @@ __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
 // ------------------------------------------------- stream kernel (LDS)
 //
 // Streams of up to 65536 positions.  LDS: the padded symbol row, bucket
-// offsets and a union reused across phases:
+// offsets (16-bit), the answers of the buckets' first members, and a union
+// reused across phases:
 //   A-B  cnt[4096] | firstd[4096] | firstl[2048]
 //   D    pending u16[4112] | firstd | firstl | segment tables
 //   E    cursors u16[4096] | pass id u8[4096] | positions u16[kLposCap]
@@ -689,13 +692,13 @@ __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
 // per task), which leaves room for two passes over a 65536-position stream.
 // Phase E runs in passes over ranges of bucket slots that fit kLposCap:
 // each pass scatters the range's positions into LDS (LDS atomics on the
-// cursors), puts each bucket in time order, then the waves solve the
-// range's tasks from LDS.  All results are staged as records (coalesced)
-// and put into time order by unpermute_kernel: the first member of every
-// bucket (L < d) gets its record in the bucket's first slot from phase D,
-// every other position from its task.
+// cursors), then the waves solve the range's tasks from LDS, each task
+// putting its buckets in time order first.  All results are staged as
+// records, written by whole tasks so that the stores are coalesced, and
+// put into time order by unpermute_kernel.
 constexpr int kLdsSymBytes = 65792;
-constexpr int kUnionBytes = 163840 - kLdsSymBytes - (kMaxBuckets + 16) * 4 - 128;
+constexpr int kUnionBytes = 163840 - kLdsSymBytes - (kMaxBuckets + 16) * 2 -
+                            kMaxBuckets * 2 - 128;
 constexpr int kUSegTab = 40960;
 constexpr int kSegTabLds = (kUnionBytes - kUSegTab) / 4;
 constexpr int kLposCap = (kUnionBytes - 8192 - 4096) / 2;
@@ -707,7 +710,11 @@ template <int DC>
 __global__ __launch_bounds__(kStreamThreads) void stream_kernel_lds(MatchParams p)
 {
     __shared__ __align__(16) unsigned char symrow[kLdsSymBytes];
-    __shared__ int32_t off[kMaxBuckets + 16];
+    // bucket offsets fit 16 bits: off[NB] = T - d + 1 <= 65535
+    __shared__ uint16_t off[kMaxBuckets + 16];
+    // E+1 of each bucket's first member (L < d, from phase D), written
+    // with the bucket's task so all record stores stay coalesced
+    __shared__ uint16_t qres[kMaxBuckets];
     __shared__ int32_t misc[32];
     __shared__ __align__(16) unsigned char U[kUnionBytes];
     int32_t *cnt = reinterpret_cast<int32_t *>(U);
@@ -746,32 +753,41 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_lds(MatchParams 
     phase_tasks(p, s, cnt, off, tasks, misc, kPassCap);
 
     // D: records of the first d-1 positions go to the slots T-d+1.. (no
-    // bucket holds them); the first occurrence of a d-gram takes its
-    // bucket's first slot (after the bucket sort it is the bucket's first
-    // member, which its task leaves unwritten).
+    // bucket holds them); the first occurrence of a d-gram in a singleton
+    // or large bucket takes the bucket's first slot; for buckets of 2..64
+    // members the answer waits in qres until the bucket's task writes it.
     phase_short<DC>(p, x, firstd, firstl, segtab, kSegTabLds, pend, misc,
                 [&](int t, int e, int l) {
-                    if (t < d - 1)
+                    if (t < d - 1) {
                         emit_record(o, T - d + 1 + t, t, e, l);
-                    else
-                        emit_record(o, off[dgram_key(x, t, d, K)], t, e, l);
+                        return;
+                    }
+                    const int k = dgram_key(x, t, d, K);
+                    const int c = (int)off[k + 1] - (int)off[k];
+                    if (c == 1 || c > 64) {
+                        emit_record(o, off[k], t, e, l);
+                    } else {
+                        qres[k] = (uint16_t)(e + 1);
+                        if (o.L)
+                            o.L[t] = l;
+                    }
                 });
 
     // E: passes over slot ranges.  passid[k] is the pass that scatters
     // bucket k (255: not scattered, a singleton or large bucket).
     for (int i = tid; i < NB; i += nt) {
-        const int c = off[i + 1] - off[i];
-        passid[i] = (c >= 2 && c <= 64) ? (uint8_t)(off[i] / kPassCap) : (uint8_t)255;
+        const int c = (int)off[i + 1] - (int)off[i];
+        passid[i] = (c >= 2 && c <= 64) ? (uint8_t)((int)off[i] / kPassCap) : (uint8_t)255;
     }
-    const int nslots = off[NB];
+    const int nslots = (int)off[NB];
     int tfirst = 0;
     __syncthreads();
     for (int base = 0; base < nslots; base += kPassCap) {
         const int rg = base / kPassCap;
         for (int i = tid; i < (NB + 1) / 2; i += nt) {
             const int k0 = 2 * i, k1 = 2 * i + 1;
-            const uint32_t c0 = passid[k0] == rg ? (uint32_t)(off[k0] - base) : 0u;
-            const uint32_t c1 = (k1 < NB && passid[k1] == rg) ? (uint32_t)(off[k1] - base) : 0u;
+            const uint32_t c0 = passid[k0] == rg ? (uint32_t)((int)off[k0] - base) : 0u;
+            const uint32_t c1 = (k1 < NB && passid[k1] == rg) ? (uint32_t)((int)off[k1] - base) : 0u;
             cur2[i] = c0 | (c1 << 16);
         }
         __syncthreads();
@@ -809,11 +825,15 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_lds(MatchParams 
                 tk_next = __builtin_nontemporal_load(&tasks[ti + nw]);
             const int start = (int)(tk >> 6);
             const int n = (int)(tk & 63u) + 1;
-            int t;
+            int t, k;
             const Found f = run_task<DC, true>(
-                p, x, [&](int i) { return (int)lpos[start - base + i]; }, n, t);
-            if (lane < n && f.ok)
-                emit_record(o, start + lane, t, f.e, f.l);
+                p, x, [&](int i) { return (int)lpos[start - base + i]; }, n, t, k);
+            if (lane < n) {
+                if (f.ok)
+                    emit_record(o, start + lane, t, f.e, f.l);
+                else   // a bucket's first member: its answer from phase D
+                    o.rec[start + lane] = ((uint32_t)t << 16) | (uint32_t)qres[k];
+            }
         }
         __syncthreads();
     }
@@ -877,8 +897,8 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_hbm(MatchParams 
         const uint32_t tk = tasks[ti];
         const int start = (int)(tk >> 6);
         const int n = (int)(tk & 63u) + 1;
-        int t;
-        const Found f = run_task<0, false>(p, x, [&](int i) { return pos[start + i]; }, n, t);
+        int t, k;
+        const Found f = run_task<0, false>(p, x, [&](int i) { return pos[start + i]; }, n, t, k);
         if (lane < n && f.ok)
             emit(o, t, f.e, f.l);
     }
