@@ -95,6 +95,30 @@ def test_mixed_bucket_sizes():
     _run_symbols(sym, 16, "mixed")
 
 
+def test_lds_path_maximum_length():
+    """T = 65536, the longest stream the LDS-resident kernel takes, with a
+    small alphabet (deep bucketing, d = 11 for K = 2) and K = 16."""
+    rng = np.random.default_rng(21)
+    T = 65536
+    for K in (2, 16):
+        sym = rng.integers(0, K, size=(2, T), dtype=np.uint8)
+        _say(f"T={T} K={K}")
+        _run_symbols(sym, K, f"T={T} K={K}")
+
+
+def test_streams_longer_than_lds_path():
+    """T > 65536 takes the kernel with symbols and buckets in HBM: random
+    streams of two alphabets, planted copies, a periodic stream, and T
+    one past the LDS limit."""
+    rng = np.random.default_rng(22)
+    for T in (65537, 100003):
+        rows = [rng.integers(0, 16, T), rng.integers(0, 4, T),
+                synth.planted_copies(T, 16, 23), synth.periodic(T, [1, 2, 3, 5, 8])]
+        sym = np.stack([np.asarray(r, dtype=np.uint8) for r in rows])
+        _say(f"T={T} (HBM path)")
+        _run_symbols(sym, 16, f"T={T}")
+
+
 def test_strided_symbol_rows():
     rng = np.random.default_rng(8)
     base = rng.integers(0, 16, size=(6, 1500), dtype=np.uint8)
