@@ -15,6 +15,8 @@
 //   count   cnt[s][tau]        (integer atomics: order-free)
 //   scan    off[s][tau]        (exclusive prefix, one workgroup per stream)
 //   fill    list[s][off + i]   (unordered inside a destination)
+// (for streams of up to 65536 positions all three run in one workgroup per
+// stream with the counters in LDS)
 //   sum     one thread per (b, tau, route): walks its time steps in
 //           increasing order (selection over the few entries a destination
 //           has) and writes the route's M values of row tau; rows are
@@ -167,6 +169,91 @@ __global__ __launch_bounds__(256) void scatter_sum_kernel(ScatterParams p)
         g[m] = (float)acc[m];
 }
 
+// Streams of up to 65536 positions: count, prefix and fill of one stream in
+// one workgroup, with the per-destination counters in LDS (two 16-bit
+// halves per word: a destination is read by at most T-1 <= 65535 steps,
+// and a prefix plus its count never exceeds the number of valid steps).
+constexpr int kScatterLdsT = 65536;
+
+__global__ __launch_bounds__(1024) void scatter_group_lds_kernel(ScatterParams p)
+{
+    __shared__ uint32_t c2[kScatterLdsT / 2];   // 128 KiB
+    __shared__ int wsum[16];
+    __shared__ int carry_s;
+    const int64_t s = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int T = (int)p.T;
+    const int32_t *E = p.end + s * p.T;
+    const int nwords = (T + 1) / 2;
+    for (int i = tid; i < nwords; i += 1024)
+        c2[i] = 0u;
+    if (tid == 0)
+        carry_s = 0;
+    __syncthreads();
+    for (int t = tid; t < T; t += 1024) {
+        const int e = E[t];
+        if (e >= 0 && e + 1 < T) {
+            const int tau = e + 1;
+            atomicAdd(&c2[tau >> 1], 1u << (16 * (tau & 1)));
+        }
+    }
+    __syncthreads();
+    // exclusive prefix, 4096 destinations per round (4 per thread); the
+    // prefix goes to off[] for the sum kernel and back into c2 as cursors
+    int32_t *off = p.off + s * p.Tq;
+    for (int c0 = 0; c0 < T; c0 += 4096) {
+        const int w0 = (c0 >> 1) + 2 * tid;
+        const uint32_t a = w0 < nwords ? c2[w0] : 0u;
+        const uint32_t b = w0 + 1 < nwords ? c2[w0 + 1] : 0u;
+        const int v0 = (int)(a & 0xFFFFu), v1 = (int)(a >> 16);
+        const int v2 = (int)(b & 0xFFFFu), v3 = (int)(b >> 16);
+        const int sum = v0 + v1 + v2 + v3;
+        const int incl = sc_wave_incl_scan(sum);
+        if (lane == 63)
+            wsum[wid] = incl;
+        __syncthreads();
+        if (wid == 0) {
+            const int w = lane < 16 ? wsum[lane] : 0;
+            const int wi = sc_wave_incl_scan(w);
+            if (lane < 16)
+                wsum[lane] = wi - w;
+        }
+        __syncthreads();
+        const int r0 = carry_s + wsum[wid] + incl - sum;
+        const int r1 = r0 + v0, r2 = r1 + v1, r3 = r2 + v2;
+        const int tau0 = c0 + 4 * tid;
+        if (tau0 < T)
+            off[tau0] = r0;
+        if (tau0 + 1 < T)
+            off[tau0 + 1] = r1;
+        if (tau0 + 2 < T)
+            off[tau0 + 2] = r2;
+        if (tau0 + 3 < T)
+            off[tau0 + 3] = r3;
+        if (w0 < nwords)
+            c2[w0] = (uint32_t)r0 | ((uint32_t)r1 << 16);
+        if (w0 + 1 < nwords)
+            c2[w0 + 1] = (uint32_t)r2 | ((uint32_t)r3 << 16);
+        __syncthreads();
+        if (tid == 1023)
+            carry_s = r3 + v3;
+        __syncthreads();
+    }
+    if (tid == 0)
+        off[T] = carry_s;
+    __syncthreads();
+    int32_t *list = p.list + s * p.T;
+    for (int t = tid; t < T; t += 1024) {
+        const int e = E[t];
+        if (e >= 0 && e + 1 < T) {
+            const int tau = e + 1;
+            const uint32_t sh = 16u * (uint32_t)(tau & 1);
+            const uint32_t old = atomicAdd(&c2[tau >> 1], 1u << sh);
+            list[(old >> sh) & 0xFFFFu] = t;
+        }
+    }
+}
+
 // One wave per destination with many time steps: the stream's time steps
 // are visited in order, 64 at a time; lanes m < M hold channel m's sum.
 template <int MC>
@@ -198,14 +285,20 @@ __global__ __launch_bounds__(64) void scatter_big_kernel(ScatterParams p)
 hipError_t launch_scatter(const ScatterParams &p, hipStream_t st)
 {
     const int64_t S = p.B * p.R;
-    hipLaunchKernelGGL(scatter_zero_kernel, dim3(1024), dim3(256), 0, st, p.cnt,
-                       S * p.T);
     hipLaunchKernelGGL(scatter_zero_kernel, dim3(1), dim3(64), 0, st, p.big,
                        (int64_t)64);
-    const dim3 gt((unsigned)((p.T + 255) / 256), (unsigned)S);
-    hipLaunchKernelGGL(scatter_count_kernel, gt, dim3(256), 0, st, p);
-    hipLaunchKernelGGL(scatter_scan_kernel, dim3((unsigned)S), dim3(1024), 0, st, p);
-    hipLaunchKernelGGL(scatter_fill_kernel, gt, dim3(256), 0, st, p);
+    if (p.T <= kScatterLdsT) {
+        hipLaunchKernelGGL(scatter_group_lds_kernel, dim3((unsigned)S), dim3(1024),
+                           0, st, p);
+    } else {
+        hipLaunchKernelGGL(scatter_zero_kernel, dim3(1024), dim3(256), 0, st,
+                           p.cnt, S * p.T);
+        const dim3 gt((unsigned)((p.T + 255) / 256), (unsigned)S);
+        hipLaunchKernelGGL(scatter_count_kernel, gt, dim3(256), 0, st, p);
+        hipLaunchKernelGGL(scatter_scan_kernel, dim3((unsigned)S), dim3(1024), 0,
+                           st, p);
+        hipLaunchKernelGGL(scatter_fill_kernel, gt, dim3(256), 0, st, p);
+    }
     const dim3 gs((unsigned)((p.T + 3) / 4), (unsigned)((p.R + 63) / 64),
                   (unsigned)p.B);
     const unsigned gb = 1024;

@@ -86,6 +86,19 @@ def test_scatter_out_of_range_and_padding():
              oracle.scatter_grad(theta, E, M), "range/padding")
 
 
+@pytest.mark.parametrize("T", [65536, 70001])
+def test_scatter_stream_length_limits(T):
+    """The longest streams counted in LDS (65536) and longer ones, which
+    take the counting kernels with counters in HBM."""
+    rng = np.random.default_rng(T)
+    B, D, M = 1, 8, 4
+    S = D // M
+    E = rng.integers(-1, T - 1, (S, T)).astype(np.int32)
+    E[1, : T // 2] = 7          # one destination read by half the stream
+    theta = rng.standard_normal((B, T, D)).astype(np.float32)
+    _compare(_run(theta, E, M), oracle.scatter_grad(theta, E, M), f"T={T}")
+
+
 def test_scatter_deterministic():
     rng = np.random.default_rng(5)
     B, T, D, M = 1, 4096, 256, 4
