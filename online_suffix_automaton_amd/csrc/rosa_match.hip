@@ -682,51 +682,76 @@ __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
 
 // ------------------------------------------------- stream kernel (LDS)
 //
-// Streams of up to 65536 positions.  LDS: the padded symbol row, bucket
-// offsets (16-bit), the answers of the buckets' first members, and a union
-// reused across phases:
-//   A-B  cnt[4096] | firstd[4096] | firstl[2048]
-//   D    pending u16[4112] | firstd | firstl | segment tables
-//   E    cursors u16[4096] | pass id u8[4096] | positions u16[kLposCap]
+// Streams of up to 65536 positions: one workgroup per stream with the
+// padded symbol row, 16-bit bucket offsets, the answers of the buckets'
+// first members and a union reused across phases in LDS (plan below).
 // The task list lives in the workspace (written once in phase B, read once
-// per task), which leaves room for two passes over a 65536-position stream.
-// Phase E runs in passes over ranges of bucket slots that fit kLposCap:
-// each pass scatters the range's positions into LDS (LDS atomics on the
-// cursors), then the waves solve the range's tasks from LDS, each task
-// putting its buckets in time order first.  All results are staged as
-// records, written by whole tasks so that the stores are coalesced, and
-// put into time order by unpermute_kernel.
-constexpr int kLdsSymBytes = 65792;
-constexpr int kUnionBytes = 163840 - kLdsSymBytes - (kMaxBuckets + 16) * 2 -
-                            kMaxBuckets * 2 - 128;
-constexpr int kUSegTab = 40960;
-constexpr int kSegTabLds = (kUnionBytes - kUSegTab) / 4;
-constexpr int kLposCap = (kUnionBytes - 8192 - 4096) / 2;
-constexpr int kPassCap = kLposCap - 64;
+// per task).  Phase E runs in passes over ranges of bucket slots that fit
+// the position buffer: each pass scatters the range's positions into LDS
+// (LDS atomics on the cursors), then the waves solve the range's tasks
+// from LDS, each task putting its buckets in time order first.  All
+// results are staged as records, written by whole tasks so that the stores
+// are coalesced, and put into time order by unpermute_kernel.
+// LDS plan for streams of up to TMAX positions and THREADS threads per
+// workgroup (all sizes in bytes; B buckets, F first-occurrence entries):
+//   A-B  cnt [0, 4B) | firstd [4B, 8B) | firstl [8B, 8B+4F)
+//   D    pending u16 [0, 4B) | firstd | firstl | segment tables [8B+4F, U)
+//   E    cursors [0, 2B+16) | pass id [2B+16, 3B+32) | positions u16
+// d-gram buckets: K^d <= max(min(4096, T/8), K), so B = that bound for
+// TMAX (K <= 256); first-occurrence tables: sum_{l<d} K^l < K^d, or at
+// most 11 entries when K = 1.
+template <int TMAX, int THREADS, int UNION>
+struct LdsCfg {
+    static constexpr int kThreads = THREADS;
+    static constexpr int kTMax = TMAX;
+    static constexpr int kSymBytes = (TMAX + kPadFront + kPadBack + 255) / 256 * 256;
+    static constexpr int kBuckets =
+        TMAX / 8 >= kMaxBuckets ? kMaxBuckets : (TMAX / 8 > 256 ? TMAX / 8 : 256);
+    static constexpr int kFirst = (kBuckets < kMaxFirstTab ? kBuckets : kMaxFirstTab) + 16;
+    static constexpr int kUnion = UNION;
+    static constexpr int kUFirstd = 4 * kBuckets;
+    static constexpr int kUFirstl = 8 * kBuckets;
+    static constexpr int kUSegTab = 8 * kBuckets + 4 * kFirst;
+    static constexpr int kSegTab = (kUnion - kUSegTab) / 4;
+    static constexpr int kUPassId = 2 * kBuckets + 16;
+    static constexpr int kULpos = 3 * kBuckets + 32;
+    static constexpr int kLposCap = (kUnion - kULpos) / 2;
+    static constexpr int kPassCap = kLposCap - 64;
+    static_assert(kSegTab > 0 && kLposCap > 64, "LDS plan");
+};
+
+// Streams of up to 65536 positions, one 1024-thread workgroup per CU (the
+// whole LDS: two scatter passes for a 65536-position stream).
+using CfgLarge = LdsCfg<65536, 1024,
+                        163840 - 65792 - (kMaxBuckets + 16) * 2 - kMaxBuckets * 2 - 128>;
+// Streams of up to 8192 positions: 41 KiB per 512-thread workgroup, so
+// three workgroups share a CU.
+using CfgSmall = LdsCfg<8192, 512, 28672>;
 
 // DC: the bucketing depth d as a compile-time constant (1..4), or 0 to read
 // it from p.
-template <int DC>
-__global__ __launch_bounds__(kStreamThreads) void stream_kernel_lds(MatchParams p)
+template <class Cfg, int DC>
+__global__ __launch_bounds__(Cfg::kThreads) void stream_kernel_lds(MatchParams p)
 {
-    __shared__ __align__(16) unsigned char symrow[kLdsSymBytes];
+    constexpr int kPassCap = Cfg::kPassCap;
+    __shared__ __align__(16) unsigned char symrow[Cfg::kSymBytes];
     // bucket offsets fit 16 bits: off[NB] = T - d + 1 <= 65535
-    __shared__ uint16_t off[kMaxBuckets + 16];
+    __shared__ uint16_t off[Cfg::kBuckets + 16];
     // E+1 of each bucket's first member (L < d, from phase D), written
     // with the bucket's task so all record stores stay coalesced
-    __shared__ uint16_t qres[kMaxBuckets];
+    __shared__ uint16_t qres[Cfg::kBuckets];
     __shared__ int32_t misc[32];
-    __shared__ __align__(16) unsigned char U[kUnionBytes];
+    __shared__ __align__(16) unsigned char U[Cfg::kUnion];
     int32_t *cnt = reinterpret_cast<int32_t *>(U);
-    int32_t *firstd = reinterpret_cast<int32_t *>(U + 16384);
-    int32_t *firstl = reinterpret_cast<int32_t *>(U + 32768);
+    int32_t *firstd = reinterpret_cast<int32_t *>(U + Cfg::kUFirstd);
+    int32_t *firstl = reinterpret_cast<int32_t *>(U + Cfg::kUFirstl);
     uint16_t *pend = reinterpret_cast<uint16_t *>(U);
-    int32_t *segtab = reinterpret_cast<int32_t *>(U + kUSegTab);
+    int32_t *segtab = reinterpret_cast<int32_t *>(U + Cfg::kUSegTab);
     // bucket k's cursor is half k & 1 of word k >> 1 (slot relative to the
     // pass, < 65536, so an increment never carries into the other half)
     uint32_t *cur2 = reinterpret_cast<uint32_t *>(U);
-    uint8_t *passid = U + 8192;
-    uint16_t *lpos = reinterpret_cast<uint16_t *>(U + 8192 + 4096);
+    uint8_t *passid = U + Cfg::kUPassId;
+    uint16_t *lpos = reinterpret_cast<uint16_t *>(U + Cfg::kULpos);
     uint32_t *tasks = p.tasks + (int64_t)blockIdx.x * kTaskCap;
 
     const int s = blockIdx.x;
@@ -756,7 +781,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_lds(MatchParams 
     // bucket holds them); the first occurrence of a d-gram in a singleton
     // or large bucket takes the bucket's first slot; for buckets of 2..64
     // members the answer waits in qres until the bucket's task writes it.
-    phase_short<DC>(p, x, firstd, firstl, segtab, kSegTabLds, pend, misc,
+    phase_short<DC>(p, x, firstd, firstl, segtab, Cfg::kSegTab, pend, misc,
                 [&](int t, int e, int l) {
                     if (t < d - 1) {
                         emit_record(o, T - d + 1 + t, t, e, l);
@@ -1214,27 +1239,25 @@ bool stream_uses_records(int64_t T) { return T <= 65536; }
 hipError_t launch_stream(const MatchParams &p, int64_t S, hipStream_t st)
 {
     if (stream_uses_records(p.T)) {
+        const bool small = p.T <= CfgSmall::kTMax;
+        const dim3 grid((unsigned)S);
+#define ROSA_LAUNCH_LDS(D)                                                          \
+    do {                                                                            \
+        if (small)                                                                  \
+            hipLaunchKernelGGL((stream_kernel_lds<CfgSmall, D>), grid,              \
+                               dim3(CfgSmall::kThreads), 0, st, p);                 \
+        else                                                                        \
+            hipLaunchKernelGGL((stream_kernel_lds<CfgLarge, D>), grid,              \
+                               dim3(CfgLarge::kThreads), 0, st, p);                 \
+    } while (0)
         switch (p.d) {
-        case 1:
-            hipLaunchKernelGGL(stream_kernel_lds<1>, dim3((unsigned)S),
-                               dim3(kStreamThreads), 0, st, p);
-            break;
-        case 2:
-            hipLaunchKernelGGL(stream_kernel_lds<2>, dim3((unsigned)S),
-                               dim3(kStreamThreads), 0, st, p);
-            break;
-        case 3:
-            hipLaunchKernelGGL(stream_kernel_lds<3>, dim3((unsigned)S),
-                               dim3(kStreamThreads), 0, st, p);
-            break;
-        case 4:
-            hipLaunchKernelGGL(stream_kernel_lds<4>, dim3((unsigned)S),
-                               dim3(kStreamThreads), 0, st, p);
-            break;
-        default:
-            hipLaunchKernelGGL(stream_kernel_lds<0>, dim3((unsigned)S),
-                               dim3(kStreamThreads), 0, st, p);
+        case 1: ROSA_LAUNCH_LDS(1); break;
+        case 2: ROSA_LAUNCH_LDS(2); break;
+        case 3: ROSA_LAUNCH_LDS(3); break;
+        case 4: ROSA_LAUNCH_LDS(4); break;
+        default: ROSA_LAUNCH_LDS(0); break;
         }
+#undef ROSA_LAUNCH_LDS
     } else
         hipLaunchKernelGGL(stream_kernel_hbm, dim3((unsigned)S),
                            dim3(kStreamThreads), 0, st, p);
