@@ -536,9 +536,13 @@ def main():
     if rosa.rosa_match_status(ws) != rosa.ROSA_OK:
         raise SystemExit("symbol range flag raised")
     if args.copy_reference > 0:
-        src = torch.empty(args.copy_reference, dtype=torch.uint8, device=dev)
+        # two plain copies of known size for scaling HBM byte counters: the
+        # runtime's buffer copy, and an elementwise kernel (int32 x + 1) that
+        # reads and writes with ordinary vector loads and stores
+        src = torch.zeros(args.copy_reference // 4, dtype=torch.int32, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
+        torch.add(src, 1, out=dst)
         torch.cuda.synchronize()
         del src, dst
     value = S * T / (ms_step / 1e3)
