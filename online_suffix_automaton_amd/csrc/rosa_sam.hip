@@ -278,7 +278,6 @@ __global__ __launch_bounds__(64) void sam_step_kernel(
 // have identical transition rows, and the next query update leaves the
 // state through a transition or a suffix link, so both give the same
 // result.
-constexpr int kQkMaxM = 8;
 
 // One matching update by symbol c: follow suffix links until a transition
 // on c exists, take it (length + 1), or fall to the root (length 0).
@@ -302,14 +301,20 @@ __device__ __forceinline__ void qk_advance(const SamStream &a, int &s, int &l,
     }
 }
 
+// One wave per stream: lane 0 advances the matching state and appends the
+// key units; lanes 1..M make the counterfactual updates (bit lane-1 of the
+// query symbol flipped) from the same state at the same time.  Only lane 0
+// writes the automaton; a workgroup barrier (the workgroup is this one
+// wave) orders its writes before the next unit's reads by the other lanes.
 __global__ __launch_bounds__(64) void qk_kernel(QkParams p)
 {
     const int lane = threadIdx.x;
-    if (lane >= p.spw)
-        return;
-    const int64_t s = (int64_t)blockIdx.x * p.spw + lane;
+    const int64_t s = blockIdx.x;
     if (s >= p.S)
         return;
+    const bool want_cf = p.cf_tau || p.cf_ridx;
+    const int nl = want_cf ? 1 + p.M : 1;   // active lanes
+    const bool act = lane < nl;
     const int64_t T = p.T;
     SamStream a;
     a.nd = p.nodes + s * p.Ncap;
@@ -317,65 +322,78 @@ __global__ __launch_bounds__(64) void qk_kernel(QkParams p)
     a.K = p.K;
     a.tail = 0;
     a.nst = 0;
-    sam_new_state(a, 0);
+    if (lane == 0)
+        sam_new_state(a, 0);
+    a.nst = 1;
+    __syncthreads();
     const uint8_t *qr = p.q + s * p.Tp + kPadFront;
     const uint8_t *kr = p.k + s * p.Tp + kPadFront;
     int32_t *st = p.start + s * T;
-    const bool want_cf = p.cf_tau || p.cf_ridx;
+    // lane 0: the forward pass; lane j+1: bit j forced to the other value
     int u = -1, ms = 0, ml = 0, ue = -1, ul = 0, dstart = -1, kprev = -1, qc = 0;
-    int cfe[kQkMaxM], cfs[kQkMaxM];
     for (int64_t t = 0; t < T; ++t) {
         const int kc = kr[t];
         if (!p.rle || kc != kprev) {
             ++u;
-            st[u] = (int32_t)t;
+            if (lane == 0)
+                st[u] = (int32_t)t;
             qc = qr[t];
-            if (want_cf) {
-                for (int j = 0; j < p.M; ++j) {
-                    int s2 = ms, l2 = ml;
-                    qk_advance(a, s2, l2, qc ^ (1 << j));
-                    cfe[j] = l2 > 0 ? a.nd[s2].z : -1;
-                    cfs[j] = cfe[j] >= 0 ? st[cfe[j] + 1] : -1;
+            __syncthreads();   // start of unit u visible to every lane
+            if (act) {
+                int s2 = ms, l2 = ml;
+                qk_advance(a, s2, l2, lane == 0 ? qc : (qc ^ (1 << (lane - 1))));
+                ue = l2 > 0 ? a.nd[s2].z : -1;
+                ul = l2;
+                dstart = ue >= 0 ? st[ue + 1] : -1;
+                if (lane == 0) {
+                    ms = s2;
+                    ml = l2;
                 }
             }
-            qk_advance(a, ms, ml, qc);
-            ul = ml;
-            ue = ml > 0 ? a.nd[ms].z : -1;
-            dstart = ue >= 0 ? st[ue + 1] : -1;
-            const int cur = sam_extend(a, kc);
-            for (int w = cur; w != -1; w = a.nd[w].y)
-                a.nd[w].z = u;
+            __syncthreads();   // every read of this unit before the append
+            if (lane == 0) {
+                const int cur = sam_extend(a, kc);
+                for (int w = cur; w != -1; w = a.nd[w].y)
+                    a.nd[w].z = u;
+            }
+            // every lane follows lane 0's matching state
+            ms = __shfl(ms, 0);
+            ml = __shfl(ml, 0);
+            __syncthreads();   // this unit's appends before the next reads
             kprev = kc;
         }
         const int64_t o = s * T + t;
-        const int tt = (ue >= 0 && dstart < t) ? dstart : -1;
-        p.tau[o] = tt;
-        if (p.end)
-            p.end[o] = ue;
-        if (p.len)
-            p.len[o] = ul;
-        if (p.run_of)
-            p.run_of[o] = u;
-        if (p.ridx)
-            p.ridx[o] = tt >= 0 ? ue + 1 : -1;
-        if (want_cf) {
-            for (int j = 0; j < p.M; ++j) {
-                const int b = (qc >> j) & 1;
-                const int ct = (cfe[j] >= 0 && cfs[j] < t) ? cfs[j] : -1;
-                const int64_t c0 = (o * p.M + j) * 2;
-                if (p.cf_tau) {
-                    p.cf_tau[c0 + b] = tt;
-                    p.cf_tau[c0 + 1 - b] = ct;
-                }
-                if (p.cf_ridx) {
-                    p.cf_ridx[c0 + b] = tt >= 0 ? ue + 1 : -1;
-                    p.cf_ridx[c0 + 1 - b] = ct >= 0 ? cfe[j] + 1 : -1;
-                }
+        // lane v's destination for this time step
+        const int tv = (ue >= 0 && dstart < t) ? dstart : -1;
+        const int rv = tv >= 0 ? ue + 1 : -1;
+        const int tt = __shfl(tv, 0), rt = __shfl(rv, 0);
+        if (lane == 0) {
+            p.tau[o] = tt;
+            if (p.end)
+                p.end[o] = ue;
+            if (p.len)
+                p.len[o] = ul;
+            if (p.run_of)
+                p.run_of[o] = u;
+            if (p.ridx)
+                p.ridx[o] = rt;
+        }
+        if (want_cf && lane >= 1 && lane <= p.M) {
+            const int j = lane - 1;
+            const int b = (qc >> j) & 1;
+            const int64_t c0 = (o * p.M + j) * 2;
+            if (p.cf_tau) {
+                p.cf_tau[c0 + b] = tt;
+                p.cf_tau[c0 + 1 - b] = tv;
+            }
+            if (p.cf_ridx) {
+                p.cf_ridx[c0 + b] = rt;
+                p.cf_ridx[c0 + 1 - b] = rv;
             }
         }
     }
     if (p.run_start)
-        for (int64_t v = 0; v < T; ++v)
+        for (int64_t v = lane; v < T; v += 64)
             p.run_start[s * T + v] = v <= u ? st[v] : -1;
 }
 
@@ -461,13 +479,10 @@ hipError_t launch_sam_step(void *buf, int64_t S, int64_t K, int64_t Tcap,
     return hipGetLastError();
 }
 
-constexpr int kQkStreamsPerWave = 1;
-
 hipError_t launch_qk(QkParams p, hipStream_t st)
 {
-    p.spw = kQkStreamsPerWave;
-    dim3 grid((unsigned)((p.S + p.spw - 1) / p.spw));
-    hipLaunchKernelGGL(qk_kernel, grid, dim3(64), 0, st, p);
+    p.spw = 1;
+    hipLaunchKernelGGL(qk_kernel, dim3((unsigned)p.S), dim3(64), 0, st, p);
     return hipGetLastError();
 }
 
