@@ -397,6 +397,267 @@ __global__ __launch_bounds__(64) void qk_kernel(QkParams p)
             p.run_start[s * T + v] = v <= u ? st[v] : -1;
 }
 
+// ---------------------------------- query / key retrieval, tables in LDS
+//
+// The same automaton and matching state as qk_kernel for streams of at most
+// MT time steps over at most 64 symbols, with every table in the
+// workgroup's LDS instead of HBM:
+//   ll[v]     len(v) | (link(v) + 1) << 16        (2T - 1 states at most)
+//   lastu[v]  last end unit of v (0xFFFF: none)
+//   st[u]     start time of unit u
+//   ht        transitions as an open-addressing hash table: entry
+//             (v*K + c) << 13 | target, linear probing; the automaton has at
+//             most 3T - 4 transitions (Blumer et al.), so the table (6 MT
+//             slots) is at most half full and every probe ends at a free slot.
+// 152 KiB at MT = 4096 (one stream per CU), 76 KiB at 2048 (two), 38 KiB at
+// 1024 (four).  One wave per stream.  The append is computed by every lane
+// on the same values (LDS reads of one address are broadcasts) and written
+// by lane 0; the transitions of a split state are copied by lanes 0..K-1,
+// one symbol each.  The wave's LDS instructions complete in issue order, so
+// the lanes see each other's writes in program order with no barrier (the
+// workgroup is this one wave), and no global store is waited for inside
+// the loop.  Outputs are staged in registers, lane i holding time step
+// t0 + i, and written 64 steps at a time.
+constexpr int kQlTgtBits = 13;
+constexpr uint32_t kQlEmpty = 0xFFFFFFFFu;
+constexpr int kQlMaxK = 64;   // (states * K) << 13 must fit 32 bits
+
+template <int MT>
+struct QlCfg {
+    static constexpr int kStates = 2 * MT;
+    static constexpr int kSlots = 6 * MT;
+    static constexpr size_t kLds = (size_t)kSlots * 4 + (size_t)kStates * 6 + (size_t)MT * 2;
+};
+
+struct QlHit {
+    int tgt;    // target state, or -1
+    int slot;   // slot holding the key, else the free slot that ends the probe
+};
+
+template <int NS>
+__device__ __forceinline__ QlHit ql_find(const uint32_t *ht, uint32_t key)
+{
+    uint32_t slot = __umulhi(key * 0x9E3779B1u, (uint32_t)NS);
+    for (;;) {
+        const uint32_t e = ht[slot];
+        if (e == kQlEmpty)
+            return {-1, (int)slot};
+        if ((e >> kQlTgtBits) == key)
+            return {(int)(e & ((1u << kQlTgtBits) - 1)), (int)slot};
+        slot = slot + 1 == (uint32_t)NS ? 0u : slot + 1;
+    }
+}
+
+__device__ __forceinline__ int ql_link(uint32_t w) { return (int)(w >> 16) - 1; }
+__device__ __forceinline__ int ql_len(uint32_t w) { return (int)(w & 0xFFFFu); }
+__device__ __forceinline__ int ql_uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+template <int MT>
+__global__ __launch_bounds__(64) void qk_lds_kernel(QkParams p)
+{
+    using C = QlCfg<MT>;
+    constexpr int NS = C::kSlots;
+    __shared__ __align__(16) uint32_t ht[NS];
+    __shared__ uint32_t ll[C::kStates];
+    __shared__ uint16_t lastu[C::kStates];
+    __shared__ uint16_t st[MT];
+    const int lane = threadIdx.x;
+    const int64_t s = blockIdx.x;
+    const int T = (int)p.T, K = p.K, M = p.M;
+    const bool want_cf = p.cf_tau || p.cf_ridx;
+    const int nl = want_cf ? 1 + M : 1;
+    {
+        uint4 *h4 = reinterpret_cast<uint4 *>(ht);
+        for (int i = lane; i < NS / 4; i += 64)
+            h4[i] = make_uint4(kQlEmpty, kQlEmpty, kQlEmpty, kQlEmpty);
+        if (lane == 0) {
+            ll[0] = 0;          // root: len 0, no link
+            lastu[0] = 0xFFFF;
+        }
+    }
+    __syncthreads();
+    const uint8_t *qr = p.q + s * p.Tp + kPadFront;
+    const uint8_t *kr = p.k + s * p.Tp + kPadFront;
+    const int64_t base = s * (int64_t)T;
+    int u = -1, ms = 0, ml = 0, kprev = -1, qc = 0;
+    int tail = 0, tlen = 0, nst = 1;
+    int ue = -1, ul = 0, dstart = -1;   // this lane's chain (lane j+1: bit j flipped)
+    // the rows carry 64 bytes of padding after T: chunk loads stay in the row
+    int kn = kr[lane], qn = qr[lane];
+    for (int t0 = 0; t0 < T; t0 += 64) {
+        const int kch = kn, qch = qn;
+        if (t0 + 64 < T) {
+            kn = kr[t0 + 64 + lane];
+            qn = qr[t0 + 64 + lane];
+        }
+        int o_tau = -1, o_end = -1, o_len = 0, o_run = -1, o_ridx = -1;
+        int o_ct[16], o_cr[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            o_ct[i] = -1;
+            o_cr[i] = -1;
+        }
+        const int n = T - t0 < 64 ? T - t0 : 64;
+        for (int j = 0; j < n; ++j) {
+            const int t = t0 + j;
+            const int kc = __builtin_amdgcn_readlane(kch, j);
+            if (!p.rle || kc != kprev) {
+                ++u;
+                qc = __builtin_amdgcn_readlane(qch, j);
+                if (lane == 0)
+                    st[u] = (uint16_t)t;
+                // matching updates: lane 0 by q, lane j+1 by q with bit j flipped
+                int s2 = ms, l2 = ml;
+                if (lane < nl) {
+                    const int c = lane == 0 ? qc : (qc ^ (1 << ((lane - 1) & 7)));
+                    for (;;) {
+                        const QlHit h = ql_find<NS>(ht, (uint32_t)(s2 * K + c));
+                        if (h.tgt >= 0) {
+                            s2 = h.tgt;
+                            ++l2;
+                            break;
+                        }
+                        if (s2 == 0) {
+                            l2 = 0;
+                            break;
+                        }
+                        s2 = ql_link(ll[s2]);
+                        l2 = ql_len(ll[s2]);
+                    }
+                    const int lu = lastu[s2];
+                    ue = l2 > 0 ? lu : -1;
+                    ul = l2;
+                    dstart = ue >= 0 ? (int)st[ue + 1] : -1;
+                }
+                ms = __builtin_amdgcn_readlane(s2, 0);
+                ml = __builtin_amdgcn_readlane(l2, 0);
+                // append key symbol kc
+                const int cur = nst++;
+                int pp = tail, q = -1, lp = 0;
+                while (pp >= 0) {
+                    const uint32_t key = (uint32_t)(pp * K + kc);
+                    const uint32_t wp = ll[pp];
+                    const QlHit h = ql_find<NS>(ht, key);
+                    const int tg = ql_uni(h.tgt);
+                    if (tg >= 0) {
+                        q = tg;
+                        lp = ql_len(wp);
+                        break;
+                    }
+                    if (lane == 0)
+                        ht[h.slot] = key << kQlTgtBits | (uint32_t)cur;
+                    pp = ql_uni(ql_link(wp));
+                }
+                int lk = 0;
+                if (pp >= 0) {
+                    const uint32_t wq = (uint32_t)ql_uni((int)ll[q]);
+                    if (lp + 1 == ql_len(wq)) {
+                        lk = q;
+                    } else {
+                        const int cl = nst++;
+                        if (lane == 0) {
+                            ll[cl] = (uint32_t)(lp + 1) | (wq & 0xFFFF0000u);
+                            lastu[cl] = lastu[q];
+                        }
+                        if (lane < K) {
+                            const QlHit h = ql_find<NS>(ht, (uint32_t)(q * K + lane));
+                            if (h.tgt >= 0) {
+                                const uint32_t key = (uint32_t)(cl * K + lane);
+                                const uint32_t e = key << kQlTgtBits | (uint32_t)h.tgt;
+                                uint32_t slot = __umulhi(key * 0x9E3779B1u, (uint32_t)NS);
+                                while (atomicCAS(&ht[slot], kQlEmpty, e) != kQlEmpty)
+                                    slot = slot + 1 == (uint32_t)NS ? 0u : slot + 1;
+                            }
+                        }
+                        // redirect (v, kc) -> q to the clone up the suffix path
+                        while (pp >= 0) {
+                            const uint32_t key = (uint32_t)(pp * K + kc);
+                            const uint32_t wp = ll[pp];
+                            const QlHit h = ql_find<NS>(ht, key);
+                            if (ql_uni(h.tgt) != q)
+                                break;
+                            if (lane == 0)
+                                ht[h.slot] = key << kQlTgtBits | (uint32_t)cl;
+                            pp = ql_uni(ql_link(wp));
+                        }
+                        if (lane == 0)
+                            ll[q] = (wq & 0xFFFFu) | (uint32_t)(cl + 1) << 16;
+                        lk = cl;
+                    }
+                }
+                if (lane == 0)
+                    ll[cur] = (uint32_t)(tlen + 1) | (uint32_t)(lk + 1) << 16;
+                // every state on the new state's suffix path ends at unit u
+                for (int w = cur; w >= 0; w = ql_uni(ql_link(ll[w])))
+                    if (lane == 0)
+                        lastu[w] = (uint16_t)u;
+                tail = cur;
+                ++tlen;
+                kprev = kc;
+            }
+            // this step's outputs, staged in lane j
+            const int tv = (ue >= 0 && dstart < t) ? dstart : -1;
+            const int rv = tv >= 0 ? ue + 1 : -1;
+            const int tt = __builtin_amdgcn_readlane(tv, 0);
+            const int rt = __builtin_amdgcn_readlane(rv, 0);
+            const int e0 = __builtin_amdgcn_readlane(ue, 0);
+            const int l0 = __builtin_amdgcn_readlane(ul, 0);
+            if (lane == j) {
+                o_tau = tt;
+                o_end = e0;
+                o_len = l0;
+                o_run = u;
+                o_ridx = rt;
+            }
+            if (want_cf) {
+#pragma unroll
+                for (int b = 0; b < 8; ++b) {
+                    if (b < M) {
+                        const int tb = __builtin_amdgcn_readlane(tv, b + 1);
+                        const int rb = __builtin_amdgcn_readlane(rv, b + 1);
+                        const int bit = (qc >> b) & 1;
+                        if (lane == j) {
+                            o_ct[2 * b] = bit ? tb : tt;
+                            o_ct[2 * b + 1] = bit ? tt : tb;
+                            o_cr[2 * b] = bit ? rb : rt;
+                            o_cr[2 * b + 1] = bit ? rt : rb;
+                        }
+                    }
+                }
+            }
+        }
+        if (lane < n) {
+            const int64_t o = base + t0 + lane;
+            p.tau[o] = o_tau;
+            if (p.end)
+                p.end[o] = o_end;
+            if (p.len)
+                p.len[o] = o_len;
+            if (p.run_of)
+                p.run_of[o] = o_run;
+            if (p.ridx)
+                p.ridx[o] = o_ridx;
+            if (want_cf) {
+#pragma unroll
+                for (int b = 0; b < 8; ++b) {
+                    if (b < M) {
+                        const int64_t c0 = (o * M + b) * 2;
+                        if (p.cf_tau)
+                            *reinterpret_cast<int2 *>(p.cf_tau + c0) =
+                                make_int2(o_ct[2 * b], o_ct[2 * b + 1]);
+                        if (p.cf_ridx)
+                            *reinterpret_cast<int2 *>(p.cf_ridx + c0) =
+                                make_int2(o_cr[2 * b], o_cr[2 * b + 1]);
+                    }
+                }
+            }
+        }
+    }
+    if (p.run_start)
+        for (int v = lane; v < T; v += 64)
+            p.run_start[base + v] = v <= u ? (int32_t)st[v] : -1;
+}
+
 // --------------------------------------------------------------- launchers
 
 SamView sam_view(void *buf, int64_t S, int64_t K, int64_t Tcap)
@@ -479,10 +740,36 @@ hipError_t launch_sam_step(void *buf, int64_t S, int64_t K, int64_t Tcap,
     return hipGetLastError();
 }
 
+// LDS tables when the stream fits a configuration and the streams fit the
+// device in one round (one workgroup per stream resident at once);
+// otherwise the HBM tables, whose many waves per CU hide their latency
+// better than a second round of LDS workgroups.
+template <int MT>
+static bool qk_lds_try(const QkParams &p, hipStream_t st)
+{
+    if (p.T > MT)
+        return false;
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return false;
+    if (cus[dev] == 0 &&
+        hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return false;
+    const int64_t per_cu = 163840 / (int64_t)QlCfg<MT>::kLds;
+    if (p.S > per_cu * cus[dev])
+        return false;
+    hipLaunchKernelGGL(qk_lds_kernel<MT>, dim3((unsigned)p.S), dim3(64), 0, st, p);
+    return true;
+}
+
 hipError_t launch_qk(QkParams p, hipStream_t st)
 {
     p.spw = 1;
-    hipLaunchKernelGGL(qk_kernel, dim3((unsigned)p.S), dim3(64), 0, st, p);
+    const bool lds_ok = p.K <= kQlMaxK && p.M <= 8;
+    if (!(lds_ok && (qk_lds_try<1024>(p, st) || qk_lds_try<2048>(p, st) ||
+                     qk_lds_try<4096>(p, st))))
+        hipLaunchKernelGGL(qk_kernel, dim3((unsigned)p.S), dim3(64), 0, st, p);
     return hipGetLastError();
 }
 

@@ -141,3 +141,43 @@ def test_qk_batched_shape():
     k = oracle.discretize_bf16(Hk, M)
     want = oracle.match_qk(q, k, 1 << M, M, True, cf=True)
     _compare(got, want, "batched qk")
+
+
+@pytest.mark.parametrize("K,T,kind", [(16, 4096, "iid"), (64, 4096, "iid"),
+                                      (2, 4096, "iid"), (16, 4096, "const"),
+                                      (4, 4096, "period"), (16, 4097, "iid"),
+                                      (16, 5000, "period"), (128, 3000, "iid")])
+def test_qk_table_placement_limits(K, T, kind):
+    """Streams at the largest length and alphabet whose tables live in LDS
+    (T = 4096, K = 64), binary streams (most states per step), a constant
+    and a periodic key stream (longest suffix paths), and streams just past
+    those limits, whose tables live in HBM."""
+    S = 3
+    _say(f"qk limits K={K} T={T} {kind}")
+    rng = np.random.default_rng(4000 + K + T)
+    if kind == "iid":
+        k = rng.integers(0, K, (S, T))
+    elif kind == "const":
+        k = np.full((S, T), K - 1)
+    else:
+        k = np.tile(np.arange(3) % K, T)[: T][None].repeat(S, 0)
+    k = k.astype(np.uint8)
+    q = np.where(rng.random((S, T)) < 0.8, k, rng.integers(0, K, (S, T))).astype(np.uint8)
+    M = (K - 1).bit_length()
+    for rle in (False, True):
+        got = rosa.match_qk(torch.from_numpy(q).to(DEV), torch.from_numpy(k).to(DEV),
+                            K=K, rle=rle, cf=True)
+        torch.cuda.synchronize()
+        _compare(got, oracle.match_qk(q, k, K, M, rle, cf=True),
+                 f"K={K} T={T} {kind} rle={rle}")
+
+
+def test_qk_many_short_streams():
+    """512 streams of 2000 steps: two LDS-resident streams per CU, every
+    stream resident at once."""
+    S, T, K = 512, 2000, 16
+    q, k = _streams(909, S, T, K, "mixed")
+    got = rosa.match_qk(torch.from_numpy(q).to(DEV), torch.from_numpy(k).to(DEV),
+                        K=K, rle=True, cf=True)
+    torch.cuda.synchronize()
+    _compare(got, oracle.match_qk(q, k, K, 4, True, cf=True), "512 x 2000")
