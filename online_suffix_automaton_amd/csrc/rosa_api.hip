@@ -13,13 +13,14 @@ hipError_t launch_prep_symbols(const uint8_t *in, int64_t ld, int64_t S,
                                int64_t T, int32_t K, uint8_t *rows, int64_t Tp,
                                uint8_t *copy_out, int32_t *flags,
                                hipStream_t st);
-hipError_t launch_pad_rows(uint8_t *rows, int64_t S, int64_t Tp, int64_t T,
-                           hipStream_t st);
-hipError_t launch_clear_flags(int32_t *flags, hipStream_t st);
+hipError_t launch_clear_flags(int32_t *flags, hipStream_t st,
+                              int32_t *flags2 = nullptr);
 hipError_t launch_discretize(const uint16_t *H, int64_t B, int64_t T,
                              int64_t D, int64_t ld, int M, uint8_t *rows,
                              int64_t row_stride, int64_t row_off,
-                             uint8_t *copy_out, hipStream_t st);
+                             uint8_t *copy_out, hipStream_t st,
+                             int64_t pad_end = 0, int32_t *zero_a = nullptr,
+                             int32_t *zero_b = nullptr);
 hipError_t launch_gather(const uint16_t *V, int64_t B, int64_t T, int64_t D,
                          int64_t ldv, int M, const int32_t *E, uint16_t *out,
                          int64_t ldo, hipStream_t st);
@@ -207,22 +208,25 @@ static rosa_status match_impl(const rosa_input *in, const rosa_out *out,
         return ROSA_ERR_CAPACITY;
     char *base = reinterpret_cast<char *>(ws);
     int32_t *flags = reinterpret_cast<int32_t *>(base + w.flags);
-    ROSA_TRY(launch_clear_flags(flags, stream));
-    if (sh.T == 0)
+    if (sh.T == 0) {
+        ROSA_TRY(launch_clear_flags(flags, stream));
         return ROSA_OK;
+    }
     uint8_t *rows = reinterpret_cast<uint8_t *>(base + w.sym);
+    MatchParams p = match_params(sh, base, w, out);
+    // the flags and the large-group counter start at zero; the bf16 path
+    // clears them (and pads the rows) inside the discretisation launch
     if (sh.kind == ROSA_IN_SYMBOLS) {
+        ROSA_TRY(launch_clear_flags(flags, stream, p.big));
         ROSA_TRY(launch_prep_symbols(reinterpret_cast<const uint8_t *>(in->data),
                                      sh.ld, sh.S, sh.T, sh.K, rows, w.Tp,
                                      out->symbols, flags, stream));
     } else {
         ROSA_TRY(launch_discretize(reinterpret_cast<const uint16_t *>(in->data),
                                    sh.B, sh.T, sh.D, sh.ld, sh.M, rows, w.Tp,
-                                   kPadFront, out->symbols, stream));
-        ROSA_TRY(launch_pad_rows(rows, sh.S, w.Tp, sh.T, stream));
+                                   kPadFront, out->symbols, stream, w.Tp, flags,
+                                   p.big));
     }
-    MatchParams p = match_params(sh, base, w, out);
-    ROSA_TRY(launch_clear_flags(p.big, stream));
     if (ev_begin)
         ROSA_TRY(hipEventRecord(ev_begin, stream));
     ROSA_TRY(launch_stream(p, sh.S, stream));
@@ -266,8 +270,7 @@ rosa_status prep_rows(const Shape &sh, const rosa_input *in, uint8_t *rows,
     } else {
         ROSA_TRY(launch_discretize(reinterpret_cast<const uint16_t *>(in->data),
                                    sh.B, sh.T, sh.D, sh.ld, sh.M, rows, Tp,
-                                   kPadFront, nullptr, stream));
-        ROSA_TRY(launch_pad_rows(rows, sh.S, Tp, sh.T, stream));
+                                   kPadFront, nullptr, stream, Tp));
     }
     return ROSA_OK;
 }

@@ -711,7 +711,8 @@ hipError_t launch_sam_hist(const uint8_t *in, int64_t ld, int64_t S, int64_t T,
     return hipGetLastError();
 }
 
-hipError_t launch_clear_flags(int32_t *flags, hipStream_t st);
+hipError_t launch_clear_flags(int32_t *flags, hipStream_t st,
+                              int32_t *flags2 = nullptr);
 
 hipError_t launch_sam_build(void *buf, int64_t S, int64_t K, int64_t Tcap,
                             int64_t T, int32_t *E, int16_t *SYM, int32_t *L,

@@ -45,24 +45,14 @@ __global__ void prep_symbols_kernel(const uint8_t *__restrict__ in, int64_t ld,
     rows[s * Tp + i] = v;
 }
 
-// Zero the padding of the padded rows (used after discretisation, which only
-// writes positions 0..T-1).
-__global__ void pad_rows_kernel(uint8_t *__restrict__ rows, int64_t Tp,
-                                int64_t T)
+// Zeroes the 64-word headers at a and b (b may be null).
+__global__ void clear_flags_kernel(int32_t *a, int32_t *b)
 {
-    const int64_t s = blockIdx.y;
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t nfront = kPadFront, nback = Tp - kPadFront - T;
-    if (i < nfront)
-        rows[s * Tp + i] = 0;
-    else if (i - nfront < nback)
-        rows[s * Tp + kPadFront + T + (i - nfront)] = 0;
-}
-
-__global__ void clear_flags_kernel(int32_t *flags)
-{
-    if (threadIdx.x < 64)
-        flags[threadIdx.x] = 0;
+    if (threadIdx.x < 64) {
+        a[threadIdx.x] = 0;
+        if (b)
+            b[threadIdx.x] = 0;
+    }
 }
 
 // --------------------------------------------------------- discretisation
@@ -71,12 +61,23 @@ __global__ void clear_flags_kernel(int32_t *flags)
 // wave w discretises positions t0+16w .. t0+16w+15, lane = route, reading the
 // route's M channels (coalesced along the row), into an LDS tile [route][t];
 // then the tile is written out as 64-byte runs of each stream's row.
+// With pad_end > 0 the first and last position tiles also zero the row
+// bytes before row_off and from row_off + T to pad_end, and the first block
+// zeroes the 64-word headers zero_a and zero_b (each may be null): the
+// launches that would do this separately are folded in here.
 template <int MC>
 __global__ __launch_bounds__(256) void discretize_kernel(
     const uint16_t *__restrict__ H, int64_t T, int64_t D, int64_t ld, int M,
     uint8_t *__restrict__ rows, int64_t row_stride, int64_t row_off,
-    uint8_t *__restrict__ copy_out)
+    uint8_t *__restrict__ copy_out, int64_t pad_end, int32_t *zero_a,
+    int32_t *zero_b)
 {
+    if ((blockIdx.x | blockIdx.y | blockIdx.z) == 0 && threadIdx.x < 64) {
+        if (zero_a)
+            zero_a[threadIdx.x] = 0;
+        if (zero_b)
+            zero_b[threadIdx.x] = 0;
+    }
     __shared__ uint8_t tile[64][64 + 4];
     const int64_t R = D / M;
     const int64_t b = blockIdx.z;
@@ -123,6 +124,16 @@ __global__ __launch_bounds__(256) void discretize_kernel(
     if (rg >= R)
         return;
     const int64_t s = b * R + rg;
+    if (pad_end > 0) {
+        uint8_t *row = rows + s * row_stride;
+        const int q4 = threadIdx.x & 3;
+        if (blockIdx.x == 0)
+            for (int64_t i = q4; i < row_off; i += 4)
+                row[i] = 0;
+        if (blockIdx.x == gridDim.x - 1)
+            for (int64_t i = row_off + T + q4; i < pad_end; i += 4)
+                row[i] = 0;
+    }
     uint8_t *dst = rows + s * row_stride + row_off + t0 + tc;
     if (t0 + tc + 16 <= T && (((uintptr_t)dst) & 15) == 0) {
         uint4 v;
@@ -232,25 +243,17 @@ hipError_t launch_prep_symbols(const uint8_t *in, int64_t ld, int64_t S,
     return hipGetLastError();
 }
 
-hipError_t launch_pad_rows(uint8_t *rows, int64_t S, int64_t Tp, int64_t T,
-                           hipStream_t st)
+hipError_t launch_clear_flags(int32_t *flags, hipStream_t st, int32_t *flags2)
 {
-    int64_t n = Tp - T;
-    dim3 grid((unsigned)((n + 255) / 256), (unsigned)S);
-    hipLaunchKernelGGL(pad_rows_kernel, grid, dim3(256), 0, st, rows, Tp, T);
-    return hipGetLastError();
-}
-
-hipError_t launch_clear_flags(int32_t *flags, hipStream_t st)
-{
-    hipLaunchKernelGGL(clear_flags_kernel, dim3(1), dim3(64), 0, st, flags);
+    hipLaunchKernelGGL(clear_flags_kernel, dim3(1), dim3(64), 0, st, flags, flags2);
     return hipGetLastError();
 }
 
 hipError_t launch_discretize(const uint16_t *H, int64_t B, int64_t T,
                              int64_t D, int64_t ld, int M, uint8_t *rows,
                              int64_t row_stride, int64_t row_off,
-                             uint8_t *copy_out, hipStream_t st)
+                             uint8_t *copy_out, hipStream_t st, int64_t pad_end,
+                             int32_t *zero_a, int32_t *zero_b)
 {
     const int64_t R = D / M;
     dim3 grid((unsigned)((T + 63) / 64), (unsigned)((R + 63) / 64),
@@ -259,10 +262,12 @@ hipError_t launch_discretize(const uint16_t *H, int64_t B, int64_t T,
                       (((uintptr_t)H) & 7) == 0;
     if (vec4)
         hipLaunchKernelGGL(discretize_kernel<4>, grid, dim3(256), 0, st, H, T,
-                           D, ld, M, rows, row_stride, row_off, copy_out);
+                           D, ld, M, rows, row_stride, row_off, copy_out,
+                           pad_end, zero_a, zero_b);
     else
         hipLaunchKernelGGL(discretize_kernel<0>, grid, dim3(256), 0, st, H, T,
-                           D, ld, M, rows, row_stride, row_off, copy_out);
+                           D, ld, M, rows, row_stride, row_off, copy_out,
+                           pad_end, zero_a, zero_b);
     return hipGetLastError();
 }
 
