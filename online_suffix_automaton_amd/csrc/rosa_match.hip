@@ -1145,12 +1145,17 @@ __global__ __launch_bounds__(kBigThreads) void big_kernel(MatchParams p)
 // in time order with coalesced stores, the symbol read from the stream's
 // padded row (64 KiB per stream, served from cache).  Vec: T % 4 == 0 and
 // 16-byte aligned E / 8-byte aligned SYM rows, four positions per thread.
+// Nib (alphabets of at most 16 symbols, with Vec): the row is first staged
+// in the rest of the LDS as 4-bit symbols (32 KiB), so the SYM reads are
+// LDS reads instead of scattered byte loads.
 constexpr int kTauMax = 65536;
+constexpr int kNibBytes = kTauMax / 2;
 
-template <bool Vec>
+template <bool Vec, bool Nib>
 __global__ __launch_bounds__(kStreamThreads) void unpermute_kernel(MatchParams p)
 {
     __shared__ __align__(16) uint16_t tau[kTauMax];
+    __shared__ __align__(16) uint8_t nib[Nib ? kNibBytes : 16];
     const int s = blockIdx.x;
     const int tid = threadIdx.x, nt = blockDim.x;
     const int T = p.T;
@@ -1186,6 +1191,26 @@ __global__ __launch_bounds__(kStreamThreads) void unpermute_kernel(MatchParams p
             tau[r >> 16] = (uint16_t)r;
         }
     }
+    if (Nib && SYM) {
+        // 16 symbols -> 8 bytes per thread-step (low nibble = even position)
+        const uint4 *x4 = reinterpret_cast<const uint4 *>(x);
+        uint2 *n8 = reinterpret_cast<uint2 *>(nib);
+        for (int i = tid; i < (T + 15) / 16; i += nt) {
+            const uint4 v = x4[i];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            uint32_t o[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t a = w[2 * h], b = w[2 * h + 1];
+                const uint32_t pa = (a & 0xFu) | ((a >> 4) & 0xF0u) |
+                                    ((a >> 8) & 0xF00u) | ((a >> 12) & 0xF000u);
+                const uint32_t pb = (b & 0xFu) | ((b >> 4) & 0xF0u) |
+                                    ((b >> 8) & 0xF00u) | ((b >> 12) & 0xF000u);
+                o[h] = pa | (pb << 16);
+            }
+            n8[i] = make_uint2(o[0], o[1]);
+        }
+    }
     __syncthreads();
     if (Vec) {
         const uint2 *t4 = reinterpret_cast<const uint2 *>(tau);
@@ -1204,7 +1229,15 @@ __global__ __launch_bounds__(kStreamThreads) void unpermute_kernel(MatchParams p
                     const int a = (int)(w.x & 0xFFFFu), b = (int)(w.x >> 16);
                     const int c = (int)(w.y & 0xFFFFu), d = (int)(w.y >> 16);
                     E4[i] = make_int4(a - 1, b - 1, c - 1, d - 1);
-                    if (SYM) {
+                    if (SYM && Nib) {
+                        const int v4[4] = {a, b, c, d};
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int e = min(v4[q], T - 1);
+                            sv[u][q] = v4[q] ? (uint32_t)(nib[e >> 1] >> (4 * (e & 1))) & 0xFu
+                                             : 0xFFFFu;
+                        }
+                    } else if (SYM) {
                         sv[u][0] = a ? x[min(a, T - 1)] : 0xFFFFu;
                         sv[u][1] = b ? x[min(b, T - 1)] : 0xFFFFu;
                         sv[u][2] = c ? x[min(c, T - 1)] : 0xFFFFu;
@@ -1277,11 +1310,14 @@ hipError_t launch_unpermute(const MatchParams &p, int64_t S, hipStream_t st)
         return hipSuccess;
     const bool vec = (p.T & 3) == 0 && ((uintptr_t)p.E & 15) == 0 &&
                      ((uintptr_t)p.SYM & 7) == 0;
-    if (vec)
-        hipLaunchKernelGGL(unpermute_kernel<true>, dim3((unsigned)S),
+    if (vec && p.K <= 16)
+        hipLaunchKernelGGL((unpermute_kernel<true, true>), dim3((unsigned)S),
+                           dim3(kStreamThreads), 0, st, p);
+    else if (vec)
+        hipLaunchKernelGGL((unpermute_kernel<true, false>), dim3((unsigned)S),
                            dim3(kStreamThreads), 0, st, p);
     else
-        hipLaunchKernelGGL(unpermute_kernel<false>, dim3((unsigned)S),
+        hipLaunchKernelGGL((unpermute_kernel<false, false>), dim3((unsigned)S),
                            dim3(kStreamThreads), 0, st, p);
     return hipGetLastError();
 }
