@@ -104,10 +104,22 @@ def _check(status: int, what: str) -> None:
         raise RosaError(status, what)
 
 
-def _stream(stream) -> ctypes.c_void_p:
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+# torch's raw current-stream query (a fraction of a microsecond, against a
+# few for torch.cuda.current_stream(), which builds a Stream object); the
+# public call is the fallback where the private one is absent
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream, device: torch.device | None = None) -> ctypes.c_void_p:
+    """The caller's stream, else the current stream of `device` (of the
+    current device when None)."""
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream)
+    if _raw_stream is not None:
+        idx = device.index if device is not None and device.index is not None \
+            else torch.cuda.current_device()
+        return ctypes.c_void_p(_raw_stream(idx))
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
 def _ptr(t) -> int | None:
@@ -297,7 +309,8 @@ def rosa_step(state: RosaState, row: rosa_input, V, end, sym=None,
     ldo_b = out_row.stride(0) if out_row is not None else 0
     _check(load_library().rosa_step(state.handle, ctypes.byref(row), _ptr(V),
                                     ldv, ldv_b, _ptr(end), _ptr(sym),
-                                    _ptr(out_row), ldo_b, _stream(stream)),
+                                    _ptr(out_row), ldo_b,
+                                    _stream(stream, end.device)),
            "rosa_step")
 
 

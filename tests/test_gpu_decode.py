@@ -130,3 +130,29 @@ def test_decode_workload():
     assert np.array_equal(syms.cpu().numpy(), SYMo[:, T0:].T)
     go = oracle.gather(V, Eo, 4)[0, T0:]
     assert np.array_equal(orows.cpu().numpy().view(np.uint16), go)
+
+
+def test_structured_build_then_steps():
+    """Streams with long recurrences (periodic, Fibonacci word, planted
+    copies, constant): many clones and long suffix paths across the
+    build/step boundary and from step to step."""
+    T0, n = 700, 150
+    T = T0 + n
+    rows = [synth.periodic(T, [0, 1]), synth.fibonacci_word(T), synth.constant(T),
+            synth.planted_copies(T, 4, 5, gap_mean=30, len_lo=10, len_hi=120),
+            synth.periodic(T, [0, 1, 2, 0, 1])]
+    full = np.stack([np.asarray(r, dtype=np.uint8) for r in rows])
+    S, K = full.shape[0], 4
+    Eo, SYMo, Lo = oracle.match(full, K)
+    buf = _state(S, K, T)
+    E0 = torch.empty((S, T0), dtype=torch.int32, device=DEV)
+    st = rosa.rosa_build(rosa.symbols_input(_dev(full[:, :T0]), K), T, buf,
+                         rosa.make_out(E0, None, None))
+    assert np.array_equal(E0.cpu().numpy(), Eo[:, :T0])
+    rows_d = _dev(full)
+    end = torch.empty(S, dtype=torch.int32, device=DEV)
+    sym = torch.empty(S, dtype=torch.int16, device=DEV)
+    for t in range(T0, T):
+        rosa.rosa_step(st, rosa.symbols_input(rows_d[:, t:t + 1], K), None, end, sym)
+        assert np.array_equal(end.cpu().numpy(), Eo[:, t]), f"t={t}"
+        assert np.array_equal(sym.cpu().numpy(), SYMo[:, t]), f"t={t}"
