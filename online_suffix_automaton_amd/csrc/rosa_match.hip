@@ -44,6 +44,7 @@ namespace rosa {
 constexpr uint32_t kFirstFlag = 0x80000000u;
 constexpr int kWordThresh = 3;       // level steps only for groups larger than this
 constexpr int kMiscPass = 26;        // misc[26..31]: tasks per slot range
+constexpr int kMiscNext = 20;        // misc[20]: next task of the pass (phase E)
 constexpr int kWordThreshDeep = 32;  // ... and past the first levels, larger than this
 
 // ----------------------------------------------------------- wave helpers
@@ -809,6 +810,8 @@ __global__ __launch_bounds__(Cfg::kThreads) void stream_kernel_lds(MatchParams p
     __syncthreads();
     for (int base = 0; base < nslots; base += kPassCap) {
         const int rg = base / kPassCap;
+        if (tid == 0)
+            misc[kMiscNext] = tfirst + nw;
         for (int i = tid; i < (NB + 1) / 2; i += nt) {
             const int k0 = 2 * i, k1 = 2 * i + 1;
             const uint32_t c0 = passid[k0] == rg ? (uint32_t)((int)off[k0] - base) : 0u;
@@ -839,15 +842,22 @@ __global__ __launch_bounds__(Cfg::kThreads) void stream_kernel_lds(MatchParams p
                 }
         }
         __syncthreads();
-        // this range's tasks: [tlo, thi); the next task's descriptor is
-        // loaded while this one is solved
+        // this range's tasks: [tlo, thi).  Wave w starts with task tlo + w,
+        // then takes the next one from a counter (tasks inside long
+        // recurrences cost many times the others); the next task's
+        // descriptor is loaded while this one is solved
         const int tlo = tfirst, thi = tfirst + misc[kMiscPass + rg];
         tfirst = thi;
-        uint32_t tk_next = tlo + wid < thi ? __builtin_nontemporal_load(&tasks[tlo + wid]) : 0u;
-        for (int ti = tlo + wid; ti < thi; ti += nw) {
+        int ti = tlo + wid;
+        uint32_t tk_next = ti < thi ? __builtin_nontemporal_load(&tasks[ti]) : 0u;
+        while (ti < thi) {
             const uint32_t tk = tk_next;
-            if (ti + nw < thi)
-                tk_next = __builtin_nontemporal_load(&tasks[ti + nw]);
+            int tn = 0;
+            if (lane == 0)
+                tn = atomicAdd(&misc[kMiscNext], 1);
+            tn = __builtin_amdgcn_readfirstlane(tn);
+            if (tn < thi)
+                tk_next = __builtin_nontemporal_load(&tasks[tn]);
             const int start = (int)(tk >> 6);
             const int n = (int)(tk & 63u) + 1;
             int t, k;
@@ -859,6 +869,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void stream_kernel_lds(MatchParams p
                 else   // a bucket's first member: its answer from phase D
                     o.rec[start + lane] = ((uint32_t)t << 16) | (uint32_t)qres[k];
             }
+            ti = tn;
         }
         __syncthreads();
     }
