@@ -60,7 +60,11 @@ __global__ void clear_flags_kernel(int32_t *a, int32_t *b)
 // Tile: 64 positions x 64 routes of one batch row.  256 threads = 4 waves;
 // wave w discretises positions t0+16w .. t0+16w+15, lane = route, reading the
 // route's M channels (coalesced along the row), into an LDS tile [route][t];
-// then the tile is written out as 64-byte runs of each stream's row.
+// then the tile is written out as 64-byte runs of each stream's row.  Tiles
+// are numbered route tile fastest, so consecutive workgroups read the
+// consecutive 512-byte pieces of the same rows of H (whole rows at a time:
+// 18% faster than position tiles fastest); a workgroup loops over tiles
+// with the grid's stride, so any T fits the grid.
 // With pad_end > 0 the first and last position tiles also zero the row
 // bytes before row_off and from row_off + T to pad_end, and the first block
 // zeroes the 64-word headers zero_a and zero_b (each may be null): the
@@ -72,7 +76,7 @@ __global__ __launch_bounds__(256) void discretize_kernel(
     uint8_t *__restrict__ copy_out, int64_t pad_end, int32_t *zero_a,
     int32_t *zero_b)
 {
-    if ((blockIdx.x | blockIdx.y | blockIdx.z) == 0 && threadIdx.x < 64) {
+    if ((blockIdx.x | blockIdx.y) == 0 && threadIdx.x < 64) {
         if (zero_a)
             zero_a[threadIdx.x] = 0;
         if (zero_b)
@@ -80,80 +84,85 @@ __global__ __launch_bounds__(256) void discretize_kernel(
     }
     __shared__ uint8_t tile[64][64 + 4];
     const int64_t R = D / M;
-    const int64_t b = blockIdx.z;
-    const int64_t t0 = (int64_t)blockIdx.x * 64;
-    const int64_t r0 = (int64_t)blockIdx.y * 64;
+    const int64_t b = blockIdx.y;
+    const int64_t nrt = (R + 63) / 64, ntt = (T + 63) / 64;
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    const int64_t r = r0 + lane;
-    if (MC == 4) {
-        // four channels in one 8-byte load (alignment checked on host); all
-        // 16 loads of the thread in flight before they are used
-        uint2 v[16];
+    for (int64_t tile_i = blockIdx.x; tile_i < nrt * ntt; tile_i += gridDim.x) {
+        const int64_t tt = tile_i / nrt;
+        const int64_t t0 = tt * 64;
+        const int64_t r0 = (tile_i - tt * nrt) * 64;
+        const int64_t r = r0 + lane;
+        if (MC == 4) {
+            // four channels in one 8-byte load (alignment checked on host); all
+            // 16 loads of the thread in flight before they are used
+            uint2 v[16];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int64_t t = t0 + w * 16 + k;
-            v[k] = make_uint2(0u, 0u);
-            if (t < T && r < R)
-                v[k] = *reinterpret_cast<const uint2 *>(H + (b * T + t) * ld + r * M);
-        }
-#pragma unroll
-        for (int k = 0; k < 16; ++k)
-            tile[lane][w * 16 + k] =
-                (uint8_t)(bf16_pos(v[k].x & 0xFFFFu) | (bf16_pos(v[k].x >> 16) << 1) |
-                          (bf16_pos(v[k].y & 0xFFFFu) << 2) |
-                          (bf16_pos(v[k].y >> 16) << 3));
-    } else {
-        for (int k = 0; k < 16; ++k) {
-            const int tl = w * 16 + k;
-            const int64_t t = t0 + tl;
-            uint32_t a = 0;
-            if (t < T && r < R) {
-                const uint16_t *h = H + (b * T + t) * ld + r * M;
-                for (int j = 0; j < M; ++j)
-                    a |= bf16_pos(h[j]) << j;
+            for (int k = 0; k < 16; ++k) {
+                const int64_t t = t0 + w * 16 + k;
+                v[k] = make_uint2(0u, 0u);
+                if (t < T && r < R)
+                    v[k] = *reinterpret_cast<const uint2 *>(H + (b * T + t) * ld + r * M);
             }
-            tile[lane][tl] = (uint8_t)a;
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                tile[lane][w * 16 + k] =
+                    (uint8_t)(bf16_pos(v[k].x & 0xFFFFu) | (bf16_pos(v[k].x >> 16) << 1) |
+                              (bf16_pos(v[k].y & 0xFFFFu) << 2) |
+                              (bf16_pos(v[k].y >> 16) << 3));
+        } else {
+            for (int k = 0; k < 16; ++k) {
+                const int tl = w * 16 + k;
+                const int64_t t = t0 + tl;
+                uint32_t a = 0;
+                if (t < T && r < R) {
+                    const uint16_t *h = H + (b * T + t) * ld + r * M;
+                    for (int j = 0; j < M; ++j)
+                        a |= bf16_pos(h[j]) << j;
+                }
+                tile[lane][tl] = (uint8_t)a;
+            }
         }
-    }
-    __syncthreads();
-    // write: thread i -> route i/4, 16 positions starting at (i%4)*16
-    const int rr = threadIdx.x >> 2;
-    const int tc = (threadIdx.x & 3) * 16;
-    const int64_t rg = r0 + rr;
-    if (rg >= R)
-        return;
-    const int64_t s = b * R + rg;
-    if (pad_end > 0) {
-        uint8_t *row = rows + s * row_stride;
-        const int q4 = threadIdx.x & 3;
-        if (blockIdx.x == 0)
-            for (int64_t i = q4; i < row_off; i += 4)
-                row[i] = 0;
-        if (blockIdx.x == gridDim.x - 1)
-            for (int64_t i = row_off + T + q4; i < pad_end; i += 4)
-                row[i] = 0;
-    }
-    uint8_t *dst = rows + s * row_stride + row_off + t0 + tc;
-    if (t0 + tc + 16 <= T && (((uintptr_t)dst) & 15) == 0) {
-        uint4 v;
-        uint32_t *vv = reinterpret_cast<uint32_t *>(&v);
-        for (int q = 0; q < 4; ++q)
-            vv[q] = (uint32_t)tile[rr][tc + 4 * q] |
-                    ((uint32_t)tile[rr][tc + 4 * q + 1] << 8) |
-                    ((uint32_t)tile[rr][tc + 4 * q + 2] << 16) |
-                    ((uint32_t)tile[rr][tc + 4 * q + 3] << 24);
-        *reinterpret_cast<uint4 *>(dst) = v;
-    } else {
-        for (int q = 0; q < 16; ++q)
-            if (t0 + tc + q < T)
-                dst[q] = tile[rr][tc + q];
-    }
-    if (copy_out) {
-        uint8_t *c = copy_out + s * T + t0 + tc;
-        for (int q = 0; q < 16; ++q)
-            if (t0 + tc + q < T)
-                c[q] = tile[rr][tc + q];
+        __syncthreads();
+        // write: thread i -> route i/4, 16 positions starting at (i%4)*16
+        const int rr = threadIdx.x >> 2;
+        const int tc = (threadIdx.x & 3) * 16;
+        const int64_t rg = r0 + rr;
+        if (rg < R) {
+            const int64_t s = b * R + rg;
+            if (pad_end > 0) {
+                uint8_t *row = rows + s * row_stride;
+                const int q4 = threadIdx.x & 3;
+                if (tt == 0)
+                    for (int64_t i = q4; i < row_off; i += 4)
+                        row[i] = 0;
+                if (tt == ntt - 1)
+                    for (int64_t i = row_off + T + q4; i < pad_end; i += 4)
+                        row[i] = 0;
+            }
+            uint8_t *dst = rows + s * row_stride + row_off + t0 + tc;
+            if (t0 + tc + 16 <= T && (((uintptr_t)dst) & 15) == 0) {
+                uint4 v;
+                uint32_t *vv = reinterpret_cast<uint32_t *>(&v);
+                for (int q = 0; q < 4; ++q)
+                    vv[q] = (uint32_t)tile[rr][tc + 4 * q] |
+                            ((uint32_t)tile[rr][tc + 4 * q + 1] << 8) |
+                            ((uint32_t)tile[rr][tc + 4 * q + 2] << 16) |
+                            ((uint32_t)tile[rr][tc + 4 * q + 3] << 24);
+                *reinterpret_cast<uint4 *>(dst) = v;
+            } else {
+                for (int q = 0; q < 16; ++q)
+                    if (t0 + tc + q < T)
+                        dst[q] = tile[rr][tc + q];
+            }
+            if (copy_out) {
+                uint8_t *c = copy_out + s * T + t0 + tc;
+                for (int q = 0; q < 16; ++q)
+                    if (t0 + tc + q < T)
+                        c[q] = tile[rr][tc + q];
+            }
+        }
+        __syncthreads();   // the tile is rewritten by the next iteration
     }
 }
 
@@ -163,11 +172,12 @@ __global__ __launch_bounds__(256) void discretize_kernel(
 // tile is read as 64 contiguous 256-byte runs (one per stream) into LDS;
 // then wave w handles positions t0+16w..+15 with lane = route: one M-wide
 // value slice read from row tau = E+1 (random rows, inherent to the method)
-// and one coalesced write of the output row segment.  Route tiles are the
-// fast grid dimension, so the blocks in flight cover a narrow band of
+// and one coalesced write of the output row segment.  Tiles are numbered
+// route tile fastest, so the workgroups in flight cover a narrow band of
 // positions: destinations cluster a few thousand rows behind t, and the
-// band of V rows they read stays cache resident, each line serving the
-// eight or more streams that share it.
+// band of V rows they read stays resident in the last-level cache, each
+// line serving the eight or more streams that share it.  A workgroup loops
+// over tiles with the grid's stride.
 template <int MC>
 __global__ __launch_bounds__(256) void gather_kernel(
     const uint16_t *__restrict__ V, int64_t T, int64_t D, int64_t ldv, int M,
@@ -175,62 +185,68 @@ __global__ __launch_bounds__(256) void gather_kernel(
 {
     __shared__ int32_t et[64][64 + 1];
     const int64_t R = D / M;
-    const int64_t b = blockIdx.z;
-    const int64_t t0 = (int64_t)blockIdx.y * 64;
-    const int64_t r0 = (int64_t)blockIdx.x * 64;
+    const int64_t b = blockIdx.y;
+    const int64_t nrt = (R + 63) / 64, ntt = (T + 63) / 64;
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    // load E tile: 16 streams per wave-iteration, lane = position
-    for (int k = 0; k < 16; ++k) {
-        const int rl = w * 16 + k;
-        const int64_t rg = r0 + rl;
-        const int64_t t = t0 + lane;
-        int32_t e = -1;
-        if (rg < R && t < T) {
-            e = E[(b * R + rg) * T + t];
-            if (e < -1) e = -1;
-            if (e > T - 2) e = (int32_t)(T - 2);
+    for (int64_t tile_i = blockIdx.x; tile_i < nrt * ntt; tile_i += gridDim.x) {
+        const int64_t tt = tile_i / nrt;
+        const int64_t t0 = tt * 64;
+        const int64_t r0 = (tile_i - tt * nrt) * 64;
+        // load E tile: 16 streams per wave-iteration, lane = position
+        for (int k = 0; k < 16; ++k) {
+            const int rl = w * 16 + k;
+            const int64_t rg = r0 + rl;
+            const int64_t t = t0 + lane;
+            int32_t e = -1;
+            if (rg < R && t < T) {
+                e = E[(b * R + rg) * T + t];
+                if (e < -1) e = -1;
+                if (e > T - 2) e = (int32_t)(T - 2);
+            }
+            et[rl][lane] = e;
         }
-        et[rl][lane] = e;
-    }
-    __syncthreads();
-    const int64_t r = r0 + lane;
-    if (r >= R)
-        return;
-    if (MC == 4) {
-        // all 16 value loads in flight before the stores
-        uint2 v[16];
+        __syncthreads();
+        const int64_t r = r0 + lane;
+        if (r < R && MC == 4) {
+            // all 16 value loads in flight before the stores
+            uint2 v[16];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int tl = w * 16 + k;
-            const int32_t e = et[lane][tl];
-            v[k] = make_uint2(0u, 0u);
-            if (t0 + tl < T && e >= 0)
-                v[k] = *reinterpret_cast<const uint2 *>(
-                    V + (b * T + (e + 1)) * ldv + r * M);
-        }
+            for (int k = 0; k < 16; ++k) {
+                const int tl = w * 16 + k;
+                const int32_t e = et[lane][tl];
+                v[k] = make_uint2(0u, 0u);
+                if (t0 + tl < T && e >= 0)
+                    v[k] = *reinterpret_cast<const uint2 *>(
+                        V + (b * T + (e + 1)) * ldv + r * M);
+            }
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int64_t t = t0 + w * 16 + k;
-            if (t < T)
-                *reinterpret_cast<uint2 *>(out + (b * T + t) * ldo + r * M) = v[k];
+            for (int k = 0; k < 16; ++k) {
+                const int64_t t = t0 + w * 16 + k;
+                if (t < T)
+                    *reinterpret_cast<uint2 *>(out + (b * T + t) * ldo + r * M) = v[k];
+            }
+        } else if (r < R) {
+            for (int k = 0; k < 16; ++k) {
+                const int tl = w * 16 + k;
+                const int64_t t = t0 + tl;
+                if (t >= T)
+                    break;
+                const int32_t e = et[lane][tl];
+                uint16_t *o = out + (b * T + t) * ldo + r * M;
+                const uint16_t *src = V + (b * T + (e + 1)) * ldv + r * M;
+                for (int m = 0; m < M; ++m)
+                    o[m] = e >= 0 ? src[m] : (uint16_t)0;
+            }
         }
-    } else {
-        for (int k = 0; k < 16; ++k) {
-            const int tl = w * 16 + k;
-            const int64_t t = t0 + tl;
-            if (t >= T)
-                break;
-            const int32_t e = et[lane][tl];
-            uint16_t *o = out + (b * T + t) * ldo + r * M;
-            const uint16_t *src = V + (b * T + (e + 1)) * ldv + r * M;
-            for (int m = 0; m < M; ++m)
-                o[m] = e >= 0 ? src[m] : (uint16_t)0;
-        }
+        __syncthreads();   // the E tile is rewritten by the next iteration
     }
 }
 
 // --------------------------------------------------------------- launchers
+
+// Workgroups of the tiled kernels (beyond this, each loops over tiles).
+constexpr int64_t kTileGrid = 1 << 20;
 
 hipError_t launch_prep_symbols(const uint8_t *in, int64_t ld, int64_t S,
                                int64_t T, int32_t K, uint8_t *rows, int64_t Tp,
@@ -256,8 +272,8 @@ hipError_t launch_discretize(const uint16_t *H, int64_t B, int64_t T,
                              int32_t *zero_a, int32_t *zero_b)
 {
     const int64_t R = D / M;
-    dim3 grid((unsigned)((T + 63) / 64), (unsigned)((R + 63) / 64),
-              (unsigned)B);
+    const int64_t ntiles = ((R + 63) / 64) * ((T + 63) / 64);
+    dim3 grid((unsigned)(ntiles < kTileGrid ? ntiles : kTileGrid), (unsigned)B);
     const bool vec4 = M == 4 && (ld % 4) == 0 &&
                       (((uintptr_t)H) & 7) == 0;
     if (vec4)
@@ -276,8 +292,8 @@ hipError_t launch_gather(const uint16_t *V, int64_t B, int64_t T, int64_t D,
                          int64_t ldo, hipStream_t st)
 {
     const int64_t R = D / M;
-    dim3 grid((unsigned)((R + 63) / 64), (unsigned)((T + 63) / 64),
-              (unsigned)B);
+    const int64_t ntiles = ((R + 63) / 64) * ((T + 63) / 64);
+    dim3 grid((unsigned)(ntiles < kTileGrid ? ntiles : kTileGrid), (unsigned)B);
     const bool vec4 = M == 4 && (ldv % 4) == 0 && (ldo % 4) == 0 &&
                       (((uintptr_t)V) & 7) == 0 && (((uintptr_t)out) & 7) == 0;
     if (vec4)
