@@ -161,6 +161,8 @@ MatchParams match_params(const Shape &sh, char *ws, const WsLayout &w,
     p.stack = reinterpret_cast<int4 *>(ws + w.stack);
     p.rec = sh.T <= 65536 ? reinterpret_cast<uint32_t *>(ws + w.rec) : nullptr;
     p.tasks = reinterpret_cast<uint32_t *>(ws + w.tasks);
+    p.deep = reinterpret_cast<uint32_t *>(ws + w.deep);
+    p.dinfo = reinterpret_cast<uint4 *>(ws + w.dinfo);
     p.E = out->end;
     p.SYM = out->sym;
     p.L = out->len;

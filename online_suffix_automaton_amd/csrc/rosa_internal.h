@@ -24,8 +24,11 @@ constexpr int kBigThreads = 64;      // one wave per large group
 // Flags word layout in the match workspace (first 256 bytes).
 constexpr int kFlagSymbol = 0;       // int32: nonzero if a symbol >= K was seen
 
+// Words of the per-stream bitmap of deferred positions (record mode).
+inline __host__ __device__ int deep_words(int64_t T) { return (int)((T + 31) / 32); }
+
 struct WsLayout {
-    size_t flags, sym, pos, pos2, rec, big, stack, tasks, total;
+    size_t flags, sym, pos, pos2, rec, big, stack, tasks, deep, dinfo, total;
     int64_t Tp;          // bytes per padded symbol row
     int64_t big_cap;     // entries in the large-group list
 };
@@ -46,6 +49,10 @@ inline WsLayout ws_layout(int64_t S, int64_t T)
     w.big = o;    o = align_up(o + 256 + (size_t)w.big_cap * 16, 256);
     w.stack = o;  o = align_up(o + (size_t)S * (T / 16 + 4) * 16, 256);
     w.tasks = o;  o = align_up(o + (size_t)S * kTaskCap * 4, 256);
+    // deferred positions exist only in record mode (T <= 65536)
+    const bool rec_mode = T <= 65536;
+    w.deep = o;   o = align_up(o + (rec_mode ? (size_t)S * deep_words(T) * 4 : 0), 256);
+    w.dinfo = o;  o = align_up(o + (rec_mode ? (size_t)S * T * 16 : 0), 256);
     w.total = o;
     return w;
 }
@@ -64,6 +71,8 @@ struct MatchParams {
     int4 *stack;                // [S][T/16+4] group stacks of the large-group pass
     uint32_t *rec;              // [S][T] result records (streams of <= 65536)
     uint32_t *tasks;            // [S][kTaskCap] task lists (LDS kernel)
+    uint32_t *deep;             // [S][deep_words(T)] deferred positions (LDS kernel)
+    uint4 *dinfo;               // [S][T] their candidates (LDS kernel)
     int32_t *E;                 // [S][T]
     int16_t *SYM;               // [S][T] or null
     int32_t *L;                 // [S][T] or null

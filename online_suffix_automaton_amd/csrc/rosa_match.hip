@@ -124,6 +124,9 @@ __device__ __forceinline__ void emit_record(const StreamOut &o, int slot,
 struct Found {
     int e, l;
     bool ok;
+    bool deep;      // CAP mode: answer deferred (see solve_wave)
+    uint4 info;     // deep: up to seven candidates (16 bits each), their count
+                    // (3 bits) and a lower bound of their common suffix (13 bits)
 };
 
 // ------------------------------------------------------------ solve_wave
@@ -142,13 +145,21 @@ struct Found {
 //    earlier member's, 16 symbols per step, up to the first mismatch or the
 //    start of that member's history; the longest common extension c (the
 //    latest member among equals) gives L = ell + c and E = that member.
+//  CAP: the comparison stops after the first 16 symbols.  An element with
+//    a member that matches all 16 and has a longer history (a recurrence of
+//    more than ell + 16 symbols, inside long repeats) is answered later, in
+//    time order (unpermute_kernel): its answer follows from the previous
+//    position's by the extension rule, and otherwise from these members (the
+//    only ones that can reach ell + 16), which the result carries (deep).
+//    More than seven such members: resolved in full here.
+template <bool CAP>
 __device__ Found solve_wave(const uint8_t *x, int nbits, int t, uint64_t g,
                             int ell, bool has)
 {
     const int lane = __lane_id();
     const uint64_t self = 1ull << lane;
     const uint64_t below = self - 1;
-    Found r = {-1, 0, false};
+    Found r = {-1, 0, false, false, make_uint4(0u, 0u, 0u, 0u)};
     if (!has)
         g = self;
     const int ell0 = ell;
@@ -194,53 +205,99 @@ __device__ Found solve_wave(const uint8_t *x, int nbits, int t, uint64_t g,
     }
     // ------------------------------------------------- direct resolution
     uint64_t rem = (has && __popcll(g) >= 2) ? (g & below) : 0;
+    const uint64_t rem0 = rem;
     int best_c = -1, best_e = -1;
+    int ntr = 0;            // CAP: members deferred (full 16-symbol match)
+    uint32_t cw0 = 0, cw1 = 0, cw2 = 0, cw3 = 0;   // their positions, 16 bits each
+    auto keep = [&](int e) {
+        const uint32_t v = (uint32_t)e << (16 * (ntr & 1));
+        if (ntr < 2)
+            cw0 |= v;
+        else if (ntr < 4)
+            cw1 |= v;
+        else if (ntr < 6)
+            cw2 |= v;
+        else if (ntr < 7)
+            cw3 |= v;
+        ++ntr;
+    };
     // every element's first 16 symbols past level ell, shared by shuffle
     uint64_t w0lo = 0, w0hi = 0;
     if (has && t - ell >= 0)
         load_window(x, t - ell - 15, w0lo, w0hi);
-    while (ballot(rem != 0)) {
-        const bool have = rem != 0;
-        const int j = have ? __ffsll((long long)rem) - 1 : lane;
-        rem &= rem - 1;
-        const int tj = __shfl(t, j);
-        const uint64_t jlo = shfl64(w0lo, j), jhi = shfl64(w0hi, j);
-        if (have) {
-            const int aj = tj - ell + 1;   // history of member j from x[tj-ell]
-            // first 16 symbols from the shared windows, further ones from
-            // memory while they keep matching
-            const uint64_t fh = w0hi ^ jhi, fl = w0lo ^ jlo;
-            int c = fh ? (__clzll((long long)fh) >> 3)
-                       : (fl ? 8 + (__clzll((long long)fl) >> 3) : 16);
-            if (!(fh | fl)) {
-                // 64 symbols per step (long recurrences); every read stays
-                // at or after position -63 because c < aj <= t - ell and
-                // tj - ell - c >= 0, inside the rows' front padding
-                while (c < aj) {
-                    uint64_t xs[8];
+    auto scan = [&](uint64_t rm, bool full) {
+        while (ballot(rm != 0)) {
+            const bool have = rm != 0;
+            const int j = have ? __ffsll((long long)rm) - 1 : lane;
+            rm &= rm - 1;
+            const int tj = __shfl(t, j);
+            const uint64_t jlo = shfl64(w0lo, j), jhi = shfl64(w0hi, j);
+            if (have) {
+                const int aj = tj - ell + 1;   // history of member j from x[tj-ell]
+                // first 16 symbols from the shared windows, further ones from
+                // memory while they keep matching
+                const uint64_t fh = w0hi ^ jhi, fl = w0lo ^ jlo;
+                int c = fh ? (__clzll((long long)fh) >> 3)
+                           : (fl ? 8 + (__clzll((long long)fl) >> 3) : 16);
+                if (!(fh | fl)) {
+                    // 64 symbols per step (long recurrences); every read stays
+                    // at or after position -63 because c < aj <= t - ell and
+                    // tj - ell - c >= 0, inside the rows' front padding
+                    while (c < aj) {
+                        if (!full) {   // CAP: deferred, c = -2 never wins below
+                            keep(tj);
+                            c = -2;
+                            break;
+                        }
+                        uint64_t xs[8];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        uint64_t alo, ahi, blo, bhi;
-                        load_window(x, t - ell - c - 15 - 16 * q, alo, ahi);
-                        load_window(x, tj - ell - c - 15 - 16 * q, blo, bhi);
-                        xs[2 * q] = ahi ^ bhi;
-                        xs[2 * q + 1] = alo ^ blo;
+                        for (int q = 0; q < 4; ++q) {
+                            uint64_t alo, ahi, blo, bhi;
+                            load_window(x, t - ell - c - 15 - 16 * q, alo, ahi);
+                            load_window(x, tj - ell - c - 15 - 16 * q, blo, bhi);
+                            xs[2 * q] = ahi ^ bhi;
+                            xs[2 * q + 1] = alo ^ blo;
+                        }
+                        int k = 0;
+                        while (k < 8 && !xs[k])
+                            ++k;
+                        if (k < 8) {
+                            c += 8 * k + (__clzll((long long)xs[k]) >> 3);
+                            break;
+                        }
+                        c += 64;
                     }
-                    int k = 0;
-                    while (k < 8 && !xs[k])
-                        ++k;
-                    if (k < 8) {
-                        c += 8 * k + (__clzll((long long)xs[k]) >> 3);
-                        break;
-                    }
-                    c += 64;
+                }
+                c = min(c, aj);
+                if (c >= best_c) {
+                    best_c = c;
+                    best_e = tj;
                 }
             }
-            c = min(c, aj);
-            if (c >= best_c) {
-                best_c = c;
-                best_e = tj;
+        }
+    };
+    scan(rem, !CAP);
+    if (CAP && ballot(ntr > 0)) {
+        // an exact 16 among the others ties with a deferred member that
+        // stops at 16: it joins the deferred ones
+        if (ntr > 0 && best_c == 16)
+            keep(best_e);
+        const bool over = ntr > 7;
+        if (ballot(over)) {
+            if (over) {
+                best_c = -1;
+                best_e = -1;
+                ntr = 0;
             }
+            scan(over ? rem0 : 0, true);
+        }
+        if (ntr > 0) {
+            // every recorded member shares at least ell + 16 symbols
+            const uint32_t lb = (uint32_t)min(ell + 16, 8191);
+            r.ok = true;
+            r.deep = true;
+            r.info = make_uint4(cw0, cw1, cw2, cw3 | ((uint32_t)ntr << 16) | (lb << 19));
+            return r;
         }
     }
     if (best_c >= 0) {
@@ -629,7 +686,7 @@ __device__ void sort_buckets(Ptr list, const OffT *off, int NB, int base,
 // range of one bucket, so inside a group lane order is time order.  Returns solve_wave's answer for the lane (not ok for
 // the first member of each bucket: its answer has L < d) and the lane's
 // position in t_out.
-template <int DC, bool SORT, class Src>
+template <int DC, bool SORT, bool CAP, class Src>
 __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
                           int n, int &t_out, int &key_out)
 {
@@ -655,7 +712,7 @@ __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
     // always suffice).
     if (!SORT) {
         t_out = t0;
-        return solve_wave(x, p.nbits, t0, g, d, has);
+        return solve_wave<CAP>(x, p.nbits, t0, g, d, has);
     }
     uint32_t key = has ? (((uint32_t)__popcll(B & upto) << 16) | (uint32_t)t0)
                        : 0xFFFFFFFFu;
@@ -678,7 +735,7 @@ __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
     }
     const int t1 = has ? (int)(key & 0xFFFFu) : 0;
     t_out = t1;
-    return solve_wave(x, p.nbits, t1, g, d, has);
+    return solve_wave<CAP>(x, p.nbits, t1, g, d, has);
 }
 
 // ------------------------------------------------- stream kernel (LDS)
@@ -754,6 +811,10 @@ __global__ __launch_bounds__(Cfg::kThreads) void stream_kernel_lds(MatchParams p
     uint8_t *passid = U + Cfg::kUPassId;
     uint16_t *lpos = reinterpret_cast<uint16_t *>(U + Cfg::kULpos);
     uint32_t *tasks = p.tasks + (int64_t)blockIdx.x * kTaskCap;
+    // positions whose answers are deferred (long repeats): one bit each,
+    // and their candidates
+    uint32_t *deepbits = p.deep + (int64_t)blockIdx.x * deep_words(p.T);
+    uint4 *dinfo = p.dinfo + (int64_t)blockIdx.x * p.T;
 
     const int s = blockIdx.x;
     const int tid = threadIdx.x, nt = blockDim.x;
@@ -767,6 +828,8 @@ __global__ __launch_bounds__(Cfg::kThreads) void stream_kernel_lds(MatchParams p
     }
     if (tid < 32)
         misc[tid] = 0;
+    for (int i = tid; i < deep_words(T); i += nt)
+        deepbits[i] = 0;
     const uint8_t *x = symrow + kPadFront;
     StreamOut o;
     o.x = x;
@@ -861,13 +924,19 @@ __global__ __launch_bounds__(Cfg::kThreads) void stream_kernel_lds(MatchParams p
             const int start = (int)(tk >> 6);
             const int n = (int)(tk & 63u) + 1;
             int t, k;
-            const Found f = run_task<DC, true>(
+            const Found f = run_task<DC, true, true>(
                 p, x, [&](int i) { return (int)lpos[start - base + i]; }, n, t, k);
             if (lane < n) {
-                if (f.ok)
+                if (f.deep) {
+                    // answered in time order after the match (unpermute_kernel)
+                    o.rec[start + lane] = (uint32_t)t << 16;
+                    dinfo[t] = f.info;
+                    atomicOr(&deepbits[t >> 5], 1u << (t & 31));
+                } else if (f.ok) {
                     emit_record(o, start + lane, t, f.e, f.l);
-                else   // a bucket's first member: its answer from phase D
+                } else {   // a bucket's first member: its answer from phase D
                     o.rec[start + lane] = ((uint32_t)t << 16) | (uint32_t)qres[k];
+                }
             }
             ti = tn;
         }
@@ -934,7 +1003,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_hbm(MatchParams 
         const int start = (int)(tk >> 6);
         const int n = (int)(tk & 63u) + 1;
         int t, k;
-        const Found f = run_task<0, false>(p, x, [&](int i) { return pos[start + i]; }, n, t, k);
+        const Found f = run_task<0, false, false>(p, x, [&](int i) { return pos[start + i]; }, n, t, k);
         if (lane < n && f.ok)
             emit(o, t, f.e, f.l);
     }
@@ -1020,7 +1089,7 @@ __global__ __launch_bounds__(kBigThreads) void big_kernel(MatchParams p)
                 const bool hs = lane < cur.n;
                 const int t = hs ? X[cur.start + lane] : 0;
                 const uint64_t g = cur.n >= 64 ? ~0ull : ((1ull << cur.n) - 1);
-                const Found f = solve_wave(x, p.nbits, t, hs ? g : self, cur.ell, hs);
+                const Found f = solve_wave<false>(x, p.nbits, t, hs ? g : self, cur.ell, hs);
                 put(hs && f.ok, t, f.e, f.l);
             } else {
                 const int a = cur.start, n = cur.n, ell = cur.ell;
@@ -1113,8 +1182,8 @@ __global__ __launch_bounds__(kBigThreads) void big_kernel(MatchParams p)
                             const bool hs = lane < c;
                             const int t = hs ? Y[cs + lane] : 0;
                             const uint64_t g = c >= 64 ? ~0ull : ((1ull << c) - 1);
-                            const Found f =
-                                solve_wave(x, p.nbits, t, hs ? g : self, ell + 1, hs);
+                            const Found f = solve_wave<false>(x, p.nbits, t, hs ? g : self,
+                                                              ell + 1, hs);
                             put(hs && f.ok, t, f.e, f.l);
                         } else if (c < bestn) {
                             if (best >= 0 && sp < stack_cap && lane == 0)
@@ -1202,7 +1271,7 @@ __global__ __launch_bounds__(kStreamThreads) void unpermute_kernel(MatchParams p
             tau[r >> 16] = (uint16_t)r;
         }
     }
-    if (Nib && SYM) {
+    if (Nib) {
         // 16 symbols -> 8 bytes per thread-step (low nibble = even position)
         const uint4 *x4 = reinterpret_cast<const uint4 *>(x);
         uint2 *n8 = reinterpret_cast<uint2 *>(nib);
@@ -1220,6 +1289,118 @@ __global__ __launch_bounds__(kStreamThreads) void unpermute_kernel(MatchParams p
                 o[h] = pa | (pb << 16);
             }
             n8[i] = make_uint2(o[0], o[1]);
+        }
+    }
+    __syncthreads();
+    // Deferred positions (inside long repeats, solve_wave's CAP mode): each
+    // run of consecutive ones is answered in time order by one wave.  When
+    // x[E(t-1)+1] = x[t], the longest earlier suffix grows by one and its
+    // latest occurrence moves by one: L(t) = L(t-1)+1, E(t) = E(t-1)+1 (an
+    // occurrence of the longer suffix ending at e makes e-1 an occurrence of
+    // the shorter one, so e <= E(t-1)+1).  The wave checks this along the
+    // run 64 positions at a time; where it fails, the answer is the maximum
+    // of (common suffix length, e) over the members the position's task
+    // recorded, each length found 64 symbols at a time.
+    {
+        const int W = deep_words(T);
+        const uint32_t *db = p.deep + (int64_t)s * W;
+        const uint4 *dinfo = p.dinfo + (int64_t)s * T;
+        int32_t *Lrow = p.L ? p.L + (int64_t)s * T : nullptr;
+        const int lane = tid & 63, wid = tid >> 6, nw = nt >> 6;
+        auto sym = [&](int i) -> int {
+            return Nib ? (int)(nib[i >> 1] >> (4 * (i & 1))) & 0xF : (int)x[i];
+        };
+        // common suffix length of x[0..t] and x[0..e] (e < t), at least c
+        auto lcs_wave = [&](int t, int e, int c) -> int {
+            for (;;) {
+                const int pi = c + lane;
+                const bool eq = pi <= e && sym(t - pi) == sym(e - pi);
+                const uint64_t em = ballot(eq);
+                if (em != ~0ull)
+                    return c + __ffsll((long long)~em) - 1;
+                c += 64;
+            }
+        };
+        auto run = [&](int t) {
+            // the run's end: the first position after t whose bit is clear
+            int tend = T;
+            for (int wb = t >> 5;; wb += 64) {
+                const int wi = wb + lane;
+                uint32_t m = wi < W ? db[wi] : 0u;
+                if (wi == (t >> 5))
+                    m |= (1u << (t & 31)) - 1;   // bits before t count as set
+                const uint64_t zm = ballot(m != ~0u);
+                if (zm) {
+                    const int l = __ffsll((long long)zm) - 1;
+                    const uint32_t ml = (uint32_t)__shfl((int)m, l);
+                    tend = min(T, (wb + l) * 32 + __ffs((int)~ml) - 1);
+                    break;
+                }
+                if (wb + 64 >= W)
+                    break;
+            }
+            int e1 = tau[t - 1];                 // final: t-1 is not deferred
+            int L = Lrow ? Lrow[t - 1] : 0;
+            while (t < tend) {
+                const int ti = t + lane;
+                const bool ok = ti < tend && sym(e1 + lane) == sym(ti);
+                const uint64_t okm = ballot(ok);
+                const int k = okm == ~0ull ? 64 : __ffsll((long long)~okm) - 1;
+                if (lane < k) {
+                    tau[ti] = (uint16_t)(e1 + lane + 1);
+                    if (Lrow)
+                        Lrow[ti] = L + lane + 1;
+                }
+                t += k;
+                e1 += k;
+                L += k;
+                if (k == 64 || t >= tend)
+                    continue;
+                const uint4 in = dinfo[t];
+                const int nc = (int)((in.w >> 16) & 7u);
+                const int lb = (int)(in.w >> 19);
+                int bc = -1, be = -1;
+                for (int j = 0; j < nc; ++j) {
+                    const uint32_t wj = j < 2 ? in.x : j < 4 ? in.y : j < 6 ? in.z : in.w;
+                    const int e = (int)((wj >> (16 * (j & 1))) & 0xFFFFu);
+                    const int c = lcs_wave(t, e, min(lb, e + 1));
+                    if (c > bc || (c == bc && e > be)) {
+                        bc = c;
+                        be = e;
+                    }
+                }
+                if (lane == 0) {
+                    tau[t] = (uint16_t)(be + 1);
+                    if (Lrow)
+                        Lrow[t] = bc;
+                }
+                e1 = be + 1;   // E(t) + 1 for the next position
+                L = bc;
+                ++t;
+            }
+        };
+        // wave w takes the runs that start in its share of the bitmap
+        const int per = (W + nw - 1) / nw;
+        const int w0 = wid * per, w1 = min(W, w0 + per);
+        for (int wb = w0; wb < w1; wb += 64) {
+            const int wi = wb + lane;
+            uint32_t st = 0;
+            if (wi < w1) {
+                const uint32_t m = db[wi];
+                const uint32_t before = wi > 0 ? db[wi - 1] >> 31 : 0u;
+                st = m & ~((m << 1) | before);
+            }
+            uint64_t has = ballot(st != 0);
+            while (has) {
+                const int l = __ffsll((long long)has) - 1;
+                has &= has - 1;
+                uint32_t sw = (uint32_t)__shfl((int)st, l);
+                while (sw) {
+                    const int bit = __ffs((int)sw) - 1;
+                    sw &= sw - 1;
+                    run((wb + l) * 32 + bit);
+                }
+            }
         }
     }
     __syncthreads();

@@ -184,6 +184,36 @@ def test_repeat_workload():
     assert Lo.max() >= 256
 
 
+def _many_copies(T, K, seed, block=60, copies=25):
+    """A random stream with one block copied many times: every position in
+    the later copies has more earlier recurrences than a deferred record of
+    the match kernel holds."""
+    rng = np.random.default_rng(seed)
+    x = rng.integers(0, K, T).astype(np.uint8)
+    src = x[100:100 + block].copy()
+    starts = np.sort(rng.choice(np.arange(300, T - block, block + 7), copies,
+                                replace=False))
+    for a in starts:
+        x[a:a + block] = src
+    return x
+
+
+def test_long_repeats_deferred_answers():
+    """Long repeats, whose answers the match kernel defers to the
+    time-ordered pass of the record kernel: a block copied many times (more
+    candidates than a deferred record holds), nested copies (where the
+    extension from the previous position fails), a length that is not a
+    multiple of 4 and an alphabet above 16 (the record kernel's other
+    variants)."""
+    for T, K in ((8192, 16), (5001, 16), (8192, 40), (5001, 200)):
+        rows = [_many_copies(T, K, 11), _many_copies(T, K, 12, block=200, copies=12),
+                synth.planted_copies(T, K, 13, gap_mean=50, len_lo=64, len_hi=400),
+                synth.planted_copies(T, K, 14, gap_mean=20, len_lo=20, len_hi=100)]
+        sym = np.stack(rows).astype(np.uint8)
+        _say(f"deferred answers T={T} K={K}")
+        _run_symbols(sym, K, f"deferred T={T} K={K}")
+
+
 def test_long_workload_with_gather():
     _say("generating long workload")
     w = synth.long()
