@@ -40,7 +40,10 @@ def test_workspace_and_state_sizes():
     assert rosa.rosa_match_workspace_bytes(1, 1 << 26, 2) == 0
     a = rosa.rosa_match_workspace_bytes(512, 65536, 16)
     b = rosa.rosa_match_workspace_bytes(512, 65537, 16)
-    assert 0 < a < b
+    assert 0 < rosa.rosa_match_workspace_bytes(512, 60000, 16) < a
+    # up to 65536 positions the workspace also holds the result records and
+    # the deferred answers (16 B per position); beyond, neither
+    assert 0 < b and a >= 512 * 65536 * (4 + 16)
     assert rosa.rosa_state_bytes(4, 2, 0) == 0
     s1 = rosa.rosa_state_bytes(512, 16, 66560)
     # dense rows: (2*Tcap-1) states x (16 B node + 4K B row) per stream
