@@ -124,9 +124,7 @@ __device__ __forceinline__ void emit_record(const StreamOut &o, int slot,
 struct Found {
     int e, l;
     bool ok;
-    bool deep;      // CAP mode: answer deferred (see solve_wave)
-    uint4 info;     // deep: up to seven candidates (16 bits each), their count
-                    // (3 bits) and a lower bound of their common suffix (13 bits)
+    bool deep;      // CAP mode: answer deferred, its record written (solve_wave)
 };
 
 // ------------------------------------------------------------ solve_wave
@@ -150,16 +148,18 @@ struct Found {
 //    more than ell + 16 symbols, inside long repeats) is answered later, in
 //    time order (unpermute_kernel): its answer follows from the previous
 //    position's by the extension rule, and otherwise from these members (the
-//    only ones that can reach ell + 16), which the result carries (deep).
-//    More than seven such members: resolved in full here.
+//    only ones that can reach ell + 16).  The deferred record of element t
+//    is drec[t]: sixteen-bit fields 0..6 hold up to seven such members,
+//    field 7 their count (3 bits; 0: more than seven) and ell + 16 above it
+//    (a lower bound of their common suffix with t).
 template <bool CAP>
 __device__ Found solve_wave(const uint8_t *x, int nbits, int t, uint64_t g,
-                            int ell, bool has)
+                            int ell, bool has, uint4 *drec = nullptr)
 {
     const int lane = __lane_id();
     const uint64_t self = 1ull << lane;
     const uint64_t below = self - 1;
-    Found r = {-1, 0, false, false, make_uint4(0u, 0u, 0u, 0u)};
+    Found r = {-1, 0, false, false};
     if (!has)
         g = self;
     const int ell0 = ell;
@@ -205,100 +205,74 @@ __device__ Found solve_wave(const uint8_t *x, int nbits, int t, uint64_t g,
     }
     // ------------------------------------------------- direct resolution
     uint64_t rem = (has && __popcll(g) >= 2) ? (g & below) : 0;
-    const uint64_t rem0 = rem;
     int best_c = -1, best_e = -1;
     int ntr = 0;            // CAP: members deferred (full 16-symbol match)
-    uint32_t cw0 = 0, cw1 = 0, cw2 = 0, cw3 = 0;   // their positions, 16 bits each
-    auto keep = [&](int e) {
-        const uint32_t v = (uint32_t)e << (16 * (ntr & 1));
-        if (ntr < 2)
-            cw0 |= v;
-        else if (ntr < 4)
-            cw1 |= v;
-        else if (ntr < 6)
-            cw2 |= v;
-        else if (ntr < 7)
-            cw3 |= v;
-        ++ntr;
-    };
+    uint16_t *dr = CAP && has ? reinterpret_cast<uint16_t *>(drec + t) : nullptr;
     // every element's first 16 symbols past level ell, shared by shuffle
     uint64_t w0lo = 0, w0hi = 0;
     if (has && t - ell >= 0)
         load_window(x, t - ell - 15, w0lo, w0hi);
-    auto scan = [&](uint64_t rm, bool full) {
-        while (ballot(rm != 0)) {
-            const bool have = rm != 0;
-            const int j = have ? __ffsll((long long)rm) - 1 : lane;
-            rm &= rm - 1;
-            const int tj = __shfl(t, j);
-            const uint64_t jlo = shfl64(w0lo, j), jhi = shfl64(w0hi, j);
-            if (have) {
-                const int aj = tj - ell + 1;   // history of member j from x[tj-ell]
-                // first 16 symbols from the shared windows, further ones from
-                // memory while they keep matching
-                const uint64_t fh = w0hi ^ jhi, fl = w0lo ^ jlo;
-                int c = fh ? (__clzll((long long)fh) >> 3)
-                           : (fl ? 8 + (__clzll((long long)fl) >> 3) : 16);
-                if (!(fh | fl)) {
-                    // 64 symbols per step (long recurrences); every read stays
-                    // at or after position -63 because c < aj <= t - ell and
-                    // tj - ell - c >= 0, inside the rows' front padding
-                    while (c < aj) {
-                        if (!full) {   // CAP: deferred, c = -2 never wins below
-                            keep(tj);
-                            c = -2;
-                            break;
-                        }
-                        uint64_t xs[8];
+    while (ballot(rem != 0)) {
+        const bool have = rem != 0;
+        const int j = have ? __ffsll((long long)rem) - 1 : lane;
+        rem &= rem - 1;
+        const int tj = __shfl(t, j);
+        const uint64_t jlo = shfl64(w0lo, j), jhi = shfl64(w0hi, j);
+        if (have) {
+            const int aj = tj - ell + 1;   // history of member j from x[tj-ell]
+            // first 16 symbols from the shared windows, further ones from
+            // memory while they keep matching
+            const uint64_t fh = w0hi ^ jhi, fl = w0lo ^ jlo;
+            int c = fh ? (__clzll((long long)fh) >> 3)
+                       : (fl ? 8 + (__clzll((long long)fl) >> 3) : 16);
+            if (CAP && !(fh | fl) && c < aj) {
+                if (ntr < 7)
+                    dr[ntr] = (uint16_t)tj;
+                ++ntr;
+                c = -2;   // never wins below
+            } else if (!CAP && !(fh | fl)) {
+                // 64 symbols per step (long recurrences); every read stays
+                // at or after position -63 because c < aj <= t - ell and
+                // tj - ell - c >= 0, inside the rows' front padding
+                while (c < aj) {
+                    uint64_t xs[8];
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            uint64_t alo, ahi, blo, bhi;
-                            load_window(x, t - ell - c - 15 - 16 * q, alo, ahi);
-                            load_window(x, tj - ell - c - 15 - 16 * q, blo, bhi);
-                            xs[2 * q] = ahi ^ bhi;
-                            xs[2 * q + 1] = alo ^ blo;
-                        }
-                        int k = 0;
-                        while (k < 8 && !xs[k])
-                            ++k;
-                        if (k < 8) {
-                            c += 8 * k + (__clzll((long long)xs[k]) >> 3);
-                            break;
-                        }
-                        c += 64;
+                    for (int q = 0; q < 4; ++q) {
+                        uint64_t alo, ahi, blo, bhi;
+                        load_window(x, t - ell - c - 15 - 16 * q, alo, ahi);
+                        load_window(x, tj - ell - c - 15 - 16 * q, blo, bhi);
+                        xs[2 * q] = ahi ^ bhi;
+                        xs[2 * q + 1] = alo ^ blo;
                     }
-                }
-                c = min(c, aj);
-                if (c >= best_c) {
-                    best_c = c;
-                    best_e = tj;
+                    int k = 0;
+                    while (k < 8 && !xs[k])
+                        ++k;
+                    if (k < 8) {
+                        c += 8 * k + (__clzll((long long)xs[k]) >> 3);
+                        break;
+                    }
+                    c += 64;
                 }
             }
+            c = min(c, aj);
+            if (c >= best_c) {
+                best_c = c;
+                best_e = tj;
+            }
         }
-    };
-    scan(rem, !CAP);
-    if (CAP && ballot(ntr > 0)) {
+    }
+    if (CAP && ntr > 0) {
         // an exact 16 among the others ties with a deferred member that
-        // stops at 16: it joins the deferred ones
-        if (ntr > 0 && best_c == 16)
-            keep(best_e);
-        const bool over = ntr > 7;
-        if (ballot(over)) {
-            if (over) {
-                best_c = -1;
-                best_e = -1;
-                ntr = 0;
-            }
-            scan(over ? rem0 : 0, true);
+        // stops at 16: it joins them
+        if (best_c == 16) {
+            if (ntr < 7)
+                dr[ntr] = (uint16_t)best_e;
+            ++ntr;
         }
-        if (ntr > 0) {
-            // every recorded member shares at least ell + 16 symbols
-            const uint32_t lb = (uint32_t)min(ell + 16, 8191);
-            r.ok = true;
-            r.deep = true;
-            r.info = make_uint4(cw0, cw1, cw2, cw3 | ((uint32_t)ntr << 16) | (lb << 19));
-            return r;
-        }
+        dr[7] = (uint16_t)((ntr > 7 ? 0 : ntr) | (min(ell + 16, 8191) << 3));
+        r.ok = true;
+        r.deep = true;
+        return r;
     }
     if (best_c >= 0) {
         r.e = best_e;
@@ -688,7 +662,7 @@ __device__ void sort_buckets(Ptr list, const OffT *off, int NB, int base,
 // position in t_out.
 template <int DC, bool SORT, bool CAP, class Src>
 __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
-                          int n, int &t_out, int &key_out)
+                          int n, int &t_out, int &key_out, uint4 *drec = nullptr)
 {
     const int lane = __lane_id();
     const uint64_t self = 1ull << lane;
@@ -712,7 +686,7 @@ __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
     // always suffice).
     if (!SORT) {
         t_out = t0;
-        return solve_wave<CAP>(x, p.nbits, t0, g, d, has);
+        return solve_wave<CAP>(x, p.nbits, t0, g, d, has, drec);
     }
     uint32_t key = has ? (((uint32_t)__popcll(B & upto) << 16) | (uint32_t)t0)
                        : 0xFFFFFFFFu;
@@ -735,7 +709,7 @@ __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
     }
     const int t1 = has ? (int)(key & 0xFFFFu) : 0;
     t_out = t1;
-    return solve_wave<CAP>(x, p.nbits, t1, g, d, has);
+    return solve_wave<CAP>(x, p.nbits, t1, g, d, has, drec);
 }
 
 // ------------------------------------------------- stream kernel (LDS)
@@ -815,6 +789,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void stream_kernel_lds(MatchParams p
     // and their candidates
     uint32_t *deepbits = p.deep + (int64_t)blockIdx.x * deep_words(p.T);
     uint4 *dinfo = p.dinfo + (int64_t)blockIdx.x * p.T;
+    int32_t *posrow = p.pos + (int64_t)blockIdx.x * p.T;
 
     const int s = blockIdx.x;
     const int tid = threadIdx.x, nt = blockDim.x;
@@ -925,18 +900,33 @@ __global__ __launch_bounds__(Cfg::kThreads) void stream_kernel_lds(MatchParams p
             const int n = (int)(tk & 63u) + 1;
             int t, k;
             const Found f = run_task<DC, true, true>(
-                p, x, [&](int i) { return (int)lpos[start - base + i]; }, n, t, k);
-            if (lane < n) {
-                if (f.deep) {
-                    // answered in time order after the match (unpermute_kernel)
+                p, x, [&](int i) { return (int)lpos[start - base + i]; }, n, t, k,
+                dinfo);
+            if (ballot(f.deep)) {
+                // answers deferred to the time-ordered pass (unpermute_kernel),
+                // their records written by solve_wave; with more candidates
+                // than a record holds, the task's positions go to the
+                // workspace and the record points there
+                const bool ovf = f.deep && (reinterpret_cast<const uint16_t *>(dinfo + t)[7] & 7u) == 0;
+                if (ballot(ovf) && lane < n)
+                    posrow[start + lane] = t;
+                if (ovf) {
+                    dinfo[t].x = (uint32_t)start;
+                    dinfo[t].y = (uint32_t)n;
+                }
+                if (lane < n && f.deep) {
                     o.rec[start + lane] = (uint32_t)t << 16;
-                    dinfo[t] = f.info;
                     atomicOr(&deepbits[t >> 5], 1u << (t & 31));
-                } else if (f.ok) {
+                } else if (lane < n && f.ok) {
                     emit_record(o, start + lane, t, f.e, f.l);
-                } else {   // a bucket's first member: its answer from phase D
+                } else if (lane < n) {
                     o.rec[start + lane] = ((uint32_t)t << 16) | (uint32_t)qres[k];
                 }
+            } else if (lane < n) {
+                if (f.ok)
+                    emit_record(o, start + lane, t, f.e, f.l);
+                else   // a bucket's first member: its answer from phase D
+                    o.rec[start + lane] = ((uint32_t)t << 16) | (uint32_t)qres[k];
             }
             ti = tn;
         }
@@ -1321,6 +1311,29 @@ __global__ __launch_bounds__(kStreamThreads) void unpermute_kernel(MatchParams p
                 c += 64;
             }
         };
+        // the same for one lane: eight symbols per step from the 4-bit copy
+        auto lcs_from = [&](int t, int e, int c) -> int {
+            if (Nib) {
+                const uint32_t *n32 = reinterpret_cast<const uint32_t *>(nib);
+                // symbols pe-7..pe, pe in the top nibble (pe >= 7; the second
+                // word is read only when the window straddles two)
+                auto win8 = [&](int pe) -> uint32_t {
+                    const int q = pe - 7, wi = q >> 3, sh = 4 * (q & 7);
+                    const uint32_t lo = n32[wi];
+                    const uint32_t hi = sh ? n32[wi + 1] : 0u;
+                    return __builtin_amdgcn_alignbit(hi, lo, (uint32_t)sh);
+                };
+                while (e - c >= 7) {
+                    const uint32_t df = win8(t - c) ^ win8(e - c);
+                    if (df)
+                        return c + (__clz((int)df) >> 2);
+                    c += 8;
+                }
+            }
+            while (c <= e && sym(t - c) == sym(e - c))
+                ++c;
+            return c;
+        };
         auto run = [&](int t) {
             // the run's end: the first position after t whose bit is clear
             int tend = T;
@@ -1367,6 +1380,25 @@ __global__ __launch_bounds__(kStreamThreads) void unpermute_kernel(MatchParams p
                     if (c > bc || (c == bc && e > be)) {
                         bc = c;
                         be = e;
+                    }
+                }
+                if (nc == 0) {
+                    // more candidates than a record holds: the position's task
+                    // (in.x: first slot, in.y: size) kept its positions; every
+                    // earlier one is compared in full, one per lane
+                    const int32_t *tp = p.pos + (int64_t)s * T + in.x;
+                    const int e = lane < (int)in.y ? tp[lane] : T;
+                    if (e < t) {
+                        bc = lcs_from(t, e, 0);
+                        be = e;
+                    }
+                    // the lexicographic maximum of (c, e) over the lanes
+                    for (int o = 32; o >= 1; o >>= 1) {
+                        const int oc = __shfl_xor(bc, o), oe = __shfl_xor(be, o);
+                        if (oc > bc || (oc == bc && oe > be)) {
+                            bc = oc;
+                            be = oe;
+                        }
                     }
                 }
                 if (lane == 0) {
