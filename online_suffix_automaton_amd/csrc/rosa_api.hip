@@ -346,6 +346,7 @@ rosa_status rosa_match_qk(const rosa_input *q, const rosa_input *k,
     p.nodes = reinterpret_cast<int4 *>(base + l.nodes);
     p.next = reinterpret_cast<int32_t *>(base + l.next);
     p.start = reinterpret_cast<int32_t *>(base + l.start);
+    p.redo = reinterpret_cast<int32_t *>(base + l.redo);
     p.tau = out->tau;
     p.end = out->end;
     p.len = out->len;

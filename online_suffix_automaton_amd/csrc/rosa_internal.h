@@ -109,13 +109,15 @@ struct QkParams {
     int32_t *next;          // [S][Ncap][K]
     int32_t *start;         // [S][T] start time of each unit
     int32_t *tau, *end, *len, *run_of, *run_start, *ridx, *cf_tau, *cf_ridx;
+    int32_t *redo;          // [S] streams the bit-parallel kernel left to the automaton
+    const int32_t *only;    // automaton kernels: when set, only streams with only[s] != 0
 };
 
 
 // Workspace of rosa_match_qk: flags, padded query and key rows, unit starts,
 // the automaton nodes and dense transition rows.
 struct QkLayout {
-    size_t flags, qrows, krows, start, nodes, next, total;
+    size_t flags, qrows, krows, start, nodes, next, redo, total;
     int64_t Tp, Ncap;
 };
 
@@ -131,6 +133,7 @@ inline QkLayout qk_layout(int64_t S, int64_t T, int64_t K)
     l.start = o;  o = align_up(o + (size_t)S * T * 4, 256);
     l.nodes = o;  o = align_up(o + (size_t)S * l.Ncap * 16, 256);
     l.next = o;   o = align_up(o + (size_t)S * l.Ncap * K * 4, 256);
+    l.redo = o;   o = align_up(o + (size_t)S * 4, 256);
     l.total = o;
     return l;
 }

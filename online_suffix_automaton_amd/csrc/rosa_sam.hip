@@ -310,7 +310,7 @@ __global__ __launch_bounds__(64) void qk_kernel(QkParams p)
 {
     const int lane = threadIdx.x;
     const int64_t s = blockIdx.x;
-    if (s >= p.S)
+    if (s >= p.S || (p.only && p.only[s] == 0))
         return;
     const bool want_cf = p.cf_tau || p.cf_ridx;
     const int nl = want_cf ? 1 + p.M : 1;   // active lanes
@@ -463,6 +463,8 @@ __global__ __launch_bounds__(64) void qk_lds_kernel(QkParams p)
     __shared__ uint16_t st[MT];
     const int lane = threadIdx.x;
     const int64_t s = blockIdx.x;
+    if (p.only && p.only[s] == 0)
+        return;
     const int T = (int)p.T, K = p.K, M = p.M;
     const bool want_cf = p.cf_tau || p.cf_ridx;
     const int nl = want_cf ? 1 + M : 1;
@@ -742,11 +744,12 @@ hipError_t launch_sam_step(void *buf, int64_t S, int64_t K, int64_t Tcap,
 }
 
 // LDS tables when the stream fits a configuration and the streams fit the
-// device in one round (one workgroup per stream resident at once);
-// otherwise the HBM tables, whose many waves per CU hide their latency
-// better than a second round of LDS workgroups.
+// device in one round (one workgroup per stream resident at once), or when
+// only a few streams are expected (`any`: the leftovers of the bit-parallel
+// kernel); otherwise the HBM tables, whose many waves per CU hide their
+// latency better than a second round of LDS workgroups.
 template <int MT>
-static bool qk_lds_try(const QkParams &p, hipStream_t st)
+static bool qk_lds_try(const QkParams &p, hipStream_t st, bool any)
 {
     if (p.T > MT)
         return false;
@@ -758,18 +761,32 @@ static bool qk_lds_try(const QkParams &p, hipStream_t st)
         hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return false;
     const int64_t per_cu = 163840 / (int64_t)QlCfg<MT>::kLds;
-    if (p.S > per_cu * cus[dev])
+    if (!any && p.S > per_cu * cus[dev])
         return false;
     hipLaunchKernelGGL(qk_lds_kernel<MT>, dim3((unsigned)p.S), dim3(64), 0, st, p);
     return true;
 }
 
+bool qk_bits_fits(const QkParams &p);
+hipError_t launch_qk_bits(const QkParams &p, hipStream_t st);
+
+// The bit-parallel kernel when the streams fit it, then an automaton kernel
+// for the streams it left (matches longer than its levels); otherwise an
+// automaton kernel for every stream.
 hipError_t launch_qk(QkParams p, hipStream_t st)
 {
     p.spw = 1;
+    p.only = nullptr;
+    const bool bits = qk_bits_fits(p);
+    if (bits) {
+        const hipError_t e = launch_qk_bits(p, st);
+        if (e != hipSuccess)
+            return e;
+        p.only = p.redo;
+    }
     const bool lds_ok = p.K <= kQlMaxK && p.M <= 8;
-    if (!(lds_ok && (qk_lds_try<1024>(p, st) || qk_lds_try<2048>(p, st) ||
-                     qk_lds_try<4096>(p, st))))
+    if (!(lds_ok && (qk_lds_try<1024>(p, st, bits) || qk_lds_try<2048>(p, st, bits) ||
+                     qk_lds_try<4096>(p, st, bits))))
         hipLaunchKernelGGL(qk_kernel, dim3((unsigned)p.S), dim3(64), 0, st, p);
     return hipGetLastError();
 }
