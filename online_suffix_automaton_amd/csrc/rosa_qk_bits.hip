@@ -14,10 +14,11 @@
 //   B_l(u) = { e < u : k_e = q_u and e-1 in B_{l-1}(u-1) },
 // so B_l(u) = (B_{l-1}(u-1) shifted up by one) & EQ(q_u), with EQ(c) the set
 // of key units so far with symbol c.  L(u) is the largest l with B_l(u)
-// nonempty and E(u) its largest member; L(u) <= L(u-1) + 1.  A stream of at
-// most 4096 units is one wave: every set is a 4096-bit vector, lane w holding
-// bits 64w..64w+63, so one update of a set is a few instructions for all
-// candidate ends at once, and the levels 1..L live in registers.  A
+// nonempty and E(u) its largest member; L(u) <= L(u-1) + 1, and B_l(u) is
+// contained in B_{l-1}(u), so the nonempty levels are 1..L(u).  A stream of
+// at most 4096 units is one wave: every set is a 4096-bit vector, lane w
+// holding bits 64w..64w+63, so one update of a set is a few instructions for
+// all candidate ends at once, and the levels 1..L live in registers.  A
 // counterfactual branch is the same update with the flipped symbol's EQ,
 // computed from the sets before the unit's own update.
 //
@@ -30,6 +31,7 @@ namespace rosa {
 constexpr int kQbLevels = 32;    // levels kept in registers
 constexpr int kQbMaxT = 4096;    // one 64-bit word per lane
 constexpr int kQbMaxK = 64;
+constexpr int kQbMaxChains = 7;  // the unit's own update + M <= 6 branches
 
 // The 4096-bit vector shifted up by one: bit e of the result is bit e-1 of v
 // (the carry into each word is the top bit of the lane below, by a
@@ -41,109 +43,120 @@ __device__ __forceinline__ uint64_t qb_shl1(uint64_t v)
     return (v << 1) | (uint64_t)(uint32_t)c;
 }
 
-// The chains of one unit: the unit's own update (chain 0) and its
-// counterfactual branches (chains 1..NCH-1), each with its symbol's EQ word,
-// its number of nonempty levels and the set at the last of them.
+// What the levels of one unit leave per chain: the set at the highest
+// nonempty level, and for chain 0 that level, L(u).
 template <int NCH>
-struct QbChains {
-    uint64_t eq[NCH], top[NCH];
-    int L[NCH];
-    bool over;   // a chain is still nonempty past kQbLevels
+struct QbAcc {
+    uint64_t top[NCH];
+    int L0;
 };
 
-// Level l of every chain: all of them shift the same set, B_{l-1} of the
-// previous unit (`prev`, read before chain 0 overwrites it), and AND it with
-// their EQ; chain 0 stores its new level in B.  A set that is empty at one
-// level is empty at every higher one (B_l is contained in B_{l-1}), so the
-// chains need no liveness of their own: the levels stop once all of them are
-// empty or the previous unit's depth is passed.  Unrolled by template
-// recursion so that B stays in registers.
+// Levels l..lim of every chain, from the bottom up: level l of a chain is
+// the previous unit's B_{l-1} (`prev`, read before chain 0 overwrites it)
+// shifted up by one and masked with the chain's EQ; chain 0 stores its new
+// level in B[l-1].  A set that is empty at one level is empty at every
+// higher one, so the last nonempty level visited is the top one.  Levels
+// above lim = L(u-1) + 1 are empty and not visited; B keeps stale values
+// there, which no later unit reads (it visits at most L(u) + 1 levels).
+// Unrolled by template recursion so that B stays in registers.
 template <int l, int NCH>
-__device__ __forceinline__ void qb_levels(uint64_t (&B)[kQbLevels], uint64_t prev,
-                                          int lim, QbChains<NCH> &c)
+__device__ __forceinline__ void qb_levels(uint64_t (&B)[kQbLevels], uint64_t prev, int lim,
+                                          const uint64_t (&e)[NCH], QbAcc<NCH> &a)
 {
     if constexpr (l <= kQbLevels) {
-        if (l > lim)
-            return;
         const uint64_t old = B[l - 1];
         const uint64_t sh = l == 1 ? ~0ull : qb_shl1(prev);
-        bool any = false;
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
-            const uint64_t nw = sh & c.eq[i];
+            const uint64_t nw = sh & e[i];
             const bool ne = __builtin_amdgcn_ballot_w64(nw != 0) != 0;
-            c.top[i] = ne ? nw : c.top[i];
-            c.L[i] = ne ? l : c.L[i];
-            any = any || ne;
-            if (i == 0)
+            a.top[i] = ne ? nw : a.top[i];
+            if (i == 0) {
+                a.L0 = ne ? l : a.L0;
                 B[l - 1] = nw;
+            }
         }
-        if (!any)
-            return;
-        qb_levels<l + 1, NCH>(B, old, lim, c);
-    } else {
-        // past the kept levels: a chain that would still grow is not followed
-        if (l <= lim) {
-            const uint64_t sh = qb_shl1(prev);
-#pragma unroll
-            for (int i = 0; i < NCH; ++i)
-                if (__builtin_amdgcn_ballot_w64((sh & c.eq[i]) != 0))
-                    c.over = true;
-        }
+        if (l < lim)
+            qb_levels<l + 1, NCH>(B, old, lim, e, a);
     }
-}
-
-// Largest member of a nonempty set (wave-uniform).
-__device__ __forceinline__ int qb_top(uint64_t v)
-{
-    const uint64_t lanes = __builtin_amdgcn_ballot_w64(v != 0);
-    const int h = 63 - __clzll((long long)lanes);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, h);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), h);
-    const uint64_t w = ((uint64_t)hi << 32) | lo;
-    return 64 * h + 63 - __clzll((long long)w);
 }
 
 // Symbol of chain i for query symbol q: q itself, then q with bit i-1 flipped.
 template <int i>
 __device__ __forceinline__ int qb_sym(int q)
 {
-    return (i == 0 ? q : (q ^ (1 << ((i - 1) & 7)))) & (kQbMaxK - 1);
+    return i == 0 ? q : (q ^ (1 << ((i - 1) & 7)));
 }
 
 // Reads the EQ words of every chain's symbol for query symbol q.
 template <int i, int NCH>
-__device__ __forceinline__ void qb_read_next(uint64_t (&eqn)[NCH],
-                                             const uint64_t (&eq)[kQbMaxK][64],
-                                             int q, int lane)
+__device__ __forceinline__ void qb_read_eq(uint64_t (&dst)[NCH], const uint64_t *eq,
+                                           int q, int kmask, int lane)
 {
     if constexpr (i < NCH) {
-        eqn[i] = eq[qb_sym<i>(q)][lane];
-        qb_read_next<i + 1, NCH>(eqn, eq, q, lane);
+        dst[i] = eq[(qb_sym<i>(q) & kmask) * 64 + lane];
+        qb_read_eq<i + 1, NCH>(dst, eq, q, kmask, lane);
     }
 }
 
+// Largest member of this lane's part of a set, or -1.
+__device__ __forceinline__ int qb_lane_top(uint64_t w, int lane)
+{
+    return w ? 64 * lane + 63 - __clzll((long long)w) : -1;
+}
+
+// Largest value of one 64-entry row of lane tops (int16).  The lanes of a
+// wave read different rows; each starts at another 16-byte piece of its row
+// so that they spread over the banks.
+__device__ __forceinline__ int qb_row_max(const int16_t *row, int r)
+{
+    typedef short v2s __attribute__((ext_vector_type(2)));
+    v2s m = {-1, -1};
+#pragma unroll
+    for (int pc = 0; pc < 8; ++pc) {
+        const uint4 w = *reinterpret_cast<const uint4 *>(row + 8 * ((pc ^ r) & 7));
+        const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v2s x;
+            __builtin_memcpy(&x, &d[k], 4);
+            m = __builtin_elementwise_max(m, x);
+        }
+    }
+    return m.x > m.y ? m.x : m.y;
+}
+
+// Shared memory of one stream: EQ words [KB][64] u64 (KB = K rounded up to a
+// power of two), lane-top rows [NCH][64 positions][64 lanes] int16, and with
+// run folding the start time of every unit [4096] u16.
+inline size_t qb_lds_bytes(int kb, int nch, bool rle)
+{
+    return (size_t)kb * 512 + (size_t)nch * 8192 + (rle ? (size_t)kQbMaxT * 2 : 0);
+}
+
 // One wave per stream.  NCH chains per unit (1, or 1 + M with the
-// counterfactual tables); RLE: key runs folded into units.
+// counterfactual tables); RLE: key runs folded into units; kmask = KB - 1.
 //
 // Per position the wave does wave-uniform work only: a new unit appends its
 // key symbol to EQ and issues the LDS reads of the next position's EQ words
-// (so their latency hides behind this unit's levels), then runs the levels.
-// The unit's answer (end, length, unit index, query symbol, branch ends) is
-// staged in lane j of the 64-position chunk by writelane; the outputs that
-// need the start time of a unit are formed after the chunk, one position per
-// lane, with the unit starts read from LDS in one gather.
+// (their latency hides behind this unit's levels), runs the levels, and
+// writes every chain's lane tops into the position's row.  After each
+// 64-position chunk every lane forms one position's outputs: the largest
+// member of each chain's top set is the maximum of its row, and the start
+// time of a unit comes from LDS.
 template <int NCH, bool RLE>
-__global__ __launch_bounds__(64) void qk_bits_kernel(QkParams p)
+__global__ __launch_bounds__(64) void qk_bits_kernel(QkParams p, int kmask)
 {
-    __shared__ uint64_t eq[kQbMaxK][64];
-    __shared__ uint16_t st[RLE ? kQbMaxT : 1];
+    extern __shared__ __align__(16) uint64_t qb_smem[];
     constexpr int M = NCH - 1;
+    uint64_t *eq = qb_smem;
+    int16_t *rows = reinterpret_cast<int16_t *>(qb_smem + (kmask + 1) * 64);
+    uint16_t *st = reinterpret_cast<uint16_t *>(rows + NCH * 4096);
     const int lane = threadIdx.x;
     const int64_t s = blockIdx.x;
     const int T = (int)p.T;
-    for (int c = 0; c < p.K; ++c)
-        eq[c][lane] = 0;
+    for (int c = 0; c <= kmask; ++c)
+        eq[c * 64 + lane] = 0;
     __syncthreads();
     const uint8_t *qr = p.q + s * p.Tp + kPadFront;
     const uint8_t *kr = p.k + s * p.Tp + kPadFront;
@@ -154,11 +167,11 @@ __global__ __launch_bounds__(64) void qk_bits_kernel(QkParams p)
         B[l] = 0;
     int Lc = 0;               // levels 1..Lc of the previous unit are nonempty
     bool over = false;
-    int u = -1, kprev = -1, qc = 0, ue = -1, ul = 0;
-    int cfe[M > 0 ? M : 1];
+    int u = -1, kprev = -1, qc = 0, ul = 0;
+    int carry[NCH];           // largest members of the unit a chunk begins in
 #pragma unroll
-    for (int b = 0; b < M; ++b)
-        cfe[b] = -1;
+    for (int i = 0; i < NCH; ++i)
+        carry[i] = -1;
     // EQ words of the next position's query symbol (nothing appended yet)
     uint64_t eqn[NCH];
 #pragma unroll
@@ -166,77 +179,102 @@ __global__ __launch_bounds__(64) void qk_bits_kernel(QkParams p)
         eqn[i] = 0;
     // the next key unit's bit: unit u is bit u%64 of lane u/64
     uint64_t wbit = lane == 0 ? 1ull : 0ull;
-    // the rows carry 64 bytes of padding after T: chunk loads stay in the row
-    int kn = kr[lane], qn = qr[lane];
+    // chunk loads, one chunk ahead: key and query symbols of each lane's
+    // position and the query symbol of the position after it (the rows carry
+    // 64 bytes of padding after T, so these loads stay in the row)
+    int kn = kr[lane], qn = qr[lane], xn = qr[lane + 1];
     for (int t0 = 0; t0 < T && !over; t0 += 64) {
-        const int kch = kn, qch = qn;
+        const int kch = kn, qch = qn, qnext = xn;
         if (t0 + 64 < T) {
             kn = kr[t0 + 64 + lane];
             qn = qr[t0 + 64 + lane];
+            xn = qr[t0 + 65 + lane];
         }
-        int o_end = -1, o_len = 0, o_run = -1, o_q = 0;
-        int o_ce[M > 0 ? M : 1];
-#pragma unroll
-        for (int b = 0; b < M; ++b)
-            o_ce[b] = -1;
+        int o_len = 0, o_run = -1, o_q = 0, o_row = -1;
+        int jrow = -1;        // row of the current unit, if it began in this chunk
         const int n = T - t0 < 64 ? T - t0 : 64;
         for (int j = 0; j < n; ++j) {
             const int kc = __builtin_amdgcn_readlane(kch, j);
-            // query symbol of the next position (the padding past T reads 0)
-            const int qx = j < 63 ? __builtin_amdgcn_readlane(qch, j + 1)
-                                  : __builtin_amdgcn_readlane(qn, 0);
+            const int qx = __builtin_amdgcn_readlane(qnext, j);
             if (!RLE || kc != kprev) {
                 ++u;
                 qc = __builtin_amdgcn_readlane(qch, j);
                 if (RLE && lane == 0)
                     st[u] = (uint16_t)(t0 + j);
-                QbChains<NCH> c;
+                uint64_t e[NCH];
 #pragma unroll
-                for (int i = 0; i < NCH; ++i) {
-                    c.eq[i] = eqn[i];
-                    c.top[i] = 0;
-                    c.L[i] = 0;
-                }
-                c.over = false;
+                for (int i = 0; i < NCH; ++i)
+                    e[i] = eqn[i];
                 // append key unit u (this unit's chains use the words read
                 // before it), then read the next position's words
-                atomicOr(reinterpret_cast<unsigned long long *>(&eq[kc & (kQbMaxK - 1)][lane]),
+                atomicOr(reinterpret_cast<unsigned long long *>(&eq[(kc & kmask) * 64 + lane]),
                          (unsigned long long)wbit);
                 wbit = qb_shl1(wbit);
-                qb_read_next<0, NCH>(eqn, eq, qx, lane);
-                qb_levels<1, NCH>(B, 0ull, Lc + 1, c);
-                over = over || c.over;
-                Lc = c.L[0];
-                ul = c.L[0];
-                ue = ul > 0 ? qb_top(c.top[0]) : -1;
+                qb_read_eq<0, NCH>(eqn, eq, qx, kmask, lane);
+                int lim = Lc + 1;
+                if (lim > kQbLevels) {
+                    // a chain that would still grow past the kept levels
+                    const uint64_t sh = qb_shl1(B[kQbLevels - 1]);
 #pragma unroll
-                for (int b = 0; b < M; ++b)
-                    cfe[b] = c.L[b + 1] > 0 ? qb_top(c.top[b + 1]) : -1;
+                    for (int i = 0; i < NCH; ++i)
+                        if (__builtin_amdgcn_ballot_w64((sh & e[i]) != 0))
+                            over = true;
+                    lim = kQbLevels;
+                }
+                QbAcc<NCH> a;
+#pragma unroll
+                for (int i = 0; i < NCH; ++i)
+                    a.top[i] = 0;
+                a.L0 = 0;
+                qb_levels<1, NCH>(B, 0ull, lim, e, a);
+                Lc = a.L0;
+                ul = a.L0;
+                jrow = j;
+#pragma unroll
+                for (int i = 0; i < NCH; ++i)
+                    rows[(i * 64 + j) * 64 + lane] = (int16_t)qb_lane_top(a.top[i], lane);
                 kprev = kc;
             } else {
-                qb_read_next<0, NCH>(eqn, eq, qx, lane);
+                qb_read_eq<0, NCH>(eqn, eq, qx, kmask, lane);
             }
-            // this position's answer, staged in lane j
+            // this position's unit, staged in lane j
             const bool mine = lane == j;
-            o_end = mine ? ue : o_end;
             o_len = mine ? ul : o_len;
-            o_run = mine ? u : o_run;
-            if (M > 0)
-                o_q = mine ? qc : o_q;
+            if (RLE) {
+                o_row = mine ? jrow : o_row;
+                o_run = mine ? u : o_run;
+                if (M > 0)
+                    o_q = mine ? qc : o_q;
+            }
+        }
+        // the rows and unit starts were written by other lanes of this wave
+        __builtin_amdgcn_wave_barrier();
+        if (!RLE) {
+            o_row = lane;
+            o_run = t0 + lane;
+            o_q = qch;
+        }
+        // every chain's largest member at this lane's position: the maximum
+        // of the unit's row, or the unit the chunk began in
+        int E[NCH];
 #pragma unroll
-            for (int b = 0; b < M; ++b)
-                o_ce[b] = mine ? cfe[b] : o_ce[b];
+        for (int i = 0; i < NCH; ++i) {
+            E[i] = o_row >= 0 ? qb_row_max(rows + (i * 64 + (o_row & 63)) * 64, o_row)
+                              : carry[i];
+            if (RLE)
+                carry[i] = __builtin_amdgcn_readlane(E[i], n - 1);
         }
         if (lane < n && !over) {
             const int t = t0 + lane;
             const int64_t o = base + t;
             // a match ending at unit e is usable once unit e+1 has started
-            const int ds = o_end >= 0 ? (RLE ? (int)st[o_end + 1] : o_end + 1) : -1;
-            const int tt = (o_end >= 0 && ds < t) ? ds : -1;
-            const int rt = tt >= 0 ? o_end + 1 : -1;
+            const int ue = E[0];
+            const int ds = ue >= 0 ? (RLE ? (int)st[ue + 1] : ue + 1) : -1;
+            const int tt = (ue >= 0 && ds < t) ? ds : -1;
+            const int rt = tt >= 0 ? ue + 1 : -1;
             p.tau[o] = tt;
             if (p.end)
-                p.end[o] = o_end;
+                p.end[o] = ue;
             if (p.len)
                 p.len[o] = o_len;
             if (p.run_of)
@@ -245,7 +283,7 @@ __global__ __launch_bounds__(64) void qk_bits_kernel(QkParams p)
                 p.ridx[o] = rt;
 #pragma unroll
             for (int b = 0; b < M; ++b) {
-                const int ce = o_ce[b];
+                const int ce = E[b + 1];
                 const int cd = ce >= 0 ? (RLE ? (int)st[ce + 1] : ce + 1) : -1;
                 const int tb = (ce >= 0 && cd < t) ? cd : -1;
                 const int rb = tb >= 0 ? ce + 1 : -1;
@@ -259,6 +297,7 @@ __global__ __launch_bounds__(64) void qk_bits_kernel(QkParams p)
                         bit ? make_int2(rb, rt) : make_int2(rt, rb);
             }
         }
+        __builtin_amdgcn_wave_barrier();
     }
     if (!over && p.run_start)
         for (int v = lane; v < T; v += 64)
@@ -267,35 +306,69 @@ __global__ __launch_bounds__(64) void qk_bits_kernel(QkParams p)
         p.redo[s] = over ? 1 : 0;
 }
 
+static int qb_kb(int K)
+{
+    int kb = 1;
+    while (kb < K)
+        kb <<= 1;
+    return kb;
+}
+
+static int qb_chains(const QkParams &p)
+{
+    return (p.cf_tau || p.cf_ridx) ? 1 + p.M : 1;
+}
+
 bool qk_bits_fits(const QkParams &p)
 {
     // with the tables, K = 2^M <= 64: at most 7 chains
-    return p.T <= kQbMaxT && p.K <= kQbMaxK &&
-           (!(p.cf_tau || p.cf_ridx) || p.M <= 6);
+    return p.T <= kQbMaxT && p.K <= kQbMaxK && qb_chains(p) <= kQbMaxChains;
+}
+
+template <int NCH, bool RLE>
+static hipError_t launch_qk_bits_n(const QkParams &p, hipStream_t st)
+{
+    const int kb = qb_kb(p.K);
+    const size_t lds = qb_lds_bytes(kb, NCH, RLE);
+    if (lds > 65536) {
+        // more dynamic shared memory than the default limit: raise it once
+        // per process (the chip has 160 KiB per workgroup)
+        static bool raised = false;
+        if (!raised) {
+            const hipError_t e = hipFuncSetAttribute(
+                reinterpret_cast<const void *>(&qk_bits_kernel<NCH, RLE>),
+                hipFuncAttributeMaxDynamicSharedMemorySize,
+                (int)qb_lds_bytes(kQbMaxK, NCH, RLE));
+            if (e != hipSuccess) {
+                (void)hipGetLastError();
+                return hipErrorNotSupported;   // not launched
+            }
+            raised = true;
+        }
+    }
+    hipLaunchKernelGGL((qk_bits_kernel<NCH, RLE>), dim3((unsigned)p.S), dim3(64), lds, st,
+                       p, kb - 1);
+    return hipGetLastError();
 }
 
 template <bool RLE>
-static hipError_t launch_qk_bits_r(const QkParams &p, int nch, hipStream_t st)
+static hipError_t launch_qk_bits_r(const QkParams &p, hipStream_t st)
 {
-    const dim3 g((unsigned)p.S), b(64);
-    switch (nch) {
-    case 1: hipLaunchKernelGGL((qk_bits_kernel<1, RLE>), g, b, 0, st, p); break;
-    case 2: hipLaunchKernelGGL((qk_bits_kernel<2, RLE>), g, b, 0, st, p); break;
-    case 3: hipLaunchKernelGGL((qk_bits_kernel<3, RLE>), g, b, 0, st, p); break;
-    case 4: hipLaunchKernelGGL((qk_bits_kernel<4, RLE>), g, b, 0, st, p); break;
-    case 5: hipLaunchKernelGGL((qk_bits_kernel<5, RLE>), g, b, 0, st, p); break;
-    case 6: hipLaunchKernelGGL((qk_bits_kernel<6, RLE>), g, b, 0, st, p); break;
-    case 7: hipLaunchKernelGGL((qk_bits_kernel<7, RLE>), g, b, 0, st, p); break;
+    switch (qb_chains(p)) {
+    case 1: return launch_qk_bits_n<1, RLE>(p, st);
+    case 2: return launch_qk_bits_n<2, RLE>(p, st);
+    case 3: return launch_qk_bits_n<3, RLE>(p, st);
+    case 4: return launch_qk_bits_n<4, RLE>(p, st);
+    case 5: return launch_qk_bits_n<5, RLE>(p, st);
+    case 6: return launch_qk_bits_n<6, RLE>(p, st);
+    case 7: return launch_qk_bits_n<7, RLE>(p, st);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_qk_bits(const QkParams &p, hipStream_t st)
 {
-    const int nch = (p.cf_tau || p.cf_ridx) ? 1 + p.M : 1;
-    return p.rle ? launch_qk_bits_r<true>(p, nch, st)
-                 : launch_qk_bits_r<false>(p, nch, st);
+    return p.rle ? launch_qk_bits_r<true>(p, st) : launch_qk_bits_r<false>(p, st);
 }
 
 }  // namespace rosa

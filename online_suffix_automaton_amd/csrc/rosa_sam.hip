@@ -777,12 +777,16 @@ hipError_t launch_qk(QkParams p, hipStream_t st)
 {
     p.spw = 1;
     p.only = nullptr;
-    const bool bits = qk_bits_fits(p);
+    bool bits = qk_bits_fits(p);
     if (bits) {
+        // hipErrorNotSupported: not launched, the automaton takes every stream
         const hipError_t e = launch_qk_bits(p, st);
-        if (e != hipSuccess)
+        if (e == hipErrorNotSupported)
+            bits = false;
+        else if (e != hipSuccess)
             return e;
-        p.only = p.redo;
+        else
+            p.only = p.redo;
     }
     const bool lds_ok = p.K <= kQlMaxK && p.M <= 8;
     if (!(lds_ok && (qk_lds_try<1024>(p, st, bits) || qk_lds_try<2048>(p, st, bits) ||
