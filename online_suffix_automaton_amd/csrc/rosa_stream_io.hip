@@ -168,71 +168,89 @@ __global__ __launch_bounds__(256) void discretize_kernel(
 
 // ----------------------------------------------------------------- gather
 
-// Tile: 64 positions x 64 routes of one batch row, 256 threads.  E for the
-// tile is read as 64 contiguous 256-byte runs (one per stream) into LDS;
-// then wave w handles positions t0+16w..+15 with lane = route: one M-wide
-// value slice read from row tau = E+1 (random rows, inherent to the method)
-// and one coalesced write of the output row segment.  Tiles are numbered
-// route tile fastest, so the workgroups in flight cover a narrow band of
-// positions: destinations cluster a few thousand rows behind t, and the
-// band of V rows they read stays resident in the last-level cache, each
-// line serving the eight or more streams that share it.  A workgroup loops
-// over tiles with the grid's stride.
+// XCDs of the chip (consecutive workgroups of a launch go to consecutive
+// XCDs, round robin); the gather's routes and positions per tile and its
+// workgroups per XCD.
+constexpr int kXcds = 8;
+constexpr int kGatherRG = 32;
+constexpr int kGatherTP = 128;
+constexpr int64_t kGatherW = 128;
+
+// Tile: kGatherTP positions x kGatherRG routes of one batch row, 256
+// threads.  The reads of a route go to random earlier rows (tau = E+1,
+// inherent to the method; half of them within about 4K rows, nine in ten
+// within 27K on i.i.d. streams), and with M = 4 each 128-byte line of a V
+// row holds the values of 16 routes, read by them at different positions.
+// So the kernel keeps those lines in L2 between the reads: the route groups
+// are dealt to the 8 XCDs (group g to XCD g % 8; workgroup i runs on XCD
+// i % 8), an XCD does its groups one after another, and inside a group its
+// W workgroups walk the positions in order, side by side.  The lines of the
+// recent rows of one group then mostly fit the XCD's 4 MiB L2.  E and the
+// output are streamed with non-temporal accesses so that they do not push
+// those lines out.  The group width, tile length and W were chosen by
+// timing on the long workload (wider groups or fewer workgroups in flight
+// lose L2 hits or memory parallelism).
 template <int MC>
 __global__ __launch_bounds__(256) void gather_kernel(
     const uint16_t *__restrict__ V, int64_t T, int64_t D, int64_t ldv, int M,
-    const int32_t *__restrict__ E, uint16_t *__restrict__ out, int64_t ldo)
+    const int32_t *__restrict__ E, uint16_t *__restrict__ out, int64_t ldo, int W)
 {
-    __shared__ int32_t et[64][64 + 1];
+    constexpr int RG = kGatherRG, TP = kGatherTP;
+    constexpr int PSTEP = 256 / RG;          // positions per round of values
+    constexpr int NV = TP / PSTEP;           // value loads per thread
+    __shared__ int32_t et[RG][TP + 1];
     const int64_t R = D / M;
     const int64_t b = blockIdx.y;
-    const int64_t nrt = (R + 63) / 64, ntt = (T + 63) / 64;
-    const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
-    for (int64_t tile_i = blockIdx.x; tile_i < nrt * ntt; tile_i += gridDim.x) {
-        const int64_t tt = tile_i / nrt;
-        const int64_t t0 = tt * 64;
-        const int64_t r0 = (tile_i - tt * nrt) * 64;
-        // load E tile: 16 streams per wave-iteration, lane = position
-        for (int k = 0; k < 16; ++k) {
-            const int rl = w * 16 + k;
-            const int64_t rg = r0 + rl;
-            const int64_t t = t0 + lane;
+    const int64_t ng = (R + RG - 1) / RG, ntt = (T + TP - 1) / TP;
+    const int x = (int)(blockIdx.x % kXcds), jw = (int)(blockIdx.x / kXcds);
+    const int tid = threadIdx.x;
+    for (int64_t k = jw;; k += W) {
+        const int64_t pass = k / ntt, tt = k - pass * ntt;
+        const int64_t g = pass * kXcds + x;
+        if (g >= ng)
+            break;
+        const int64_t t0 = tt * TP, r0 = g * RG;
+        // E tile: consecutive threads read consecutive positions of a route
+        for (int idx = tid; idx < RG * TP; idx += 256) {
+            const int rl = idx / TP, tl = idx % TP;
+            const int64_t r = r0 + rl;
             int32_t e = -1;
-            if (rg < R && t < T) {
-                e = E[(b * R + rg) * T + t];
+            if (r < R && t0 + tl < T) {
+                e = __builtin_nontemporal_load(E + (b * R + r) * T + t0 + tl);
                 if (e < -1) e = -1;
                 if (e > T - 2) e = (int32_t)(T - 2);
             }
-            et[rl][lane] = e;
+            et[rl][tl] = e;
         }
         __syncthreads();
-        const int64_t r = r0 + lane;
+        // values: RG consecutive threads = the routes of one position
+        const int rl = tid % RG;
+        const int64_t r = r0 + rl;
         if (r < R && MC == 4) {
-            // all 16 value loads in flight before the stores
-            uint2 v[16];
+            uint64_t v[NV];
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const int tl = w * 16 + k;
-                const int32_t e = et[lane][tl];
-                v[k] = make_uint2(0u, 0u);
+            for (int i = 0; i < NV; ++i) {
+                const int tl = tid / RG + PSTEP * i;
+                const int32_t e = et[rl][tl];
+                v[i] = 0;
                 if (t0 + tl < T && e >= 0)
-                    v[k] = *reinterpret_cast<const uint2 *>(
+                    v[i] = *reinterpret_cast<const uint64_t *>(
                         V + (b * T + (e + 1)) * ldv + r * M);
             }
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const int64_t t = t0 + w * 16 + k;
+            for (int i = 0; i < NV; ++i) {
+                const int64_t t = t0 + tid / RG + PSTEP * i;
                 if (t < T)
-                    *reinterpret_cast<uint2 *>(out + (b * T + t) * ldo + r * M) = v[k];
+                    __builtin_nontemporal_store(
+                        v[i], reinterpret_cast<uint64_t *>(out + (b * T + t) * ldo + r * M));
             }
         } else if (r < R) {
-            for (int k = 0; k < 16; ++k) {
-                const int tl = w * 16 + k;
+            for (int i = 0; i < NV; ++i) {
+                const int tl = tid / RG + PSTEP * i;
                 const int64_t t = t0 + tl;
                 if (t >= T)
                     break;
-                const int32_t e = et[lane][tl];
+                const int32_t e = et[rl][tl];
                 uint16_t *o = out + (b * T + t) * ldo + r * M;
                 const uint16_t *src = V + (b * T + (e + 1)) * ldv + r * M;
                 for (int m = 0; m < M; ++m)
@@ -291,17 +309,20 @@ hipError_t launch_gather(const uint16_t *V, int64_t B, int64_t T, int64_t D,
                          int64_t ldv, int M, const int32_t *E, uint16_t *out,
                          int64_t ldo, hipStream_t st)
 {
+    // W workgroups per XCD (four per CU), fewer when an XCD has fewer tiles
     const int64_t R = D / M;
-    const int64_t ntiles = ((R + 63) / 64) * ((T + 63) / 64);
-    dim3 grid((unsigned)(ntiles < kTileGrid ? ntiles : kTileGrid), (unsigned)B);
+    const int64_t per_xcd = ((R + kGatherRG - 1) / kGatherRG + kXcds - 1) / kXcds *
+                            ((T + kGatherTP - 1) / kGatherTP);
+    const int W = (int)(per_xcd < kGatherW ? per_xcd : kGatherW);
+    dim3 grid((unsigned)(kXcds * W), (unsigned)B);
     const bool vec4 = M == 4 && (ldv % 4) == 0 && (ldo % 4) == 0 &&
                       (((uintptr_t)V) & 7) == 0 && (((uintptr_t)out) & 7) == 0;
     if (vec4)
         hipLaunchKernelGGL(gather_kernel<4>, grid, dim3(256), 0, st, V, T, D,
-                           ldv, M, E, out, ldo);
+                           ldv, M, E, out, ldo, W);
     else
         hipLaunchKernelGGL(gather_kernel<0>, grid, dim3(256), 0, st, V, T, D,
-                           ldv, M, E, out, ldo);
+                           ldv, M, E, out, ldo, W);
     return hipGetLastError();
 }
 
