@@ -181,3 +181,25 @@ def test_qk_many_short_streams():
                         K=K, rle=True, cf=True)
     torch.cuda.synchronize()
     _compare(got, oracle.match_qk(q, k, K, 4, True, cf=True), "512 x 2000")
+
+
+@pytest.mark.parametrize("rle", [False, True])
+def test_qk_long_matches_mixed_with_short(rle):
+    """One call mixing streams whose matches grow past 32 units (equal query
+    and key streams; query copies of 31, 32, 33 and 40 key units planted at a
+    later time) with ordinary independent streams: every stream's outputs,
+    whichever kernel answers it, equal the oracle's."""
+    S, T, K = 10, 3000, 16
+    rng = np.random.default_rng(77 + rle)
+    k = rng.integers(0, K, (S, T)).astype(np.uint8)
+    q = rng.integers(0, K, (S, T)).astype(np.uint8)
+    q[0] = k[0]
+    q[5] = k[5]
+    for s, n in ((1, 31), (2, 32), (3, 33), (4, 40), (6, 32), (7, 33)):
+        a, b = 100 + 37 * s, 2000 + 11 * s   # key units a..a+n-1 copied to query times b..
+        q[s, b:b + n] = k[s, a:a + n]
+    _say(f"qk long/short mix rle={rle}")
+    got = rosa.match_qk(torch.from_numpy(q).to(DEV), torch.from_numpy(k).to(DEV),
+                        K=K, rle=rle, cf=True)
+    torch.cuda.synchronize()
+    _compare(got, oracle.match_qk(q, k, K, 4, rle, cf=True), f"long/short mix rle={rle}")
