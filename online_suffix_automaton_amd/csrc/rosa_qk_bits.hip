@@ -81,21 +81,22 @@ __device__ __forceinline__ void qb_levels(uint64_t (&B)[kQbLevels], uint64_t pre
     }
 }
 
-// Symbol of chain i for query symbol q: q itself, then q with bit i-1 flipped.
-template <int i>
-__device__ __forceinline__ int qb_sym(int q)
+// Symbol of chain i for query symbol q: q itself, then q with one bit
+// flipped, flip[i] = 1 << (its query bit).
+template <int i, int NCH>
+__device__ __forceinline__ int qb_sym(int q, const int (&flip)[NCH])
 {
-    return i == 0 ? q : (q ^ (1 << ((i - 1) & 7)));
+    return i == 0 ? q : (q ^ flip[i]);
 }
 
 // Reads the EQ words of every chain's symbol for query symbol q.
 template <int i, int NCH>
 __device__ __forceinline__ void qb_read_eq(uint64_t (&dst)[NCH], const uint64_t *eq,
-                                           int q, int kmask, int lane)
+                                           int q, int kmask, int lane, const int (&flip)[NCH])
 {
     if constexpr (i < NCH) {
-        dst[i] = eq[(qb_sym<i>(q) & kmask) * 64 + lane];
-        qb_read_eq<i + 1, NCH>(dst, eq, q, kmask, lane);
+        dst[i] = eq[(qb_sym<i, NCH>(q, flip) & kmask) * 64 + lane];
+        qb_read_eq<i + 1, NCH>(dst, eq, q, kmask, lane, flip);
     }
 }
 
@@ -134,8 +135,12 @@ inline size_t qb_lds_bytes(int kb, int nch, bool rle)
     return (size_t)kb * 512 + (size_t)nch * 8192 + (rle ? (size_t)kQbMaxT * 2 : 0);
 }
 
-// One wave per stream.  NCH chains per unit (1, or 1 + M with the
-// counterfactual tables); RLE: key runs folded into units; kmask = KB - 1.
+// One wave per stream, or per half of a stream's counterfactual branches
+// (halves = 2: workgroup 2s + h does the unit's own update, which drives
+// the sets, and the branches of query bits h*(NCH-1) .. h*(NCH-1) + NCH-2;
+// the first half also writes the stream's own outputs).  NCH chains per
+// unit (1, or 1 + the branches); RLE: key runs folded into units;
+// kmask = KB - 1.
 //
 // Per position the wave does wave-uniform work only: a new unit appends its
 // key symbol to EQ and issues the LDS reads of the next position's EQ words
@@ -145,15 +150,26 @@ inline size_t qb_lds_bytes(int kb, int nch, bool rle)
 // member of each chain's top set is the maximum of its row, and the start
 // time of a unit comes from LDS.
 template <int NCH, bool RLE>
-__global__ __launch_bounds__(64) void qk_bits_kernel(QkParams p, int kmask)
+__global__ __launch_bounds__(64) void qk_bits_kernel(QkParams p, int kmask, int halves)
 {
     extern __shared__ __align__(16) uint64_t qb_smem[];
-    constexpr int M = NCH - 1;
+    constexpr int NB = NCH - 1;   // branches of this workgroup
     uint64_t *eq = qb_smem;
     int16_t *rows = reinterpret_cast<int16_t *>(qb_smem + (kmask + 1) * 64);
     uint16_t *st = reinterpret_cast<uint16_t *>(rows + NCH * 4096);
     const int lane = threadIdx.x;
-    const int64_t s = blockIdx.x;
+    const int64_t s = blockIdx.x / halves;
+    const int half = (int)(blockIdx.x % halves);
+    const int bit0 = half * NB;   // query bit of branch 1
+    const bool own = half == 0;   // writes the stream's own outputs
+    // flip[i]: the query bit branch i forces (a branch past the last bit
+    // repeats the last one and writes nothing)
+    int flip[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int bq = bit0 + i - 1;
+        flip[i] = i == 0 ? 0 : 1 << (bq < p.M ? bq : p.M - 1);
+    }
     const int T = (int)p.T;
     for (int c = 0; c <= kmask; ++c)
         eq[c * 64 + lane] = 0;
@@ -181,14 +197,21 @@ __global__ __launch_bounds__(64) void qk_bits_kernel(QkParams p, int kmask)
     uint64_t wbit = lane == 0 ? 1ull : 0ull;
     // chunk loads, one chunk ahead: key and query symbols of each lane's
     // position and the query symbol of the position after it (the rows carry
-    // 64 bytes of padding after T, so these loads stay in the row)
-    int kn = kr[lane], qn = qr[lane], xn = qr[lane + 1];
+    // 64 bytes of padding after T, so these loads stay in the row).  The
+    // last goes through its own pointer, opaque to the compiler: merged with
+    // the query load into one 2-byte load, its bytes would be split, and
+    // waited for, right after the load.
+    typedef const __attribute__((address_space(1))) uint8_t *qb_gbytes;
+    const uint8_t *xp = qr + 1;
+    asm volatile("" : "+s"(xp));
+    const qb_gbytes xr = (qb_gbytes)xp;   // global memory, not flat
+    int kn = kr[lane], qn = qr[lane], xn = xr[lane];
     for (int t0 = 0; t0 < T && !over; t0 += 64) {
         const int kch = kn, qch = qn, qnext = xn;
         if (t0 + 64 < T) {
             kn = kr[t0 + 64 + lane];
             qn = qr[t0 + 64 + lane];
-            xn = qr[t0 + 65 + lane];
+            xn = xr[t0 + 64 + lane];
         }
         int o_len = 0, o_run = -1, o_q = 0, o_row = -1;
         int jrow = -1;        // row of the current unit, if it began in this chunk
@@ -210,7 +233,7 @@ __global__ __launch_bounds__(64) void qk_bits_kernel(QkParams p, int kmask)
                 atomicOr(reinterpret_cast<unsigned long long *>(&eq[(kc & kmask) * 64 + lane]),
                          (unsigned long long)wbit);
                 wbit = qb_shl1(wbit);
-                qb_read_eq<0, NCH>(eqn, eq, qx, kmask, lane);
+                qb_read_eq<0, NCH>(eqn, eq, qx, kmask, lane, flip);
                 int lim = Lc + 1;
                 if (lim > kQbLevels) {
                     // a chain that would still grow past the kept levels
@@ -235,7 +258,7 @@ __global__ __launch_bounds__(64) void qk_bits_kernel(QkParams p, int kmask)
                     rows[(i * 64 + j) * 64 + lane] = (int16_t)qb_lane_top(a.top[i], lane);
                 kprev = kc;
             } else {
-                qb_read_eq<0, NCH>(eqn, eq, qx, kmask, lane);
+                qb_read_eq<0, NCH>(eqn, eq, qx, kmask, lane, flip);
             }
             // this position's unit, staged in lane j
             const bool mine = lane == j;
@@ -243,7 +266,7 @@ __global__ __launch_bounds__(64) void qk_bits_kernel(QkParams p, int kmask)
             if (RLE) {
                 o_row = mine ? jrow : o_row;
                 o_run = mine ? u : o_run;
-                if (M > 0)
+                if (NB > 0)
                     o_q = mine ? qc : o_q;
             }
         }
@@ -272,23 +295,28 @@ __global__ __launch_bounds__(64) void qk_bits_kernel(QkParams p, int kmask)
             const int ds = ue >= 0 ? (RLE ? (int)st[ue + 1] : ue + 1) : -1;
             const int tt = (ue >= 0 && ds < t) ? ds : -1;
             const int rt = tt >= 0 ? ue + 1 : -1;
-            p.tau[o] = tt;
-            if (p.end)
-                p.end[o] = ue;
-            if (p.len)
-                p.len[o] = o_len;
-            if (p.run_of)
-                p.run_of[o] = o_run;
-            if (p.ridx)
-                p.ridx[o] = rt;
+            if (own) {
+                p.tau[o] = tt;
+                if (p.end)
+                    p.end[o] = ue;
+                if (p.len)
+                    p.len[o] = o_len;
+                if (p.run_of)
+                    p.run_of[o] = o_run;
+                if (p.ridx)
+                    p.ridx[o] = rt;
+            }
 #pragma unroll
-            for (int b = 0; b < M; ++b) {
-                const int ce = E[b + 1];
+            for (int i = 1; i < NCH; ++i) {
+                const int b = bit0 + i - 1;   // query bit of branch i
+                if (b >= p.M)
+                    break;
+                const int ce = E[i];
                 const int cd = ce >= 0 ? (RLE ? (int)st[ce + 1] : ce + 1) : -1;
                 const int tb = (ce >= 0 && cd < t) ? cd : -1;
                 const int rb = tb >= 0 ? ce + 1 : -1;
                 const bool bit = (o_q >> b) & 1;
-                const int64_t c0 = (o * M + b) * 2;
+                const int64_t c0 = (o * p.M + b) * 2;
                 if (p.cf_tau)
                     *reinterpret_cast<int2 *>(p.cf_tau + c0) =
                         bit ? make_int2(tb, tt) : make_int2(tt, tb);
@@ -299,11 +327,20 @@ __global__ __launch_bounds__(64) void qk_bits_kernel(QkParams p, int kmask)
         }
         __builtin_amdgcn_wave_barrier();
     }
-    if (!over && p.run_start)
+    if (own && !over && p.run_start)
         for (int v = lane; v < T; v += 64)
             p.run_start[base + v] = v <= u ? (RLE ? (int32_t)st[v] : v) : -1;
-    if (lane == 0)
+    // with two halves redo[] starts at zero and either half may set it
+    if (lane == 0 && (halves == 1 || over))
         p.redo[s] = over ? 1 : 0;
+}
+
+// Zeroes n int32 values.
+__global__ void qb_zero_kernel(int32_t *a, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        a[i] = 0;
 }
 
 static int qb_kb(int K)
@@ -325,8 +362,21 @@ bool qk_bits_fits(const QkParams &p)
     return p.T <= kQbMaxT && p.K <= kQbMaxK && qb_chains(p) <= kQbMaxChains;
 }
 
+// Compute units of the current device (cached per device), 0 if unknown.
+static int qb_cus()
+{
+    static int cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 0;
+    if (cus[dev] == 0 &&
+        hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus[dev] = -1;
+    return cus[dev] > 0 ? cus[dev] : 0;
+}
+
 template <int NCH, bool RLE>
-static hipError_t launch_qk_bits_n(const QkParams &p, hipStream_t st)
+static hipError_t launch_qk_bits_n(const QkParams &p, int halves, hipStream_t st)
 {
     const int kb = qb_kb(p.K);
     const size_t lds = qb_lds_bytes(kb, NCH, RLE);
@@ -346,29 +396,47 @@ static hipError_t launch_qk_bits_n(const QkParams &p, hipStream_t st)
             raised = true;
         }
     }
-    hipLaunchKernelGGL((qk_bits_kernel<NCH, RLE>), dim3((unsigned)p.S), dim3(64), lds, st,
-                       p, kb - 1);
+    if (halves > 1)
+        hipLaunchKernelGGL(qb_zero_kernel, dim3((unsigned)((p.S + 255) / 256)), dim3(256), 0,
+                           st, p.redo, p.S);
+    hipLaunchKernelGGL((qk_bits_kernel<NCH, RLE>), dim3((unsigned)(p.S * halves)), dim3(64),
+                       lds, st, p, kb - 1, halves);
     return hipGetLastError();
 }
 
 template <bool RLE>
-static hipError_t launch_qk_bits_r(const QkParams &p, hipStream_t st)
+static hipError_t launch_qk_bits_r(const QkParams &p, int nch, int halves, hipStream_t st)
 {
-    switch (qb_chains(p)) {
-    case 1: return launch_qk_bits_n<1, RLE>(p, st);
-    case 2: return launch_qk_bits_n<2, RLE>(p, st);
-    case 3: return launch_qk_bits_n<3, RLE>(p, st);
-    case 4: return launch_qk_bits_n<4, RLE>(p, st);
-    case 5: return launch_qk_bits_n<5, RLE>(p, st);
-    case 6: return launch_qk_bits_n<6, RLE>(p, st);
-    case 7: return launch_qk_bits_n<7, RLE>(p, st);
+    switch (nch) {
+    case 1: return launch_qk_bits_n<1, RLE>(p, halves, st);
+    case 2: return launch_qk_bits_n<2, RLE>(p, halves, st);
+    case 3: return launch_qk_bits_n<3, RLE>(p, halves, st);
+    case 4: return launch_qk_bits_n<4, RLE>(p, halves, st);
+    case 5: return launch_qk_bits_n<5, RLE>(p, halves, st);
+    case 6: return launch_qk_bits_n<6, RLE>(p, halves, st);
+    case 7: return launch_qk_bits_n<7, RLE>(p, halves, st);
     default: return hipErrorInvalidValue;
     }
 }
 
+// One wave per stream, or two per stream with the counterfactual branches
+// split between them when the doubled grid still gives every wave a SIMD of
+// its own and fits the LDS at once (each wave is bound by its own
+// instruction issue, so the second wave uses otherwise idle SIMDs).
 hipError_t launch_qk_bits(const QkParams &p, hipStream_t st)
 {
-    return p.rle ? launch_qk_bits_r<true>(p, st) : launch_qk_bits_r<false>(p, st);
+    int nch = qb_chains(p), halves = 1;
+    if (nch >= 3) {
+        const int nh = 1 + (p.M + 1) / 2;
+        const int64_t cus = qb_cus();
+        const int64_t per_cu = 163840 / (int64_t)qb_lds_bytes(qb_kb(p.K), nh, p.rle != 0);
+        if (cus > 0 && 2 * p.S <= 4 * cus && 2 * p.S <= per_cu * cus) {
+            nch = nh;
+            halves = 2;
+        }
+    }
+    return p.rle ? launch_qk_bits_r<true>(p, nch, halves, st)
+                 : launch_qk_bits_r<false>(p, nch, halves, st);
 }
 
 }  // namespace rosa
