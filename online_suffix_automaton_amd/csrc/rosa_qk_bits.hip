@@ -184,6 +184,7 @@ __global__ __launch_bounds__(64) void qk_bits_kernel(QkParams p, int kmask, int 
     int Lc = 0;               // levels 1..Lc of the previous unit are nonempty
     bool over = false;
     int u = -1, kprev = -1, qc = 0, ul = 0;
+    int eqn_q = -1;           // query symbol the words in eqn were read for
     int carry[NCH];           // largest members of the unit a chunk begins in
 #pragma unroll
     for (int i = 0; i < NCH; ++i)
@@ -214,69 +215,98 @@ __global__ __launch_bounds__(64) void qk_bits_kernel(QkParams p, int kmask, int 
             xn = xr[t0 + 64 + lane];
         }
         int o_len = 0, o_run = -1, o_q = 0, o_row = -1;
-        int jrow = -1;        // row of the current unit, if it began in this chunk
         const int n = T - t0 < 64 ? T - t0 : 64;
-        for (int j = 0; j < n; ++j) {
-            const int kc = __builtin_amdgcn_readlane(kch, j);
-            const int qx = __builtin_amdgcn_readlane(qnext, j);
-            if (!RLE || kc != kprev) {
-                ++u;
-                qc = __builtin_amdgcn_readlane(qch, j);
-                if (RLE && lane == 0)
-                    st[u] = (uint16_t)(t0 + j);
-                uint64_t e[NCH];
+        // One unit, starting at chunk position j with key symbol kc and
+        // query symbol qcu; qx is the query symbol of the next unit's start,
+        // whose EQ words are read ahead.
+        auto unit = [&](int j, int kc, int qcu, int qx) {
+            ++u;
+            qc = qcu;
+            if (RLE && lane == 0)
+                st[u] = (uint16_t)(t0 + j);
+            uint64_t e[NCH];
+#pragma unroll
+            for (int i = 0; i < NCH; ++i)
+                e[i] = eqn[i];
+            if (RLE && qcu != eqn_q)   // the read-ahead was for another symbol
+                qb_read_eq<0, NCH>(e, eq, qcu, kmask, lane, flip);
+            // append key unit u (this unit's chains use the words read
+            // before it), then read the next unit's words
+            atomicOr(reinterpret_cast<unsigned long long *>(&eq[(kc & kmask) * 64 + lane]),
+                     (unsigned long long)wbit);
+            wbit = qb_shl1(wbit);
+            qb_read_eq<0, NCH>(eqn, eq, qx, kmask, lane, flip);
+            eqn_q = qx;
+            int lim = Lc + 1;
+            if (lim > kQbLevels) {
+                // a chain that would still grow past the kept levels
+                const uint64_t sh = qb_shl1(B[kQbLevels - 1]);
 #pragma unroll
                 for (int i = 0; i < NCH; ++i)
-                    e[i] = eqn[i];
-                // append key unit u (this unit's chains use the words read
-                // before it), then read the next position's words
-                atomicOr(reinterpret_cast<unsigned long long *>(&eq[(kc & kmask) * 64 + lane]),
-                         (unsigned long long)wbit);
-                wbit = qb_shl1(wbit);
-                qb_read_eq<0, NCH>(eqn, eq, qx, kmask, lane, flip);
-                int lim = Lc + 1;
-                if (lim > kQbLevels) {
-                    // a chain that would still grow past the kept levels
-                    const uint64_t sh = qb_shl1(B[kQbLevels - 1]);
-#pragma unroll
-                    for (int i = 0; i < NCH; ++i)
-                        if (__builtin_amdgcn_ballot_w64((sh & e[i]) != 0))
-                            over = true;
-                    lim = kQbLevels;
-                }
-                QbAcc<NCH> a;
-#pragma unroll
-                for (int i = 0; i < NCH; ++i)
-                    a.top[i] = 0;
-                a.L0 = 0;
-                qb_levels<1, NCH>(B, 0ull, lim, e, a);
-                Lc = a.L0;
-                ul = a.L0;
-                jrow = j;
-#pragma unroll
-                for (int i = 0; i < NCH; ++i)
-                    rows[(i * 64 + j) * 64 + lane] = (int16_t)qb_lane_top(a.top[i], lane);
-                kprev = kc;
-            } else {
-                qb_read_eq<0, NCH>(eqn, eq, qx, kmask, lane, flip);
+                    if (__builtin_amdgcn_ballot_w64((sh & e[i]) != 0))
+                        over = true;
+                lim = kQbLevels;
             }
-            // this position's unit, staged in lane j
-            const bool mine = lane == j;
-            o_len = mine ? ul : o_len;
-            if (RLE) {
-                o_row = mine ? jrow : o_row;
-                o_run = mine ? u : o_run;
-                if (NB > 0)
-                    o_q = mine ? qc : o_q;
+            QbAcc<NCH> a;
+#pragma unroll
+            for (int i = 0; i < NCH; ++i)
+                a.top[i] = 0;
+            a.L0 = 0;
+            qb_levels<1, NCH>(B, 0ull, lim, e, a);
+            Lc = a.L0;
+            ul = a.L0;
+#pragma unroll
+            for (int i = 0; i < NCH; ++i)
+                rows[(i * 64 + j) * 64 + lane] = (int16_t)qb_lane_top(a.top[i], lane);
+        };
+        if constexpr (!RLE) {
+            // every position is a unit
+            for (int j = 0; j < n; ++j) {
+                unit(j, __builtin_amdgcn_readlane(kch, j), __builtin_amdgcn_readlane(qch, j),
+                     __builtin_amdgcn_readlane(qnext, j));
+                o_len = lane == j ? ul : o_len;   // staged in lane j
             }
-        }
-        // the rows and unit starts were written by other lanes of this wave
-        __builtin_amdgcn_wave_barrier();
-        if (!RLE) {
             o_row = lane;
             o_run = t0 + lane;
             o_q = qch;
+        } else {
+            // units start where the key symbol changes; the loop visits the
+            // starts only, and each staged its unit in the start's lane
+            const int kup = __builtin_amdgcn_update_dpp(0, kch, 0x138, 0xF, 0xF, false);
+            const uint64_t S0 = __builtin_amdgcn_ballot_w64(
+                lane < n && kch != (lane == 0 ? kprev : kup));
+            const int ul_c = ul, u_c = u, qc_c = qc;   // the unit the chunk begins in
+            uint64_t S = S0;
+            while (S) {
+                const int j = __builtin_ctzll(S);
+                S &= S - 1;
+                // the next unit's query symbol: its start in this chunk, else
+                // a guess, the next chunk's first position (checked there)
+                const int qx = S ? __builtin_amdgcn_readlane(qch, __builtin_ctzll(S))
+                                 : __builtin_amdgcn_readlane(qn, 0);
+                unit(j, __builtin_amdgcn_readlane(kch, j), __builtin_amdgcn_readlane(qch, j), qx);
+                const bool mine = lane == j;
+                o_len = mine ? ul : o_len;
+                o_run = mine ? u : o_run;
+                o_q = mine ? qc : o_q;
+            }
+            kprev = __builtin_amdgcn_readlane(kch, n - 1);
+            // each position's unit: the last start at or before it in this
+            // chunk (values from that lane), else the unit the chunk began in
+            const uint64_t upto = lane == 63 ? ~0ull : ((2ull << lane) - 1);
+            const uint64_t m = S0 & upto;
+            const int js = m ? 63 - __clzll((long long)m) : -1;
+            const int src = (js < 0 ? 0 : js) * 4;
+            const int bl = __builtin_amdgcn_ds_bpermute(src, o_len);
+            const int br = __builtin_amdgcn_ds_bpermute(src, o_run);
+            const int bq = __builtin_amdgcn_ds_bpermute(src, o_q);
+            o_len = js >= 0 ? bl : ul_c;
+            o_run = js >= 0 ? br : u_c;
+            o_q = js >= 0 ? bq : qc_c;
+            o_row = js;
         }
+        // the rows and unit starts were written by other lanes of this wave
+        __builtin_amdgcn_wave_barrier();
         // every chain's largest member at this lane's position: the maximum
         // of the unit's row, or the unit the chunk began in
         int E[NCH];
