@@ -203,3 +203,31 @@ def test_qk_long_matches_mixed_with_short(rle):
                         K=K, rle=rle, cf=True)
     torch.cuda.synchronize()
     _compare(got, oracle.match_qk(q, k, K, 4, rle, cf=True), f"long/short mix rle={rle}")
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_qk_random_shapes(case):
+    """Seeded sweep over the shapes the bit-parallel kernel takes (ragged T
+    up to its 4096-unit limit, alphabets 2..64, with and without folding and
+    tables, stream counts on both sides of the two-waves-per-stream split),
+    each against the oracle."""
+    rng = np.random.default_rng(5000 + case)
+    K = int(rng.choice([2, 3, 5, 8, 16, 32, 64]))
+    T = int(rng.integers(1, 4097))
+    S = int(rng.choice([1, 3, 17, 40, 600]))
+    if S * T > 600 * 1200:
+        T = max(1, (600 * 1200) // S)
+    rle = bool(rng.integers(0, 2))
+    cf = (K & (K - 1)) == 0 and bool(rng.integers(0, 2))
+    mode = ["same", "indep", "mixed", "runs"][int(rng.integers(0, 4))]
+    M = (K - 1).bit_length()
+    _say(f"qk random case {case}: K={K} T={T} S={S} rle={rle} cf={cf} mode={mode}")
+    q, k = _streams(6000 + case, S, T, K, mode)
+    got = rosa.match_qk(torch.from_numpy(q).to(DEV), torch.from_numpy(k).to(DEV),
+                        K=K, rle=rle, cf=cf)
+    torch.cuda.synchronize()
+    want = oracle.match_qk(q, k, K, M if cf else 0, rle, cf=cf)
+    if not cf:
+        want.pop("cf_tau", None)
+        want.pop("cf_ridx", None)
+    _compare(got, want, f"random case {case}")
