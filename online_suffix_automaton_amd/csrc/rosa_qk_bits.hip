@@ -251,7 +251,11 @@ __global__ __launch_bounds__(64) void qk_bits_kernel(QkParams p, int kmask, int 
 #pragma unroll
             for (int i = 0; i < NCH; ++i)
                 a.top[i] = 0;
-            a.L0 = 0;
+            // L(u) starts at 0; through an opaque register, so that level 1
+            // sets it with a scalar select, not a vector select read back
+            int zero = 0;
+            asm volatile("" : "+s"(zero));
+            a.L0 = zero;
             qb_levels<1, NCH>(B, 0ull, lim, e, a);
             Lc = a.L0;
             ul = a.L0;
