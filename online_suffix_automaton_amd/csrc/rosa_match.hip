@@ -164,31 +164,34 @@ __device__ Found solve_wave(const uint8_t *x, int nbits, int t, uint64_t g,
         g = self;
     const int ell0 = ell;
     for (;;) {
-        const bool live = has && __popcll(g) >= 2;
-        if (ballot(live) == 0)
+        // the lane's group size, 0 without an element (the predicates below
+        // are compares of it, so each ballot is one vector compare)
+        const int pc = has ? __popcll(g) : 0;
+        const bool live = pc >= 2;
+        const uint64_t liveb = ballot(pc >= 2);
+        if (liveb == 0)
             return r;
         // level steps while some group is larger than kWordThresh during the
         // first two levels after bucketing (groups still split fast there),
         // later only while some group is larger than kWordThreshDeep
-        if (ell <= ell0 + 1) {
-            if (ballot(live && __popcll(g) > kWordThresh) == 0)
-                break;
-        } else if (ballot(live && __popcll(g) > kWordThreshDeep) == 0) {
+        const int th = ell <= ell0 + 1 ? kWordThresh : kWordThreshDeep;
+        if (ballot(pc > th) == 0)
             break;
-        }
         // ---------------------------------------------------- level step
         // split every group by the symbol x[t-ell]: lanes agree on it iff
         // they agree on each of its nbits bits (one ballot per bit)
-        const bool valid = live && (t - ell >= 0);
+        const bool valid = pc >= 2 && (t - ell >= 0);
         const uint32_t dig = valid ? (uint32_t)x[t - ell] : 0u;
-        uint64_t eq = ballot(valid);
+        // (a compare straight to a lane mask: the compiler would rebuild the
+        // ballot of the compare it already made for `valid` in a register)
+        uint64_t eq = liveb & __builtin_amdgcn_sicmp(t - ell, 0, 39 /* >= */);
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
-            if (b < nbits) {
-                const uint32_t bit = (dig >> b) & 1u;
-                const uint64_t B = ballot(bit != 0);
-                eq &= ~(B ^ (0ull - (uint64_t)bit));
-            }
+            const uint32_t bit = (dig >> b) & 1u;
+            const uint64_t B = ballot(bit != 0);
+            eq &= ~(B ^ (0ull - (uint64_t)bit));
+            if (b + 1 >= nbits)
+                break;
         }
         const uint64_t ng = valid ? (g & eq) : self;
         const uint64_t prev = g & below;
@@ -691,7 +694,7 @@ __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
     uint32_t key = has ? (((uint32_t)__popcll(B & upto) << 16) | (uint32_t)t0)
                        : 0xFFFFFFFFu;
     for (int r = 0; r < 64; r += 2) {
-        bool swapped = false;
+        uint64_t swapped = 0;   // lanes whose key changed (direct compares)
 #pragma unroll
         for (int par = 0; par < 2; ++par) {
             // wave_shl:1 / wave_shr:1: the keys of lanes i+1 and i-1
@@ -701,10 +704,10 @@ __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
                 0, (int)key, 0x138, 0xF, 0xF, false);
             const bool left = (lane & 1) == par;
             const uint32_t nk = left ? min(key, nx) : max(key, pv);
-            swapped |= nk != key;
+            swapped |= ballot(nk != key);
             key = nk;
         }
-        if (ballot(swapped) == 0)
+        if (swapped == 0)
             break;
     }
     const int t1 = has ? (int)(key & 0xFFFFu) : 0;
