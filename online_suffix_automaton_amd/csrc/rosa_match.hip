@@ -185,14 +185,20 @@ __device__ Found solve_wave(const uint8_t *x, int nbits, int t, uint64_t g,
         // (a compare straight to a lane mask: the compiler would rebuild the
         // ballot of the compare it already made for `valid` in a register)
         uint64_t eq = liveb & __builtin_amdgcn_sicmp(t - ell, 0, 39 /* >= */);
+        // eq &= lanes whose bit b equals mine: with m = all ones where my bit
+        // is set, each 32-bit half is e & (B == m), one 3-input bit op
+        // (table 0x90 over (e, B, m))
+        uint32_t eql = (uint32_t)eq, eqh = (uint32_t)(eq >> 32);
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
-            const uint32_t bit = (dig >> b) & 1u;
-            const uint64_t B = ballot(bit != 0);
-            eq &= ~(B ^ (0ull - (uint64_t)bit));
+            const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)dig, b, 1);
+            const uint64_t B = ballot(m != 0);
+            eql = __builtin_amdgcn_bitop3_b32(eql, (uint32_t)B, m, 0x90);
+            eqh = __builtin_amdgcn_bitop3_b32(eqh, (uint32_t)(B >> 32), m, 0x90);
             if (b + 1 >= nbits)
                 break;
         }
+        eq = ((uint64_t)eqh << 32) | eql;
         const uint64_t ng = valid ? (g & eq) : self;
         const uint64_t prev = g & below;
         const int p = prev ? 63 - __clzll((long long)prev) : lane;
