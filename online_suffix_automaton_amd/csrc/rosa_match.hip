@@ -232,8 +232,10 @@ __device__ Found solve_wave(const uint8_t *x, int nbits, int t, uint64_t g,
             // first 16 symbols from the shared windows, further ones from
             // memory while they keep matching
             const uint64_t fh = w0hi ^ jhi, fl = w0lo ^ jlo;
-            int c = fh ? (__clzll((long long)fh) >> 3)
-                       : (fl ? 8 + (__clzll((long long)fl) >> 3) : 16);
+            // leading equal bytes of (fh, fl), at most 16 (both counts
+            // computed and one selected: no divergent branch)
+            const int zh = __clzll((long long)fh), zl = __clzll((long long)fl);
+            int c = (fh != 0 ? zh : 64 + zl) >> 3;
             if (CAP && !(fh | fl) && c < aj) {
                 if (ntr < 7)
                     dr[ntr] = (uint16_t)tj;
