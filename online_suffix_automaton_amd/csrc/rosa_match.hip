@@ -585,16 +585,20 @@ __device__ void phase_short(const MatchParams &p, const uint8_t *x,
                 const bool v = inr && t >= l - 1;
                 const int dig = v ? (d <= 4 ? sym_of(w, l - 1) : (int)x[t - l + 1]) : 0;
                 gk = (int)__umul24((uint32_t)gk, (uint32_t)K) + dig;
-                uint64_t m = ballot(v);
+                // lanes with the same l-th symbol: per bit, each 32-bit half
+                // is e & (B == m) with m = all ones where my bit is set
+                const uint64_t m0 = ballot(v);
+                uint32_t ml = (uint32_t)m0, mh = (uint32_t)(m0 >> 32);
 #pragma unroll
                 for (int b = 0; b < 8; ++b) {
-                    if (b < p.nbits) {
-                        const uint32_t bit = ((uint32_t)dig >> b) & 1u;
-                        const uint64_t B = ballot(bit != 0);
-                        m &= ~(B ^ (0ull - (uint64_t)bit));
-                    }
+                    const uint32_t mb = (uint32_t)__builtin_amdgcn_sbfe(dig, b, 1);
+                    const uint64_t B = ballot(mb != 0);
+                    ml = __builtin_amdgcn_bitop3_b32(ml, (uint32_t)B, mb, 0x90);
+                    mh = __builtin_amdgcn_bitop3_b32(mh, (uint32_t)(B >> 32), mb, 0x90);
+                    if (b + 1 >= p.nbits)
+                        break;
                 }
-                eq &= m;
+                eq &= ((uint64_t)mh << 32) | ml;
                 const int slot = p.fl_off[l] + gk;
                 if (q && v && firstl[slot] < t) {
                     Lq = l;
