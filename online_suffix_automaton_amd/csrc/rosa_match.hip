@@ -184,11 +184,12 @@ __device__ Found solve_wave(const uint8_t *x, int nbits, int t, uint64_t g,
         const uint32_t dig = valid ? (uint32_t)x[t - ell] : 0u;
         // (a compare straight to a lane mask: the compiler would rebuild the
         // ballot of the compare it already made for `valid` in a register)
-        uint64_t eq = liveb & __builtin_amdgcn_sicmp(t - ell, 0, 39 /* >= */);
-        // eq &= lanes whose bit b equals mine: with m = all ones where my bit
-        // is set, each 32-bit half is e & (B == m), one 3-input bit op
-        // (table 0x90 over (e, B, m))
-        uint32_t eql = (uint32_t)eq, eqh = (uint32_t)(eq >> 32);
+        const uint64_t vmask = liveb & __builtin_amdgcn_sicmp(t - ell, 0, 39 /* >= */);
+        // eq = lanes of vmask whose symbol equals mine; per bit b, with m =
+        // all ones where my bit is set, each 32-bit half is e & (B == m), one
+        // 3-input bit op (table 0x90 over (e, B, m)); vmask is applied last,
+        // so that no bit op takes two scalar operands
+        uint32_t eql = ~0u, eqh = ~0u;
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
             const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)dig, b, 1);
@@ -198,7 +199,7 @@ __device__ Found solve_wave(const uint8_t *x, int nbits, int t, uint64_t g,
             if (b + 1 >= nbits)
                 break;
         }
-        eq = ((uint64_t)eqh << 32) | eql;
+        const uint64_t eq = vmask & (((uint64_t)eqh << 32) | eql);
         const uint64_t ng = valid ? (g & eq) : self;
         const uint64_t prev = g & below;
         const int p = prev ? 63 - __clzll((long long)prev) : lane;
@@ -586,9 +587,11 @@ __device__ void phase_short(const MatchParams &p, const uint8_t *x,
                 const int dig = v ? (d <= 4 ? sym_of(w, l - 1) : (int)x[t - l + 1]) : 0;
                 gk = (int)__umul24((uint32_t)gk, (uint32_t)K) + dig;
                 // lanes with the same l-th symbol: per bit, each 32-bit half
-                // is e & (B == m) with m = all ones where my bit is set
-                const uint64_t m0 = ballot(v);
-                uint32_t ml = (uint32_t)m0, mh = (uint32_t)(m0 >> 32);
+                // is e & (B == m) with m = all ones where my bit is set; the
+                // lanes of v (two compares straight to lane masks) at the end
+                const uint64_t m0 = __builtin_amdgcn_sicmp(t, hi, 40 /* < */) &
+                                    __builtin_amdgcn_sicmp(t, l - 1, 39 /* >= */);
+                uint32_t ml = ~0u, mh = ~0u;
 #pragma unroll
                 for (int b = 0; b < 8; ++b) {
                     const uint32_t mb = (uint32_t)__builtin_amdgcn_sbfe(dig, b, 1);
@@ -598,7 +601,7 @@ __device__ void phase_short(const MatchParams &p, const uint8_t *x,
                     if (b + 1 >= p.nbits)
                         break;
                 }
-                eq &= ((uint64_t)mh << 32) | ml;
+                eq &= m0 & (((uint64_t)mh << 32) | ml);
                 const int slot = p.fl_off[l] + gk;
                 if (q && v && firstl[slot] < t) {
                     Lq = l;
@@ -687,7 +690,10 @@ __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
     const int k0 = has ? dgram_key(x, t0, d, p.K) : -1;
     key_out = k0;   // the lane's bucket (sorting stays inside buckets)
     const int kprev = __shfl_up(k0, 1);
-    const uint64_t B = ballot(has && (lane == 0 || kprev != k0));
+    // bucket starts: lane 0 and key changes, among the task's lanes (compares
+    // straight to lane masks)
+    const uint64_t B = __builtin_amdgcn_sicmp(lane, n, 40 /* < */) &
+                       (1ull | __builtin_amdgcn_sicmp(kprev, k0, 33 /* != */));
     const uint64_t upto = (self << 1) - 1;   // lanes 0..lane (lane 63: all)
     const uint64_t nxt = B & ~upto;          // bucket starts above this lane
     const int ss = 63 - __clzll((long long)(B & upto | 1ull));
