@@ -480,6 +480,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the oracle baseline and parity check")
     ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--v-pad", type=int, default=64, metavar="ELEMS",
+                    help="long workload: V rows stored at a pitch of D + ELEMS "
+                         "bf16 (0: dense rows)")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="BYTES",
                     help="after timing, run one plain device-to-device copy of "
                          "BYTES (the reference for scaling HBM byte counters)")
@@ -511,8 +514,14 @@ def main():
 
     if w["kind"] == "bf16":
         Hd = torch.from_numpy(w["H"].view(np.int16)).to(dev)
-        Vd = (torch.from_numpy(w["V"].view(np.int16)).to(dev)
-              if w["V"] is not None else None)
+        Vd = None
+        if w["V"] is not None:
+            # V's rows at a pitch of D + v_pad elements (the gather takes any
+            # pitch; one that is not a multiple of 2 KiB keeps its L2 sets apart)
+            Bv, Tv, Dv = w["V"].shape
+            Vbuf = torch.zeros((Bv, Tv, Dv + args.v_pad), dtype=torch.int16, device=dev)
+            Vbuf[:, :, :Dv] = torch.from_numpy(w["V"].view(np.int16)).to(dev)
+            Vd = Vbuf[:, :, :Dv]
         inp = rosa.bf16_input(Hd, w["M"])
         K = 1 << w["M"]
     else:
@@ -522,7 +531,8 @@ def main():
         K = w["K"]
     E = torch.empty((S, T), dtype=torch.int32, device=dev)
     SYM = torch.empty((S, T), dtype=torch.int16, device=dev)
-    out = torch.empty_like(Vd) if Vd is not None else None
+    out = (torch.empty(tuple(Vd.shape), dtype=torch.int16, device=dev)
+           if Vd is not None else None)
     ws = torch.empty(rosa.rosa_match_workspace_bytes(S, T, K), dtype=torch.uint8,
                      device=dev)
     outs = rosa.make_out(E, SYM)
@@ -607,7 +617,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "u8", "data": "synthetic",
         "config": {"workload": w["desc"], "streams": S, "T": T, "K": K,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU",
+                   **({"v_row_pitch": int(Vd.stride(1))} if Vd is not None else {})},
         "roofline": roof,
         "kernel_ms": k_avg,
         "cpu_baseline": cpu,

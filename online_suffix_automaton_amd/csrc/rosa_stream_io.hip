@@ -169,15 +169,12 @@ __global__ __launch_bounds__(256) void discretize_kernel(
 // ----------------------------------------------------------------- gather
 
 // XCDs of the chip (consecutive workgroups of a launch go to consecutive
-// XCDs, round robin); the gather's routes and positions per tile and its
-// workgroups per XCD.
+// XCDs, round robin); the gather's positions per tile and workgroups per XCD.
 constexpr int kXcds = 8;
-constexpr int kGatherRG = 32;
 constexpr int kGatherTP = 128;
 constexpr int64_t kGatherW = 128;
 
-// Tile: kGatherTP positions x kGatherRG routes of one batch row, 256
-// threads.  The reads of a route go to random earlier rows (tau = E+1,
+// Tile: kGatherTP positions x RG routes of one batch row, 256 threads.  The reads of a route go to random earlier rows (tau = E+1,
 // inherent to the method; half of them within about 4K rows, nine in ten
 // within 27K on i.i.d. streams), and with M = 4 each 128-byte line of a V
 // row holds the values of 16 routes, read by them at different positions.
@@ -187,15 +184,17 @@ constexpr int64_t kGatherW = 128;
 // W workgroups walk the positions in order, side by side.  The lines of the
 // recent rows of one group then mostly fit the XCD's 4 MiB L2.  E and the
 // output are streamed with non-temporal accesses so that they do not push
-// those lines out.  The group width, tile length and W were chosen by
-// timing on the long workload (wider groups or fewer workgroups in flight
-// lose L2 hits or memory parallelism).
-template <int MC>
+// those lines out.  With a row pitch that is a multiple of 2 KiB every row's
+// line of a group falls into the same few L2 sets, which holds far fewer
+// rows: there two lines per row and group (RG = 32) do best, otherwise one
+// (RG = 16).  Tile length and W were chosen by timing on the long workload
+// (fewer workgroups in flight lose memory parallelism).
+template <int MC, int RG>
 __global__ __launch_bounds__(256) void gather_kernel(
     const uint16_t *__restrict__ V, int64_t T, int64_t D, int64_t ldv, int M,
     const int32_t *__restrict__ E, uint16_t *__restrict__ out, int64_t ldo, int W)
 {
-    constexpr int RG = kGatherRG, TP = kGatherTP;
+    constexpr int TP = kGatherTP;
     constexpr int PSTEP = 256 / RG;          // positions per round of values
     constexpr int NV = TP / PSTEP;           // value loads per thread
     __shared__ int32_t et[RG][TP + 1];
@@ -309,19 +308,28 @@ hipError_t launch_gather(const uint16_t *V, int64_t B, int64_t T, int64_t D,
                          int64_t ldv, int M, const int32_t *E, uint16_t *out,
                          int64_t ldo, hipStream_t st)
 {
-    // W workgroups per XCD (four per CU), fewer when an XCD has fewer tiles
+    // W workgroups per XCD (four per CU), fewer when an XCD has fewer tiles;
+    // route groups of one 128-byte line per row unless the row pitch aliases
     const int64_t R = D / M;
-    const int64_t per_xcd = ((R + kGatherRG - 1) / kGatherRG + kXcds - 1) / kXcds *
+    const bool aliased = ((ldv * 2) % 2048) == 0;
+    const int rg = aliased ? 32 : 16;
+    const int64_t per_xcd = ((R + rg - 1) / rg + kXcds - 1) / kXcds *
                             ((T + kGatherTP - 1) / kGatherTP);
     const int W = (int)(per_xcd < kGatherW ? per_xcd : kGatherW);
     dim3 grid((unsigned)(kXcds * W), (unsigned)B);
     const bool vec4 = M == 4 && (ldv % 4) == 0 && (ldo % 4) == 0 &&
                       (((uintptr_t)V) & 7) == 0 && (((uintptr_t)out) & 7) == 0;
-    if (vec4)
-        hipLaunchKernelGGL(gather_kernel<4>, grid, dim3(256), 0, st, V, T, D,
+    if (vec4 && aliased)
+        hipLaunchKernelGGL((gather_kernel<4, 32>), grid, dim3(256), 0, st, V, T, D,
+                           ldv, M, E, out, ldo, W);
+    else if (vec4)
+        hipLaunchKernelGGL((gather_kernel<4, 16>), grid, dim3(256), 0, st, V, T, D,
+                           ldv, M, E, out, ldo, W);
+    else if (aliased)
+        hipLaunchKernelGGL((gather_kernel<0, 32>), grid, dim3(256), 0, st, V, T, D,
                            ldv, M, E, out, ldo, W);
     else
-        hipLaunchKernelGGL(gather_kernel<0>, grid, dim3(256), 0, st, V, T, D,
+        hipLaunchKernelGGL((gather_kernel<0, 16>), grid, dim3(256), 0, st, V, T, D,
                            ldv, M, E, out, ldo, W);
     return hipGetLastError();
 }

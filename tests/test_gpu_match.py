@@ -257,3 +257,23 @@ def test_launch_geometry_independence():
     assert np.array_equal(E_perm, E_all[perm])
     E_one = rosa.match(_dev(sym[3:4]), K=16)[0].cpu().numpy()
     assert np.array_equal(E_one[0], E_all[3])
+
+
+@pytest.mark.parametrize("B,T,D,M,pad", [(1, 3000, 1024, 4, 0), (1, 3000, 1024, 4, 64),
+                                         (1, 2000, 1024, 8, 0), (2, 900, 96, 3, 5)])
+def test_gather_row_pitch(B, T, D, M, pad):
+    """The value gather on V rows stored at a pitch of D + pad elements: a
+    pitch that is a multiple of 2 KiB (32-route groups) and ones that are not
+    (16-route groups), with and without the 8-byte vector path."""
+    rng = np.random.default_rng(11 + pad + M)
+    V = rng.integers(0, 65536, size=(B, T, D), dtype=np.uint16)
+    S = B * D // M
+    E = np.empty((S, T), dtype=np.int32)
+    for t in range(T):
+        E[:, t] = rng.integers(-1, t, size=S) if t > 0 else -1
+    Vbuf = torch.zeros((B, T, D + pad), dtype=torch.int16, device=DEV)
+    Vbuf[:, :, :D] = _dev(V.view(np.int16))
+    out = torch.empty((B, T, D), dtype=torch.int16, device=DEV)
+    _say(f"gather pitch B={B} T={T} D={D} M={M} pad={pad}")
+    rosa.rosa_gather(Vbuf[:, :, :D], M, _dev(E), out)
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), oracle.gather(V, E, M))
