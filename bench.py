@@ -410,8 +410,12 @@ def run_scatter(args):
     E, _, _, _ = rosa.match(Hd, M=M, want_len=False)
     del Hd
     theta = np.random.default_rng(45).standard_normal((B, T, D), dtype=np.float32)
-    th = torch.from_numpy(theta).to(dev)
-    G = torch.empty_like(th)
+    # theta's rows at a pitch of D + theta_pad floats (any pitch is taken; one
+    # that is not a multiple of 2 KiB keeps the rows' L2 sets apart)
+    thbuf = torch.zeros((B, T, D + args.theta_pad), dtype=torch.float32, device=dev)
+    thbuf[:, :, :D] = torch.from_numpy(theta).to(dev)
+    th = thbuf[:, :, :D]
+    G = torch.empty((B, T, D), dtype=torch.float32, device=dev)
     ws = torch.empty(rosa.rosa_scatter_grad_workspace_bytes(S, T),
                      dtype=torch.uint8, device=dev)
     for _ in range(args.warmup):
@@ -455,7 +459,8 @@ def run_scatter(args):
         "config": {"workload": "scatter: destinations of the long workload "
                                "(512 streams x 65536, K=16), theta "
                                "[1,65536,2048] f32 N(0,1)",
-                   "streams": S, "T": T, "K": 16, "parallelism": "single GPU"},
+                   "streams": S, "T": T, "K": 16, "parallelism": "single GPU",
+                   "theta_row_pitch": int(th.stride(1))},
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9,
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK, "traffic": None},
@@ -480,6 +485,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the oracle baseline and parity check")
     ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--theta-pad", type=int, default=32, metavar="ELEMS",
+                    help="scatter workload: theta rows stored at a pitch of D + "
+                         "ELEMS floats (0: dense rows)")
     ap.add_argument("--v-pad", type=int, default=64, metavar="ELEMS",
                     help="long workload: V rows stored at a pitch of D + ELEMS "
                          "bf16 (0: dense rows)")

@@ -123,16 +123,17 @@ __global__ void scatter_fill_kernel(ScatterParams p)
     }
 }
 
-// 256 threads: 4 destination rows x 64 routes; grid (rows/4, routes/64, B).
+// XCDs of the chip: consecutive workgroups of a launch go to consecutive
+// XCDs, round robin.
+constexpr int kScXcds = 8;
+constexpr int kSumTP = 64;          // destination rows per tile
+constexpr int64_t kSumW = 128;      // workgroups per XCD
+
+// One destination row tau of route r: its time steps in increasing order.
 template <int MC>
-__global__ __launch_bounds__(256) void scatter_sum_kernel(ScatterParams p)
+__device__ __forceinline__ void scatter_sum_one(const ScatterParams &p, int64_t b, int64_t r,
+                                                int64_t tau)
 {
-    const int tid = threadIdx.x;
-    const int64_t r = (int64_t)blockIdx.y * 64 + (tid & 63);
-    const int64_t tau = (int64_t)blockIdx.x * 4 + (tid >> 6);
-    const int64_t b = blockIdx.z;
-    if (r >= p.R || tau >= p.T)
-        return;
     const int64_t s = b * p.R + r;
     const int o0 = p.off[s * p.Tq + tau], o1 = p.off[s * p.Tq + tau + 1];
     const int n = o1 - o0;
@@ -167,6 +168,40 @@ __global__ __launch_bounds__(256) void scatter_sum_kernel(ScatterParams p)
 #pragma unroll
     for (int m = 0; m < MC; ++m)
         g[m] = (float)acc[m];
+}
+
+// Tile: kSumTP destination rows x RG routes of one batch row, 256 threads
+// (RG consecutive threads = the routes of one row, so the rows of G are
+// written RG routes at a time).  The theta rows a destination reads lie a
+// few thousand rows after it, at random, each read MC floats wide; as in the
+// value gather, the route groups are dealt to the XCDs in passes and each
+// XCD walks its group's destinations in order with W workgroups, so the
+// theta lines of a group stay in that XCD's L2 between the reads of the
+// group's routes.  RG = 8 (one 128-byte line of theta per row at MC = 4)
+// unless the row pitch is a multiple of 2 KiB, where rows alias into few L2
+// sets and RG = 16 does better (chosen by timing on the long workload).
+template <int MC, int RG>
+__global__ __launch_bounds__(256) void scatter_sum_kernel(ScatterParams p, int W)
+{
+    constexpr int PSTEP = 256 / RG;
+    const int64_t ng = (p.R + RG - 1) / RG, ntt = (p.T + kSumTP - 1) / kSumTP;
+    const int x = (int)(blockIdx.x % kScXcds), jw = (int)(blockIdx.x / kScXcds);
+    const int64_t b = blockIdx.y;
+    const int tid = threadIdx.x;
+    for (int64_t k = jw;; k += W) {
+        const int64_t pass = k / ntt, tt = k - pass * ntt;
+        const int64_t g = pass * kScXcds + x;
+        if (g >= ng)
+            break;
+        const int64_t r = g * RG + tid % RG;
+        if (r >= p.R)
+            continue;
+        for (int i = 0; i < kSumTP / PSTEP; ++i) {
+            const int64_t tau = tt * kSumTP + tid / RG + (int64_t)PSTEP * i;
+            if (tau < p.T)
+                scatter_sum_one<MC>(p, b, r, tau);
+        }
+    }
 }
 
 // Streams of up to 65536 positions: count, prefix and fill of one stream in
@@ -299,14 +334,21 @@ hipError_t launch_scatter(const ScatterParams &p, hipStream_t st)
                            st, p);
         hipLaunchKernelGGL(scatter_fill_kernel, gt, dim3(256), 0, st, p);
     }
-    const dim3 gs((unsigned)((p.T + 3) / 4), (unsigned)((p.R + 63) / 64),
-                  (unsigned)p.B);
+    const bool aliased = ((p.ldt * 4) % 2048) == 0;
+    const int rg = aliased ? 16 : 8;
+    const int64_t per_xcd = ((p.R + rg - 1) / rg + kScXcds - 1) / kScXcds *
+                            ((p.T + kSumTP - 1) / kSumTP);
+    const int W = (int)(per_xcd < kSumW ? per_xcd : kSumW);
+    const dim3 gs((unsigned)(kScXcds * W), (unsigned)p.B);
     const unsigned gb = 1024;
     switch (p.M) {
-#define ROSA_SCATTER_M(MM)                                                        \
-    case MM:                                                                      \
-        hipLaunchKernelGGL(scatter_sum_kernel<MM>, gs, dim3(256), 0, st, p);      \
-        hipLaunchKernelGGL(scatter_big_kernel<MM>, dim3(gb), dim3(64), 0, st, p); \
+#define ROSA_SCATTER_M(MM)                                                             \
+    case MM:                                                                           \
+        if (aliased)                                                                   \
+            hipLaunchKernelGGL((scatter_sum_kernel<MM, 16>), gs, dim3(256), 0, st, p, W); \
+        else                                                                           \
+            hipLaunchKernelGGL((scatter_sum_kernel<MM, 8>), gs, dim3(256), 0, st, p, W);  \
+        hipLaunchKernelGGL(scatter_big_kernel<MM>, dim3(gb), dim3(64), 0, st, p);      \
         break;
         ROSA_SCATTER_M(1)
         ROSA_SCATTER_M(2)

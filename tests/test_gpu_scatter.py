@@ -128,3 +128,22 @@ def test_scatter_long_workload():
     _say("oracle")
     want = oracle.scatter_grad(theta, E.cpu().numpy(), 4)
     _compare(G.cpu().numpy(), want, "long")
+
+
+@pytest.mark.parametrize("pad", [0, 32, 3])
+def test_scatter_theta_row_pitch(pad):
+    """The scatter with theta rows at a pitch of D + pad floats (a pitch that
+    is a multiple of 2 KiB and ones that are not) equals the oracle."""
+    rng = np.random.default_rng(20 + pad)
+    B, T, D, M = 1, 3000, 512, 4
+    S = B * D // M
+    theta = rng.standard_normal((B, T, D)).astype(np.float32)
+    E = np.empty((S, T), dtype=np.int32)
+    for t in range(T):
+        E[:, t] = rng.integers(-1, t, size=S) if t > 0 else -1
+    tb = torch.zeros((B, T, D + pad), dtype=torch.float32, device=DEV)
+    tb[:, :, :D] = torch.from_numpy(theta).to(DEV)
+    G = torch.empty((B, T, D), dtype=torch.float32, device=DEV)
+    rosa.rosa_scatter_grad(tb[:, :, :D], M, torch.from_numpy(E).to(DEV), G)
+    torch.cuda.synchronize()
+    assert np.array_equal(G.cpu().numpy(), oracle.scatter_grad(theta, E, M))
