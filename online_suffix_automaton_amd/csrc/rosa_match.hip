@@ -122,7 +122,7 @@ __device__ __forceinline__ void emit_record(const StreamOut &o, int slot,
 }
 
 struct Found {
-    int e, l;
+    int e, l;       // deep: e = 1 when the record overflowed (more than seven members)
     bool ok;
     bool deep;      // CAP mode: answer deferred, its record written (solve_wave)
 };
@@ -282,6 +282,7 @@ __device__ Found solve_wave(const uint8_t *x, int nbits, int t, uint64_t g,
             ++ntr;
         }
         dr[7] = (uint16_t)((ntr > 7 ? 0 : ntr) | (min(ell + 16, 8191) << 3));
+        r.e = ntr > 7 ? 1 : 0;   // more members than the record holds
         r.ok = true;
         r.deep = true;
         return r;
@@ -904,53 +905,67 @@ __global__ __launch_bounds__(Cfg::kThreads) void stream_kernel_lds(MatchParams p
         // this range's tasks: [tlo, thi).  Wave w starts with task tlo + w,
         // then takes the next one from a counter (tasks inside long
         // recurrences cost many times the others); the next task's
-        // descriptor is loaded while this one is solved
+        // descriptor is loaded while this one is solved.  A task's records
+        // are stored at the start of the wave's next task, after the wait
+        // for that task's descriptor: vector loads and stores complete
+        // under one counter, so a wait for the descriptor right after the
+        // stores would wait for the stores too.
         const int tlo = tfirst, thi = tfirst + misc[kMiscPass + rg];
         tfirst = thi;
         int ti = tlo + wid;
         uint32_t tk_next = ti < thi ? __builtin_nontemporal_load(&tasks[ti]) : 0u;
+        Found pf = {-1, 0, false, false};   // the previous task's answers
+        int pt = 0, pk = 0, pstart = 0, pn = 0;
+        auto store_prev = [&]() {
+            if (ballot(pf.deep)) {
+                // answers deferred to the time-ordered pass (unpermute_kernel),
+                // their records written by solve_wave; with more candidates
+                // than a record holds, the task's positions go to the
+                // workspace and the record points there
+                const bool ovf = pf.deep && pf.e != 0;
+                if (ballot(ovf) && lane < pn)
+                    posrow[pstart + lane] = pt;
+                if (ovf) {
+                    dinfo[pt].x = (uint32_t)pstart;
+                    dinfo[pt].y = (uint32_t)pn;
+                }
+                if (lane < pn && pf.deep) {
+                    o.rec[pstart + lane] = (uint32_t)pt << 16;
+                    atomicOr(&deepbits[pt >> 5], 1u << (pt & 31));
+                } else if (lane < pn && pf.ok) {
+                    emit_record(o, pstart + lane, pt, pf.e, pf.l);
+                } else if (lane < pn) {
+                    o.rec[pstart + lane] = ((uint32_t)pt << 16) | (uint32_t)qres[pk];
+                }
+            } else if (lane < pn) {
+                if (pf.ok)
+                    emit_record(o, pstart + lane, pt, pf.e, pf.l);
+                else   // a bucket's first member: its answer from phase D
+                    o.rec[pstart + lane] = ((uint32_t)pt << 16) | (uint32_t)qres[pk];
+            }
+        };
         while (ti < thi) {
-            const uint32_t tk = tk_next;
+            const uint32_t tk = __builtin_amdgcn_readfirstlane(tk_next);
+            const int start = (int)(tk >> 6);
+            const int n = (int)(tk & 63u) + 1;
             int tn = 0;
             if (lane == 0)
                 tn = atomicAdd(&misc[kMiscNext], 1);
             tn = __builtin_amdgcn_readfirstlane(tn);
             if (tn < thi)
                 tk_next = __builtin_nontemporal_load(&tasks[tn]);
-            const int start = (int)(tk >> 6);
-            const int n = (int)(tk & 63u) + 1;
+            store_prev();
             int t, k;
-            const Found f = run_task<DC, true, true>(
+            pf = run_task<DC, true, true>(
                 p, x, [&](int i) { return (int)lpos[start - base + i]; }, n, t, k,
                 dinfo);
-            if (ballot(f.deep)) {
-                // answers deferred to the time-ordered pass (unpermute_kernel),
-                // their records written by solve_wave; with more candidates
-                // than a record holds, the task's positions go to the
-                // workspace and the record points there
-                const bool ovf = f.deep && (reinterpret_cast<const uint16_t *>(dinfo + t)[7] & 7u) == 0;
-                if (ballot(ovf) && lane < n)
-                    posrow[start + lane] = t;
-                if (ovf) {
-                    dinfo[t].x = (uint32_t)start;
-                    dinfo[t].y = (uint32_t)n;
-                }
-                if (lane < n && f.deep) {
-                    o.rec[start + lane] = (uint32_t)t << 16;
-                    atomicOr(&deepbits[t >> 5], 1u << (t & 31));
-                } else if (lane < n && f.ok) {
-                    emit_record(o, start + lane, t, f.e, f.l);
-                } else if (lane < n) {
-                    o.rec[start + lane] = ((uint32_t)t << 16) | (uint32_t)qres[k];
-                }
-            } else if (lane < n) {
-                if (f.ok)
-                    emit_record(o, start + lane, t, f.e, f.l);
-                else   // a bucket's first member: its answer from phase D
-                    o.rec[start + lane] = ((uint32_t)t << 16) | (uint32_t)qres[k];
-            }
+            pt = t;
+            pk = k;
+            pstart = start;
+            pn = n;
             ti = tn;
         }
+        store_prev();
         __syncthreads();
     }
 }
