@@ -571,13 +571,83 @@ __device__ void phase_short(const MatchParams &p, const uint8_t *x,
     if (tid == 0)
         misc[25] = 0;
     __syncthreads();
-    if (wid < nseg) {
+    // lanes with the same digit as mine among those of m0: per bit, with
+    // mb = all ones where my bit is set, each 32-bit half is e & (B == mb),
+    // one 3-input bit op (table 0x90); m0 (two compares straight to lane
+    // masks) is applied at the end
+    auto same_digit = [&](int dig, uint64_t m0) {
+        uint32_t ml = ~0u, mh = ~0u;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const uint32_t mb = (uint32_t)__builtin_amdgcn_sbfe(dig, b, 1);
+            const uint64_t B = ballot(mb != 0);
+            ml = __builtin_amdgcn_bitop3_b32(ml, (uint32_t)B, mb, 0x90);
+            mh = __builtin_amdgcn_bitop3_b32(mh, (uint32_t)(B >> 32), mb, 0x90);
+            if (b + 1 >= p.nbits)
+                break;
+        }
+        return m0 & (((uint64_t)mh << 32) | ml);
+    };
+    if constexpr (DC >= 1 && DC <= 4) {
+        // d <= 4: a chunk's symbols x[t-3..t] are one word per lane, so every
+        // table read of the chunk is issued at once, right after that word
+        // (the next chunk's word is fetched with them).  The last-end reads
+        // see the tables left by the earlier chunks, as in time order: this
+        // chunk's writes come after them.
+        if (wid < nseg) {
+            int32_t *tab = segtab + wid * FL;
+            const int lo = wid * Ts, hi = min(T, lo + Ts);
+            uint32_t wn = lo < hi ? load4_end(x, lo + lane) : 0u;
+            for (int c0 = lo; c0 < hi; c0 += 64) {
+                const int t = c0 + lane;
+                const bool inr = t < hi;
+                const uint32_t w = wn;
+                const int fd = firstd[key_of_word(w, DC, K)];
+                int slot[DC], fl[DC], tb[DC];
+                int gk = 0;
+#pragma unroll
+                for (int l = 1; l < DC; ++l) {
+                    const bool v = inr && t >= l - 1;
+                    gk = (int)__umul24((uint32_t)gk, (uint32_t)K) + (v ? sym_of(w, l - 1) : 0);
+                    slot[l] = p.fl_off[l] + gk;
+                    fl[l] = firstl[slot[l]];
+                    tb[l] = tab[slot[l]];
+                }
+                if (c0 + 64 < hi)
+                    wn = load4_end(x, t + 64);
+                const bool q = inr && (t < DC - 1 || fd == t);
+                int Lq = 0, Eq = -1;
+                bool miss = false;
+                uint64_t eq = ~0ull;
+#pragma unroll
+                for (int l = 1; l < DC; ++l) {
+                    const bool v = inr && t >= l - 1;
+                    const int dig = v ? sym_of(w, l - 1) : 0;
+                    eq &= same_digit(dig, __builtin_amdgcn_sicmp(t, hi, 40 /* < */) &
+                                              __builtin_amdgcn_sicmp(t, l - 1, 39 /* >= */));
+                    if (q && v && fl[l] < t) {
+                        Lq = l;
+                        const uint64_t pm = eq & below;
+                        Eq = pm ? c0 + 63 - __clzll((long long)pm) : tb[l];
+                        miss = !pm && tb[l] < 0;
+                    }
+                    if (v && !(eq & above))
+                        tab[slot[l]] = t;
+                }
+                if (q) {
+                    if (miss)
+                        pend[atomicAdd(&misc[25], 1)] = (PendT)t;
+                    else
+                        put(t, Lq > 0 ? Eq : -1, Lq);
+                }
+            }
+        }
+    } else if (wid < nseg) {
         int32_t *tab = segtab + wid * FL;
         const int lo = wid * Ts, hi = min(T, lo + Ts);
         for (int c0 = lo; c0 < hi; c0 += 64) {
             const int t = c0 + lane;
             const bool inr = t < hi;
-            const uint32_t w = d <= 4 ? load4_end(x, t) : 0u;
             const bool q = inr && (t < d - 1 || firstd[dgram_key(x, t, d, K)] == t);
             int Lq = 0, Eq = -1;
             bool miss = false;
@@ -585,24 +655,10 @@ __device__ void phase_short(const MatchParams &p, const uint8_t *x,
             uint64_t eq = ~0ull;
             for (int l = 1; l < d; ++l) {
                 const bool v = inr && t >= l - 1;
-                const int dig = v ? (d <= 4 ? sym_of(w, l - 1) : (int)x[t - l + 1]) : 0;
+                const int dig = v ? (int)x[t - l + 1] : 0;
                 gk = (int)__umul24((uint32_t)gk, (uint32_t)K) + dig;
-                // lanes with the same l-th symbol: per bit, each 32-bit half
-                // is e & (B == m) with m = all ones where my bit is set; the
-                // lanes of v (two compares straight to lane masks) at the end
-                const uint64_t m0 = __builtin_amdgcn_sicmp(t, hi, 40 /* < */) &
-                                    __builtin_amdgcn_sicmp(t, l - 1, 39 /* >= */);
-                uint32_t ml = ~0u, mh = ~0u;
-#pragma unroll
-                for (int b = 0; b < 8; ++b) {
-                    const uint32_t mb = (uint32_t)__builtin_amdgcn_sbfe(dig, b, 1);
-                    const uint64_t B = ballot(mb != 0);
-                    ml = __builtin_amdgcn_bitop3_b32(ml, (uint32_t)B, mb, 0x90);
-                    mh = __builtin_amdgcn_bitop3_b32(mh, (uint32_t)(B >> 32), mb, 0x90);
-                    if (b + 1 >= p.nbits)
-                        break;
-                }
-                eq &= m0 & (((uint64_t)mh << 32) | ml);
+                eq &= same_digit(dig, __builtin_amdgcn_sicmp(t, hi, 40 /* < */) &
+                                          __builtin_amdgcn_sicmp(t, l - 1, 39 /* >= */));
                 const int slot = p.fl_off[l] + gk;
                 if (q && v && firstl[slot] < t) {
                     Lq = l;
