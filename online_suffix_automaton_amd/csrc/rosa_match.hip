@@ -45,6 +45,7 @@ constexpr uint32_t kFirstFlag = 0x80000000u;
 constexpr int kWordThresh = 3;       // level steps only for groups larger than this
 constexpr int kMiscPass = 26;        // misc[26..31]: tasks per slot range
 constexpr int kMiscNext = 20;        // misc[20]: next task of the pass (phase E)
+constexpr int kMiscLastQ = 21;       // misc[21]: last position with L < d (phase D)
 constexpr int kWordThreshDeep = 32;  // ... and past the first levels, larger than this
 
 // ----------------------------------------------------------- wave helpers
@@ -550,8 +551,8 @@ __device__ void phase_tasks(const MatchParams &p, int s, const int32_t *cnt,
 // last end of every l-gram seen so far in segment w (segtab[w]); inside a
 // chunk, the latest earlier lane with the same l-gram comes from a ballot
 // match.  Queries with no earlier end inside their segment are resolved
-// after the scan from the tables of earlier segments.  `put(t, e, l)`
-// receives every answer.
+// after the scan from the tables of earlier segments.  `put(t, e, l, k)`
+// receives every answer, with k the d-gram key of t when t >= d-1.
 template <int DC, class Put, class PendT>
 __device__ void phase_short(const MatchParams &p, const uint8_t *x,
                             const int32_t *firstd, const int32_t *firstl,
@@ -570,7 +571,24 @@ __device__ void phase_short(const MatchParams &p, const uint8_t *x,
         segtab[i] = -1;
     if (tid == 0)
         misc[25] = 0;
+    // The last query: the latest first occurrence of a d-gram (or d-2).  The
+    // tables are read only by queries, for their own or earlier segments, so
+    // the scan stops after it (misc[kMiscLastQ] starts at zero).
+    {
+        int m = 0;
+        for (int i = tid; i < p.NB; i += nt) {
+            const int f = firstd[i];
+            if (f < T)
+                m = max(m, f);
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1)
+            m = max(m, __shfl_xor(m, o));
+        if (lane == 0)
+            atomicMax(&misc[kMiscLastQ], m);
+    }
     __syncthreads();
+    const int tend = min(T, max(misc[kMiscLastQ], d - 2) + 1);
     // lanes with the same digit as mine among those of m0: per bit, with
     // mb = all ones where my bit is set, each 32-bit half is e & (B == mb),
     // one 3-input bit op (table 0x90); m0 (two compares straight to lane
@@ -596,13 +614,14 @@ __device__ void phase_short(const MatchParams &p, const uint8_t *x,
         // chunk's writes come after them.
         if (wid < nseg) {
             int32_t *tab = segtab + wid * FL;
-            const int lo = wid * Ts, hi = min(T, lo + Ts);
+            const int lo = wid * Ts, hi = min(tend, lo + Ts);
             uint32_t wn = lo < hi ? load4_end(x, lo + lane) : 0u;
             for (int c0 = lo; c0 < hi; c0 += 64) {
                 const int t = c0 + lane;
                 const bool inr = t < hi;
                 const uint32_t w = wn;
-                const int fd = firstd[key_of_word(w, DC, K)];
+                const int kq = key_of_word(w, DC, K);
+                const int fd = firstd[kq];
                 int slot[DC], fl[DC], tb[DC];
                 int gk = 0;
 #pragma unroll
@@ -638,17 +657,18 @@ __device__ void phase_short(const MatchParams &p, const uint8_t *x,
                     if (miss)
                         pend[atomicAdd(&misc[25], 1)] = (PendT)t;
                     else
-                        put(t, Lq > 0 ? Eq : -1, Lq);
+                        put(t, Lq > 0 ? Eq : -1, Lq, kq);
                 }
             }
         }
     } else if (wid < nseg) {
         int32_t *tab = segtab + wid * FL;
-        const int lo = wid * Ts, hi = min(T, lo + Ts);
+        const int lo = wid * Ts, hi = min(tend, lo + Ts);
         for (int c0 = lo; c0 < hi; c0 += 64) {
             const int t = c0 + lane;
             const bool inr = t < hi;
-            const bool q = inr && (t < d - 1 || firstd[dgram_key(x, t, d, K)] == t);
+            const int kq = inr && t >= d - 1 ? dgram_key(x, t, d, K) : 0;
+            const bool q = inr && (t < d - 1 || firstd[kq] == t);
             int Lq = 0, Eq = -1;
             bool miss = false;
             int gk = 0;
@@ -678,7 +698,7 @@ __device__ void phase_short(const MatchParams &p, const uint8_t *x,
                 if (miss)
                     pend[atomicAdd(&misc[25], 1)] = (PendT)t;
                 else
-                    put(t, Lq > 0 ? Eq : -1, Lq);
+                    put(t, Lq > 0 ? Eq : -1, Lq, kq);
             }
         }
     }
@@ -697,7 +717,7 @@ __device__ void phase_short(const MatchParams &p, const uint8_t *x,
         int e = -1;
         for (int w = t / Ts - 1; w >= 0 && e < 0; --w)
             e = segtab[w * FL + p.fl_off[Lq] + gq];
-        put(t, e, Lq);
+        put(t, e, Lq, t >= d - 1 ? dgram_key(x, t, d, K) : 0);
     }
     __syncthreads();
 }
@@ -899,12 +919,11 @@ __global__ __launch_bounds__(Cfg::kThreads) void stream_kernel_lds(MatchParams p
     // or large bucket takes the bucket's first slot; for buckets of 2..64
     // members the answer waits in qres until the bucket's task writes it.
     phase_short<DC>(p, x, firstd, firstl, segtab, Cfg::kSegTab, pend, misc,
-                [&](int t, int e, int l) {
+                [&](int t, int e, int l, int k) {
                     if (t < d - 1) {
                         emit_record(o, T - d + 1 + t, t, e, l);
                         return;
                     }
-                    const int k = dgram_key(x, t, d, K);
                     const int c = (int)off[k + 1] - (int)off[k];
                     if (c == 1 || c > 64) {
                         emit_record(o, off[k], t, e, l);
@@ -1078,7 +1097,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_hbm(MatchParams 
     });
     __syncthreads();
     phase_short<0>(p, x, firstd, firstl, segtab, kSegTabInts, pend, misc,
-                [&](int t, int e, int l) { emit(o, t, e, l); });
+                [&](int t, int e, int l, int) { emit(o, t, e, l); });
     const int ntasks = misc[24];
     for (int ti = wid; ti < ntasks; ti += nw) {
         const uint32_t tk = tasks[ti];
