@@ -566,7 +566,6 @@ __device__ void phase_short(const MatchParams &p, const uint8_t *x,
     const uint64_t above = ~(below | self);
     const int T = p.T, K = p.K, d = DC > 0 ? DC : p.d, FL = p.fl_total;
     const int nseg = FL > 0 ? max(1, min(nw, segcap / FL)) : nw;
-    const int Ts = (((T + nseg - 1) / nseg) + 63) & ~63;
     for (int i = tid; i < nseg * FL; i += nt)
         segtab[i] = -1;
     if (tid == 0)
@@ -589,6 +588,8 @@ __device__ void phase_short(const MatchParams &p, const uint8_t *x,
     }
     __syncthreads();
     const int tend = min(T, max(misc[kMiscLastQ], d - 2) + 1);
+    // segments of whole chunks over [0, tend)
+    const int Ts = (((tend + nseg - 1) / nseg) + 63) & ~63;
     // lanes with the same digit as mine among those of m0: per bit, with
     // mb = all ones where my bit is set, each 32-bit half is e & (B == mb),
     // one 3-input bit op (table 0x90); m0 (two compares straight to lane
