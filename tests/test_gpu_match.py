@@ -63,6 +63,32 @@ def test_random_streams_all_alphabets(K):
         _run_symbols(sym, K, f"random K={K} T={T}")
 
 
+@pytest.mark.parametrize("T", [8192, 65536])
+def test_last_new_dgram_late(T):
+    """The positions with L < d end at the latest first occurrence of a
+    d-gram; the short-match scan stops there and spreads its segments over
+    that range.  Streams whose last new d-gram sits at chosen places: the
+    very end, chunk and segment boundaries, mid-stream, early (a periodic
+    stream), after a random prefix."""
+    rng = np.random.default_rng(7 + T)
+    K = 16
+    base = np.resize(np.array([0, 1, 2, 3, 4, 5, 6], dtype=np.uint8), T)
+    rows = []
+    for q in (T - 1, T - 2, T - 3, T // 2, T // 16 * 3 - 1, T // 16 * 3,
+              4095, 4096, 63, 64):
+        r = base.copy()
+        r[q] = 15   # new d-grams end at q .. q+d-1 (inside the stream)
+        rows.append(r)
+    rows.append(base.copy())
+    for pre in (100, T // 3, T - 70):
+        r = base.copy()
+        r[:pre] = rng.integers(0, K, pre)
+        rows.append(r)
+    sym = np.stack(rows)
+    _say(f"late new d-grams: S={sym.shape[0]} T={T}")
+    _run_symbols(sym, K, f"late new d-grams T={T}")
+
+
 def test_structured_streams():
     T = 3000
     rows = [synth.constant(T), synth.periodic(T, [0, 1]),
