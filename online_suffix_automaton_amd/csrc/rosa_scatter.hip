@@ -220,18 +220,46 @@ __global__ __launch_bounds__(1024) void scatter_group_lds_kernel(ScatterParams p
     const int T = (int)p.T;
     const int32_t *E = p.end + s * p.T;
     const int nwords = (T + 1) / 2;
+    // visits (t, E[t]) for every t of the stream; with 16-byte aligned rows
+    // of a multiple of 4 positions, 4 per load and all of a thread's loads
+    // (16 at T = 65536) in flight before the first is used, so the pass
+    // waits for memory once rather than once per position
+    constexpr int kEIt = kScatterLdsT / (4 * 1024);
+    const bool vec = (T & 3) == 0 && (((uintptr_t)E) & 15) == 0;
+    auto each = [&](auto fn) {
+        if (vec) {
+            const int4 *E4 = reinterpret_cast<const int4 *>(E);
+            const int n4 = T >> 2;
+            int4 ev[kEIt];
+#pragma unroll
+            for (int j = 0; j < kEIt; ++j) {
+                const int i = tid + j * 1024;
+                ev[j] = i < n4 ? E4[i] : make_int4(-1, -1, -1, -1);
+            }
+#pragma unroll
+            for (int j = 0; j < kEIt; ++j) {
+                const int t0 = 4 * (tid + j * 1024);
+                fn(t0, ev[j].x);
+                fn(t0 + 1, ev[j].y);
+                fn(t0 + 2, ev[j].z);
+                fn(t0 + 3, ev[j].w);
+            }
+        } else {
+            for (int t = tid; t < T; t += 1024)
+                fn(t, E[t]);
+        }
+    };
     for (int i = tid; i < nwords; i += 1024)
         c2[i] = 0u;
     if (tid == 0)
         carry_s = 0;
     __syncthreads();
-    for (int t = tid; t < T; t += 1024) {
-        const int e = E[t];
+    each([&](int, int e) {
         if (e >= 0 && e + 1 < T) {
             const int tau = e + 1;
             atomicAdd(&c2[tau >> 1], 1u << (16 * (tau & 1)));
         }
-    }
+    });
     __syncthreads();
     // exclusive prefix, 4096 destinations per round (4 per thread); the
     // prefix goes to off[] for the sum kernel and back into c2 as cursors
@@ -278,15 +306,14 @@ __global__ __launch_bounds__(1024) void scatter_group_lds_kernel(ScatterParams p
         off[T] = carry_s;
     __syncthreads();
     int32_t *list = p.list + s * p.T;
-    for (int t = tid; t < T; t += 1024) {
-        const int e = E[t];
+    each([&](int t, int e) {
         if (e >= 0 && e + 1 < T) {
             const int tau = e + 1;
             const uint32_t sh = 16u * (uint32_t)(tau & 1);
             const uint32_t old = atomicAdd(&c2[tau >> 1], 1u << sh);
             list[(old >> sh) & 0xFFFFu] = t;
         }
-    }
+    });
 }
 
 // One wave per destination with many time steps: the stream's time steps
