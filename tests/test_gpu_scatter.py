@@ -76,9 +76,12 @@ def test_scatter_many_per_destination():
     _compare(_run(theta, E, M), oracle.scatter_grad(theta, E, M), "many")
 
 
-def test_scatter_out_of_range_and_padding():
-    rng = np.random.default_rng(4)
-    B, T, D, M = 2, 301, 32, 4
+@pytest.mark.parametrize("T", [301, 300])
+def test_scatter_out_of_range_and_padding(T):
+    """Destinations outside [0, T-1) are ignored; T = 300 takes the grouping
+    kernel's 16-byte destination loads, T = 301 the one-by-one path."""
+    rng = np.random.default_rng(4 + T)
+    B, D, M = 2, 32, 4
     S = B * D // M
     E = rng.integers(-5, T + 5, (S, T)).astype(np.int32)
     theta = rng.standard_normal((B, T, D)).astype(np.float32)
