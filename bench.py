@@ -5,14 +5,18 @@ One step = the whole path over one batch: bf16 hidden states -> sign bits ->
 65,536 positions of every stream (E and next symbol) -> gather of the matched
 value slices from V.  Inputs are resident in HBM before timing starts.
 
-Prints one JSON line: throughput in matched positions/s, the roofline of the
-dominant kernel (the retrieval kernel, timed with HIP events on its own
-stream), and the CPU oracle timed on the host as a reported baseline.  Every
-output of the timed run is compared with the oracle before the line is
-printed.
+Prints one JSON line: throughput in matched positions/s; the roofline of the
+dominant kernel (the retrieval kernel, timed with HIP events recorded on the
+stream it is launched on: its VALU issue rate against the vector issue peak
+when a counter summary of the current source is committed, with its bytes
+against HBM peak beside it) and of the whole step (30 B per stream-position
+against HBM peak); the same steps with V's rows at the dense pitch; and the
+CPU oracle timed on the host on 16 threads and on one thread, as a reported
+baseline.  Every output of the timed run is compared with the oracle before
+the line is printed.
 
-    python bench.py [--steps K] [--warmup W]
-                    [--workload long|batched|repeat|decode] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-dense]
+                    [--workload long|batched|repeat|decode|qk|scatter]
 
 The decode workload builds one automaton per stream over the long
 workload's 65,536-position prefix, then appends 1024 positions with one
@@ -42,7 +46,15 @@ HBM_PEAK = 8.0e12     # MI355X HBM3E, bytes/s
 # up to 65536 positions): the symbol read (1 B) and one 4-byte result record
 # (position, E+1) written; a separate kernel puts the records in time order.
 KERNEL_BYTES_PER_POS = 1 + 4
+# Compulsory bytes per stream-position of the whole step on the long
+# workload: 4 bf16 channels in (8 B), E and SYM out (4 + 2 B), the gathered
+# 4 bf16 values read (8 B) and written (8 B).
+STEP_BYTES_PER_POS = 8 + 6 + 16
+# Vector issue peak: 256 CUs x 4 SIMDs x 2.4 GHz, one wave64 VALU instruction
+# per SIMD every 4 cycles (16 lanes per cycle), in wave instructions/s.
+VALU_PEAK = 256 * 4 * 2.4e9 / 4
 PMC_FILE = os.path.join(ROOT, "profiles", "stream_kernel_long_pmc.txt")
+ISSUE_FILE = os.path.join(ROOT, "profiles", "stream_kernel_long_issue.txt")
 
 
 def _log(msg):
@@ -70,6 +82,71 @@ def measured_traffic():
     if not m or not b or m.group(1) != kernel_source_hash():
         return None
     return float(b.group(1))
+
+
+def measured_valu():
+    """VALU wave instructions per launch of the retrieval kernel from the
+    committed instruction-issue counter summary, if it was taken on the
+    current source."""
+    try:
+        txt = open(ISSUE_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"^source_sha\s*=\s*(\w+)", txt, re.M)
+    v = re.search(r"^stream_kernel_valu_per_launch\s*=\s*([0-9.eE+]+)", txt, re.M)
+    if not m or not v or m.group(1) != kernel_source_hash():
+        return None
+    return float(v.group(1))
+
+
+def kernel_roofline(npos, k_ms, workload):
+    """Roofline of the retrieval kernel.  It is bound by vector instruction
+    issue: `achieved` is its VALU wave instructions per launch (counters of
+    the committed summary, same source) over the live event-timed duration,
+    against VALU_PEAK.  Its bytes (5 B per stream-position, symbol in and
+    result record out) against HBM peak are reported beside it; without a
+    current counter summary the bytes are the reported bound."""
+    kbytes = KERNEL_BYTES_PER_POS * npos
+    hbm = kbytes / (k_ms / 1e3)
+    traffic = measured_traffic() if workload == "long" else None
+    valu = measured_valu() if workload == "long" else None
+    if valu is None:
+        return {"bound": "hbm", "achieved": hbm / 1e9, "peak": HBM_PEAK / 1e9,
+                "unit": "GB/s", "frac": hbm / HBM_PEAK, "traffic": traffic}
+    rate = valu / (k_ms / 1e3)
+    return {"bound": "alu", "achieved": rate / 1e9, "peak": VALU_PEAK / 1e9,
+            "unit": "G VALU wave instructions/s", "frac": rate / VALU_PEAK,
+            "traffic": traffic, "valu_per_position": valu / npos,
+            "hbm_achieved": hbm / 1e9, "hbm_peak": HBM_PEAK / 1e9,
+            "hbm_frac": hbm / HBM_PEAK}
+
+
+def host_cpu_info(threads):
+    """The host the oracle ran on: CPU model, SMT state, logical CPUs and the
+    CPUs this process may use."""
+    info = {"threads_used": threads, "nproc": os.cpu_count()}
+    try:
+        info["affinity"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        pass
+    try:
+        import subprocess
+        txt = subprocess.run(["lscpu"], capture_output=True, text=True,
+                             timeout=10).stdout
+        for key, name in (("Model name", "model"), ("Thread(s) per core",
+                                                     "threads_per_core"),
+                          ("Socket(s)", "sockets")):
+            m = re.search(rf"^{re.escape(key)}:\s*(.+)$", txt, re.M)
+            if m:
+                info[name] = m.group(1).strip()
+    except Exception:
+        pass
+    try:
+        with open("/sys/devices/system/cpu/smt/active") as f:
+            info["smt_active"] = f.read().strip() == "1"
+    except OSError:
+        pass
+    return info
 
 
 # ------------------------------------------------------------- workloads
@@ -491,6 +568,9 @@ def main():
     ap.add_argument("--v-pad", type=int, default=64, metavar="ELEMS",
                     help="long workload: V rows stored at a pitch of D + ELEMS "
                          "bf16 (0: dense rows)")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="long workload: skip the second timed pass with V's "
+                         "rows at the dense pitch")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="BYTES",
                     help="after timing, run one plain device-to-device copy of "
                          "BYTES (the reference for scaling HBM byte counters)")
@@ -520,22 +600,23 @@ def main():
     w = make_workload(args.workload)
     S, T = w["S"], w["T"]
 
+    Vd = Vdense = None
     if w["kind"] == "bf16":
         Hd = torch.from_numpy(w["H"].view(np.int16)).to(dev)
-        Vd = None
         if w["V"] is not None:
             # V's rows at a pitch of D + v_pad elements (the gather takes any
-            # pitch; one that is not a multiple of 2 KiB keeps its L2 sets apart)
+            # pitch; one that is not a multiple of 2 KiB keeps its L2 sets
+            # apart), and a dense copy for the second timed pass
             Bv, Tv, Dv = w["V"].shape
+            Vdense = torch.from_numpy(w["V"].view(np.int16)).to(dev)
             Vbuf = torch.zeros((Bv, Tv, Dv + args.v_pad), dtype=torch.int16, device=dev)
-            Vbuf[:, :, :Dv] = torch.from_numpy(w["V"].view(np.int16)).to(dev)
+            Vbuf[:, :, :Dv] = Vdense
             Vd = Vbuf[:, :, :Dv]
         inp = rosa.bf16_input(Hd, w["M"])
         K = 1 << w["M"]
     else:
         Xd = torch.from_numpy(w["sym"]).to(dev)
         inp = rosa.symbols_input(Xd, w["K"])
-        Vd = None
         K = w["K"]
     E = torch.empty((S, T), dtype=torch.int32, device=dev)
     SYM = torch.empty((S, T), dtype=torch.int16, device=dev)
@@ -549,31 +630,43 @@ def main():
     n_ev = args.steps
     kb = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     ke = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    gb = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ge = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
 
-    def step(i=None):
+    def step(V, i=None):
         if i is None:
             rosa.rosa_match(inp, outs, ws, stream)
         else:
             rosa.rosa_match_timed(inp, outs, ws, kb[i], ke[i], stream)
-        if Vd is not None:
-            rosa.rosa_gather(Vd, w["M"], E, out, stream)
+        if V is not None:
+            if i is not None:
+                gb[i].record(stream)
+            rosa.rosa_gather(V, w["M"], E, out, stream)
+            if i is not None:
+                ge[i].record(stream)
 
-    _log(f"warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    _log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
-    k_ms = [kb[i].elapsed_time(ke[i]) for i in range(n_ev)]
-    k_avg = float(np.mean(k_ms))
+    def timed(V):
+        """Warm-up, then `steps` steps between two events on the stream;
+        returns ms per step and the mean event-timed retrieval and gather
+        kernel durations."""
+        for _ in range(args.warmup):
+            step(V)
+        torch.cuda.synchronize()
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        t_start.record(stream)
+        for i in range(args.steps):
+            step(V, i)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        ms = t_start.elapsed_time(t_end) / args.steps
+        k = float(np.mean([kb[i].elapsed_time(ke[i]) for i in range(n_ev)]))
+        g = (float(np.mean([gb[i].elapsed_time(ge[i]) for i in range(n_ev)]))
+             if V is not None else None)
+        return ms, k, g
+
+    _log(f"warmup {args.warmup}, timing {args.steps} steps")
+    ms_step, k_avg, g_avg = timed(Vd)
     if rosa.rosa_match_status(ws) != rosa.ROSA_OK:
         raise SystemExit("symbol range flag raised")
     if args.copy_reference > 0:
@@ -587,13 +680,26 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     value = S * T / (ms_step / 1e3)
-    _log(f"ms/step {ms_step:.4f}  retrieval kernel {k_avg:.4f} ms")
+    _log(f"ms/step {ms_step:.4f}  retrieval kernel {k_avg:.4f} ms"
+         + (f"  gather {g_avg:.4f} ms" if g_avg is not None else ""))
+    dense = None
+    if Vd is not None and args.v_pad != 0 and not args.no_dense:
+        # the same steps with V's rows at the dense pitch (D elements); the
+        # outputs are compared with the padded run's
+        out_pad = out.clone()
+        ms_d, k_d, g_d = timed(Vdense)
+        if not torch.equal(out, out_pad):
+            raise SystemExit("dense-pitch gather differs from the padded one")
+        dense = {"ms_per_step": ms_d, "retrieval_ms": k_d, "gather_ms": g_d,
+                 "v_row_pitch": int(Vdense.stride(1))}
+        _log(f"dense V rows: ms/step {ms_d:.4f}  gather {g_d:.4f} ms")
 
-    kbytes = KERNEL_BYTES_PER_POS * S * T
-    achieved = kbytes / (k_avg / 1e3)
-    roof = {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
-            "unit": "GB/s", "frac": achieved / HBM_PEAK,
-            "traffic": measured_traffic() if args.workload == "long" else None}
+    roof = kernel_roofline(S * T, k_avg, args.workload)
+    if w["kind"] == "bf16" and Vd is not None:
+        sb = STEP_BYTES_PER_POS * S * T
+        roof["step_bytes_per_position"] = STEP_BYTES_PER_POS
+        roof["step_achieved"] = sb / (ms_step / 1e3) / 1e9
+        roof["step_frac"] = sb / (ms_step / 1e3) / HBM_PEAK
 
     cpu = None
     if not args.no_cpu:
@@ -611,13 +717,20 @@ def main():
         if Go is not None and not np.array_equal(
                 out.cpu().numpy().view(np.uint16), Go):
             raise SystemExit("parity failure: gathered values differ")
-        _log(f"parity ok; oracle {wall:.3f} s")
+        _log(f"parity ok; oracle {wall:.3f} s on {threads} threads")
+        what = ("discretize + match + gather" if w["kind"] == "bf16"
+                and w["V"] is not None else "match")
         cpu = {"value": S * T / wall, "unit": "positions/s", "cores": threads,
                "kind": "oracle",
-               "sample": f"whole workload ({S} streams x {T}), "
-                         + ("discretize + match + gather" if w["kind"] == "bf16"
-                            and w["V"] is not None else "match")
-                         + f", streams split over {threads} threads, median of 3"}
+               "sample": f"whole workload ({S} streams x {T}), {what}, streams "
+                         f"split over {threads} threads, median of 3"}
+        if threads > 1:
+            _log("oracle on 1 thread")
+            wall1, _, _, _ = oracle_run(w, 1)
+            cpu["one_thread"] = {"value": S * T / wall1, "cores": 1,
+                                 "sample": f"whole workload, {what}, one "
+                                           "thread, one run"}
+        cpu["host"] = host_cpu_info(threads)
 
     line = {
         "metric": w["metric"], "value": value, "unit": "positions/s", "n_gpus": 1,
@@ -628,7 +741,9 @@ def main():
                    "parallelism": "single GPU",
                    **({"v_row_pitch": int(Vd.stride(1))} if Vd is not None else {})},
         "roofline": roof,
-        "kernel_ms": k_avg,
+        "kernel_ms": {"retrieval": k_avg,
+                      **({"gather": g_avg} if g_avg is not None else {})},
+        **({"dense_v_rows": dense} if dense is not None else {}),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -14,8 +14,11 @@
  *  - Every call only enqueues work on the caller's `stream` and returns; no
  *    implicit device synchronisation, no internal streams.  The exceptions,
  *    which synchronise `stream`, are rosa_match_status and rosa_state_status.
- *  - On any return other than ROSA_OK nothing has been enqueued and no output
- *    has been written.
+ *  - Errors found on the host (ROSA_ERR_ARG, ROSA_ERR_CAPACITY,
+ *    ROSA_ERR_STATE, ROSA_ERR_NOMEM) are returned before anything is
+ *    enqueued, so no output has been written.  ROSA_ERR_HIP means a HIP call
+ *    failed (a launch or an event record): work of the same call enqueued
+ *    before it may still run, and the outputs of that call are unspecified.
  *  - Streams: stream s = b*R + r with R = D/M routes per batch row (Sec. 4.1:
  *    one symbol stream per (b, r) pair).  Time is 0-based.  Per-stream outputs
  *    are laid out [S][T], contiguous in t.
@@ -30,6 +33,14 @@
  *               (App. C.4), or -1.
  *    These values are unique, so results are bit-exact and independent of
  *    launch geometry.
+ *  - Causality of the destination.  The self-match (rosa_match, rosa_build,
+ *    rosa_step) gives tau = E+1 <= t: tau = t happens when the previous
+ *    position is the latest occurrence (E = t-1), and row t of the values
+ *    is then read at position t.  The page states the range of Eq. (16) as
+ *    tau <= t-1, which its run-length folding guarantees (adjacent runs
+ *    differ); without folding that range does not hold.  rosa_match_qk
+ *    applies the strict-past rule as a mask (tau = -1 unless tau < t); a
+ *    self-match caller that needs it sets tau = -1 where E = t-1.
  */
 #ifndef ROSA_H
 #define ROSA_H
@@ -50,7 +61,8 @@ typedef enum rosa_status {
     ROSA_ERR_SYMBOL = 3,   /* an input symbol >= K was seen (reported by
                               rosa_match_status / rosa_state_status)        */
     ROSA_ERR_HIP = 4,      /* a HIP runtime call failed                     */
-    ROSA_ERR_STATE = 5     /* null, freed or foreign state handle           */
+    ROSA_ERR_STATE = 5,    /* null, freed or foreign state handle           */
+    ROSA_ERR_NOMEM = 6     /* a host memory allocation failed               */
 } rosa_status;
 
 /* Input kinds. */
@@ -162,8 +174,15 @@ size_t rosa_match_qk_workspace_bytes(int64_t S, int64_t T, int32_t K);
  * as for rosa_match.  `ws`: at least rosa_match_qk_workspace_bytes(S, T, K)
  * bytes, 256-byte aligned, not shared by calls in flight; its first 256
  * bytes hold the symbol flag, so rosa_match_status(ws, stream) reports a
- * symbol >= K in q or k.  The work is sequential per stream (one lane per
- * stream walks its automaton in device memory). */
+ * symbol >= K in q or k.
+ * Kernels: for at most 4096 units per stream and K <= 64, one or two waves
+ * per stream hold the sets of candidate end units of every match length as
+ * 4096-bit vectors (one 64-bit word per lane) and advance them per unit
+ * with shifts and ANDs; a stream whose match grows past 32 units is handed
+ * to the automaton kernels, which also take every stream beyond those
+ * limits: one wave per stream walks the pages' automaton, with its tables
+ * in LDS when every stream fits the device at once, else in device memory
+ * (sequential per stream, so much slower). */
 rosa_status rosa_match_qk(const rosa_input *q, const rosa_input *k,
                           int32_t flags, const rosa_qk_out *out, void *ws,
                           size_t ws_bytes, hipStream_t stream);
@@ -226,10 +245,15 @@ rosa_status rosa_build(const rosa_input *in, int64_t t_capacity,
                        rosa_state **handle, const rosa_out *out,
                        hipStream_t stream);
 
-/* One online step for every stream at position t = current length: extend
- * each automaton by the new symbol (`row`: T == 1, same kind, S, B, D, M/K
- * as at build), then write end[S] = E(t), sym[S] = SYM(t) (may be NULL) and,
- * if out_row is not NULL, the gathered values
+/* Sec. 4.1 (per position, the stream's symbol extends its structure and the
+ * retrieval emits the destination), Sec. 2.2 (the automaton's online
+ * extension) and App. B.3 (destination = end of the latest earlier
+ * occurrence, plus one).  One online step for every stream at position
+ * t = current length: extend each automaton by the new symbol (`row`:
+ * T == 1, same kind, S, B, D, M/K as at build), read E(t) from the new
+ * state's suffix link, then set the last end of every state on the new
+ * state's suffix path to t.  Writes end[S] = E(t), sym[S] = SYM(t) (may be
+ * NULL) and, if out_row is not NULL, the gathered values
  *   out_row[b*ldo_b + r*M + m] = V[b*ldv_b + (E+1)*ldv + r*M + m]  (0 if E<0)
  * V must already hold position t (tau = E+1 can equal t).  Returns
  * ROSA_ERR_CAPACITY (checked on the host) once t_capacity positions exist. */

@@ -4,6 +4,10 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+#include <new>
+#include <unordered_set>
+
 #include "rosa.h"
 #include "rosa_internal.h"
 
@@ -61,6 +65,43 @@ struct rosa_state {
 };
 
 static const uint64_t kStateMagic = 0x524f53415354ull;  // "ROSAST"
+
+// Live handles.  A handle is looked up here before it is dereferenced, so a
+// freed, foreign or null pointer is rejected (ROSA_ERR_STATE; rosa_free
+// ignores it) without reading its memory.
+static std::mutex g_handles_mu;
+static std::unordered_set<const rosa_state *> *g_handles = nullptr;
+
+static bool handle_live(const rosa_state *h)
+{
+    if (!h)
+        return false;
+    std::lock_guard<std::mutex> lk(g_handles_mu);
+    return g_handles && g_handles->count(h) != 0;
+}
+
+static bool handle_add(const rosa_state *h)
+{
+    std::lock_guard<std::mutex> lk(g_handles_mu);
+    if (!g_handles) {
+        g_handles = new (std::nothrow) std::unordered_set<const rosa_state *>();
+        if (!g_handles)
+            return false;
+    }
+    try {
+        g_handles->insert(h);
+    } catch (...) {
+        return false;
+    }
+    return true;
+}
+
+static bool handle_remove(const rosa_state *h)
+{
+    std::lock_guard<std::mutex> lk(g_handles_mu);
+    return g_handles && g_handles->erase(h) != 0;
+}
+
 static const int64_t kMaxT = (int64_t)1 << 26;
 static const int64_t kMaxST = (int64_t)1 << 40;
 
@@ -182,6 +223,7 @@ const char *rosa_error_string(rosa_status st)
     case ROSA_ERR_SYMBOL: return "input symbol outside [0, K)";
     case ROSA_ERR_HIP: return "HIP runtime error";
     case ROSA_ERR_STATE: return "invalid state handle";
+    case ROSA_ERR_NOMEM: return "host memory allocation failed";
     }
     return "unknown status";
 }
@@ -461,7 +503,11 @@ rosa_status rosa_build(const rosa_input *in, int64_t t_capacity,
         return ROSA_ERR_CAPACITY;
     rosa_state *h = (rosa_state *)calloc(1, sizeof(rosa_state));
     if (!h)
-        return ROSA_ERR_ARG;
+        return ROSA_ERR_NOMEM;
+    if (!handle_add(h)) {
+        free(h);
+        return ROSA_ERR_NOMEM;
+    }
     int32_t *flags = sam_flags(state_buf);
     hipError_t e = launch_clear_flags(flags, stream);
     int64_t Hs = 0;
@@ -481,6 +527,7 @@ rosa_status rosa_build(const rosa_input *in, int64_t t_capacity,
                              out ? out->end : nullptr, out ? out->sym : nullptr,
                              out ? out->len : nullptr, stream);
     if (e != hipSuccess) {
+        handle_remove(h);
         free(h);
         return ROSA_ERR_HIP;
     }
@@ -504,7 +551,7 @@ rosa_status rosa_step(rosa_state *h, const rosa_input *row, const uint16_t *V,
                       int64_t ldv, int64_t ldv_b, int32_t *end, int16_t *sym,
                       uint16_t *out_row, int64_t ldo_b, hipStream_t stream)
 {
-    if (!h || h->magic != kStateMagic)
+    if (!handle_live(h))
         return ROSA_ERR_STATE;
     Shape sh;
     rosa_status st = resolve(row, &sh, false);
@@ -535,14 +582,14 @@ rosa_status rosa_step(rosa_state *h, const rosa_input *row, const uint16_t *V,
 
 int64_t rosa_state_length(const rosa_state *h)
 {
-    if (!h || h->magic != kStateMagic)
+    if (!handle_live(h))
         return -1;
     return h->len;
 }
 
 rosa_status rosa_state_status(rosa_state *h, hipStream_t stream)
 {
-    if (!h || h->magic != kStateMagic)
+    if (!handle_live(h))
         return ROSA_ERR_STATE;
     if (hipStreamSynchronize(stream) != hipSuccess)
         return ROSA_ERR_HIP;
@@ -555,7 +602,8 @@ rosa_status rosa_state_status(rosa_state *h, hipStream_t stream)
 
 void rosa_free(rosa_state *h)
 {
-    if (!h || h->magic != kStateMagic)
+    // the registry decides, so a double free never reads the freed handle
+    if (!handle_remove(h))
         return;
     h->magic = 0;
     free(h);

@@ -145,6 +145,7 @@ struct ScatterParams {
     const int32_t *end;     // [S][T], destination E+1 where E >= 0
     int64_t ldt, ldg, B, T, D, R, Tq, big_cap;
     int32_t M;
+    int32_t skip0;          // lists leave out t = 0 (the sum adds its term first)
     int32_t *cnt;           // [S][T] counts, then fill cursors
     int32_t *off;           // [S][Tq] exclusive prefix, Tq = T + 1
     int32_t *list;          // [S][T] time steps grouped by destination

@@ -150,6 +150,16 @@ __device__ __forceinline__ void scatter_sum_one(const ScatterParams &p, int64_t 
 #pragma unroll
     for (int m = 0; m < MC; ++m)
         acc[m] = 0.0;
+    if (p.skip0) {
+        // the lists leave out t = 0, the first term of the sum in t order
+        const int32_t e0 = p.end[s * p.T];
+        if (e0 >= 0 && (int64_t)e0 + 1 == tau) {
+            const float *th = p.theta + b * p.T * p.ldt + r * MC;
+#pragma unroll
+            for (int m = 0; m < MC; ++m)
+                acc[m] += (double)th[m];
+        }
+    }
     const int32_t *lst = p.list + s * p.T;
     int prev = -1;
     for (int k = 0; k < n; ++k) {
@@ -206,8 +216,10 @@ __global__ __launch_bounds__(256) void scatter_sum_kernel(ScatterParams p, int W
 
 // Streams of up to 65536 positions: count, prefix and fill of one stream in
 // one workgroup, with the per-destination counters in LDS (two 16-bit
-// halves per word: a destination is read by at most T-1 <= 65535 steps,
-// and a prefix plus its count never exceeds the number of valid steps).
+// halves per word).  The time step t = 0 is left out of the lists (the sum
+// kernel adds its term first), so at most T-1 <= 65535 steps are counted:
+// no count, prefix or list slot leaves 16 bits, whatever the destinations
+// (a prefix plus its count never exceeds the number of counted steps).
 constexpr int kScatterLdsT = 65536;
 
 __global__ __launch_bounds__(1024) void scatter_group_lds_kernel(ScatterParams p)
@@ -254,8 +266,8 @@ __global__ __launch_bounds__(1024) void scatter_group_lds_kernel(ScatterParams p
     if (tid == 0)
         carry_s = 0;
     __syncthreads();
-    each([&](int, int e) {
-        if (e >= 0 && e + 1 < T) {
+    each([&](int t, int e) {
+        if (t > 0 && e >= 0 && e + 1 < T) {
             const int tau = e + 1;
             atomicAdd(&c2[tau >> 1], 1u << (16 * (tau & 1)));
         }
@@ -307,7 +319,7 @@ __global__ __launch_bounds__(1024) void scatter_group_lds_kernel(ScatterParams p
     __syncthreads();
     int32_t *list = p.list + s * p.T;
     each([&](int t, int e) {
-        if (e >= 0 && e + 1 < T) {
+        if (t > 0 && e >= 0 && e + 1 < T) {
             const int tau = e + 1;
             const uint32_t sh = 16u * (uint32_t)(tau & 1);
             const uint32_t old = atomicAdd(&c2[tau >> 1], 1u << sh);
@@ -344,8 +356,10 @@ __global__ __launch_bounds__(64) void scatter_big_kernel(ScatterParams p)
     }
 }
 
-hipError_t launch_scatter(const ScatterParams &p, hipStream_t st)
+hipError_t launch_scatter(const ScatterParams &p_in, hipStream_t st)
 {
+    ScatterParams p = p_in;
+    p.skip0 = p.T <= kScatterLdsT ? 1 : 0;
     const int64_t S = p.B * p.R;
     hipLaunchKernelGGL(scatter_zero_kernel, dim3(1), dim3(64), 0, st, p.big,
                        (int64_t)64);

@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librosa.so")
 
 ROSA_OK, ROSA_ERR_ARG, ROSA_ERR_CAPACITY, ROSA_ERR_SYMBOL, ROSA_ERR_HIP, \
-    ROSA_ERR_STATE = range(6)
+    ROSA_ERR_STATE, ROSA_ERR_NOMEM = range(7)
 ROSA_IN_SYMBOLS, ROSA_IN_BF16 = 0, 1
 ROSA_QK_RLE = 1
 
@@ -233,11 +233,38 @@ def rosa_match_status(ws: torch.Tensor, stream=None) -> int:
     return int(load_library().rosa_match_status(ws.data_ptr(), _stream(stream)))
 
 
+def _rows_3d(x: torch.Tensor, what: str, shape=None) -> None:
+    """x must be [B, T, D] with unit channel stride and rows of one pitch
+    (batch stride T * row stride), the layout the C-ABI reads and writes."""
+    if x.dim() != 3 or (shape is not None and tuple(x.shape) != tuple(shape)):
+        raise ValueError(f"{what} must be a [B, T, D] tensor"
+                         + (f" of shape {tuple(shape)}" if shape is not None else ""))
+    B, T, D = x.shape
+    if x.stride(2) != 1 or (T > 1 and x.stride(1) < D) or \
+            (B > 1 and x.stride(0) != T * x.stride(1)):
+        raise ValueError(f"{what} must be [B][T][ld] with unit channel stride "
+                         "and batch stride T * ld")
+
+
+def _end_rows(end: torch.Tensor, S: int, T: int) -> None:
+    if end.dtype != torch.int32 or tuple(end.shape) != (S, T) or \
+            (T > 0 and not end.is_contiguous()):
+        raise ValueError(f"end must be a contiguous int32 [{S}, {T}] tensor")
+
+
 def rosa_gather(V: torch.Tensor, M: int, end: torch.Tensor, out: torch.Tensor,
                 stream=None) -> None:
     """V, out: 16-bit [B, T, D] (unit channel stride); end: int32 [S, T]."""
     _require_device(V, end, out)
+    if V.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or \
+            out.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError("V and out must be 16-bit tensors")
+    _rows_3d(V, "V")
+    _rows_3d(out, "out", V.shape)
     B, T, D = V.shape
+    if M < 1 or D % M:
+        raise ValueError("D must be a multiple of M")
+    _end_rows(end, B * (D // M), T)
     _check(load_library().rosa_gather(V.data_ptr(), B, T, D,
                                       V.stride(1) if T > 1 else D, M,
                                       end.data_ptr(), out.data_ptr(),
@@ -257,7 +284,12 @@ def rosa_scatter_grad(theta: torch.Tensor, M: int, end: torch.Tensor,
     _require_device(theta, end, G, ws)
     if theta.dtype != torch.float32 or G.dtype != torch.float32:
         raise ValueError("theta and G must be float32")
+    _rows_3d(theta, "theta")
+    _rows_3d(G, "G", theta.shape)
     B, T, D = theta.shape
+    if M < 1 or D % M:
+        raise ValueError("D must be a multiple of M")
+    _end_rows(end, B * (D // M), T)
     if ws is None:
         ws = torch.empty(rosa_scatter_grad_workspace_bytes(B * (D // M), T),
                          dtype=torch.uint8, device=theta.device)

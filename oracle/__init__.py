@@ -36,7 +36,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "rosa_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ROSA_ORACLE_LIB selects another build of the same source (the sanitizer
+# build of build_sanitized(), loaded by the sanitizer test)
+_LIB_PATH = os.environ.get("ROSA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
+SANITIZED_LIB = os.path.join(_HERE, "liboracle_san.so")
 _lib = None
 
 
@@ -48,6 +51,21 @@ def build(force: bool = True) -> str:
                                "-o", tmp, _SRC])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
+
+
+def build_sanitized() -> str:
+    """Compile rosa_oracle.c with AddressSanitizer and UndefinedBehavior-
+    Sanitizer (host code only; every UB report aborts) into
+    oracle/liboracle_san.so.  A process loads it with the sanitizer runtime
+    preloaded and ROSA_ORACLE_LIB pointing at it."""
+    tmp = SANITIZED_LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call(["gcc", "-O1", "-g", "-std=c99", "-shared", "-fPIC",
+                           "-fno-omit-frame-pointer",
+                           "-fsanitize=address,undefined",
+                           "-fno-sanitize-recover=undefined",
+                           "-o", tmp, _SRC])
+    os.replace(tmp, SANITIZED_LIB)
+    return SANITIZED_LIB
 
 
 def _load():

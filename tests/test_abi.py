@@ -28,7 +28,7 @@ def test_library_exports_header_symbols():
 
 
 def test_error_strings():
-    for st in range(6):
+    for st in range(7):
         assert rosa.rosa_error_string(st)
     assert "unknown" in rosa.rosa_error_string(99)
 
@@ -131,6 +131,42 @@ def test_state_api_rejects_bad_handles_and_args():
     assert lib.rosa_build(ctypes.byref(inp2), 200, 0x100000, 64,
                           ctypes.byref(h), None, None) == rosa.ROSA_ERR_CAPACITY
     assert not h.value
+
+
+def test_state_api_never_reads_unknown_handles():
+    """Handles are looked up in the library's registry of live handles
+    before they are read: a pointer the library never returned (here one
+    into unmapped memory, which would fault if read) is rejected, and a
+    double free is ignored."""
+    lib = rosa.load_library()
+    bogus = ctypes.c_void_p(0x10)
+    assert lib.rosa_state_length(bogus) == -1
+    assert lib.rosa_state_status(bogus, None) == rosa.ROSA_ERR_STATE
+    inp = _inp(T=1, ld=1)
+    assert lib.rosa_step(bogus, ctypes.byref(inp), None, 0, 0, FAKE.value,
+                         None, None, 0, None) == rosa.ROSA_ERR_STATE
+    lib.rosa_free(bogus)
+    lib.rosa_free(bogus)
+
+
+def test_gather_and_scatter_bindings_check_layouts():
+    """The binding refuses tensors whose layout the C-ABI would read wrongly
+    (CPU tensors never reach the library: the device check comes first, so
+    the layout checks are exercised through the helpers)."""
+    import torch
+    V = torch.zeros((2, 10, 8), dtype=torch.int16)
+    rosa._rows_3d(V, "V")
+    with pytest.raises(ValueError):
+        rosa._rows_3d(torch.zeros((2, 20, 8), dtype=torch.int16)[:, :10], "V")
+    with pytest.raises(ValueError):
+        rosa._rows_3d(V, "out", (2, 10, 4))
+    with pytest.raises(ValueError):
+        rosa._rows_3d(torch.zeros((2, 8, 10), dtype=torch.int16).transpose(1, 2), "V")
+    rosa._end_rows(torch.zeros((4, 10), dtype=torch.int32), 4, 10)
+    with pytest.raises(ValueError):
+        rosa._end_rows(torch.zeros((4, 10), dtype=torch.int64), 4, 10)
+    with pytest.raises(ValueError):
+        rosa._end_rows(torch.zeros((4, 11), dtype=torch.int32), 4, 10)
 
 
 def test_match_qk_rejects_bad_arguments():

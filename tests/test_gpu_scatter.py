@@ -76,6 +76,28 @@ def test_scatter_many_per_destination():
     _compare(_run(theta, E, M), oracle.scatter_grad(theta, E, M), "many")
 
 
+@pytest.mark.parametrize("first", [7, -1, 65534])
+def test_scatter_every_step_to_one_row_at_65536(first):
+    """T = 65536 with (nearly) every time step, t = 0 included, pointing at
+    one row: a count of 65536 would not fit the grouping kernel's 16-bit
+    counters, which therefore leave t = 0 to the sum.  Stream 0 sends every
+    t > 0 to row 8 and t = 0 to row E[0] + 1; stream 1 sends t = 0 to a row
+    of its own; stream 2 sends every t > 0 to row 1 (65535 steps); stream 3
+    is random, out-of-range entries included."""
+    B, T, D, M = 1, 65536, 16, 4
+    S = D // M
+    rng = np.random.default_rng(11)
+    E = np.full((S, T), 7, np.int32)
+    E[0, 0] = first
+    E[1, 0] = 100
+    E[2, 0] = -1
+    E[2, 1:] = 0
+    E[3, :] = rng.integers(-2, T, T)
+    theta = rng.standard_normal((B, T, D)).astype(np.float32)
+    _compare(_run(theta, E, M), oracle.scatter_grad(theta, E, M),
+             f"one row at 65536 (E[0] = {first})")
+
+
 @pytest.mark.parametrize("T", [301, 300])
 def test_scatter_out_of_range_and_padding(T):
     """Destinations outside [0, T-1) are ignored; T = 300 takes the grouping
