@@ -11,6 +11,8 @@
  *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
  *    library never allocates device memory; scratch comes from a caller
  *    workspace (rosa_match) or a caller state buffer (rosa_build/rosa_step).
+ *    The one exception is the fixed device array behind rosa_match_noalloc,
+ *    which the HIP runtime places on each device the library runs on.
  *  - Every call only enqueues work on the caller's `stream` and returns; no
  *    implicit device synchronisation, no internal streams.  The exceptions,
  *    which synchronise `stream`, are rosa_match_status and rosa_state_status.
@@ -125,6 +127,23 @@ rosa_status rosa_match_timed(const rosa_input *in, const rosa_out *out,
 /* Synchronises `stream`, then returns ROSA_ERR_SYMBOL if the last rosa_match
  * that used `ws` saw a symbol >= K, else ROSA_OK (or ROSA_ERR_HIP). */
 rosa_status rosa_match_status(const void *ws, hipStream_t stream);
+
+/* Size of the fixed device array rosa_match_noalloc works in. */
+#define ROSA_NOALLOC_MAX_WORKSPACE_BYTES ((size_t)96 << 20)
+
+/* For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid allocation): rosa_match with no
+ * workspace argument.  The workspace is a fixed array of
+ * ROSA_NOALLOC_MAX_WORKSPACE_BYTES in the library, one per device, held
+ * until the process ends; inputs and outputs are the caller's, as for
+ * rosa_match.  Shapes whose rosa_match_workspace_bytes(S, T, K) exceeds
+ * that size give ROSA_ERR_CAPACITY (512 streams of 4096 positions fit).
+ * The call makes no allocation of any kind.  Every call on a device shares
+ * that device's array: calls that overlap on one device (e.g. on two
+ * streams) race, and rosa_match_status does not apply (a symbol >= K still
+ * leaves the outputs unspecified). */
+rosa_status rosa_match_noalloc(const rosa_input *in, const rosa_out *out,
+                               hipStream_t stream);
 
 /* --------------------------------------------------- query / key retrieval */
 

@@ -299,6 +299,58 @@ rosa_status rosa_match_timed(const rosa_input *in, const rosa_out *out,
     return match_impl(in, out, ws, ws_bytes, stream, ev_begin, ev_end);
 }
 
+// ------------------------------------------------- allocation-free match
+//
+// For callers that cannot allocate device memory (code under graph capture,
+// tight serving loops, harnesses that forbid it): rosa_match with its
+// workspace in a fixed device array of this library.  The array's name is a
+// host-side stand-in in host code; its device address is looked up once per
+// device with hipGetSymbolAddress and only that address is used.  Every call
+// on a device shares the device's one array, which keeps the last call's
+// contents (the launches clear what must start at zero): calls that overlap
+// on one device, e.g. on two streams, race.
+
+static_assert(kNoAllocScratchBytes == ROSA_NOALLOC_MAX_WORKSPACE_BYTES,
+              "the header states the array's size");
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+static std::mutex g_scratch_mu;
+constexpr int kScratchDevices = 64;
+static void *g_scratch_ptr[kScratchDevices];
+
+// Device address of `scratch` on the current device (null on a HIP error).
+static void *scratch_ptr()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+            return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+rosa_status rosa_match_noalloc(const rosa_input *in, const rosa_out *out,
+                               hipStream_t stream)
+{
+    Shape sh;
+    rosa_status st = resolve(in, &sh, true);
+    if (st != ROSA_OK)
+        return st;
+    if (!out || (!out->end && sh.T > 0))
+        return ROSA_ERR_ARG;
+    if (ws_layout(sh.S, sh.T).total > kNoAllocScratchBytes)
+        return ROSA_ERR_CAPACITY;
+    void *ws = scratch_ptr();
+    if (!ws)
+        return ROSA_ERR_HIP;
+    return match_impl(in, out, ws, kNoAllocScratchBytes, stream, nullptr, nullptr);
+}
+
 }  // extern "C"
 
 namespace {

@@ -21,6 +21,10 @@ constexpr int kStreamThreads = 1024; // one workgroup per stream
 constexpr int kTaskCap = 4128;       // tasks per stream (<= kMaxBuckets)
 constexpr int kBigThreads = 64;      // one wave per large group
 
+// Size of the fixed device array behind rosa_match_noalloc (the match
+// workspace of 512 streams x 4096 positions, 69 MiB, fits).
+constexpr size_t kNoAllocScratchBytes = (size_t)96 << 20;
+
 // Flags word layout in the match workspace (first 256 bytes).
 constexpr int kFlagSymbol = 0;       // int32: nonzero if a symbol >= K was seen
 

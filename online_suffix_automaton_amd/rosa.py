@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(_HERE, "librosa.so")
 
 ROSA_OK, ROSA_ERR_ARG, ROSA_ERR_CAPACITY, ROSA_ERR_SYMBOL, ROSA_ERR_HIP, \
     ROSA_ERR_STATE, ROSA_ERR_NOMEM = range(7)
+# size of the fixed device array behind rosa_match_noalloc
+ROSA_NOALLOC_MAX_WORKSPACE_BYTES = 96 << 20
 ROSA_IN_SYMBOLS, ROSA_IN_BF16 = 0, 1
 ROSA_QK_RLE = 1
 
@@ -49,7 +51,7 @@ class rosa_qk_out(ctypes.Structure):
 
 _lib = None
 _SYMBOLS = ["rosa_match_workspace_bytes", "rosa_match", "rosa_match_timed",
-            "rosa_match_status", "rosa_match_qk_workspace_bytes",
+            "rosa_match_status", "rosa_match_noalloc", "rosa_match_qk_workspace_bytes",
             "rosa_match_qk", "rosa_scatter_grad_workspace_bytes",
             "rosa_scatter_grad",
             "rosa_gather", "rosa_state_bytes", "rosa_build", "rosa_step",
@@ -73,6 +75,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "rosa_match": ([P, P, P, SZ, P], ctypes.c_int),
         "rosa_match_timed": ([P, P, P, SZ, P, P, P], ctypes.c_int),
         "rosa_match_status": ([P, P], ctypes.c_int),
+        "rosa_match_noalloc": ([P, P, P], ctypes.c_int),
         "rosa_match_qk_workspace_bytes": ([I64, I64, I32], SZ),
         "rosa_match_qk": ([P, P, I32, P, P, SZ, P], ctypes.c_int),
         "rosa_scatter_grad_workspace_bytes": ([I64, I64], SZ),
@@ -201,6 +204,15 @@ def rosa_match_timed(inp: rosa_input, out: rosa_out, ws: torch.Tensor,
         ws.numel() * ws.element_size(), _stream(stream),
         ctypes.c_void_p(ev_begin.cuda_event), ctypes.c_void_p(ev_end.cuda_event)),
         "rosa_match_timed")
+
+
+def rosa_match_noalloc(inp: rosa_input, out: rosa_out, stream=None) -> None:
+    """rosa_match in the library's fixed device array: no workspace argument
+    and no allocation (shapes whose workspace exceeds
+    ROSA_NOALLOC_MAX_WORKSPACE_BYTES raise with ROSA_ERR_CAPACITY)."""
+    _check(load_library().rosa_match_noalloc(ctypes.byref(inp), ctypes.byref(out),
+                                             _stream(stream)),
+           "rosa_match_noalloc")
 
 
 def rosa_match_qk_workspace_bytes(S: int, T: int, K: int) -> int:
