@@ -172,7 +172,51 @@ def make_workload(name):
                     metric="matched positions/sec (streams×T), 1024 streams x 32768",
                     desc="repeat: 1024 streams x 32768, K=16, planted copies "
                          "(U{32..512}) over ~30% of positions; match")
+    if name == "lowent":
+        w = synth.long()
+        H = w["H"].copy()
+        R, M = 512, 4
+        mag = H & np.uint16(0x7FFF)
+        for r in range(R):
+            c = slice(r * M, (r + 1) * M)
+            if r < 128:
+                # dead channel group: every channel <= 0, the symbol is 0
+                H[:, :, c] = mag[:, :, c] | np.uint16(0x8000)
+            elif r < 256:
+                # period 2 .. 9 over distinct symbols: channel j carries
+                # bit j of the symbol as its sign
+                per = 2 + (r % 8)
+                sym = (np.arange(65536) % per).astype(np.uint16)
+                for j in range(M):
+                    neg = ((sym >> j) & 1) == 0
+                    H[0, :, r * M + j] = np.where(neg, mag[0, :, r * M + j] | np.uint16(0x8000),
+                                                  mag[0, :, r * M + j])
+        return dict(kind="bf16", H=H, V=w["V"], M=M, S=512, T=65536,
+                    metric="matched positions/sec (streams×T), 512 low-entropy "
+                           "streams x 65536",
+                    desc="lowent: hidden [1,65536,2048] bf16 N(0,1) with routes "
+                         "0-127 dead (every channel <= 0: constant streams) and "
+                         "routes 128-255 periodic (periods 2-9), M=4 -> 512 "
+                         "streams x 65536, K=16; match + gather of V",
+                    closed_form=256)
     raise ValueError(name)
+
+
+def closed_form_streams(Sym, n):
+    """E of the first n streams of the low-entropy workload from their
+    closed forms (constant: E = t-1; period p over p distinct symbols: -1
+    before p, then t-p), identified from the packed symbols."""
+    T = Sym.shape[1]
+    t = np.arange(T)
+    E = np.empty((n, T), np.int32)
+    for s in range(n):
+        x = Sym[s]
+        p = 1
+        while p < 16 and x[p] != x[0]:
+            p += 1
+        assert np.array_equal(x, np.resize(x[:p], T)) and len(set(x[:p])) == p
+        E[s] = np.where(t < p, -1, t - p)
+    return E
 
 
 # ------------------------------------------------------------ CPU oracle
@@ -184,6 +228,12 @@ def oracle_run(w, threads):
     import oracle
     S, T = w["S"], w["T"]
     chunks = np.array_split(np.arange(S), threads)
+    if w["kind"] == "bf16":
+        # a job never crosses a batch row (its streams are a contiguous
+        # channel slice of one row)
+        R = w["H"].shape[2] // w["M"]
+        chunks = [part for c in chunks if len(c)
+                  for part in np.split(c, np.nonzero(np.diff(c // R))[0] + 1)]
     jobs = []
     for c in chunks:
         if len(c) == 0:
@@ -193,9 +243,8 @@ def oracle_run(w, threads):
             H = w["H"]
             B, _, D = H.shape
             R = D // w["M"]
-            # streams of one batch row, as contiguous channel slices
             b0, b1 = s0 // R, (s1 - 1) // R
-            assert b0 == b1, "thread chunk crosses a batch row"
+            assert b0 == b1, "job crosses a batch row"
             M = w["M"]
             h = np.ascontiguousarray(H[b0:b0 + 1, :, (s0 % R) * M:((s1 - 1) % R + 1) * M])
             v = None
@@ -553,8 +602,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long",
-                    choices=["long", "batched", "repeat", "decode", "qk",
-                             "scatter"])
+                    choices=["long", "batched", "repeat", "lowent", "decode",
+                             "qk", "scatter"])
     ap.add_argument("--rle", action="store_true",
                     help="qk workload: fold the key stream into runs")
     ap.add_argument("--cf", action="store_true",
@@ -702,7 +751,32 @@ def main():
         roof["step_frac"] = sb / (ms_step / 1e3) / HBM_PEAK
 
     cpu = None
-    if not args.no_cpu:
+    if not args.no_cpu and w.get("closed_form"):
+        # the constant and periodic streams against their closed forms (the
+        # oracle's automaton walks every state of a constant stream's suffix
+        # path, O(T^2)); the other streams, the symbols and the gather against
+        # the oracle; no CPU baseline
+        import oracle
+        n = w["closed_form"]
+        Hs = w["H"]
+        Sym = oracle.discretize_bf16(Hs, w["M"])
+        Ec = closed_form_streams(Sym, n)
+        Eg = E.cpu().numpy()
+        if not np.array_equal(Eg[:n], Ec):
+            raise SystemExit("parity failure: low-entropy E differs from the closed form")
+        Eo, SYMo, _ = oracle.match(Sym[n:], 1 << w["M"])
+        if not np.array_equal(Eg[n:], Eo):
+            raise SystemExit("parity failure: E differs from the oracle")
+        Eall = np.concatenate([Ec, Eo])
+        SYMw = np.where(Eall >= 0, np.take_along_axis(Sym, np.maximum(Eall + 1, 0),
+                                                      1).astype(np.int16), -1)
+        if not np.array_equal(SYM.cpu().numpy(), SYMw):
+            raise SystemExit("parity failure: SYM differs")
+        if not np.array_equal(out.cpu().numpy().view(np.uint16),
+                              oracle.gather(w["V"], Eall, w["M"])):
+            raise SystemExit("parity failure: gathered values differ")
+        _log("parity ok (closed forms and oracle)")
+    elif not args.no_cpu:
         threads = max(1, min(args.cpu_threads, os.cpu_count() or 1))
         _log(f"oracle on {threads} threads (parity check + baseline)")
         walls = []

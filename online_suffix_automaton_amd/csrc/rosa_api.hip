@@ -41,8 +41,9 @@ hipError_t launch_sam_hist(const uint8_t *in, int64_t ld, int64_t S, int64_t T,
                            int32_t K, void *buf, int64_t Tcap,
                            uint8_t *copy_out, hipStream_t st);
 hipError_t launch_sam_build(void *buf, int64_t S, int64_t K, int64_t Tcap,
-                            int64_t T, int32_t *E, int16_t *SYM, int32_t *L,
-                            hipStream_t st);
+                            int64_t T, hipStream_t st);
+void *sam_match_ws(void *buf, int64_t S, int64_t K, int64_t Tcap,
+                   size_t *bytes);
 hipError_t launch_sam_step(void *buf, int64_t S, int64_t K, int64_t Tcap,
                            int64_t t, int kind, const void *row, int64_t ld,
                            int64_t R, int M, const uint16_t *V, int64_t ldv,
@@ -574,14 +575,31 @@ rosa_status rosa_build(const rosa_input *in, int64_t t_capacity,
                                   sh.B, sh.T, sh.D, sh.ld, sh.M, hist, Hs, 0,
                                   out ? out->symbols : nullptr, stream);
     }
-    if (e == hipSuccess)
-        e = launch_sam_build(state_buf, sh.S, sh.K, t_capacity, sh.T,
-                             out ? out->end : nullptr, out ? out->sym : nullptr,
-                             out ? out->len : nullptr, stream);
-    if (e != hipSuccess) {
+    // the prefix's outputs come from the batch retrieval over the history
+    // rows (already clamped to [0, K)), with its workspace in the region
+    // the automaton is built in next
+    rosa_status ms = ROSA_OK;
+    if (e == hipSuccess && sh.T > 0 && out) {
+        size_t wsb = 0;
+        void *ws = sam_match_ws(state_buf, sh.S, sh.K, t_capacity, &wsb);
+        rosa_input hin;
+        memset(&hin, 0, sizeof hin);
+        hin.kind = ROSA_IN_SYMBOLS;
+        hin.K = (int32_t)sh.K;
+        hin.S = sh.S;
+        hin.T = sh.T;
+        hin.ld = Hs;
+        hin.data = hist;
+        rosa_out o2 = *out;
+        o2.symbols = nullptr;   // written with the history rows
+        ms = match_impl(&hin, &o2, ws, wsb, stream, nullptr, nullptr);
+    }
+    if (e == hipSuccess && ms == ROSA_OK)
+        e = launch_sam_build(state_buf, sh.S, sh.K, t_capacity, sh.T, stream);
+    if (e != hipSuccess || ms != ROSA_OK) {
         handle_remove(h);
         free(h);
-        return ROSA_ERR_HIP;
+        return ms != ROSA_OK ? ms : ROSA_ERR_HIP;
     }
     h->magic = kStateMagic;
     h->buf = state_buf;

@@ -46,9 +46,18 @@ constexpr int kWordThresh = 3;       // level steps only for groups larger than 
 constexpr int kMiscPass = 26;        // misc[26..31]: tasks per slot range
 constexpr int kMiscNext = 20;        // misc[20]: next task of the pass (phase E)
 constexpr int kMiscLastQ = 21;       // misc[21]: last position with L < d (phase D)
+constexpr int kMiscBig = 22;         // misc[22]: the stream's large buckets (LDS kernel)
 constexpr int kWordThreshDeep = 32;  // ... and past the first levels, larger than this
 
 // ----------------------------------------------------------- wave helpers
+
+// The stream's own list of buckets of more than 64 members (LDS kernel):
+// {s, key, start, n} entries, at most T/65 + 1 per stream (the global list's
+// capacity is S times that).
+__device__ __forceinline__ int32_t *big_own(const MatchParams &p, int s)
+{
+    return p.big + 64 + 4 * (int64_t)s * (p.T / 65 + 1);
+}
 
 __device__ __forceinline__ uint64_t ballot(bool p)
 {
@@ -128,6 +137,28 @@ struct Found {
     bool deep;      // CAP mode: answer deferred, its record written (solve_wave)
 };
 
+// Lanes of the wave with `sel` set whose symbol `dig` (< 16) equals mine, by
+// one LDS OR and one LDS read on the wave's 16-word table `tab` (cleared
+// first).  A wave's LDS operations are performed in issue order, so the
+// clear, the ORs and the reads need no wait between them; the wave
+// barriers only keep the compiler from moving them past each other.  The
+// result is 0 for lanes without `sel`.
+__device__ __forceinline__ uint64_t wave_symbol_mask(uint64_t *tab, bool sel,
+                                                     uint32_t dig, uint64_t self)
+{
+    const int lane = __lane_id();
+    if (lane < 16)
+        tab[lane] = 0;
+    __builtin_amdgcn_wave_barrier();
+    if (sel)
+        __hip_atomic_fetch_or(tab + dig, self, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_WORKGROUP);
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t r = sel ? tab[dig] : 0ull;
+    __builtin_amdgcn_wave_barrier();
+    return r;
+}
+
 // ------------------------------------------------------------ solve_wave
 //
 // Each lane holds one element t (or none).  g is the lane mask of its group:
@@ -155,7 +186,8 @@ struct Found {
 //    (a lower bound of their common suffix with t).
 template <bool CAP>
 __device__ Found solve_wave(const uint8_t *x, int nbits, int t, uint64_t g,
-                            int ell, bool has, uint4 *drec = nullptr)
+                            int ell, bool has, uint4 *drec = nullptr,
+                            uint64_t *eqw = nullptr)
 {
     const int lane = __lane_id();
     const uint64_t self = 1ull << lane;
@@ -183,24 +215,34 @@ __device__ Found solve_wave(const uint8_t *x, int nbits, int t, uint64_t g,
         // they agree on each of its nbits bits (one ballot per bit)
         const bool valid = pc >= 2 && (t - ell >= 0);
         const uint32_t dig = valid ? (uint32_t)x[t - ell] : 0u;
-        // (a compare straight to a lane mask: the compiler would rebuild the
-        // ballot of the compare it already made for `valid` in a register)
-        const uint64_t vmask = liveb & __builtin_amdgcn_sicmp(t - ell, 0, 39 /* >= */);
-        // eq = lanes of vmask whose symbol equals mine; per bit b, with m =
-        // all ones where my bit is set, each 32-bit half is e & (B == m), one
-        // 3-input bit op (table 0x90 over (e, B, m)); vmask is applied last,
-        // so that no bit op takes two scalar operands
-        uint32_t eql = ~0u, eqh = ~0u;
+        uint64_t eq;
+        if (eqw) {
+            // alphabets of at most 16 symbols: every valid lane ORs its bit
+            // into its symbol's word of the wave's LDS table and reads the
+            // word back (one wave's LDS operations complete in issue order,
+            // so the clear, the ORs and the reads need no wait between them)
+            eq = wave_symbol_mask(eqw, valid, dig, self);
+        } else {
+            // (a compare straight to a lane mask: the compiler would rebuild
+            // the ballot of the compare it already made for `valid`)
+            const uint64_t vmask = liveb & __builtin_amdgcn_sicmp(t - ell, 0, 39 /* >= */);
+            // eq = lanes of vmask whose symbol equals mine; per bit b, with
+            // m = all ones where my bit is set, each 32-bit half is
+            // e & (B == m), one 3-input bit op (table 0x90 over (e, B, m));
+            // vmask is applied last, so that no bit op takes two scalar
+            // operands
+            uint32_t eql = ~0u, eqh = ~0u;
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)dig, b, 1);
-            const uint64_t B = ballot(m != 0);
-            eql = __builtin_amdgcn_bitop3_b32(eql, (uint32_t)B, m, 0x90);
-            eqh = __builtin_amdgcn_bitop3_b32(eqh, (uint32_t)(B >> 32), m, 0x90);
-            if (b + 1 >= nbits)
-                break;
+            for (int b = 0; b < 8; ++b) {
+                const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)dig, b, 1);
+                const uint64_t B = ballot(m != 0);
+                eql = __builtin_amdgcn_bitop3_b32(eql, (uint32_t)B, m, 0x90);
+                eqh = __builtin_amdgcn_bitop3_b32(eqh, (uint32_t)(B >> 32), m, 0x90);
+                if (b + 1 >= nbits)
+                    break;
+            }
+            eq = vmask & (((uint64_t)eqh << 32) | eql);
         }
-        const uint64_t eq = vmask & (((uint64_t)eqh << 32) | eql);
         const uint64_t ng = valid ? (g & eq) : self;
         const uint64_t prev = g & below;
         const int p = prev ? 63 - __clzll((long long)prev) : lane;
@@ -447,7 +489,7 @@ __device__ void phase_hist(const MatchParams &p, const uint8_t *x, int32_t *cnt,
 template <class OffT>
 __device__ void phase_tasks(const MatchParams &p, int s, const int32_t *cnt,
                             OffT *off, uint32_t *tasks, int32_t *misc,
-                            int pcap)
+                            int pcap, bool own_big = false)
 {
     const int tid = threadIdx.x, nt = blockDim.x;
     const int NB = p.NB;
@@ -516,9 +558,19 @@ __device__ void phase_tasks(const MatchParams &p, int s, const int32_t *cnt,
                 cur = 0;
             }
             if (c > 64) {
-                const int idx = atomicAdd(&p.big[0], 1);
-                if (idx < p.big_cap) {
-                    int32_t *ent = p.big + 64 + 4 * (int64_t)idx;
+                // own_big: the stream's own list (misc[kMiscBig] entries from
+                // big_own(p, s)), solved by the stream's workgroup; else the
+                // global list of big_kernel
+                int32_t *ent = nullptr;
+                if (own_big) {
+                    const int idx = atomicAdd(&misc[kMiscBig], 1);
+                    ent = big_own(p, s) + 4 * (int64_t)idx;   // < T/65 + 1 entries
+                } else {
+                    const int idx = atomicAdd(&p.big[0], 1);
+                    if (idx < p.big_cap)
+                        ent = p.big + 64 + 4 * (int64_t)idx;
+                }
+                if (ent) {
                     ent[0] = s;
                     ent[1] = b;
                     ent[2] = (int32_t)off[b];
@@ -557,7 +609,7 @@ template <int DC, class Put, class PendT>
 __device__ void phase_short(const MatchParams &p, const uint8_t *x,
                             const int32_t *firstd, const int32_t *firstl,
                             int32_t *segtab, int segcap, PendT *pend,
-                            int32_t *misc, Put put)
+                            int32_t *misc, Put put, uint64_t *eqw = nullptr)
 {
     const int tid = threadIdx.x, nt = blockDim.x;
     const int lane = tid & 63, wid = tid >> 6, nw = nt >> 6;
@@ -643,8 +695,12 @@ __device__ void phase_short(const MatchParams &p, const uint8_t *x,
                 for (int l = 1; l < DC; ++l) {
                     const bool v = inr && t >= l - 1;
                     const int dig = v ? sym_of(w, l - 1) : 0;
-                    eq &= same_digit(dig, __builtin_amdgcn_sicmp(t, hi, 40 /* < */) &
-                                              __builtin_amdgcn_sicmp(t, l - 1, 39 /* >= */));
+                    // lanes with t < hi and t >= l-1 (= v) and my digit
+                    if (eqw)
+                        eq &= wave_symbol_mask(eqw, v, (uint32_t)dig, self);
+                    else
+                        eq &= same_digit(dig, __builtin_amdgcn_sicmp(t, hi, 40 /* < */) &
+                                                  __builtin_amdgcn_sicmp(t, l - 1, 39 /* >= */));
                     if (q && v && fl[l] < t) {
                         Lq = l;
                         const uint64_t pm = eq & below;
@@ -758,7 +814,8 @@ __device__ void sort_buckets(Ptr list, const OffT *off, int NB, int base,
 // position in t_out.
 template <int DC, bool SORT, bool CAP, class Src>
 __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
-                          int n, int &t_out, int &key_out, uint4 *drec = nullptr)
+                          int n, int &t_out, int &key_out, uint4 *drec = nullptr,
+                          uint64_t *eqw = nullptr)
 {
     const int lane = __lane_id();
     const uint64_t self = 1ull << lane;
@@ -785,7 +842,7 @@ __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
     // always suffice).
     if (!SORT) {
         t_out = t0;
-        return solve_wave<CAP>(x, p.nbits, t0, g, d, has, drec);
+        return solve_wave<CAP>(x, p.nbits, t0, g, d, has, drec, eqw);
     }
     uint32_t key = has ? (((uint32_t)__popcll(B & upto) << 16) | (uint32_t)t0)
                        : 0xFFFFFFFFu;
@@ -808,7 +865,259 @@ __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
     }
     const int t1 = has ? (int)(key & 0xFFFFu) : 0;
     t_out = t1;
-    return solve_wave<CAP>(x, p.nbits, t1, g, d, has, drec);
+    return solve_wave<CAP>(x, p.nbits, t1, g, d, has, drec, eqw);
+}
+
+// ------------------------------------------------------- large buckets
+//
+struct GroupRef {
+    int start, n, ell, buf;
+};
+
+// Every LDS access below is made by one wave, whose LDS operations are
+// performed in issue order; the wave barriers only keep the compiler from
+// moving accesses across them.
+__device__ __forceinline__ void wave_sync() { __builtin_amdgcn_wave_barrier(); }
+
+// One wave solves the bucket of stream s with d-gram key `key`, n0 > 64
+// members from bucket slot `start` on (x: the stream's padded symbol row;
+// bcnt, bbase, bbase0: the wave's own LDS arrays of at least K + 2 ints).
+//
+// DEFER (record mode): a group of more than 64 members that stays uniform
+// (every member followed by the same symbol) for kBigDeferLevels levels in
+// a row -- constant or periodic stretches, where refining level by level
+// would cost O(T) levels of O(n) work -- is not refined further.  Its
+// members other than the first are deferred to the time-ordered pass of
+// unpermute_kernel, like the long repeats of solve_wave's CAP mode: each
+// gets a placeholder record, its bit in the deferred bitmap and a record
+// pointing at the group's position list (slot a, n members, buffer), which
+// holds every earlier position sharing its reversed level-gram, so the
+// list is complete for the fallback of the extension rule there.
+constexpr int kBigDeferLevels = 2;
+
+template <bool DEFER>
+__device__ void solve_big_bucket(const MatchParams &p, const uint8_t *x, int s,
+                                 int key, int start, int n0, int32_t *bcnt,
+                                 int32_t *bbase, int32_t *bbase0)
+{
+    const int K = p.K;
+    const int lane = __lane_id();
+    const uint64_t self = 1ull << lane;
+    const uint64_t below = self - 1;
+    const int T = p.T, d = p.d;
+    int32_t *buf0 = p.pos + (int64_t)s * T;
+    int32_t *buf1 = p.pos2 + (int64_t)s * T;
+    StreamOut o;
+    o.x = x;
+    o.E = p.E ? p.E + (int64_t)s * T : nullptr;
+    o.SYM = p.SYM ? p.SYM + (int64_t)s * T : nullptr;
+    o.L = p.L ? p.L + (int64_t)s * T : nullptr;
+    o.rec = p.rec ? p.rec + (int64_t)s * T : nullptr;
+    int4 *stk = p.stack + (int64_t)s * (T / 16 + 4) + start / 16;
+    const int stack_cap = n0 / 16;
+    int nrec = 0;   // records written so far (uniform)
+    // emits the answers of the lanes with `want`, compacting record slots
+    auto put = [&](bool want, int t, int e, int l) {
+        if (o.rec) {
+            const uint64_t m = ballot(want);
+            if (want)
+                emit_record(o, start + 1 + nrec + __popcll(m & below), t, e, l);
+            nrec += __popcll(m);
+        } else if (want) {
+            emit(o, t, e, l);
+        }
+    };
+
+    // the bucket's positions in time order, 256 per round (the four key
+    // reads of a lane issued together)
+    {
+        int w = 0;
+        for (int t0 = d - 1; t0 < T; t0 += 256) {
+            bool m[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int t = t0 + 64 * u + lane;
+                m[u] = t < T && dgram_key(x, t, d, K) == key;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint64_t bm = ballot(m[u]);
+                if (m[u])
+                    buf0[start + w + __popcll(bm & below)] = t0 + 64 * u + lane;
+                w += __popcll(bm);
+            }
+        }
+    }
+    int sp = 0;
+    GroupRef cur = {start, n0, d, 0};
+    int uni_run = 0;   // uniform levels in a row of the current group
+    bool have = true;
+    while (have) {
+        const int32_t *X = cur.buf ? buf1 : buf0;
+        int32_t *Y = cur.buf ? buf0 : buf1;
+        if (cur.n <= 64) {
+            const bool hs = lane < cur.n;
+            const int t = hs ? X[cur.start + lane] : 0;
+            const uint64_t g = cur.n >= 64 ? ~0ull : ((1ull << cur.n) - 1);
+            const Found f = solve_wave<false>(x, p.nbits, t, hs ? g : self, cur.ell, hs);
+            put(hs && f.ok, t, f.e, f.l);
+        } else {
+            const int a = cur.start, n = cur.n, ell = cur.ell;
+            // uniform level?  reference symbol from the last member
+            const int tl = X[a + n - 1];
+            const int dref = x[tl - ell];
+            // 256 members per round, a lane's four loads in flight together
+            bool uni = true;
+            for (int i0 = 0; i0 < n; i0 += 256) {
+                int tt[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int i = i0 + 64 * u + lane;
+                    tt[u] = i < n ? X[a + i] : -1;
+                }
+                bool bad = false;
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    bad = bad || (tt[u] - ell >= 0 && x[tt[u] - ell] != dref);
+                if (ballot(bad)) {
+                    uni = false;
+                    break;
+                }
+            }
+            if (uni) {
+                const int t0 = X[a];
+                if (t0 - ell < 0) {
+                    // the first member's history ends: the next member
+                    // loses its only predecessor at this level
+                    put(lane == 0, X[a + 1], t0, ell);
+                    cur.start = a + 1;
+                    cur.n = n - 1;
+                }
+                cur.ell = ell + 1;
+                ++uni_run;
+                if (DEFER && uni_run >= kBigDeferLevels && cur.n > 64) {
+                    // defer members 1 .. n-1 of the group (see above)
+                    const int ga = cur.start, gn = cur.n;
+                    uint32_t *deepbits = p.deep + (int64_t)s * deep_words(T);
+                    uint4 *dinfo = p.dinfo + (int64_t)s * T;
+                    const uint32_t lb = (uint32_t)min(cur.ell, 8191);
+                    for (int i0 = 1; i0 < gn; i0 += 64) {
+                        const int i = i0 + lane;
+                        const bool hs = i < gn;
+                        const uint64_t m = ballot(hs);
+                        if (hs) {
+                            const int t = X[ga + i];
+                            o.rec[start + 1 + nrec + __popcll(m & below)] = (uint32_t)t << 16;
+                            atomicOr(&deepbits[t >> 5], 1u << (t & 31));
+                            dinfo[t] = make_uint4((uint32_t)ga,
+                                                  (uint32_t)gn | ((uint32_t)cur.buf << 31),
+                                                  0u, (lb << 3) << 16);
+                        }
+                        nrec += __popcll(m);
+                    }
+                } else if (cur.n >= 2) {
+                    continue;
+                }
+            } else {
+                uni_run = 0;
+                // stable partition by x[t-ell] into Y[a .. a+n)
+                for (int q = lane; q <= K; q += 64)
+                    bcnt[q] = 0;
+                wave_sync();
+                for (int i0 = 0; i0 < n; i0 += 64) {
+                    const int i = i0 + lane;
+                    if (i < n) {
+                        const int t = X[a + i];
+                        const int dg = (t - ell >= 0) ? x[t - ell] : K;
+                        atomicAdd(&bcnt[dg], 1);
+                    }
+                }
+                wave_sync();
+                if (lane == 0) {
+                    int acc = 0;
+                    for (int q = 0; q <= K; ++q) {
+                        bbase[q] = acc;
+                        bbase0[q] = acc;
+                        acc += bcnt[q];
+                    }
+                }
+                wave_sync();
+                for (int i0 = 0; i0 < n; i0 += 64) {
+                    const int i = i0 + lane;
+                    const bool hs = i < n;
+                    const int t = hs ? X[a + i] : 0;
+                    const int dg = hs ? ((t - ell >= 0) ? x[t - ell] : K) : K + 1;
+                    uint64_t eq = ballot(hs);
+                    for (int b = 0; b < 9; ++b) {
+                        const bool bit = (dg >> b) & 1;
+                        const uint64_t Bb = ballot(hs && bit);
+                        eq &= bit ? Bb : ~Bb;
+                    }
+                    const int rank = __popcll(eq & below);
+                    int dest = 0;
+                    if (hs)
+                        dest = bbase[dg] + rank;
+                    wave_sync();
+                    if (hs && !(eq & ~(below | self)))   // last of its class
+                        bbase[dg] = dest + 1;
+                    wave_sync();
+                    const bool moved = hs && dg < K;
+                    if (moved)
+                        Y[a + dest] = t;
+                    const bool fin = moved && dest == bbase0[dg] && i > 0;
+                    put(fin, t, fin ? X[a + i - 1] : 0, ell);
+                }
+                wave_sync();
+                // children: small ones solved now, large ones stacked;
+                // continue with the smallest large child
+                int best = -1, bestn = 0x7FFFFFFF;
+                for (int q = 0; q < K; ++q) {
+                    const int c = bcnt[q];
+                    if (c < 2)
+                        continue;
+                    const int cs = a + bbase0[q];
+                    if (c <= 64) {
+                        const bool hs = lane < c;
+                        const int t = hs ? Y[cs + lane] : 0;
+                        const uint64_t g = c >= 64 ? ~0ull : ((1ull << c) - 1);
+                        const Found f = solve_wave<false>(x, p.nbits, t, hs ? g : self,
+                                                          ell + 1, hs);
+                        put(hs && f.ok, t, f.e, f.l);
+                    } else if (c < bestn) {
+                        if (best >= 0 && sp < stack_cap && lane == 0)
+                            stk[sp] = make_int4(a + bbase0[best], bcnt[best],
+                                                ell + 1, cur.buf ^ 1);
+                        if (best >= 0 && sp < stack_cap)
+                            ++sp;
+                        best = q;
+                        bestn = c;
+                    } else if (sp < stack_cap) {
+                        if (lane == 0)
+                            stk[sp] = make_int4(cs, c, ell + 1, cur.buf ^ 1);
+                        ++sp;
+                    }
+                }
+                if (best >= 0) {
+                    cur = GroupRef{a + bbase0[best], bcnt[best], ell + 1,
+                                   cur.buf ^ 1};
+                    uni_run = 0;
+                    continue;
+                }
+            }
+        }
+        if (sp > 0) {
+            // the stack entry was written by lane 0 in an earlier iteration;
+            // global stores and loads of one wave to the same address are
+            // ordered once the store has completed
+            __builtin_amdgcn_s_waitcnt(0);
+            wave_sync();
+            const int4 e = stk[--sp];
+            cur = GroupRef{e.x, e.y, e.z, e.w};
+            uni_run = 0;
+        } else {
+            have = false;
+        }
+    }
 }
 
 // ------------------------------------------------- stream kernel (LDS)
@@ -831,9 +1140,10 @@ __device__ Found run_task(const MatchParams &p, const uint8_t *x, Src src,
 // d-gram buckets: K^d <= max(min(4096, T/8), K), so B = that bound for
 // TMAX (K <= 256); first-occurrence tables: sum_{l<d} K^l < K^d, or at
 // most 11 entries when K = 1.
-template <int TMAX, int THREADS, int UNION>
+template <int TMAX, int THREADS, int UNION, int MINBLOCKS = 1>
 struct LdsCfg {
     static constexpr int kThreads = THREADS;
+    static constexpr int kMinBlocks = MINBLOCKS;   // workgroups per CU
     static constexpr int kTMax = TMAX;
     static constexpr int kSymBytes = (TMAX + kPadFront + kPadBack + 255) / 256 * 256;
     static constexpr int kBuckets =
@@ -854,15 +1164,18 @@ struct LdsCfg {
 // Streams of up to 65536 positions, one 1024-thread workgroup per CU (the
 // whole LDS: two scatter passes for a 65536-position stream).
 using CfgLarge = LdsCfg<65536, 1024,
-                        163840 - 65792 - (kMaxBuckets + 16) * 2 - kMaxBuckets * 2 - 128>;
-// Streams of up to 8192 positions: 41 KiB per 512-thread workgroup, so
-// three workgroups share a CU.
-using CfgSmall = LdsCfg<8192, 512, 28672>;
+                        163840 - 65792 - (kMaxBuckets + 16) * 2 - kMaxBuckets * 2 - 128 -
+                            16 * 16 * 8>;
+// Streams of up to 8192 positions: 42 KiB per 1024-thread workgroup, so two
+// workgroups (32 waves) share a CU and 512 streams run in one round.
+using CfgSmall = LdsCfg<8192, 1024, 28672, 2>;
 
 // DC: the bucketing depth d as a compile-time constant (1..4), or 0 to read
 // it from p.
 template <class Cfg, int DC>
-__global__ __launch_bounds__(Cfg::kThreads) void stream_kernel_lds(MatchParams p)
+__global__ __launch_bounds__(Cfg::kThreads)
+__attribute__((amdgpu_waves_per_eu(Cfg::kThreads / 256 * Cfg::kMinBlocks)))
+void stream_kernel_lds(MatchParams p)
 {
     constexpr int kPassCap = Cfg::kPassCap;
     __shared__ __align__(16) unsigned char symrow[Cfg::kSymBytes];
@@ -872,6 +1185,9 @@ __global__ __launch_bounds__(Cfg::kThreads) void stream_kernel_lds(MatchParams p
     // with the bucket's task so all record stores stay coalesced
     __shared__ uint16_t qres[Cfg::kBuckets];
     __shared__ int32_t misc[32];
+    // per wave: 16 words for the symbol splits of alphabets of at most 16
+    // symbols (wave_symbol_mask)
+    __shared__ uint64_t eqtab[Cfg::kThreads / 64][16];
     __shared__ __align__(16) unsigned char U[Cfg::kUnion];
     int32_t *cnt = reinterpret_cast<int32_t *>(U);
     int32_t *firstd = reinterpret_cast<int32_t *>(U + Cfg::kUFirstd);
@@ -894,6 +1210,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void stream_kernel_lds(MatchParams p
     const int tid = threadIdx.x, nt = blockDim.x;
     const int lane = tid & 63, wid = tid >> 6, nw = nt >> 6;
     const int T = p.T, K = p.K, d = DC > 0 ? DC : p.d, NB = p.NB;
+    uint64_t *eqw = p.nbits <= 4 ? eqtab[wid] : nullptr;
     {
         const uint4 *src = reinterpret_cast<const uint4 *>(p.sym + (int64_t)s * p.Tp);
         uint4 *dst = reinterpret_cast<uint4 *>(symrow);
@@ -913,7 +1230,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void stream_kernel_lds(MatchParams p
     o.rec = p.rec + (int64_t)s * T;
 
     phase_hist<DC>(p, x, cnt, firstd, firstl);
-    phase_tasks(p, s, cnt, off, tasks, misc, kPassCap);
+    phase_tasks(p, s, cnt, off, tasks, misc, kPassCap, true);
 
     // D: records of the first d-1 positions go to the slots T-d+1.. (no
     // bucket holds them); the first occurrence of a d-gram in a singleton
@@ -933,7 +1250,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void stream_kernel_lds(MatchParams p
                         if (o.L)
                             o.L[t] = l;
                     }
-                });
+                }, eqw);
 
     // E: passes over slot ranges.  passid[k] is the pass that scatters
     // bucket k (255: not scattered, a singleton or large bucket).
@@ -1034,7 +1351,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void stream_kernel_lds(MatchParams p
             int t, k;
             pf = run_task<DC, true, true>(
                 p, x, [&](int i) { return (int)lpos[start - base + i]; }, n, t, k,
-                dinfo);
+                dinfo, eqw);
             pt = t;
             pk = k;
             pstart = start;
@@ -1043,6 +1360,23 @@ __global__ __launch_bounds__(Cfg::kThreads) void stream_kernel_lds(MatchParams p
         }
         store_prev();
         __syncthreads();
+    }
+    // buckets of more than 64 members (low-entropy streams), listed by
+    // phase B: one wave each, with its partition counters in the union
+    const int nbig = misc[kMiscBig];
+    if (nbig > 0) {
+        constexpr int kBigInts = 3 * 264;
+        const int nbw = min(nw, Cfg::kUnion / (kBigInts * 4));
+        if (wid < nbw) {
+            int32_t *bl = reinterpret_cast<int32_t *>(U) + wid * kBigInts;
+            const int32_t *list = big_own(p, s);
+            for (int i = wid; i < nbig; i += nbw) {
+                const int32_t *ent = list + 4 * (int64_t)i;
+                solve_big_bucket<true>(p, x, s, ent[1], ent[2], ent[3], bl, bl + 264,
+                                       bl + 528);
+                wave_sync();
+            }
+        }
     }
 }
 
@@ -1113,209 +1447,32 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel_hbm(MatchParams 
 
 // ------------------------------------------------------------- big kernel
 //
-// One wave per bucket with more than 64 members.  Stack entries
+// Streams of more than 65536 positions (direct mode): one wave per bucket
+// with more than 64 members, from the global list.  Stack entries
 // {start, n, level, buffer} describe groups (contiguous, time-ordered,
 // sharing the level-gram).  Only groups of more than 64 members are
-// stacked (smaller ones are solved at once) and stacked groups are disjoint,
-// so a bucket of n members never has more than n/65 entries; the bucket
-// starting at offset `start` of its stream keeps its stack in the stream's
-// stack region from entry start/16 on (n/16 >= n/65 + 2 entries for
-// n >= 65, and ranges of different buckets do not overlap).  A level where
-// every member has the same next symbol only drops the first member if its
-// history ends (t = level-1).  In record mode the bucket's members other
-// than the first (answered by the stream kernel in slot `start`) fill slots
-// start+1 .. start+n-1 in completion order.
-
-struct GroupRef {
-    int start, n, ell, buf;
-};
-
+// stacked (smaller ones are solved at once) and stacked groups are
+// disjoint, so a bucket of n members never has more than n/65 entries; the
+// bucket starting at offset `start` of its stream keeps its stack in the
+// stream's stack region from entry start/16 on (n/16 >= n/65 + 2 entries
+// for n >= 65, and ranges of different buckets do not overlap).  A level
+// where every member has the same next symbol only drops the first member
+// if its history ends (t = level-1).  In record mode (streams of at most
+// 65536 positions, solved by the stream kernel itself) the bucket's members
+// other than the first (answered in slot `start`) fill slots start+1 ..
+// start+n-1 in completion order.
 __global__ __launch_bounds__(kBigThreads) void big_kernel(MatchParams p)
 {
     __shared__ int32_t bcnt[264];     // K+1 counts (digit K = drop)
     __shared__ int32_t bbase[264];    // running bases
     __shared__ int32_t bbase0[264];   // initial bases
-    const int K = p.K;
-    const int lane = threadIdx.x;
-    const uint64_t self = 1ull << lane;
-    const uint64_t below = self - 1;
-    const int T = p.T, d = p.d;
     const int count = min((int64_t)p.big[0], p.big_cap);
-
     for (int item = blockIdx.x; item < count; item += gridDim.x) {
         const int32_t *ent = p.big + 64 + 4 * (int64_t)item;
         const int s = ent[0], key = ent[1], start = ent[2], n0 = ent[3];
         const uint8_t *x = p.sym + (int64_t)s * p.Tp + kPadFront;
-        int32_t *buf0 = p.pos + (int64_t)s * T;
-        int32_t *buf1 = p.pos2 + (int64_t)s * T;
-        StreamOut o;
-        o.x = x;
-        o.E = p.E ? p.E + (int64_t)s * T : nullptr;
-        o.SYM = p.SYM ? p.SYM + (int64_t)s * T : nullptr;
-        o.L = p.L ? p.L + (int64_t)s * T : nullptr;
-        o.rec = p.rec ? p.rec + (int64_t)s * T : nullptr;
-        int4 *stk = p.stack + (int64_t)s * (T / 16 + 4) + start / 16;
-        const int stack_cap = n0 / 16;
-        int nrec = 0;   // records written so far (uniform)
-        // emits the answers of the lanes with `want`, compacting record slots
-        auto put = [&](bool want, int t, int e, int l) {
-            if (o.rec) {
-                const uint64_t m = ballot(want);
-                if (want)
-                    emit_record(o, start + 1 + nrec + __popcll(m & below), t, e, l);
-                nrec += __popcll(m);
-            } else if (want) {
-                emit(o, t, e, l);
-            }
-        };
-
-        // the bucket's positions in time order
-        {
-            int w = 0;
-            for (int t0 = d - 1; t0 < T; t0 += 64) {
-                const int t = t0 + lane;
-                const bool m = t < T && dgram_key(x, t, d, K) == key;
-                const uint64_t bm = ballot(m);
-                if (m)
-                    buf0[start + w + __popcll(bm & below)] = t;
-                w += __popcll(bm);
-            }
-        }
-        int sp = 0;
-        GroupRef cur = {start, n0, d, 0};
-        bool have = true;
-        while (have) {
-            const int32_t *X = cur.buf ? buf1 : buf0;
-            int32_t *Y = cur.buf ? buf0 : buf1;
-            if (cur.n <= 64) {
-                const bool hs = lane < cur.n;
-                const int t = hs ? X[cur.start + lane] : 0;
-                const uint64_t g = cur.n >= 64 ? ~0ull : ((1ull << cur.n) - 1);
-                const Found f = solve_wave<false>(x, p.nbits, t, hs ? g : self, cur.ell, hs);
-                put(hs && f.ok, t, f.e, f.l);
-            } else {
-                const int a = cur.start, n = cur.n, ell = cur.ell;
-                // uniform level?  reference symbol from the last member
-                const int tl = X[a + n - 1];
-                const int dref = x[tl - ell];
-                bool uni = true;
-                for (int i0 = 0; i0 < n; i0 += 64) {
-                    const int i = i0 + lane;
-                    bool bad = false;
-                    if (i < n) {
-                        const int t = X[a + i];
-                        bad = (t - ell >= 0) && x[t - ell] != dref;
-                    }
-                    if (ballot(bad)) {
-                        uni = false;
-                        break;
-                    }
-                }
-                if (uni) {
-                    const int t0 = X[a];
-                    if (t0 - ell < 0) {
-                        // the first member's history ends: the next member
-                        // loses its only predecessor at this level
-                        put(lane == 0, X[a + 1], t0, ell);
-                        cur.start = a + 1;
-                        cur.n = n - 1;
-                    }
-                    cur.ell = ell + 1;
-                    if (cur.n >= 2)
-                        continue;
-                } else {
-                    // stable partition by x[t-ell] into Y[a .. a+n)
-                    for (int q = lane; q <= K; q += 64)
-                        bcnt[q] = 0;
-                    __syncthreads();
-                    for (int i0 = 0; i0 < n; i0 += 64) {
-                        const int i = i0 + lane;
-                        if (i < n) {
-                            const int t = X[a + i];
-                            const int dg = (t - ell >= 0) ? x[t - ell] : K;
-                            atomicAdd(&bcnt[dg], 1);
-                        }
-                    }
-                    __syncthreads();
-                    if (lane == 0) {
-                        int acc = 0;
-                        for (int q = 0; q <= K; ++q) {
-                            bbase[q] = acc;
-                            bbase0[q] = acc;
-                            acc += bcnt[q];
-                        }
-                    }
-                    __syncthreads();
-                    for (int i0 = 0; i0 < n; i0 += 64) {
-                        const int i = i0 + lane;
-                        const bool hs = i < n;
-                        const int t = hs ? X[a + i] : 0;
-                        const int dg = hs ? ((t - ell >= 0) ? x[t - ell] : K) : K + 1;
-                        uint64_t eq = ballot(hs);
-                        for (int b = 0; b < 9; ++b) {
-                            const bool bit = (dg >> b) & 1;
-                            const uint64_t Bb = ballot(hs && bit);
-                            eq &= bit ? Bb : ~Bb;
-                        }
-                        const int rank = __popcll(eq & below);
-                        int dest = 0;
-                        if (hs)
-                            dest = bbase[dg] + rank;
-                        __syncthreads();
-                        if (hs && !(eq & ~(below | self)))   // last of its class
-                            bbase[dg] = dest + 1;
-                        __syncthreads();
-                        const bool moved = hs && dg < K;
-                        if (moved)
-                            Y[a + dest] = t;
-                        const bool fin = moved && dest == bbase0[dg] && i > 0;
-                        put(fin, t, fin ? X[a + i - 1] : 0, ell);
-                    }
-                    __syncthreads();
-                    // children: small ones solved now, large ones stacked;
-                    // continue with the smallest large child
-                    int best = -1, bestn = 0x7FFFFFFF;
-                    for (int q = 0; q < K; ++q) {
-                        const int c = bcnt[q];
-                        if (c < 2)
-                            continue;
-                        const int cs = a + bbase0[q];
-                        if (c <= 64) {
-                            const bool hs = lane < c;
-                            const int t = hs ? Y[cs + lane] : 0;
-                            const uint64_t g = c >= 64 ? ~0ull : ((1ull << c) - 1);
-                            const Found f = solve_wave<false>(x, p.nbits, t, hs ? g : self,
-                                                              ell + 1, hs);
-                            put(hs && f.ok, t, f.e, f.l);
-                        } else if (c < bestn) {
-                            if (best >= 0 && sp < stack_cap && lane == 0)
-                                stk[sp] = make_int4(a + bbase0[best], bcnt[best],
-                                                    ell + 1, cur.buf ^ 1);
-                            if (best >= 0 && sp < stack_cap)
-                                ++sp;
-                            best = q;
-                            bestn = c;
-                        } else if (sp < stack_cap) {
-                            if (lane == 0)
-                                stk[sp] = make_int4(cs, c, ell + 1, cur.buf ^ 1);
-                            ++sp;
-                        }
-                    }
-                    if (best >= 0) {
-                        cur = GroupRef{a + bbase0[best], bcnt[best], ell + 1,
-                                       cur.buf ^ 1};
-                        continue;
-                    }
-                }
-            }
-            if (sp > 0) {
-                __syncthreads();
-                const int4 e = stk[--sp];
-                cur = GroupRef{e.x, e.y, e.z, e.w};
-            } else {
-                have = false;
-            }
-        }
+        solve_big_bucket<false>(p, x, s, key, start, n0, bcnt, bbase, bbase0);
+        wave_sync();
     }
 }
 
@@ -1330,14 +1487,13 @@ __global__ __launch_bounds__(kBigThreads) void big_kernel(MatchParams p)
 // Nib (alphabets of at most 16 symbols, with Vec): the row is first staged
 // in the rest of the LDS as 4-bit symbols (32 KiB), so the SYM reads are
 // LDS reads instead of scattered byte loads.
-constexpr int kTauMax = 65536;
-constexpr int kNibBytes = kTauMax / 2;
-
-template <bool Vec, bool Nib>
+// TMAX: the longest stream the LDS arrays hold (65536, or 8192 for short
+// streams, whose workgroups then share a CU).
+template <bool Vec, bool Nib, int TMAX>
 __global__ __launch_bounds__(kStreamThreads) void unpermute_kernel(MatchParams p)
 {
-    __shared__ __align__(16) uint16_t tau[kTauMax];
-    __shared__ __align__(16) uint8_t nib[Nib ? kNibBytes : 16];
+    __shared__ __align__(16) uint16_t tau[TMAX];
+    __shared__ __align__(16) uint8_t nib[Nib ? TMAX / 2 : 16];
     const int s = blockIdx.x;
     const int tid = threadIdx.x, nt = blockDim.x;
     const int T = p.T;
@@ -1495,14 +1651,23 @@ __global__ __launch_bounds__(kStreamThreads) void unpermute_kernel(MatchParams p
                     }
                 }
                 if (nc == 0) {
-                    // more candidates than a record holds: the position's task
-                    // (in.x: first slot, in.y: size) kept its positions; every
-                    // earlier one is compared in full, one per lane
-                    const int32_t *tp = p.pos + (int64_t)s * T + in.x;
-                    const int e = lane < (int)in.y ? tp[lane] : T;
-                    if (e < t) {
-                        bc = lcs_from(t, e, 0);
-                        be = e;
+                    // more candidates than a record holds: a list of positions
+                    // (in.x: first slot, in.y: size, top bit: the second
+                    // buffer) that holds every earlier position that can be
+                    // the answer -- the position's task (at most 64), or its
+                    // group of a large bucket; every earlier one is compared
+                    // in full, one per lane
+                    const int nl = (int)(in.y & 0x7FFFFFFFu);
+                    const int32_t *tp = (in.y >> 31 ? p.pos2 : p.pos) + (int64_t)s * T + in.x;
+                    for (int i0 = 0; i0 < nl; i0 += 64) {
+                        const int e = i0 + lane < nl ? tp[i0 + lane] : T;
+                        if (e < t) {
+                            const int c = lcs_from(t, e, 0);
+                            if (c > bc || (c == bc && e > be)) {
+                                bc = c;
+                                be = e;
+                            }
+                        }
                     }
                     // the lexicographic maximum of (c, e) over the lanes
                     for (int o = 32; o >= 1; o >>= 1) {
@@ -1635,6 +1800,9 @@ hipError_t launch_stream(const MatchParams &p, int64_t S, hipStream_t st)
 
 hipError_t launch_big(const MatchParams &p, int grid, hipStream_t st)
 {
+    // streams of up to 65536 positions: the stream kernel solved its own
+    if (stream_uses_records(p.T))
+        return hipSuccess;
     hipLaunchKernelGGL(big_kernel, dim3((unsigned)grid), dim3(kBigThreads), 0,
                        st, p);
     return hipGetLastError();
@@ -1646,15 +1814,24 @@ hipError_t launch_unpermute(const MatchParams &p, int64_t S, hipStream_t st)
         return hipSuccess;
     const bool vec = (p.T & 3) == 0 && ((uintptr_t)p.E & 15) == 0 &&
                      ((uintptr_t)p.SYM & 7) == 0;
-    if (vec && p.K <= 16)
-        hipLaunchKernelGGL((unpermute_kernel<true, true>), dim3((unsigned)S),
-                           dim3(kStreamThreads), 0, st, p);
-    else if (vec)
-        hipLaunchKernelGGL((unpermute_kernel<true, false>), dim3((unsigned)S),
-                           dim3(kStreamThreads), 0, st, p);
+    const dim3 grid((unsigned)S), block(kStreamThreads);
+#define ROSA_LAUNCH_UNPERMUTE(TM)                                                   \
+    do {                                                                            \
+        if (vec && p.K <= 16)                                                       \
+            hipLaunchKernelGGL((unpermute_kernel<true, true, TM>), grid, block, 0,  \
+                               st, p);                                              \
+        else if (vec)                                                               \
+            hipLaunchKernelGGL((unpermute_kernel<true, false, TM>), grid, block, 0, \
+                               st, p);                                              \
+        else                                                                        \
+            hipLaunchKernelGGL((unpermute_kernel<false, false, TM>), grid, block,   \
+                               0, st, p);                                           \
+    } while (0)
+    if (p.T <= 8192)
+        ROSA_LAUNCH_UNPERMUTE(8192);
     else
-        hipLaunchKernelGGL((unpermute_kernel<false, false>), dim3((unsigned)S),
-                           dim3(kStreamThreads), 0, st, p);
+        ROSA_LAUNCH_UNPERMUTE(65536);
+#undef ROSA_LAUNCH_UNPERMUTE
     return hipGetLastError();
 }
 

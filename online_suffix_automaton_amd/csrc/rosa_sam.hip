@@ -12,23 +12,43 @@
 // that inherits the target's transitions, link and last end position); the
 // new state's suffix link is the longest suffix that occurred before: its
 // length is L and its last end position (read before the update) is E; then
-// every state on the new state's suffix path gets last = t.
+// every state on the new state's suffix path gets last = t.  A step costs
+// the length of that suffix path, which is short on varied streams but
+// grows with t on a constant or short-period stream (t+1 states).
+//
+// The prefix build (rosa_build) takes the prefix's outputs from the batch
+// retrieval kernels and appends the prefix without the last-end walks; the
+// last end of every state is then set in one pass: the last end of a state
+// is the largest end position in its suffix-link subtree, i.e. the latest
+// position whose prefix state (a non-clone state, created at that position
+// with length position + 1) lies in the subtree.  Visiting the non-clone
+// states from the latest position down, each walks up its suffix path
+// until it meets a state already set, so every state is written once: O(T)
+// per stream on any input.
 //
 // Layout in the caller's state buffer (all per stream, stream-major):
 //   flags    [64]   int32 (flags[0]: symbol >= K seen)
 //   meta     [S]    int2 {tail state, number of states}
-//   nodes    [S][Ncap] int4 {len, link, last, 0}, Ncap = max(2, 2*Tcap-1)
-//   next     [S][Ncap][K] int32 dense transition rows (-1 = none)
+//   states   [S][Ncap] records of RS bytes: node int4 {len, link, last,
+//            clone ? 1 : 0}, then the dense transition row int32 [K]
+//            (-1 = none); RS = 16 + 4K rounded up to 64 bytes (one 128-byte
+//            line at K = 16), Ncap = max(2, 2*Tcap-1)
 //   hist     [S][Hs] uint8 symbol history (SYM = hist[E+1])
+// A state's node and row share a record, so each state the append's chain
+// visits costs one cache line.  The states region (padded if needed) first
+// serves as the batch retrieval's workspace during rosa_build; the
+// automaton overwrites it after that (same stream, so in order).
 // One lane owns one stream, so every access to a stream's tables is ordered
 // by program order; lanes of a wave work on different streams.
 #include "rosa_internal.h"
+#include "rosa_sam_core.h"
 
 namespace rosa {
 
 struct SamLayout {
-    size_t flags, meta, nodes, next, hist, total;
-    int64_t Ncap, Hs;
+    size_t flags, meta, states, hist, total;
+    size_t ws_bytes;   // workspace of the prefix retrieval, from `states` on
+    int64_t Ncap, Hs, RS;
 };
 
 SamLayout sam_layout(int64_t S, int64_t K, int64_t Tcap)
@@ -39,8 +59,17 @@ SamLayout sam_layout(int64_t S, int64_t K, int64_t Tcap)
     size_t o = 0;
     l.flags = o;  o += 256;
     l.meta = o;   o = align_up(o + (size_t)S * 8, 256);
-    l.nodes = o;  o = align_up(o + (size_t)S * l.Ncap * 16, 256);
-    l.next = o;   o = align_up(o + (size_t)S * l.Ncap * K * 4, 256);
+    l.RS = (int64_t)align_up((size_t)(16 + 4 * K), 64);
+    l.states = o; o = align_up(o + (size_t)S * l.Ncap * l.RS, 256);
+    // the batch retrieval's workspace for any prefix length up to Tcap
+    // (record mode ends at 65536 positions, so its size can drop past it)
+    const int64_t Tr = Tcap < 65536 ? Tcap : 65536;
+    size_t ws = ws_layout(S, Tcap).total;
+    if (ws_layout(S, Tr).total > ws)
+        ws = ws_layout(S, Tr).total;
+    if (l.states + ws > o)
+        o = align_up(l.states + ws, 256);
+    l.ws_bytes = o - l.states;
     l.hist = o;   o = align_up(o + (size_t)S * l.Hs, 256);
     l.total = o;
     return l;
@@ -49,102 +78,30 @@ SamLayout sam_layout(int64_t S, int64_t K, int64_t Tcap)
 struct SamView {
     int32_t *flags;
     int2 *meta;
-    int4 *nodes;
-    int32_t *next;
+    int32_t *states;   // records of RSi ints
     uint8_t *hist;
-    int64_t Ncap, Hs;
+    int64_t Ncap, Hs, RSi;
     int32_t K;
 };
 
-struct SamStream {
-    int4 *nd;
-    int32_t *nx;
-    int K;
-    int tail, nst;
-};
-
-__device__ __forceinline__ int sam_new_state(SamStream &a, int len)
+// Stream s's automaton in the decode state (tail and size not set).
+__device__ __forceinline__ SamStream sam_stream(const SamView &v, int64_t s)
 {
-    const int v = a.nst++;
-    a.nd[v] = make_int4(len, -1, -1, 0);
-    int32_t *row = a.nx + (int64_t)v * a.K;
-    if ((a.K & 3) == 0) {
-        int4 *r4 = reinterpret_cast<int4 *>(row);
-        for (int c = 0; c < (a.K >> 2); ++c)
-            r4[c] = make_int4(-1, -1, -1, -1);
-    } else {
-        for (int c = 0; c < a.K; ++c)
-            row[c] = -1;
-    }
-    return v;
-}
-
-// Append symbol c; returns the new state.
-__device__ int sam_extend(SamStream &a, int c)
-{
-    const int K = a.K;
-    const int cur = sam_new_state(a, a.nd[a.tail].x + 1);
-    int p = a.tail;
-    while (p != -1 && a.nx[(int64_t)p * K + c] == -1) {
-        a.nx[(int64_t)p * K + c] = cur;
-        p = a.nd[p].y;
-    }
-    if (p == -1) {
-        a.nd[cur].y = 0;
-    } else {
-        const int q = a.nx[(int64_t)p * K + c];
-        const int4 nq = a.nd[q];
-        const int lp = a.nd[p].x;
-        if (lp + 1 == nq.x) {
-            a.nd[cur].y = q;
-        } else {
-            const int clone = a.nst++;
-            a.nd[clone] = make_int4(lp + 1, nq.y, nq.z, 0);
-            const int32_t *src = a.nx + (int64_t)q * K;
-            int32_t *dst = a.nx + (int64_t)clone * K;
-            if ((K & 3) == 0) {
-                const int4 *s4 = reinterpret_cast<const int4 *>(src);
-                int4 *d4 = reinterpret_cast<int4 *>(dst);
-                for (int k = 0; k < (K >> 2); ++k)
-                    d4[k] = s4[k];
-            } else {
-                for (int k = 0; k < K; ++k)
-                    dst[k] = src[k];
-            }
-            while (p != -1 && a.nx[(int64_t)p * K + c] == q) {
-                a.nx[(int64_t)p * K + c] = clone;
-                p = a.nd[p].y;
-            }
-            a.nd[q].y = clone;
-            a.nd[cur].y = clone;
-        }
-    }
-    a.tail = cur;
-    return cur;
-}
-
-// Match for position t after the extension, then the last-end update.
-__device__ __forceinline__ void sam_match(SamStream &a, int cur, int t,
-                                          int &E, int &L)
-{
-    const int v = a.nd[cur].y;
-    E = -1;
-    L = 0;
-    if (v > 0) {
-        const int4 nv = a.nd[v];
-        L = nv.x;
-        E = nv.z;
-    }
-    for (int u = cur; u != -1; u = a.nd[u].y)
-        a.nd[u].z = t;
+    SamStream a;
+    int32_t *rec = v.states + s * v.Ncap * v.RSi;
+    a.nd = reinterpret_cast<int4 *>(rec);
+    a.nds = v.RSi / 4;
+    a.nx = rec + 4;
+    a.nxs = v.RSi;
+    a.K = v.K;
+    a.tail = 0;
+    a.nst = 0;
+    return a;
 }
 
 __device__ __forceinline__ SamStream sam_open(const SamView &v, int64_t s)
 {
-    SamStream a;
-    a.nd = v.nodes + s * v.Ncap;
-    a.nx = v.next + s * v.Ncap * v.K;
-    a.K = v.K;
+    SamStream a = sam_stream(v, s);
     const int2 m = v.meta[s];
     a.tail = m.x;
     a.nst = m.y;
@@ -152,9 +109,10 @@ __device__ __forceinline__ SamStream sam_open(const SamView &v, int64_t s)
 }
 
 // Build over hist[s][0..T): one lane per stream, `spw` streams per wave.
-__global__ __launch_bounds__(64) void sam_build_kernel(
-    SamView v, int64_t S, int64_t T, int spw, int32_t *__restrict__ E,
-    int16_t *__restrict__ SYM, int32_t *__restrict__ L)
+// The appends run without last-end walks; then the last ends are set in one
+// pass over the states (see the top of this file).
+__global__ __launch_bounds__(64) void sam_build_kernel(SamView v, int64_t S,
+                                                       int64_t T, int spw)
 {
     const int lane = threadIdx.x;
     if (lane >= spw)
@@ -162,27 +120,12 @@ __global__ __launch_bounds__(64) void sam_build_kernel(
     const int64_t s = (int64_t)blockIdx.x * spw + lane;
     if (s >= S)
         return;
-    SamStream a;
-    a.nd = v.nodes + s * v.Ncap;
-    a.nx = v.next + s * v.Ncap * v.K;
-    a.K = v.K;
-    a.tail = 0;
-    a.nst = 0;
+    SamStream a = sam_stream(v, s);
     sam_new_state(a, 0);   // root: len 0, no link
     const uint8_t *h = v.hist + s * v.Hs;
-    for (int64_t t = 0; t < T; ++t) {
-        const int c = h[t];
-        const int cur = sam_extend(a, c);
-        int e, l;
-        sam_match(a, cur, (int)t, e, l);
-        if (E) {
-            E[s * T + t] = e;
-            if (L)
-                L[s * T + t] = l;
-            if (SYM)
-                SYM[s * T + t] = e >= 0 ? (int16_t)h[e + 1] : (int16_t)-1;
-        }
-    }
+    for (int64_t t = 0; t < T; ++t)
+        sam_extend(a, h[t]);
+    sam_fill_last(a);
     v.meta[s] = make_int2(a.tail, a.nst);
 }
 
@@ -286,7 +229,7 @@ __device__ __forceinline__ void qk_advance(const SamStream &a, int &s, int &l,
 {
     const int K = a.K;
     for (;;) {
-        const int nx = a.nx[(int64_t)s * K + c];
+        const int nx = a.row(s)[c];
         if (nx != -1) {
             s = nx;
             ++l;
@@ -296,8 +239,8 @@ __device__ __forceinline__ void qk_advance(const SamStream &a, int &s, int &l,
             l = 0;
             return;
         }
-        s = a.nd[s].y;
-        l = a.nd[s].x;
+        s = a.node(s).y;
+        l = a.node(s).x;
     }
 }
 
@@ -318,7 +261,9 @@ __global__ __launch_bounds__(64) void qk_kernel(QkParams p)
     const int64_t T = p.T;
     SamStream a;
     a.nd = p.nodes + s * p.Ncap;
+    a.nds = 1;
     a.nx = p.next + s * p.Ncap * p.K;
+    a.nxs = p.K;
     a.K = p.K;
     a.tail = 0;
     a.nst = 0;
@@ -342,7 +287,7 @@ __global__ __launch_bounds__(64) void qk_kernel(QkParams p)
             if (act) {
                 int s2 = ms, l2 = ml;
                 qk_advance(a, s2, l2, lane == 0 ? qc : (qc ^ (1 << (lane - 1))));
-                ue = l2 > 0 ? a.nd[s2].z : -1;
+                ue = l2 > 0 ? a.node(s2).z : -1;
                 ul = l2;
                 dstart = ue >= 0 ? st[ue + 1] : -1;
                 if (lane == 0) {
@@ -353,8 +298,8 @@ __global__ __launch_bounds__(64) void qk_kernel(QkParams p)
             __syncthreads();   // every read of this unit before the append
             if (lane == 0) {
                 const int cur = sam_extend(a, kc);
-                for (int w = cur; w != -1; w = a.nd[w].y)
-                    a.nd[w].z = u;
+                for (int w = cur; w != -1; w = a.node(w).y)
+                    a.node(w).z = u;
             }
             // every lane follows lane 0's matching state
             ms = __shfl(ms, 0);
@@ -669,11 +614,11 @@ SamView sam_view(void *buf, int64_t S, int64_t K, int64_t Tcap)
     SamView v;
     v.flags = reinterpret_cast<int32_t *>(base + l.flags);
     v.meta = reinterpret_cast<int2 *>(base + l.meta);
-    v.nodes = reinterpret_cast<int4 *>(base + l.nodes);
-    v.next = reinterpret_cast<int32_t *>(base + l.next);
+    v.states = reinterpret_cast<int32_t *>(base + l.states);
     v.hist = base ? reinterpret_cast<uint8_t *>(base + l.hist) : nullptr;
     v.Ncap = l.Ncap;
     v.Hs = l.Hs;
+    v.RSi = l.RS / 4;
     v.K = (int32_t)K;
     return v;
 }
@@ -717,15 +662,23 @@ hipError_t launch_clear_flags(int32_t *flags, hipStream_t st,
                               int32_t *flags2 = nullptr);
 
 hipError_t launch_sam_build(void *buf, int64_t S, int64_t K, int64_t Tcap,
-                            int64_t T, int32_t *E, int16_t *SYM, int32_t *L,
-                            hipStream_t st)
+                            int64_t T, hipStream_t st)
 {
     SamView v = sam_view(buf, S, K, Tcap);
     const int spw = kSamStreamsPerWave;
     dim3 grid((unsigned)((S + spw - 1) / spw));
-    hipLaunchKernelGGL(sam_build_kernel, grid, dim3(64), 0, st, v, S, T, spw,
-                       E, SYM, L);
+    hipLaunchKernelGGL(sam_build_kernel, grid, dim3(64), 0, st, v, S, T, spw);
     return hipGetLastError();
+}
+
+// The batch retrieval's workspace inside a state buffer (valid until the
+// automaton is built over it).
+void *sam_match_ws(void *buf, int64_t S, int64_t K, int64_t Tcap,
+                   size_t *bytes)
+{
+    const SamLayout l = sam_layout(S, K, Tcap);
+    *bytes = l.ws_bytes;
+    return reinterpret_cast<char *>(buf) + l.states;
 }
 
 hipError_t launch_sam_step(void *buf, int64_t S, int64_t K, int64_t Tcap,

@@ -110,6 +110,55 @@ def test_constant_and_periodic_long():
     _run_symbols(sym, 8, "constant/periodic 8192")
 
 
+def _closed_form_periodic(T, p):
+    """E, L of a stream of period p with p distinct symbols (the oracle's
+    closed form, pinned in tests/test_oracle.py): no match before t = p,
+    then the suffix of length t-p+1 ends at t-p; p = 1 is the constant
+    stream."""
+    t = np.arange(T)
+    E = np.where(t < p, -1, t - p).astype(np.int32)
+    L = np.where(t < p, 0, t - p + 1).astype(np.int32)
+    return E, L
+
+
+def test_low_entropy_streams_at_65536():
+    """Constant and periodic streams of 65,536 positions: one bucket holds
+    (nearly) the whole stream and stays uniform level after level; the
+    large-bucket solver defers such groups to the time-ordered pass (the
+    extension rule), so the call is O(T) per stream instead of O(T^2).
+    Checked against the closed forms; streams mixing constant stretches with
+    random ones against the oracle."""
+    T = 65536
+    rows, forms = [], []
+    for sym0, p in ((5, 1), (0, 1), (None, 3), (None, 7), (None, 2)):
+        x = synth.constant(T, sym0) if p == 1 else synth.periodic(T, list(range(p)))
+        rows.append(np.asarray(x, dtype=np.uint8))
+        forms.append(_closed_form_periodic(T, p))
+    x = np.stack(rows)
+    xd = _dev(x)
+    E, SYM, L, _ = rosa.match(xd, K=16)
+    torch.cuda.synchronize()
+    E, L, SYM = E.cpu().numpy(), L.cpu().numpy(), SYM.cpu().numpy()
+    for i, (Ef, Lf) in enumerate(forms):
+        assert np.array_equal(E[i], Ef), f"low-entropy stream {i}: E"
+        assert np.array_equal(L[i], Lf), f"low-entropy stream {i}: L"
+        want_sym = np.where(Ef >= 0, x[i][np.maximum(Ef, -1) + 1].astype(np.int16), -1)
+        assert np.array_equal(SYM[i], want_sym), f"low-entropy stream {i}: SYM"
+    # constant stretches inside random streams (the oracle's cost grows
+    # with the square of a constant stretch, so these stay moderate)
+    rng = np.random.default_rng(31)
+    mixed = []
+    for lo, hi in ((1000, 21000), (40000, 60000), (0, 15000)):
+        m = rng.integers(0, 16, T).astype(np.uint8)
+        m[lo:hi] = 9
+        mixed.append(m)
+    m = rng.integers(0, 16, T).astype(np.uint8)
+    m[5000:25000] = np.tile(np.array([1, 4, 1, 6], np.uint8), 5000)
+    mixed.append(m)
+    _say("mixed constant/periodic stretches T=65536")
+    _run_symbols(np.stack(mixed), 16, "low-entropy stretches 65536")
+
+
 def test_mixed_bucket_sizes():
     # some streams random, some low-entropy, in one call
     rng = np.random.default_rng(7)
