@@ -32,6 +32,7 @@ hipError_t launch_gather(const uint16_t *V, int64_t B, int64_t T, int64_t D,
 hipError_t launch_stream(const MatchParams &p, int64_t S, hipStream_t st);
 hipError_t launch_big(const MatchParams &p, int grid, hipStream_t st);
 hipError_t launch_unpermute(const MatchParams &p, int64_t S, hipStream_t st);
+bool stream_can_stage(int64_t T);
 // rosa_sam.hip
 size_t sam_total_bytes(int64_t S, int64_t K, int64_t Tcap);
 uint8_t *sam_hist_base(void *buf, int64_t S, int64_t K, int64_t Tcap,
@@ -266,6 +267,17 @@ static rosa_status match_impl(const rosa_input *in, const rosa_out *out,
         ROSA_TRY(launch_prep_symbols(reinterpret_cast<const uint8_t *>(in->data),
                                      sh.ld, sh.S, sh.T, sh.K, rows, w.Tp,
                                      out->symbols, flags, stream));
+    } else if (sh.M == 4 && sh.ld % 4 == 0 &&
+               (reinterpret_cast<uintptr_t>(in->data) & 7) == 0 &&
+               stream_can_stage(sh.T)) {
+        // short streams: the stream kernel reads its symbols from the rows
+        // itself (and clears the flags); no discretisation launch
+        p.stage = 1;
+        p.R = (int32_t)sh.R;
+        p.H = reinterpret_cast<const uint16_t *>(in->data);
+        p.Hld = sh.ld;
+        p.sym_copy = out->symbols;
+        p.flags = flags;
     } else {
         ROSA_TRY(launch_discretize(reinterpret_cast<const uint16_t *>(in->data),
                                    sh.B, sh.T, sh.D, sh.ld, sh.M, rows, w.Tp,

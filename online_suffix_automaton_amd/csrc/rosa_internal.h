@@ -66,6 +66,15 @@ struct MatchParams {
     const uint8_t *sym;  // padded rows: stream s at sym + s*Tp + kPadFront
     int64_t Tp;
     int32_t T, K, d, NB, nbits, fl_total;
+    int32_t fuse;               // the stream kernel runs the time-ordered pass itself
+    // stage: the stream kernel reads its symbols straight from bf16 hidden
+    // states H [B][T][Hld] (M = 4, route r of batch row b = stream b*R + r),
+    // writes the optional symbol copy and clears the flags itself
+    int32_t stage, R;
+    const uint16_t *H;
+    int64_t Hld;
+    uint8_t *sym_copy;          // [S][T] or null
+    int32_t *flags;
     int32_t pw[kMaxD + 1];      // K^i
     int32_t fl_off[kMaxD + 1];  // first-occurrence table offset of level l
     int32_t *pos;               // [S][T] bucket-ordered positions
@@ -81,6 +90,13 @@ struct MatchParams {
     int16_t *SYM;               // [S][T] or null
     int32_t *L;                 // [S][T] or null
 };
+
+// I[h > 0] on a bf16 bit pattern, as an integer range test: the positive
+// non-NaN patterns are exactly 0x0001 (smallest subnormal) .. 0x7F80 (+inf).
+__device__ __forceinline__ uint32_t bf16_is_pos(uint32_t h)
+{
+    return (h - 1u) < 0x7F80u ? 1u : 0u;
+}
 
 // Choice of the bucketing depth d for alphabet K and stream length T: the
 // largest d with K^d <= min(4096, T/8) (about 8+ positions per bucket on

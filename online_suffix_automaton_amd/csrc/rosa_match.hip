@@ -883,17 +883,57 @@ __device__ __forceinline__ void wave_sync() { __builtin_amdgcn_wave_barrier(); }
 // members from bucket slot `start` on (x: the stream's padded symbol row;
 // bcnt, bbase, bbase0: the wave's own LDS arrays of at least K + 2 ints).
 //
-// DEFER (record mode): a group of more than 64 members that stays uniform
-// (every member followed by the same symbol) for kBigDeferLevels levels in
-// a row -- constant or periodic stretches, where refining level by level
-// would cost O(T) levels of O(n) work -- is not refined further.  Its
-// members other than the first are deferred to the time-ordered pass of
-// unpermute_kernel, like the long repeats of solve_wave's CAP mode: each
-// gets a placeholder record, its bit in the deferred bitmap and a record
-// pointing at the group's position list (slot a, n members, buffer), which
-// holds every earlier position sharing its reversed level-gram, so the
-// list is complete for the fallback of the extension rule there.
-constexpr int kBigDeferLevels = 2;
+// DEFER (record mode): a group of more than 64 members whose members all
+// agree on the next kBigDeferLevels symbols (one pass comparing each
+// member's window of that many symbols with the last member's) -- constant
+// or periodic stretches, where refining level by level would cost O(T)
+// levels of O(n) work -- is not refined further.  Its members other than
+// the first are deferred to the time-ordered pass of unpermute_kernel, like
+// the long repeats of solve_wave's CAP mode: each gets a placeholder
+// record, its bit in the deferred bitmap and a record pointing at the
+// group's position list (slot a, n members, buffer), which holds every
+// earlier position sharing its reversed level-gram, so the list is
+// complete for the fallback of the extension rule there.  (A group that
+// is uniform for fewer levels, e.g. a periodic stream with a disturbance,
+// is refined level by level: the fallback would compare with every member
+// once per period.)
+constexpr int kBigDeferLevels = 8;
+
+// Whether the n members (positions X[0 .. n), in time order) of a group at
+// level ell agree for the next kBigDeferLevels (= 8) levels: member t's
+// symbols x[t-ell-7 .. t-ell] against the last member's (the longest
+// history), one 8-byte window per member, 256 members per round.  Symbols
+// before position 0 do not exist: a member compares only the symbols of its
+// own history, as a level step treats a member whose history has ended as
+// agreeing (such members are the group's first ones, which the level steps
+// would drop one by one).  Every member has t >= ell - 1, so the window
+// reads stay inside the row's zero padding.
+__device__ bool big_group_uniform(const int32_t *X, int n, const uint8_t *x, int ell)
+{
+    static_assert(kBigDeferLevels == 8, "one 8-symbol window per member");
+    const int lane = __lane_id();
+    const uint64_t ref = load8_end(x, X[n - 1] - ell);
+    for (int i0 = 0; i0 < n; i0 += 256) {
+        int tt[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + 64 * u + lane;
+            tt[u] = i < n ? X[i] : -1;
+        }
+        bool bad = false;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int v = tt[u] - ell + 1;   // symbols of the member's history in the window
+            if (tt[u] >= 0 && v > 0) {
+                const uint64_t m = v >= 8 ? ~0ull : ~0ull << (8 * (8 - v));
+                bad = bad || ((load8_end(x, tt[u] - ell) ^ ref) & m) != 0;
+            }
+        }
+        if (ballot(bad))
+            return false;
+    }
+    return true;
+}
 
 template <bool DEFER>
 __device__ void solve_big_bucket(const MatchParams &p, const uint8_t *x, int s,
@@ -950,17 +990,57 @@ __device__ void solve_big_bucket(const MatchParams &p, const uint8_t *x, int s,
     }
     int sp = 0;
     GroupRef cur = {start, n0, d, 0};
-    int uni_run = 0;   // uniform levels in a row of the current group
+    // after a failed window check, the next one waits kBigDeferLevels
+    // levels (groups that split at every few levels pay it once per 8)
+    int next_wcheck = 0;
     bool have = true;
     while (have) {
         const int32_t *X = cur.buf ? buf1 : buf0;
         int32_t *Y = cur.buf ? buf0 : buf1;
+        bool defer_now = false;
+        if (DEFER && cur.n > 64 && cur.ell >= next_wcheck) {
+            defer_now = big_group_uniform(X + cur.start, cur.n, x, cur.ell);
+            if (!defer_now)
+                next_wcheck = cur.ell + kBigDeferLevels;
+        }
         if (cur.n <= 64) {
             const bool hs = lane < cur.n;
             const int t = hs ? X[cur.start + lane] : 0;
             const uint64_t g = cur.n >= 64 ? ~0ull : ((1ull << cur.n) - 1);
             const Found f = solve_wave<false>(x, p.nbits, t, hs ? g : self, cur.ell, hs);
             put(hs && f.ok, t, f.e, f.l);
+        } else if (defer_now) {
+            // members 1 .. n-1 deferred (see above): whatever answers the
+            // level steps would give the first members as they drop, the
+            // group's list holds every candidate of every member
+            const int ga = cur.start, gn = cur.n;
+            uint32_t *deepbits = p.deep + (int64_t)s * deep_words(T);
+            uint4 *dinfo = p.dinfo + (int64_t)s * T;
+            const uint32_t lb = (uint32_t)min(cur.ell + kBigDeferLevels, 8191);
+            const uint4 drec = make_uint4((uint32_t)ga,
+                                          (uint32_t)gn | ((uint32_t)cur.buf << 31),
+                                          0u, (lb << 3) << 16);
+            // 256 members per round, a lane's four position loads in flight
+            for (int i0 = 1; i0 < gn; i0 += 256) {
+                int tt[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int i = i0 + 64 * u + lane;
+                    tt[u] = i < gn ? X[ga + i] : -1;
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const bool hs = tt[u] >= 0;
+                    const uint64_t m = ballot(hs);
+                    if (hs) {
+                        const int t = tt[u];
+                        o.rec[start + 1 + nrec + __popcll(m & below)] = (uint32_t)t << 16;
+                        atomicOr(&deepbits[t >> 5], 1u << (t & 31));
+                        dinfo[t] = drec;
+                    }
+                    nrec += __popcll(m);
+                }
+            }
         } else {
             const int a = cur.start, n = cur.n, ell = cur.ell;
             // uniform level?  reference symbol from the last member
@@ -994,32 +1074,9 @@ __device__ void solve_big_bucket(const MatchParams &p, const uint8_t *x, int s,
                     cur.n = n - 1;
                 }
                 cur.ell = ell + 1;
-                ++uni_run;
-                if (DEFER && uni_run >= kBigDeferLevels && cur.n > 64) {
-                    // defer members 1 .. n-1 of the group (see above)
-                    const int ga = cur.start, gn = cur.n;
-                    uint32_t *deepbits = p.deep + (int64_t)s * deep_words(T);
-                    uint4 *dinfo = p.dinfo + (int64_t)s * T;
-                    const uint32_t lb = (uint32_t)min(cur.ell, 8191);
-                    for (int i0 = 1; i0 < gn; i0 += 64) {
-                        const int i = i0 + lane;
-                        const bool hs = i < gn;
-                        const uint64_t m = ballot(hs);
-                        if (hs) {
-                            const int t = X[ga + i];
-                            o.rec[start + 1 + nrec + __popcll(m & below)] = (uint32_t)t << 16;
-                            atomicOr(&deepbits[t >> 5], 1u << (t & 31));
-                            dinfo[t] = make_uint4((uint32_t)ga,
-                                                  (uint32_t)gn | ((uint32_t)cur.buf << 31),
-                                                  0u, (lb << 3) << 16);
-                        }
-                        nrec += __popcll(m);
-                    }
-                } else if (cur.n >= 2) {
+                if (cur.n >= 2)
                     continue;
-                }
             } else {
-                uni_run = 0;
                 // stable partition by x[t-ell] into Y[a .. a+n)
                 for (int q = lane; q <= K; q += 64)
                     bcnt[q] = 0;
@@ -1100,7 +1157,6 @@ __device__ void solve_big_bucket(const MatchParams &p, const uint8_t *x, int s,
                 if (best >= 0) {
                     cur = GroupRef{a + bbase0[best], bcnt[best], ell + 1,
                                    cur.buf ^ 1};
-                    uni_run = 0;
                     continue;
                 }
             }
@@ -1113,11 +1169,27 @@ __device__ void solve_big_bucket(const MatchParams &p, const uint8_t *x, int s,
             wave_sync();
             const int4 e = stk[--sp];
             cur = GroupRef{e.x, e.y, e.z, e.w};
-            uni_run = 0;
         } else {
             have = false;
         }
     }
+}
+
+template <bool Vec, bool Nib>
+__device__ void unpermute_stream(const MatchParams &p, int s, uint16_t *tau,
+                                 uint8_t *nib, const uint8_t *x);
+
+// The stream a workgroup of the stream kernel takes.  Workgroup i runs on
+// XCD i % 8; with S a multiple of 128, the 16 consecutive streams of a
+// route group (the routes whose channels share a 128-byte line of a hidden
+// row) go to workgroups of one XCD, so when they read their symbols from
+// the rows themselves each line is fetched into one L2.
+__device__ __forceinline__ int stream_of_block(int b, int S)
+{
+    if (S % 128 != 0)
+        return b;
+    const int x = b & 7, j = b >> 3;
+    return ((j >> 4) * 8 + x) * 16 + (j & 15);
 }
 
 // ------------------------------------------------- stream kernel (LDS)
@@ -1166,9 +1238,11 @@ struct LdsCfg {
 using CfgLarge = LdsCfg<65536, 1024,
                         163840 - 65792 - (kMaxBuckets + 16) * 2 - kMaxBuckets * 2 - 128 -
                             16 * 16 * 8>;
-// Streams of up to 8192 positions: 42 KiB per 1024-thread workgroup, so two
-// workgroups (32 waves) share a CU and 512 streams run in one round.
-using CfgSmall = LdsCfg<8192, 1024, 28672, 2>;
+// Streams of up to 8192 positions: 42 KiB per 512-thread workgroup; two
+// workgroups per CU run 512 streams in one round, with the register budget
+// of four waves per SIMD (the large-bucket and time-ordered passes at the
+// end of the kernel need it).
+using CfgSmall = LdsCfg<8192, 512, 28672, 2>;
 
 // DC: the bucketing depth d as a compile-time constant (1..4), or 0 to read
 // it from p.
@@ -1199,19 +1273,54 @@ void stream_kernel_lds(MatchParams p)
     uint32_t *cur2 = reinterpret_cast<uint32_t *>(U);
     uint8_t *passid = U + Cfg::kUPassId;
     uint16_t *lpos = reinterpret_cast<uint16_t *>(U + Cfg::kULpos);
-    uint32_t *tasks = p.tasks + (int64_t)blockIdx.x * kTaskCap;
+    const int s = stream_of_block(blockIdx.x, gridDim.x);
+    uint32_t *tasks = p.tasks + (int64_t)s * kTaskCap;
     // positions whose answers are deferred (long repeats): one bit each,
     // and their candidates
-    uint32_t *deepbits = p.deep + (int64_t)blockIdx.x * deep_words(p.T);
-    uint4 *dinfo = p.dinfo + (int64_t)blockIdx.x * p.T;
-    int32_t *posrow = p.pos + (int64_t)blockIdx.x * p.T;
+    uint32_t *deepbits = p.deep + (int64_t)s * deep_words(p.T);
+    uint4 *dinfo = p.dinfo + (int64_t)s * p.T;
+    int32_t *posrow = p.pos + (int64_t)s * p.T;
 
-    const int s = blockIdx.x;
     const int tid = threadIdx.x, nt = blockDim.x;
     const int lane = tid & 63, wid = tid >> 6, nw = nt >> 6;
     const int T = p.T, K = p.K, d = DC > 0 ? DC : p.d, NB = p.NB;
     uint64_t *eqw = p.nbits <= 4 ? eqtab[wid] : nullptr;
-    {
+    if (p.stage) {
+        // the padding, then the symbols straight from the bf16 rows: route
+        // r packs channels 4r .. 4r+3 (one 8-byte load per position), bit j
+        // = I[h > 0] of channel 4r+j (Sec. 3.2, Eq. (10)-(15)); eight loads
+        // of a thread in flight at once
+        if (s == 0 && tid < 64)
+            p.flags[tid] = 0;
+        for (int i = tid; i < kPadFront; i += nt)
+            symrow[i] = 0;
+        for (int i = kPadFront + T + tid; i < Cfg::kSymBytes; i += nt)
+            symrow[i] = 0;
+        const int64_t b = s / p.R, r = s % p.R;
+        const uint16_t *h = p.H + b * (int64_t)T * p.Hld + r * 4;
+        for (int t0 = tid; t0 < T; t0 += 8 * nt) {
+            uint2 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int t = t0 + u * nt;
+                v[u] = t < T ? *reinterpret_cast<const uint2 *>(h + (int64_t)t * p.Hld)
+                             : make_uint2(0u, 0u);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int t = t0 + u * nt;
+                if (t < T) {
+                    const uint8_t c = (uint8_t)(bf16_is_pos(v[u].x & 0xFFFFu) |
+                                                (bf16_is_pos(v[u].x >> 16) << 1) |
+                                                (bf16_is_pos(v[u].y & 0xFFFFu) << 2) |
+                                                (bf16_is_pos(v[u].y >> 16) << 3));
+                    symrow[kPadFront + t] = c;
+                    if (p.sym_copy)
+                        p.sym_copy[(int64_t)s * T + t] = c;
+                }
+            }
+        }
+    } else {
         const uint4 *src = reinterpret_cast<const uint4 *>(p.sym + (int64_t)s * p.Tp);
         uint4 *dst = reinterpret_cast<uint4 *>(symrow);
         for (int i = tid; i < (int)(p.Tp >> 4); i += nt)
@@ -1378,6 +1487,22 @@ void stream_kernel_lds(MatchParams p)
             }
         }
     }
+    // streams whose u16 destinations fit the union (fuse, set by the
+    // launcher): the time-ordered pass here, on this workgroup's records
+    // (still in cache) and its LDS copy of the symbols, instead of a launch
+    // of unpermute_kernel
+    if (p.fuse) {
+        // the records were stored by this workgroup's waves; the barrier
+        // (a workgroup-scope fence) makes them visible to all of them
+        __syncthreads();
+        uint16_t *tau = reinterpret_cast<uint16_t *>(U);
+        const bool vec = (T & 3) == 0 && ((uintptr_t)p.E & 15) == 0 &&
+                         ((uintptr_t)p.SYM & 7) == 0;
+        if (vec)
+            unpermute_stream<true, false>(p, s, tau, nullptr, x);
+        else
+            unpermute_stream<false, false>(p, s, tau, nullptr, x);
+    }
 }
 
 // ---------------------------------------------- stream kernel (HBM rows)
@@ -1489,12 +1614,14 @@ __global__ __launch_bounds__(kBigThreads) void big_kernel(MatchParams p)
 // LDS reads instead of scattered byte loads.
 // TMAX: the longest stream the LDS arrays hold (65536, or 8192 for short
 // streams, whose workgroups then share a CU).
-template <bool Vec, bool Nib, int TMAX>
-__global__ __launch_bounds__(kStreamThreads) void unpermute_kernel(MatchParams p)
+// The time-ordered pass of stream s, by one workgroup: `tau` holds T u16
+// in LDS, `nib` (Nib) T/2 bytes of LDS for the 4-bit copy of the symbols,
+// `x` the stream's padded symbol row (device memory, or the stream
+// kernel's LDS copy when it runs this pass itself).
+template <bool Vec, bool Nib>
+__device__ void unpermute_stream(const MatchParams &p, int s, uint16_t *tau,
+                                 uint8_t *nib, const uint8_t *x)
 {
-    __shared__ __align__(16) uint16_t tau[TMAX];
-    __shared__ __align__(16) uint8_t nib[Nib ? TMAX / 2 : 16];
-    const int s = blockIdx.x;
     const int tid = threadIdx.x, nt = blockDim.x;
     const int T = p.T;
     const uint32_t *rec = p.rec + (int64_t)s * T;
@@ -1503,7 +1630,6 @@ __global__ __launch_bounds__(kStreamThreads) void unpermute_kernel(MatchParams p
     // every record names a position t < T <= 65536 (16-bit field), so the
     // scatter stays inside tau; tau <= T-1 for every record, the clamp
     // below only keeps the symbol read inside the row
-    const uint8_t *x = p.sym + (int64_t)s * p.Tp + kPadFront;
     if (Vec) {
         // four 16-byte loads in flight per thread before the LDS scatter
         const uint4 *r4 = reinterpret_cast<const uint4 *>(rec);
@@ -1766,12 +1892,41 @@ __global__ __launch_bounds__(kStreamThreads) void unpermute_kernel(MatchParams p
     }
 }
 
+template <bool Vec, bool Nib, int TMAX>
+__global__ __launch_bounds__(kStreamThreads) void unpermute_kernel(MatchParams p)
+{
+    __shared__ __align__(16) uint16_t tau[TMAX];
+    __shared__ __align__(16) uint8_t nib[Nib ? TMAX / 2 : 16];
+    const int s = blockIdx.x;
+    unpermute_stream<Vec, Nib>(p, s, tau, nib, p.sym + (int64_t)s * p.Tp + kPadFront);
+}
+
 // --------------------------------------------------------------- launchers
 
 bool stream_uses_records(int64_t T) { return T <= 65536; }
 
-hipError_t launch_stream(const MatchParams &p, int64_t S, hipStream_t st)
+// Whether the stream kernel runs the time-ordered pass itself: its u16
+// destinations must fit the union of the LDS plan that takes the stream.
+bool stream_fuses_unpermute(int64_t T)
 {
+    if (!stream_uses_records(T))
+        return false;
+    const int64_t uni = T <= CfgSmall::kTMax ? CfgSmall::kUnion : CfgLarge::kUnion;
+    return 2 * T <= uni;
+}
+
+// Whether the stream kernel can read bf16 symbols itself (stage): streams
+// of the small LDS plan, which also runs the time-ordered pass itself (no
+// later kernel reads the padded symbol rows).
+bool stream_can_stage(int64_t T)
+{
+    return T <= CfgSmall::kTMax && stream_fuses_unpermute(T);
+}
+
+hipError_t launch_stream(const MatchParams &p_in, int64_t S, hipStream_t st)
+{
+    MatchParams p = p_in;
+    p.fuse = stream_fuses_unpermute(p.T) ? 1 : 0;
     if (stream_uses_records(p.T)) {
         const bool small = p.T <= CfgSmall::kTMax;
         const dim3 grid((unsigned)S);
@@ -1810,7 +1965,7 @@ hipError_t launch_big(const MatchParams &p, int grid, hipStream_t st)
 
 hipError_t launch_unpermute(const MatchParams &p, int64_t S, hipStream_t st)
 {
-    if (!stream_uses_records(p.T))
+    if (!stream_uses_records(p.T) || stream_fuses_unpermute(p.T))
         return hipSuccess;
     const bool vec = (p.T & 3) == 0 && ((uintptr_t)p.E & 15) == 0 &&
                      ((uintptr_t)p.SYM & 7) == 0;

@@ -28,7 +28,8 @@
 //
 // Layout in the caller's state buffer (all per stream, stream-major):
 //   flags    [64]   int32 (flags[0]: symbol >= K seen)
-//   meta     [S]    int2 {tail state, number of states}
+//   meta     [S]    int4 {tail state, number of states, tail length,
+//                         tail suffix link}
 //   states   [S][Ncap] records of RS bytes: node int4 {len, link, last,
 //            clone ? 1 : 0}, then the dense transition row int32 [K]
 //            (-1 = none); RS = 16 + 4K rounded up to 64 bytes (one 128-byte
@@ -58,7 +59,7 @@ SamLayout sam_layout(int64_t S, int64_t K, int64_t Tcap)
     l.Hs = (int64_t)align_up((size_t)Tcap + 16, 16);
     size_t o = 0;
     l.flags = o;  o += 256;
-    l.meta = o;   o = align_up(o + (size_t)S * 8, 256);
+    l.meta = o;   o = align_up(o + (size_t)S * 16, 256);
     l.RS = (int64_t)align_up((size_t)(16 + 4 * K), 64);
     l.states = o; o = align_up(o + (size_t)S * l.Ncap * l.RS, 256);
     // the batch retrieval's workspace for any prefix length up to Tcap
@@ -77,7 +78,7 @@ SamLayout sam_layout(int64_t S, int64_t K, int64_t Tcap)
 
 struct SamView {
     int32_t *flags;
-    int2 *meta;
+    int4 *meta;
     int32_t *states;   // records of RSi ints
     uint8_t *hist;
     int64_t Ncap, Hs, RSi;
@@ -96,15 +97,19 @@ __device__ __forceinline__ SamStream sam_stream(const SamView &v, int64_t s)
     a.K = v.K;
     a.tail = 0;
     a.nst = 0;
+    a.tail_len = 0;
+    a.tail_link = -1;
     return a;
 }
 
 __device__ __forceinline__ SamStream sam_open(const SamView &v, int64_t s)
 {
     SamStream a = sam_stream(v, s);
-    const int2 m = v.meta[s];
+    const int4 m = v.meta[s];
     a.tail = m.x;
     a.nst = m.y;
+    a.tail_len = m.z;
+    a.tail_link = m.w;
     return a;
 }
 
@@ -126,7 +131,7 @@ __global__ __launch_bounds__(64) void sam_build_kernel(SamView v, int64_t S,
     for (int64_t t = 0; t < T; ++t)
         sam_extend(a, h[t]);
     sam_fill_last(a);
-    v.meta[s] = make_int2(a.tail, a.nst);
+    v.meta[s] = make_int4(a.tail, a.nst, a.tail_len, a.tail_link);
 }
 
 // Validate/clamp symbols of a SYMBOLS prefix into the history rows.
@@ -188,7 +193,7 @@ __global__ __launch_bounds__(64) void sam_step_kernel(
     const int cur = sam_extend(a, c);
     int e, l;
     sam_match(a, cur, (int)t, e, l);
-    v.meta[s] = make_int2(a.tail, a.nst);
+    v.meta[s] = make_int4(a.tail, a.nst, a.tail_len, a.tail_link);
     end[s] = e;
     if (sym)
         sym[s] = e >= 0 ? (int16_t)h[e + 1] : (int16_t)-1;
@@ -267,6 +272,8 @@ __global__ __launch_bounds__(64) void qk_kernel(QkParams p)
     a.K = p.K;
     a.tail = 0;
     a.nst = 0;
+    a.tail_len = 0;
+    a.tail_link = -1;
     if (lane == 0)
         sam_new_state(a, 0);
     a.nst = 1;
@@ -613,7 +620,7 @@ SamView sam_view(void *buf, int64_t S, int64_t K, int64_t Tcap)
     char *base = reinterpret_cast<char *>(buf);
     SamView v;
     v.flags = reinterpret_cast<int32_t *>(base + l.flags);
-    v.meta = reinterpret_cast<int2 *>(base + l.meta);
+    v.meta = reinterpret_cast<int4 *>(base + l.meta);
     v.states = reinterpret_cast<int32_t *>(base + l.states);
     v.hist = base ? reinterpret_cast<uint8_t *>(base + l.hist) : nullptr;
     v.Ncap = l.Ncap;

@@ -22,6 +22,7 @@ struct SamStream {
     int64_t nds, nxs;
     int K;
     int tail, nst;
+    int tail_len, tail_link;   // the tail state's length and suffix link
     __host__ __device__ int4 &node(int v) const { return nd[(int64_t)v * nds]; }
     __host__ __device__ int32_t *row(int v) const { return nx + (int64_t)v * nxs; }
 };
@@ -42,36 +43,37 @@ __host__ __device__ inline int sam_new_state(SamStream &a, int len)
     return v;
 }
 
-// Append symbol c; returns the new state.
+// Append symbol c; returns the new state.  The tail (the newest state) has
+// no transition yet, so its row needs no read; its length and link are
+// kept in the stream's registers rather than read back.
 __host__ __device__ inline int sam_extend(SamStream &a, int c)
 {
-    const int K = a.K;
-    const int cur = sam_new_state(a, a.node(a.tail).x + 1);
-    int p = a.tail;
+    const int cur = sam_new_state(a, a.tail_len + 1);
+    a.row(a.tail)[c] = cur;
+    int p = a.tail_link;
     while (p != -1 && a.row(p)[c] == -1) {
         a.row(p)[c] = cur;
         p = a.node(p).y;
     }
-    if (p == -1) {
-        a.node(cur).y = 0;
-    } else {
+    int lk = 0;
+    if (p != -1) {
         const int q = a.row(p)[c];
         const int4 nq = a.node(q);
         const int lp = a.node(p).x;
         if (lp + 1 == nq.x) {
-            a.node(cur).y = q;
+            lk = q;
         } else {
             const int clone = a.nst++;
             a.node(clone) = make_int4(lp + 1, nq.y, nq.z, 1);
             const int32_t *src = a.row(q);
             int32_t *dst = a.row(clone);
-            if ((K & 3) == 0) {
+            if ((a.K & 3) == 0) {
                 const int4 *s4 = reinterpret_cast<const int4 *>(src);
                 int4 *d4 = reinterpret_cast<int4 *>(dst);
-                for (int k = 0; k < (K >> 2); ++k)
+                for (int k = 0; k < (a.K >> 2); ++k)
                     d4[k] = s4[k];
             } else {
-                for (int k = 0; k < K; ++k)
+                for (int k = 0; k < a.K; ++k)
                     dst[k] = src[k];
             }
             while (p != -1 && a.row(p)[c] == q) {
@@ -79,10 +81,13 @@ __host__ __device__ inline int sam_extend(SamStream &a, int c)
                 p = a.node(p).y;
             }
             a.node(q).y = clone;
-            a.node(cur).y = clone;
+            lk = clone;
         }
     }
+    a.node(cur).y = lk;
     a.tail = cur;
+    a.tail_len += 1;
+    a.tail_link = lk;
     return cur;
 }
 

@@ -36,6 +36,8 @@ int main(int argc, char **argv)
     a.K = K;
     a.tail = 0;
     a.nst = 0;
+    a.tail_len = 0;
+    a.tail_link = -1;
     rosa::sam_new_state(a, 0);
     for (long t = 0; t < T0; ++t)
         rosa::sam_extend(a, x[(size_t)t]);
