@@ -432,12 +432,15 @@ def run_decode(args):
 # ---------------------------------------------------------------------- qk
 
 def run_qk(args):
-    """Query/key retrieval on the batched shape: separate query and key
-    hidden states [8, 4096, 256] bf16, M = 4 (512 streams, K = 16)."""
+    """Query/key retrieval: separate query and key hidden states
+    [B, T, 256] bf16, M = 4 (K = 16), B = 8 at the batched shape T = 4096
+    (512 streams) and B = 32768 / T past it (64 streams of 65536 at
+    T = 65536)."""
     import torch
     from online_suffix_automaton_amd import rosa, synth
     dev = torch.device("cuda:0")
-    B, T, D, M = 8, 4096, 256, 4
+    T, D, M = args.T, 256, 4
+    B = 8 if T <= 4096 else max(1, 32768 // T)
     S, K = B * (D // M), 1 << M
     _log("workload qk: generating")
     Hq = synth.bf16_normal((B, T, D), 31)
@@ -460,7 +463,7 @@ def run_qk(args):
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    steps = max(1, min(args.steps, 5))
+    steps = max(1, min(args.steps, 20))
     _log(f"timing {steps} steps")
     e0.record()
     for _ in range(steps):
@@ -502,13 +505,13 @@ def run_qk(args):
                          f"{' and counterfactual tables' if args.cf else ''}, "
                          f"streams split over {threads} threads"}
     return {
-        "metric": "query/key matched positions/sec (512 streams x 4096)",
+        "metric": f"query/key matched positions/sec ({S} streams x {T})",
         "value": S * T / (ms / 1e3), "unit": "positions/s", "n_gpus": 1,
         "steps": steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "u8", "data": "synthetic",
-        "config": {"workload": "qk: query and key hidden states [8,4096,256] "
-                               "bf16 N(0,1) (seeds 31, 32), M=4 -> 512 streams, "
+        "config": {"workload": f"qk: query and key hidden states [{B},{T},256] "
+                               f"bf16 N(0,1) (seeds 31, 32), M=4 -> {S} streams, "
                                "K=16" + (", key runs folded" if args.rle else "")
                                + (", counterfactual tables" if args.cf else ""),
                    "streams": S, "T": T, "K": K, "parallelism": "single GPU"},
@@ -611,6 +614,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the oracle baseline and parity check")
     ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--T", type=int, default=4096,
+                    help="qk workload: steps per stream (B = 8 at 4096, "
+                         "32768 / T streams of 256 channels past it)")
     ap.add_argument("--theta-pad", type=int, default=32, metavar="ELEMS",
                     help="scatter workload: theta rows stored at a pitch of D + "
                          "ELEMS floats (0: dense rows)")

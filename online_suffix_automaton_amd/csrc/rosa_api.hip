@@ -454,6 +454,14 @@ rosa_status rosa_match_qk(const rosa_input *q, const rosa_input *k,
     p.next = reinterpret_cast<int32_t *>(base + l.next);
     p.start = reinterpret_cast<int32_t *>(base + l.start);
     p.redo = reinterpret_cast<int32_t *>(base + l.redo);
+    p.qu = reinterpret_cast<uint8_t *>(base + l.qu);
+    p.ku = reinterpret_cast<uint8_t *>(base + l.ku);
+    p.nunit = reinterpret_cast<int32_t *>(base + l.nunit);
+    p.ucnt = reinterpret_cast<int32_t *>(base + l.ucnt);
+    p.hcnt = reinterpret_cast<int32_t *>(base + l.hcnt);
+    p.koff = reinterpret_cast<int32_t *>(base + l.koff);
+    p.klist = reinterpret_cast<int2 *>(base + l.klist);
+    p.ptab = reinterpret_cast<int32_t *>(base + l.ptab);
     p.tau = out->tau;
     p.end = out->end;
     p.len = out->len;

@@ -131,13 +131,69 @@ struct QkParams {
     int32_t *tau, *end, *len, *run_of, *run_start, *ridx, *cf_tau, *cf_ridx;
     int32_t *redo;          // [S] streams the bit-parallel kernel left to the automaton
     const int32_t *only;    // automaton kernels: when set, only streams with only[s] != 0
+    // grouped-key kernels (rosa_qk_batch.hip); sizes in QkLayout
+    uint8_t *qu, *ku;       // [S][Tp] unit query / key symbols (run folding), padded
+    int32_t *nunit;         // [S] units of each stream (run folding)
+    int32_t *ucnt;          // [S][G] run starts per segment
+    int32_t *hcnt;          // [S][G][NB] keys per group and segment, then prefixes
+    int32_t *koff;          // [S][NB + 1] first slot of each key group
+    int2 *klist;            // [S][T] keys by group: {unit, packed history}
+    int32_t *ptab;          // [S][FL][nch] latest key per short gram up to each chunk
 };
+
+// Grouped-key q/k kernels: units per segment workgroup, key groups (K^d)
+// and short-gram tables (sum of K^l over l < d) at most, deepest d.
+constexpr int kQbtSeg = 4096;
+constexpr int kQbtMaxNB = 16384;
+constexpr int kQbtMaxFL = 1024;
+constexpr int kQbtMaxD = 10;
+
+// Group depth d for alphabet K and T units: the largest d with
+// K^d <= min(16384, max(K, T/4)) (a few keys per group at least) whose short
+// tables keep within kQbtMaxFL entries.
+inline int qbt_choose_d(int64_t K, int64_t T)
+{
+    int64_t cap = T / 4;
+    if (cap > kQbtMaxNB) cap = kQbtMaxNB;
+    if (cap < K) cap = K;
+    int d = 1;
+    int64_t pw = K, fl = 0;
+    while (d < kQbtMaxD) {
+        const int64_t nb_next = pw * K, fl_next = fl + pw;
+        if (nb_next > cap || fl_next > kQbtMaxFL) break;
+        pw = nb_next;
+        fl = fl_next;
+        ++d;
+    }
+    return d;
+}
+
+struct QbtShape {
+    int d;
+    int64_t nb, fl, nseg, nch;  // K^d, sum_{l<d} K^l, ceil(T/kQbtSeg), ceil(T/64)
+};
+
+inline QbtShape qbt_shape(int64_t T, int64_t K)
+{
+    QbtShape q;
+    q.d = qbt_choose_d(K, T);
+    q.nb = 1;
+    q.fl = 0;
+    for (int l = 0; l < q.d; ++l) {
+        if (l > 0) q.fl += q.nb;
+        q.nb *= K;
+    }
+    q.nseg = (T + kQbtSeg - 1) / kQbtSeg;
+    q.nch = (T + 63) / 64;
+    return q;
+}
 
 
 // Workspace of rosa_match_qk: flags, padded query and key rows, unit starts,
 // the automaton nodes and dense transition rows.
 struct QkLayout {
     size_t flags, qrows, krows, start, nodes, next, redo, total;
+    size_t qu, ku, nunit, ucnt, hcnt, koff, klist, ptab;   // grouped-key kernels
     int64_t Tp, Ncap;
 };
 
@@ -154,6 +210,15 @@ inline QkLayout qk_layout(int64_t S, int64_t T, int64_t K)
     l.nodes = o;  o = align_up(o + (size_t)S * l.Ncap * 16, 256);
     l.next = o;   o = align_up(o + (size_t)S * l.Ncap * K * 4, 256);
     l.redo = o;   o = align_up(o + (size_t)S * 4, 256);
+    const QbtShape q = qbt_shape(T, K);
+    l.qu = o;     o = align_up(o + (size_t)S * l.Tp, 256);
+    l.ku = o;     o = align_up(o + (size_t)S * l.Tp, 256);
+    l.nunit = o;  o = align_up(o + (size_t)S * 4, 256);
+    l.ucnt = o;   o = align_up(o + (size_t)S * q.nseg * 4, 256);
+    l.hcnt = o;   o = align_up(o + (size_t)S * q.nseg * q.nb * 4, 256);
+    l.koff = o;   o = align_up(o + (size_t)S * (q.nb + 1) * 4, 256);
+    l.klist = o;  o = align_up(o + (size_t)S * T * 8, 256);
+    l.ptab = o;   o = align_up(o + (size_t)S * q.fl * q.nch * 4, 256);
     l.total = o;
     return l;
 }

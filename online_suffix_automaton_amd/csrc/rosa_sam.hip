@@ -729,9 +729,11 @@ static bool qk_lds_try(const QkParams &p, hipStream_t st, bool any)
 
 bool qk_bits_fits(const QkParams &p);
 hipError_t launch_qk_bits(const QkParams &p, hipStream_t st);
+hipError_t launch_qk_batch(const QkParams &p, hipStream_t st);
 
-// The bit-parallel kernel when the streams fit it, then an automaton kernel
-// for the streams it left (matches longer than its levels); otherwise an
+// The bit-parallel kernel when the streams fit it, or the grouped-key
+// kernels for streams of more than 4096 steps, then an automaton kernel for
+// the streams they left (matches longer than their limits); otherwise an
 // automaton kernel for every stream.
 hipError_t launch_qk(QkParams p, hipStream_t st)
 {
@@ -747,6 +749,14 @@ hipError_t launch_qk(QkParams p, hipStream_t st)
             return e;
         else
             p.only = p.redo;
+    } else if (p.T > 4096) {
+        const hipError_t e = launch_qk_batch(p, st);
+        if (e == hipSuccess) {
+            bits = true;   // leftovers only
+            p.only = p.redo;
+        } else if (e != hipErrorNotSupported) {
+            return e;
+        }
     }
     const bool lds_ok = p.K <= kQlMaxK && p.M <= 8;
     if (!(lds_ok && (qk_lds_try<1024>(p, st, bits) || qk_lds_try<2048>(p, st, bits) ||
