@@ -445,6 +445,23 @@ def run_qk(args):
     _log("workload qk: generating")
     Hq = synth.bf16_normal((B, T, D), 31)
     Hk = synth.bf16_normal((B, T, D), 32)
+    if args.qk_data == "lowent":
+        # routes 0-15: dead (every channel <= 0, constant symbol 0) in both
+        # streams; routes 16-31: the same period 2..9 in query and key
+        # (matches as long as the stream); routes 32-63 independent N(0,1)
+        mag = Hk & np.uint16(0x7FFF)
+        for r in range(32):
+            c = slice(r * M, (r + 1) * M)
+            if r < 16:
+                Hk[:, :, c] = mag[:, :, c] | np.uint16(0x8000)
+            else:
+                per = 2 + (r % 8)
+                sym = (np.arange(T) % per).astype(np.uint16)
+                for j in range(M):
+                    neg = ((sym >> j) & 1) == 0
+                    Hk[:, :, r * M + j] = np.where(neg[None], mag[:, :, r * M + j] | np.uint16(0x8000),
+                                                   mag[:, :, r * M + j])
+            Hq[:, :, c] = Hk[:, :, c]
     dq = torch.from_numpy(Hq.view(np.int16)).to(dev)
     dk = torch.from_numpy(Hk.view(np.int16)).to(dev)
     qi, ki = rosa.bf16_input(dq, M), rosa.bf16_input(dk, M)
@@ -513,6 +530,9 @@ def run_qk(args):
         "config": {"workload": f"qk: query and key hidden states [{B},{T},256] "
                                f"bf16 N(0,1) (seeds 31, 32), M=4 -> {S} streams, "
                                "K=16" + (", key runs folded" if args.rle else "")
+                               + (", routes 0-15 dead and 16-31 periodic (2-9) "
+                                  "with equal query and key"
+                                  if args.qk_data == "lowent" else "")
                                + (", counterfactual tables" if args.cf else ""),
                    "streams": S, "T": T, "K": K, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9,
@@ -614,6 +634,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the oracle baseline and parity check")
     ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--qk-data", default="iid", choices=["iid", "lowent"],
+                    help="qk workload: independent N(0,1) states, or half the "
+                         "routes dead / periodic with equal query and key")
     ap.add_argument("--T", type=int, default=4096,
                     help="qk workload: steps per stream (B = 8 at 4096, "
                          "32768 / T streams of 256 channels past it)")

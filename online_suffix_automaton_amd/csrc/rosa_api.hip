@@ -462,6 +462,13 @@ rosa_status rosa_match_qk(const rosa_input *q, const rosa_input *k,
     p.koff = reinterpret_cast<int32_t *>(base + l.koff);
     p.klist = reinterpret_cast<int2 *>(base + l.klist);
     p.ptab = reinterpret_cast<int32_t *>(base + l.ptab);
+    p.dfl = reinterpret_cast<uint32_t *>(base + l.dfl);
+    p.eo = reinterpret_cast<int4 *>(base + l.eo);
+    p.cfe = reinterpret_cast<int2 *>(base + l.cfe);
+    p.uof = reinterpret_cast<int32_t *>(base + l.uof);
+    p.dstream = reinterpret_cast<int32_t *>(base + l.dstream);
+    p.xl = reinterpret_cast<int2 *>(base + l.xl);
+    p.xn = reinterpret_cast<int32_t *>(base + l.xn);
     p.tau = out->tau;
     p.end = out->end;
     p.len = out->len;

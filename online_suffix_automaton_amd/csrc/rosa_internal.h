@@ -139,7 +139,19 @@ struct QkParams {
     int32_t *koff;          // [S][NB + 1] first slot of each key group
     int2 *klist;            // [S][T] keys by group: {unit, packed history}
     int32_t *ptab;          // [S][FL][nch] latest key per short gram up to each chunk
+    uint32_t *dfl;          // [S][T] query symbols of each unit left to the time-ordered pass
+    int4 *eo;               // [S][T] (E, L, destination, 0) of each unit's own query symbol
+    int2 *cfe;              // [S][T][M] (E, destination) of each unit's counterfactual symbols
+    int32_t *uof;           // [S][T] unit of each time step (run folding)
+    int32_t *dstream;       // [S] nonzero: the stream has units in dfl
+    int2 *xl;               // [S][qbt_xcap(T)] (unit, first step) of output pieces left
+    int32_t *xn;            // [S] entries in xl
 };
+
+// Output pieces per stream the grouped-key kernels may leave to their
+// expansion kernel: 64 time steps each, one per unit at most beyond the
+// pieces of the steps themselves.
+inline __host__ __device__ int64_t qbt_xcap(int64_t T) { return T + T / 64 + 64; }
 
 // Grouped-key q/k kernels: units per segment workgroup, key groups (K^d)
 // and short-gram tables (sum of K^l over l < d) at most, deepest d.
@@ -168,9 +180,13 @@ inline int qbt_choose_d(int64_t K, int64_t T)
     return d;
 }
 
+// Entries per stream of the grouped-key list: T rounded up to even, so
+// that entry pairs are 16-byte aligned.
+inline __host__ __device__ int64_t qbt_kpitch(int64_t T) { return (T + 1) & ~(int64_t)1; }
+
 struct QbtShape {
     int d;
-    int64_t nb, fl, nseg, nch;  // K^d, sum_{l<d} K^l, ceil(T/kQbtSeg), ceil(T/64)
+    int64_t nb, fl, nseg, nch;  // K^d, sum_{l<d} K^l, ceil(T/kQbtSeg), ceil(T/64) -> x16
 };
 
 inline QbtShape qbt_shape(int64_t T, int64_t K)
@@ -184,7 +200,7 @@ inline QbtShape qbt_shape(int64_t T, int64_t K)
         q.nb *= K;
     }
     q.nseg = (T + kQbtSeg - 1) / kQbtSeg;
-    q.nch = (T + 63) / 64;
+    q.nch = ((T + 63) / 64 + 15) / 16 * 16;   // short-table row pitch, 64-byte rows
     return q;
 }
 
@@ -193,7 +209,7 @@ inline QbtShape qbt_shape(int64_t T, int64_t K)
 // the automaton nodes and dense transition rows.
 struct QkLayout {
     size_t flags, qrows, krows, start, nodes, next, redo, total;
-    size_t qu, ku, nunit, ucnt, hcnt, koff, klist, ptab;   // grouped-key kernels
+    size_t qu, ku, nunit, ucnt, hcnt, koff, klist, ptab, dfl, eo, cfe, uof, dstream, xl, xn;
     int64_t Tp, Ncap;
 };
 
@@ -217,8 +233,15 @@ inline QkLayout qk_layout(int64_t S, int64_t T, int64_t K)
     l.ucnt = o;   o = align_up(o + (size_t)S * q.nseg * 4, 256);
     l.hcnt = o;   o = align_up(o + (size_t)S * q.nseg * q.nb * 4, 256);
     l.koff = o;   o = align_up(o + (size_t)S * (q.nb + 1) * 4, 256);
-    l.klist = o;  o = align_up(o + (size_t)S * T * 8, 256);
+    l.klist = o;  o = align_up(o + (size_t)S * qbt_kpitch(T) * 8, 256);
     l.ptab = o;   o = align_up(o + (size_t)S * q.fl * q.nch * 4, 256);
+    l.dfl = o;    o = align_up(o + (size_t)S * T * 4, 256);
+    l.eo = o;     o = align_up(o + (size_t)S * T * 16, 256);
+    l.cfe = o;    o = align_up(o + (size_t)S * T * 8 * 8, 256);   // M <= 8
+    l.uof = o;    o = align_up(o + (size_t)S * T * 4, 256);
+    l.dstream = o; o = align_up(o + (size_t)S * 4, 256);
+    l.xl = o;     o = align_up(o + (size_t)S * qbt_xcap(T) * 8, 256);
+    l.xn = o;     o = align_up(o + (size_t)S * 4, 256);
     l.total = o;
     return l;
 }
