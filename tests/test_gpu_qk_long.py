@@ -1,11 +1,12 @@
 """GPU parity of rosa_match_qk on streams of more than 4096 steps: the
 grouped-key kernels (keys sorted by their last d symbols, one thread per
-query unit), with the automaton answering the streams they hand back (key
-groups past their cap, matches running more than 1024 units past d).  Every
-output is compared bit-exact with the CPU oracle: independent, correlated and
-equal query and key streams, key runs, alphabets 2..256 (powers of two with
-the counterfactual tables, 3 without), ragged lengths, low-entropy streams,
-planted long matches and the 64 x 65536 bf16 shape."""
+query unit), with the time-ordered pass answering the query symbols they
+leave (key groups past their cap, matches running more than 1024 units past
+d).  Every output is compared bit-exact with the CPU oracle: independent,
+correlated and equal query and key streams, key runs, alphabets 2..256
+(powers of two with the counterfactual tables, 3 without), ragged lengths,
+low-entropy streams up to 65536 steps, planted long matches and the
+64 x 65536 bf16 shape."""
 import concurrent.futures as cf_pool
 import os
 
@@ -165,3 +166,30 @@ def test_qk_grouped_random_shapes(case):
     q, k = _streams(8200 + case, S, T, K, mode)
     _run(q, k, K, rle, cf,
          f"grouped random case {case}: K={K} T={T} S={S} rle={rle} cf={cf} mode={mode}")
+
+
+@pytest.mark.parametrize("rle", [False, True])
+def test_qk_grouped_low_entropy_65536(rle):
+    """The time-ordered pass at the long-context length: a constant key
+    stream under a random query, equal constant streams, equal period-3
+    streams, a period-5 pattern with a repeated symbol (counterfactual
+    symbols match the pattern shifted, long past the groups' limit), a
+    period-7 key stream with rare noise under its clean query, and an
+    independent pair."""
+    S, T, K = 6, 65536, 16
+    rng = np.random.default_rng(4242 + rle)
+    k = rng.integers(0, K, (S, T)).astype(np.uint8)
+    q = rng.integers(0, K, (S, T)).astype(np.uint8)
+    k[0] = 9
+    k[1] = 4
+    q[1] = 4
+    k[2] = np.tile([1, 2, 3], T)[:T]
+    q[2] = k[2]
+    k[3] = np.tile([6, 6, 2, 11, 2], T)[:T]
+    q[3] = k[3]
+    pat = rng.integers(0, K, 7)
+    k[4] = np.tile(pat, T)[:T]
+    noise = rng.random(T) < 0.0005
+    k[4, noise] = rng.integers(0, K, int(noise.sum()))
+    q[4] = np.tile(pat, T)[:T]
+    _run(q, k, K, rle, True, f"grouped low entropy 65536 rle={rle}")
