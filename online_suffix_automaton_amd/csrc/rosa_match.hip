@@ -489,7 +489,7 @@ __device__ void phase_hist(const MatchParams &p, const uint8_t *x, int32_t *cnt,
 template <class OffT>
 __device__ void phase_tasks(const MatchParams &p, int s, const int32_t *cnt,
                             OffT *off, uint32_t *tasks, int32_t *misc,
-                            int pcap, bool own_big = false)
+                            int pcap, bool own_big = false, int run_pos = 256)
 {
     const int tid = threadIdx.x, nt = blockDim.x;
     const int NB = p.NB;
@@ -511,11 +511,13 @@ __device__ void phase_tasks(const MatchParams &p, int s, const int32_t *cnt,
             off[NB] = (OffT)total;
     }
     __syncthreads();
-    // Each thread packs a run of `bpl` consecutive buckets (about 256
+    // Each thread packs a run of `bpl` consecutive buckets (about run_pos
     // positions' worth, at least NB/nt so every bucket is covered); tasks
-    // do not span runs, so longer runs pack tasks fuller.
+    // do not span runs, so longer runs pack tasks fuller, while shorter ones
+    // spread the packing over more threads (the better trade on short
+    // streams, whose packing is a larger share of the kernel).
     const int avg = max(1, (int)off[NB] / NB);
-    const int bpl = max((NB + nt - 1) / nt, min(64, max(1, 256 / avg)));
+    const int bpl = max((NB + nt - 1) / nt, min(64, max(1, run_pos / avg)));
     const int b0 = min(NB, tid * bpl), b1 = min(NB, b0 + bpl);
     int ntask = 0, cur = 0, crange = -1;
     for (int b = b0; b < b1; ++b) {
@@ -1339,7 +1341,7 @@ void stream_kernel_lds(MatchParams p)
     o.rec = p.rec + (int64_t)s * T;
 
     phase_hist<DC>(p, x, cnt, firstd, firstl);
-    phase_tasks(p, s, cnt, off, tasks, misc, kPassCap, true);
+    phase_tasks(p, s, cnt, off, tasks, misc, kPassCap, true, Cfg::kTMax <= 8192 ? 128 : 256);
 
     // D: records of the first d-1 positions go to the slots T-d+1.. (no
     // bucket holds them); the first occurrence of a d-gram in a singleton
