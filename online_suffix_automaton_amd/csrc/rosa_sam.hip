@@ -116,22 +116,172 @@ __device__ __forceinline__ SamStream sam_open(const SamView &v, int64_t s)
 // Build over hist[s][0..T): one lane per stream, `spw` streams per wave.
 // The appends run without last-end walks; then the last ends are set in one
 // pass over the states (see the top of this file).
+// Last ends after appends made without the last-end walks, by the 64 lanes
+// of the stream's wave (the result of sam_fill_last): a state's last end is
+// the latest position among the non-clone states of its link subtree (a
+// non-clone state of length n was created at position n-1).  Rounds of 64
+// states from the newest down; each lane with a non-clone state raises its
+// last end and its ancestors' to the state's position by atomic max, and
+// stops at a node that already holds a later or equal one: whatever walk
+// put that value there raises every ancestor above it as well.  Taking the
+// states from the newest down makes most walks stop within a few links.
+__device__ void sam_fill_last_wave(const SamStream &a, int nst)
+{
+    const int lane = __lane_id();
+    for (int top = nst - 1; top >= 1; top -= 64) {
+        const int w = top - lane;
+        int u = -1, pos = 0;
+        if (w >= 1) {
+            const int4 nw = a.node(w);
+            if (nw.w == 0) {
+                u = w;
+                pos = nw.x - 1;
+            }
+        }
+        while (u != -1) {
+            int *lastp = &a.node(u).z;
+            const int up = a.node(u).y;   // links do not change here
+            const int old = atomicMax(lastp, pos);
+            if (old >= pos)
+                break;
+            u = up;
+        }
+    }
+}
+
+// Appends by the whole wave, for K <= 60: a state's record (node ints 0..3,
+// transition c at int 4+c) is one 4-byte load per lane, lane i holding int i,
+// so a record is one coalesced round trip and any field is a lane read.
+// Every int of a record is stored by the lane that loads it (lane i for int
+// i), so each lane reads its own earlier stores in program order and no
+// fence is needed between appends.  The record of the tail's suffix link
+// (the state the next append's walk starts from: the matched state, its
+// clone, or the root) is kept in the lanes between appends, with every
+// store this wave makes to it mirrored, so most appends need one or two
+// round trips (the record of the transition's target) instead of one per
+// field.  Same steps and results as sam_extend.
+struct WaveSam {
+    int cid;    // state whose record the lanes hold (-2: none)
+    int cval;   // this lane's int of that record
+};
+
+__device__ __forceinline__ int32_t *sam_rec(const SamStream &a, int v)
+{
+    return reinterpret_cast<int32_t *>(&a.node(v));
+}
+
+__device__ __forceinline__ int wave_rec_load(const SamStream &a, int v, int nint)
+{
+    const int lane = __lane_id();
+    return lane < nint ? sam_rec(a, v)[lane] : -1;
+}
+
+__device__ void sam_extend_wave(SamStream &a, WaveSam &ws, int c)
+{
+    const int lane = __lane_id();
+    const int nint = 4 + a.K;
+    const int cur = a.nst++;
+    if (lane == 4 + c)
+        sam_rec(a, a.tail)[4 + c] = cur;   // the tail has no transitions
+    int p = a.tail_link;
+    int val = -1, pc = -1;
+    while (p != -1) {
+        val = p == ws.cid ? ws.cval : wave_rec_load(a, p, nint);
+        pc = __builtin_amdgcn_readlane(val, 4 + c);
+        if (pc != -1)
+            break;
+        if (lane == 4 + c)
+            sam_rec(a, p)[4 + c] = cur;
+        val = lane == 4 + c ? cur : val;
+        if (p == ws.cid)
+            ws.cval = val;
+        if (p == 0) {   // the root: keep its record for the next walk
+            ws.cid = 0;
+            ws.cval = val;
+        }
+        p = __builtin_amdgcn_readlane(val, 1);
+    }
+    int lk = 0;
+    if (p != -1) {
+        const int q = pc;
+        const int lp = __builtin_amdgcn_readlane(val, 0);
+        const int qval = q == ws.cid ? ws.cval : wave_rec_load(a, q, nint);
+        if (lp + 1 == __builtin_amdgcn_readlane(qval, 0)) {
+            lk = q;
+            ws.cid = q;
+            ws.cval = qval;
+        } else {
+            // clone of q with length lp + 1: q's link, last end and
+            // transitions, the clone flag set
+            const int clone = a.nst++;
+            const int cv = lane == 0 ? lp + 1 : lane == 3 ? 1 : qval;
+            if (lane < nint)
+                sam_rec(a, clone)[lane] = cv;
+            // transitions on c into q from p and its ancestors go to the clone
+            int rv = val;
+            while (p != -1) {
+                if (__builtin_amdgcn_readlane(rv, 4 + c) != q)
+                    break;
+                if (lane == 4 + c)
+                    sam_rec(a, p)[4 + c] = clone;
+                if (p == ws.cid)
+                    ws.cval = lane == 4 + c ? clone : ws.cval;
+                p = __builtin_amdgcn_readlane(rv, 1);
+                if (p != -1)
+                    rv = p == ws.cid ? ws.cval : wave_rec_load(a, p, nint);
+            }
+            if (lane == 1)
+                sam_rec(a, q)[1] = clone;
+            lk = clone;
+            ws.cid = clone;
+            ws.cval = cv;
+        }
+    }
+    // the new state's record: length, link, no last end, not a clone, no
+    // transitions
+    if (lane < nint)
+        sam_rec(a, cur)[lane] = lane == 0 ? a.tail_len + 1 : lane == 1 ? lk : lane == 3 ? 0 : -1;
+    a.tail = cur;
+    a.tail_len += 1;
+    a.tail_link = lk;
+}
+
+// One stream per wave: the wave appends the prefix (lane 0 alone for
+// alphabets over 60 symbols), then fills the last ends.
 __global__ __launch_bounds__(64) void sam_build_kernel(SamView v, int64_t S,
-                                                       int64_t T, int spw)
+                                                       int64_t T)
 {
     const int lane = threadIdx.x;
-    if (lane >= spw)
-        return;
-    const int64_t s = (int64_t)blockIdx.x * spw + lane;
+    const int64_t s = blockIdx.x;
     if (s >= S)
         return;
     SamStream a = sam_stream(v, s);
-    sam_new_state(a, 0);   // root: len 0, no link
+    int nst = 0;
     const uint8_t *h = v.hist + s * v.Hs;
-    for (int64_t t = 0; t < T; ++t)
-        sam_extend(a, h[t]);
-    sam_fill_last(a);
-    v.meta[s] = make_int4(a.tail, a.nst, a.tail_len, a.tail_link);
+    if (a.K <= 60) {
+        // root: len 0, no link, no last end, no transitions (each int by its lane)
+        if (lane < 4 + a.K)
+            sam_rec(a, 0)[lane] = lane == 0 ? 0 : lane == 3 ? 0 : -1;
+        a.nst = 1;
+        WaveSam ws = {-2, -1};
+        for (int64_t t = 0; t < T; ++t)
+            sam_extend_wave(a, ws, h[t]);
+        if (lane == 0)
+            v.meta[s] = make_int4(a.tail, a.nst, a.tail_len, a.tail_link);
+        nst = a.nst;
+    } else {
+        if (lane == 0) {
+            sam_new_state(a, 0);
+            for (int64_t t = 0; t < T; ++t)
+                sam_extend(a, h[t]);
+            v.meta[s] = make_int4(a.tail, a.nst, a.tail_len, a.tail_link);
+            nst = a.nst;
+        }
+        nst = __shfl(nst, 0);
+    }
+    // the records visible to every lane (the workgroup is this wave)
+    __syncthreads();
+    sam_fill_last_wave(a, nst);
 }
 
 // Validate/clamp symbols of a SYMBOLS prefix into the history rows.
@@ -672,9 +822,7 @@ hipError_t launch_sam_build(void *buf, int64_t S, int64_t K, int64_t Tcap,
                             int64_t T, hipStream_t st)
 {
     SamView v = sam_view(buf, S, K, Tcap);
-    const int spw = kSamStreamsPerWave;
-    dim3 grid((unsigned)((S + spw - 1) / spw));
-    hipLaunchKernelGGL(sam_build_kernel, grid, dim3(64), 0, st, v, S, T, spw);
+    hipLaunchKernelGGL(sam_build_kernel, dim3((unsigned)S), dim3(64), 0, st, v, S, T);
     return hipGetLastError();
 }
 
