@@ -194,14 +194,14 @@ size_t rosa_match_qk_workspace_bytes(int64_t S, int64_t T, int32_t K);
  * bytes, 256-byte aligned, not shared by calls in flight; its first 256
  * bytes hold the symbol flag, so rosa_match_status(ws, stream) reports a
  * symbol >= K in q or k.
- * Kernels: for at most 4096 units per stream and K <= 64, one or two waves
- * per stream hold the sets of candidate end units of every match length as
- * 4096-bit vectors (one 64-bit word per lane) and advance them per unit
- * with shifts and ANDs; a stream whose match grows past 32 units is handed
- * to the automaton kernels, which also take every stream beyond those
- * limits: one wave per stream walks the pages' automaton, with its tables
- * in LDS when every stream fits the device at once, else in device memory
- * (sequential per stream, so much slower). */
+ * Kernels (the same results whichever runs): for K >= 2, the key units
+ * sorted by their last d symbols into groups, one thread per query unit
+ * comparing the packed histories of its group's earlier keys (and, below d
+ * symbols, tables of the latest key per shorter gram), for the unit's own
+ * and every counterfactual symbol; symbols whose group is very large or
+ * whose match runs more than 1024 units past d are answered in time order
+ * by the extension rule.  For K = 1, a bit-parallel kernel (at most 4096
+ * units) or one wave per stream walking the pages' automaton. */
 rosa_status rosa_match_qk(const rosa_input *q, const rosa_input *k,
                           int32_t flags, const rosa_qk_out *out, void *ws,
                           size_t ws_bytes, hipStream_t stream);

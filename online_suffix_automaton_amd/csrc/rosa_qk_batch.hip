@@ -31,9 +31,10 @@
 //     from ballots of the key symbols) or from the short table of the chunk
 //     before; L is the largest l with one.
 //
-// A stream with a key group of more than kcap keys, or a match that runs
-// more than kQtLcap symbols past d, is marked in redo[] and answered by the
-// automaton kernel afterwards (long repeats; low-entropy streams).
+// A query symbol whose key group holds more than kcap keys, or whose match
+// runs more than kQtLcap units past d (low-entropy streams, long repeats),
+// is left to a time-ordered pass per stream (qt_defer_kernel) that answers
+// it by the extension rule from the previous unit's answer, else directly.
 #include "rosa_internal.h"
 
 namespace rosa {
@@ -1068,9 +1069,9 @@ bool raise_lds(const void *fn, size_t bytes)
 
 }  // namespace
 
-// Launches the grouped-key kernels for every stream; streams they give up
-// on are marked in redo[] (zeroed here first).  hipErrorNotSupported: this
-// path does not apply to the shape, nothing launched.
+// Launches the grouped-key kernels, which answer every stream (redo[] is
+// cleared and stays clear).  hipErrorNotSupported: this path does not apply
+// to the shape (one symbol; grids past their limits), nothing launched.
 hipError_t launch_qk_batch(const QkParams &p, hipStream_t st)
 {
     if (p.K < 2 || p.T < 1 || p.M > 8)

@@ -879,14 +879,20 @@ bool qk_bits_fits(const QkParams &p);
 hipError_t launch_qk_bits(const QkParams &p, hipStream_t st);
 hipError_t launch_qk_batch(const QkParams &p, hipStream_t st);
 
-// The bit-parallel kernel when the streams fit it, or the grouped-key
-// kernels for streams of more than 4096 steps, then an automaton kernel for
-// the streams they left (matches longer than their limits); otherwise an
-// automaton kernel for every stream.
+// The grouped-key kernels for every shape they take (alphabets of two
+// symbols or more; they answer every stream themselves).  Otherwise the
+// bit-parallel kernel when the streams fit it, then an automaton kernel for
+// the streams it left (matches longer than its levels), or an automaton
+// kernel for every stream.
 hipError_t launch_qk(QkParams p, hipStream_t st)
 {
     p.spw = 1;
     p.only = nullptr;
+    {
+        const hipError_t e = launch_qk_batch(p, st);
+        if (e != hipErrorNotSupported)
+            return e;
+    }
     bool bits = qk_bits_fits(p);
     if (bits) {
         // hipErrorNotSupported: not launched, the automaton takes every stream
@@ -897,14 +903,6 @@ hipError_t launch_qk(QkParams p, hipStream_t st)
             return e;
         else
             p.only = p.redo;
-    } else if (p.T > 4096) {
-        const hipError_t e = launch_qk_batch(p, st);
-        if (e == hipSuccess) {
-            bits = true;   // leftovers only
-            p.only = p.redo;
-        } else if (e != hipErrorNotSupported) {
-            return e;
-        }
     }
     const bool lds_ok = p.K <= kQlMaxK && p.M <= 8;
     if (!(lds_ok && (qk_lds_try<1024>(p, st, bits) || qk_lds_try<2048>(p, st, bits) ||
