@@ -231,3 +231,22 @@ def test_qk_random_shapes(case):
         want.pop("cf_tau", None)
         want.pop("cf_ridx", None)
     _compare(got, want, f"random case {case}")
+
+
+@pytest.mark.parametrize("T", [1, 100, 3000, 5000])
+@pytest.mark.parametrize("rle", [False, True])
+def test_qk_one_symbol(T, rle):
+    """A one-symbol alphabet (every stream constant), the shape the grouped
+    kernels leave to the bit-parallel kernel (T <= 4096) and the automaton
+    (beyond): matches as long as the key history."""
+    S = 3
+    q = np.zeros((S, T), np.uint8)
+    k = np.zeros((S, T), np.uint8)
+    _say(f"qk one symbol T={T} rle={rle}")
+    got = rosa.match_qk(torch.from_numpy(q).to(DEV), torch.from_numpy(k).to(DEV),
+                        K=1, rle=rle)
+    torch.cuda.synchronize()
+    want = oracle.match_qk(q, k, 1, 0, rle, cf=False)
+    want.pop("cf_tau", None)
+    want.pop("cf_ridx", None)
+    _compare(got, want, f"one symbol T={T} rle={rle}")
