@@ -275,7 +275,11 @@ rosa_status rosa_build(const rosa_input *in, int64_t t_capacity,
  * NULL) and, if out_row is not NULL, the gathered values
  *   out_row[b*ldo_b + r*M + m] = V[b*ldv_b + (E+1)*ldv + r*M + m]  (0 if E<0)
  * V must already hold position t (tau = E+1 can equal t).  Returns
- * ROSA_ERR_CAPACITY (checked on the host) once t_capacity positions exist. */
+ * ROSA_ERR_CAPACITY (checked on the host) once t_capacity positions exist.
+ * Cost per stream: the append is O(1) amortised (Sec. 2.2); the last-end
+ * walk visits the new state's suffix path, a few states on typical streams
+ * but up to t on a constant or short-period stream, where a step is then t
+ * dependent memory accesses. */
 rosa_status rosa_step(rosa_state *h, const rosa_input *row, const uint16_t *V,
                       int64_t ldv, int64_t ldv_b, int32_t *end, int16_t *sym,
                       uint16_t *out_row, int64_t ldo_b, hipStream_t stream);
