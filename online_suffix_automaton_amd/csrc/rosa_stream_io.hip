@@ -169,34 +169,120 @@ __global__ __launch_bounds__(256) void discretize_kernel(
 // ----------------------------------------------------------------- gather
 
 // XCDs of the chip (consecutive workgroups of a launch go to consecutive
-// XCDs, round robin); the gather's positions per tile and workgroups per XCD.
+// XCDs, round robin).
 constexpr int kXcds = 8;
+
+// The reads of a route go to random earlier rows (tau = E+1, inherent to
+// the method; half of them within about 4K rows, nine in ten within 27K on
+// i.i.d. streams), and with M = 4 each 128-byte line of a V row holds the
+// values of 16 routes (a route group), read by them at different positions.
+// The 8-byte path keeps those lines in L2 between the reads: route groups
+// are dealt to the XCDs (workgroup i runs on XCD i % 8), an XCD does its
+// groups one after another, and its waves walk a group's positions in order,
+// side by side, so the lines of the recent rows of that group sit in the
+// XCD's 4 MiB L2.  E and the output are streamed with non-temporal accesses
+// so that they do not push those lines out.
+//
+// Wave layout: a wave covers the 16 routes of a group (lane & 15) and
+// kGatherU chunks of 16 positions; lane quad q = lane >> 4 holds positions
+// 4q .. 4q+3 of each chunk (one 16-byte E load), so its i-th store writes
+// positions i, i+4, i+8, i+12 of the chunk: four whole 128-byte output lines.
+// No LDS and no barrier, so each wave keeps its 32 value loads in flight
+// independently.  The positions an XCD has in flight (waves x 128) trade
+// memory parallelism against the span of rows its L2 must hold; one
+// workgroup of 4 waves per CU did best on the long workload.  With a row
+// pitch that is a multiple of 2 KiB every row's line of one group falls into
+// the same few L2 sets; there an XCD walks two adjacent groups at once
+// (GPX = 2: chunks alternate between them), which spreads the lines over
+// twice the sets.
+constexpr int kGatherU = 8;
+constexpr int kGatherChunk = 16 * kGatherU;
+constexpr int kGatherWG = 32;   // workgroups of 4 waves per XCD
+
+typedef int32_t gather_v4i __attribute__((ext_vector_type(4)));
+
+template <int GPX>
+__global__ __launch_bounds__(256) void gather_wave_kernel(
+    const uint16_t *__restrict__ V, int64_t T, int64_t R, int64_t ldv,
+    const int32_t *__restrict__ E, uint16_t *__restrict__ out, int64_t ldo,
+    int vec_e)
+{
+    constexpr int U = kGatherU, CH = kGatherChunk;
+    const int64_t b = blockIdx.y;
+    const int64_t ng = (R + 15) / 16, nch = (T + CH - 1) / CH;
+    const int x = (int)(blockIdx.x % kXcds);
+    const int lane = threadIdx.x & 63;
+    const int64_t wv = (int64_t)(blockIdx.x / kXcds) * 4 + (threadIdx.x >> 6);
+    const int64_t Wv = (int64_t)(gridDim.x / kXcds) * 4;
+    const int rl = lane & 15, q = lane >> 4;
+    for (int64_t c = wv;; c += Wv) {
+        // chunk c of this XCD: pass, then GPX groups side by side, chunks
+        // alternating between them
+        const int64_t pass = c / (nch * GPX), cw = c - pass * (nch * GPX);
+        const int64_t first = (pass * kXcds + x) * GPX;
+        if (first >= ng)
+            break;
+        const int64_t g = first + cw % GPX, t0 = (cw / GPX) * CH;
+        const int64_t r = g * 16 + rl;
+        if (g >= ng || r >= R)
+            continue;
+        const int32_t *er = E + (b * R + r) * T;
+        int32_t e[U][4];
+        if (vec_e && t0 + CH <= T) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const gather_v4i w = __builtin_nontemporal_load(
+                    reinterpret_cast<const gather_v4i *>(er + t0 + 16 * u + 4 * q));
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    e[u][i] = w[i];
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t t = t0 + 16 * u + 4 * q + i;
+                    e[u][i] = t < T ? __builtin_nontemporal_load(er + t) : -1;
+                }
+        }
+        uint64_t v[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int32_t ee = e[u][i] > T - 2 ? (int32_t)(T - 2) : e[u][i];
+                v[u][i] = 0;
+                if (ee >= 0)
+                    v[u][i] = *reinterpret_cast<const uint64_t *>(
+                        V + (b * T + (ee + 1)) * ldv + r * 4);
+            }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t t = t0 + 16 * u + 4 * q + i;
+                if (t < T)
+                    __builtin_nontemporal_store(
+                        v[u][i], reinterpret_cast<uint64_t *>(out + (b * T + t) * ldo + r * 4));
+            }
+    }
+}
+
+// Any M, pitch and alignment: tiles of 128 positions x RG routes of one
+// batch row, 256 threads, the E tile staged through LDS so that its loads
+// coalesce; route groups dealt to the XCDs as in the 8-byte path.
 constexpr int kGatherTP = 128;
 constexpr int64_t kGatherW = 128;
 
-// Tile: kGatherTP positions x RG routes of one batch row, 256 threads.  The reads of a route go to random earlier rows (tau = E+1,
-// inherent to the method; half of them within about 4K rows, nine in ten
-// within 27K on i.i.d. streams), and with M = 4 each 128-byte line of a V
-// row holds the values of 16 routes, read by them at different positions.
-// So the kernel keeps those lines in L2 between the reads: the route groups
-// are dealt to the 8 XCDs (group g to XCD g % 8; workgroup i runs on XCD
-// i % 8), an XCD does its groups one after another, and inside a group its
-// W workgroups walk the positions in order, side by side.  The lines of the
-// recent rows of one group then mostly fit the XCD's 4 MiB L2.  E and the
-// output are streamed with non-temporal accesses so that they do not push
-// those lines out.  With a row pitch that is a multiple of 2 KiB every row's
-// line of a group falls into the same few L2 sets, which holds far fewer
-// rows: there two lines per row and group (RG = 32) do best, otherwise one
-// (RG = 16).  Tile length and W were chosen by timing on the long workload
-// (fewer workgroups in flight lose memory parallelism).
-template <int MC, int RG>
+template <int RG>
 __global__ __launch_bounds__(256) void gather_kernel(
     const uint16_t *__restrict__ V, int64_t T, int64_t D, int64_t ldv, int M,
     const int32_t *__restrict__ E, uint16_t *__restrict__ out, int64_t ldo, int W)
 {
     constexpr int TP = kGatherTP;
     constexpr int PSTEP = 256 / RG;          // positions per round of values
-    constexpr int NV = TP / PSTEP;           // value loads per thread
+    constexpr int NV = TP / PSTEP;           // positions per thread
     __shared__ int32_t et[RG][TP + 1];
     const int64_t R = D / M;
     const int64_t b = blockIdx.y;
@@ -225,25 +311,7 @@ __global__ __launch_bounds__(256) void gather_kernel(
         // values: RG consecutive threads = the routes of one position
         const int rl = tid % RG;
         const int64_t r = r0 + rl;
-        if (r < R && MC == 4) {
-            uint64_t v[NV];
-#pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const int tl = tid / RG + PSTEP * i;
-                const int32_t e = et[rl][tl];
-                v[i] = 0;
-                if (t0 + tl < T && e >= 0)
-                    v[i] = *reinterpret_cast<const uint64_t *>(
-                        V + (b * T + (e + 1)) * ldv + r * M);
-            }
-#pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const int64_t t = t0 + tid / RG + PSTEP * i;
-                if (t < T)
-                    __builtin_nontemporal_store(
-                        v[i], reinterpret_cast<uint64_t *>(out + (b * T + t) * ldo + r * M));
-            }
-        } else if (r < R) {
+        if (r < R) {
             for (int i = 0; i < NV; ++i) {
                 const int tl = tid / RG + PSTEP * i;
                 const int64_t t = t0 + tl;
@@ -308,28 +376,41 @@ hipError_t launch_gather(const uint16_t *V, int64_t B, int64_t T, int64_t D,
                          int64_t ldv, int M, const int32_t *E, uint16_t *out,
                          int64_t ldo, hipStream_t st)
 {
-    // W workgroups per XCD (four per CU), fewer when an XCD has fewer tiles;
-    // route groups of one 128-byte line per row unless the row pitch aliases
     const int64_t R = D / M;
+    // a pitch that is a multiple of 2 KiB puts every row's line of a group
+    // into the same few L2 sets
     const bool aliased = ((ldv * 2) % 2048) == 0;
+    const bool vec8 = M == 4 && (ldv % 4) == 0 && (ldo % 4) == 0 &&
+                      (((uintptr_t)V) & 7) == 0 && (((uintptr_t)out) & 7) == 0;
+    if (vec8) {
+        const int gpx = aliased ? 2 : 1;
+        const int64_t ng = (R + 15) / 16;
+        const int64_t chunks = (ng + kXcds * gpx - 1) / (kXcds * gpx) * gpx *
+                               ((T + kGatherChunk - 1) / kGatherChunk);
+        const int64_t wgs = (chunks + 3) / 4;   // 4 waves per workgroup
+        const int W = (int)(wgs < kGatherWG ? wgs : kGatherWG);
+        const int vec_e = (T % 4) == 0 && (((uintptr_t)E) & 15) == 0;
+        dim3 grid((unsigned)(kXcds * W), (unsigned)B);
+        if (aliased)
+            hipLaunchKernelGGL(gather_wave_kernel<2>, grid, dim3(256), 0, st, V, T,
+                               R, ldv, E, out, ldo, vec_e);
+        else
+            hipLaunchKernelGGL(gather_wave_kernel<1>, grid, dim3(256), 0, st, V, T,
+                               R, ldv, E, out, ldo, vec_e);
+        return hipGetLastError();
+    }
+    // other widths: one 128-byte line per row and group unless the pitch
+    // aliases; W workgroups per XCD (four per CU), fewer for small inputs
     const int rg = aliased ? 32 : 16;
     const int64_t per_xcd = ((R + rg - 1) / rg + kXcds - 1) / kXcds *
                             ((T + kGatherTP - 1) / kGatherTP);
     const int W = (int)(per_xcd < kGatherW ? per_xcd : kGatherW);
     dim3 grid((unsigned)(kXcds * W), (unsigned)B);
-    const bool vec4 = M == 4 && (ldv % 4) == 0 && (ldo % 4) == 0 &&
-                      (((uintptr_t)V) & 7) == 0 && (((uintptr_t)out) & 7) == 0;
-    if (vec4 && aliased)
-        hipLaunchKernelGGL((gather_kernel<4, 32>), grid, dim3(256), 0, st, V, T, D,
-                           ldv, M, E, out, ldo, W);
-    else if (vec4)
-        hipLaunchKernelGGL((gather_kernel<4, 16>), grid, dim3(256), 0, st, V, T, D,
-                           ldv, M, E, out, ldo, W);
-    else if (aliased)
-        hipLaunchKernelGGL((gather_kernel<0, 32>), grid, dim3(256), 0, st, V, T, D,
+    if (aliased)
+        hipLaunchKernelGGL(gather_kernel<32>, grid, dim3(256), 0, st, V, T, D,
                            ldv, M, E, out, ldo, W);
     else
-        hipLaunchKernelGGL((gather_kernel<0, 16>), grid, dim3(256), 0, st, V, T, D,
+        hipLaunchKernelGGL(gather_kernel<16>, grid, dim3(256), 0, st, V, T, D,
                            ldv, M, E, out, ldo, W);
     return hipGetLastError();
 }

@@ -352,3 +352,29 @@ def test_gather_row_pitch(B, T, D, M, pad):
     _say(f"gather pitch B={B} T={T} D={D} M={M} pad={pad}")
     rosa.rosa_gather(Vbuf[:, :, :D], M, _dev(E), out)
     assert np.array_equal(out.cpu().numpy().view(np.uint16), oracle.gather(V, E, M))
+
+
+@pytest.mark.parametrize("B,T,D,pad,e_off", [(2, 1001, 80, 0, 0), (1, 1000, 1024, 0, 1),
+                                             (3, 515, 1024, 0, 0), (1, 4109, 512, 64, 0),
+                                             (1, 129, 64, 0, 3)])
+def test_gather_wave_path_edges(B, T, D, pad, e_off):
+    """The 8-byte (M = 4) gather: positions not a multiple of its 128-position
+    chunk or of 4 (E then read one value at a time), a last route group of
+    fewer than 16 routes, several batch rows, an E buffer not 16-byte aligned,
+    pitches that alias (two groups per XCD) and ones that do not."""
+    M = 4
+    rng = np.random.default_rng(1200 + T + e_off)
+    V = rng.integers(0, 65536, size=(B, T, D), dtype=np.uint16)
+    S = B * D // M
+    E = np.empty((S, T), dtype=np.int32)
+    for t in range(T):
+        E[:, t] = rng.integers(-1, t, size=S) if t > 0 else -1
+    Vbuf = torch.zeros((B, T, D + pad), dtype=torch.int16, device=DEV)
+    Vbuf[:, :, :D] = _dev(V.view(np.int16))
+    flat = torch.empty(S * T + e_off, dtype=torch.int32, device=DEV)
+    Ed = flat[e_off:].view(S, T)
+    Ed.copy_(_dev(E))
+    out = torch.empty((B, T, D), dtype=torch.int16, device=DEV)
+    _say(f"gather wave path B={B} T={T} D={D} pad={pad} e_off={e_off}")
+    rosa.rosa_gather(Vbuf[:, :, :D], M, Ed, out)
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), oracle.gather(V, E, M))
