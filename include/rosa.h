@@ -258,7 +258,8 @@ size_t rosa_state_bytes(int64_t S, int32_t K, int64_t t_capacity);
  * L/E/SYM for the prefix positions, identical to rosa_match.  in->K (or
  * 2^M) fixes the alphabet; t_capacity >= T bounds the total length.
  * The handle must be released with rosa_free (which does not free
- * state_buf).  A handle must not be used on two streams concurrently. */
+ * state_buf).  A handle must not be used on two streams concurrently.
+ * rosa_step_qk does not take it (ROSA_ERR_ARG). */
 rosa_status rosa_build(const rosa_input *in, int64_t t_capacity,
                        void *state_buf, size_t state_bytes,
                        rosa_state **handle, const rosa_out *out,
@@ -275,7 +276,8 @@ rosa_status rosa_build(const rosa_input *in, int64_t t_capacity,
  * NULL) and, if out_row is not NULL, the gathered values
  *   out_row[b*ldo_b + r*M + m] = V[b*ldv_b + (E+1)*ldv + r*M + m]  (0 if E<0)
  * V must already hold position t (tau = E+1 can equal t).  Returns
- * ROSA_ERR_CAPACITY (checked on the host) once t_capacity positions exist.
+ * ROSA_ERR_CAPACITY (checked on the host) once t_capacity positions exist;
+ * ROSA_ERR_ARG for a query/key handle (rosa_build_qk).
  * Cost per stream: the append is O(1) amortised (Sec. 2.2); the last-end
  * walk visits the new state's suffix path, a few states on typical streams
  * but up to t on a constant or short-period stream, where a step is then t
@@ -283,6 +285,52 @@ rosa_status rosa_build(const rosa_input *in, int64_t t_capacity,
 rosa_status rosa_step(rosa_state *h, const rosa_input *row, const uint16_t *V,
                       int64_t ldv, int64_t ldv_b, int32_t *end, int16_t *sym,
                       uint16_t *out_row, int64_t ldo_b, hipStream_t stream);
+
+/* Bytes of device state for the query/key decode of S streams, alphabet K,
+ * up to t_capacity time steps per stream: one suffix automaton per stream
+ * over the key units (at most max(2, 2*t_capacity - 1) states, Sec. 2.2
+ * bound), the matching state and the current unit's answers, and the start
+ * time of every unit.  0 on bad arguments. */
+size_t rosa_qk_state_bytes(int64_t S, int32_t K, int64_t t_capacity);
+
+/* Sec. 3.3 and Sec. 4.1 for separate query and key streams, online: the
+ * pages update each stream's automaton and matching state once per time
+ * step (with ROSA_QK_RLE, once per key run, App. C.6), which is what a
+ * decoder needs.  Builds, in the caller's buffer `state_buf` (256-byte
+ * aligned, at least rosa_qk_state_bytes(S, K, t_capacity) bytes), the state
+ * after the prefix q, k (same kind and shape as for rosa_match_qk; T may be
+ * 0) and returns a host handle in *handle.  If `out` is not NULL it
+ * receives the prefix's outputs exactly as rosa_match_qk would write them
+ * ([S][T] arrays; tau required when T > 0; the counterfactual tables need
+ * K = 2^M).  `flags`: 0 or ROSA_QK_RLE, fixed for the handle.  The handle
+ * works with rosa_state_length, rosa_state_status and rosa_free, not with
+ * rosa_step.  Cost: the prefix is walked in time order, one wave per
+ * stream (latency-bound, like the pages' per-stream automaton). */
+rosa_status rosa_build_qk(const rosa_input *q, const rosa_input *k,
+                          int32_t flags, int64_t t_capacity, void *state_buf,
+                          size_t state_bytes, rosa_state **handle,
+                          const rosa_qk_out *out, hipStream_t stream);
+
+/* One online query/key time step t = current length for every stream (Sec.
+ * 3.3; Eq. (16): the destination is strictly before t; App. C.5: the
+ * counterfactual branches are one more matching update from the same
+ * state).  q_row, k_row: T == 1, same kind, S, B, D, M/K as at build.  With
+ * ROSA_QK_RLE, a key symbol equal to the previous one continues the current
+ * run: the automaton and the matching state do not move and the outputs
+ * are the run's (its destination now kept if it is before t).  Writes the
+ * step's outputs into `out` as [S] arrays (cf_tau, cf_ridx: [S][M][2]):
+ * tau required, end, len, run_of, ridx, cf_tau, cf_ridx optional,
+ * run_start must be NULL.  The values equal rosa_match_qk's at time t over
+ * the concatenated streams.  ROSA_ERR_CAPACITY (checked on the host) once
+ * t_capacity steps exist; ROSA_ERR_ARG for a self-match handle.  A symbol
+ * >= K sets the handle's sticky flag (rosa_state_status).  Cost per stream:
+ * the append is O(1) amortised and the matching update follows suffix
+ * links; the last-unit walk after an append visits the new state's suffix
+ * path (up to the number of units on a periodic key stream without run
+ * folding). */
+rosa_status rosa_step_qk(rosa_state *h, const rosa_input *q_row,
+                         const rosa_input *k_row, const rosa_qk_out *out,
+                         hipStream_t stream);
 
 /* Positions processed so far by the handle (host value, no sync). */
 int64_t rosa_state_length(const rosa_state *h);

@@ -64,6 +64,9 @@ struct rosa_state {
     int64_t S, K, Tcap, len;
     int32_t kind, M;
     int64_t B, D, R;
+    int32_t qk;      // 0: self-match (rosa_build), 1: query/key (rosa_build_qk)
+    int32_t rle;     // query/key: ROSA_QK_RLE given at build
+    int32_t cfbits;  // query/key: query bits of the counterfactual branches (0: none)
 };
 
 static const uint64_t kStateMagic = 0x524f53415354ull;  // "ROSAST"
@@ -386,6 +389,69 @@ rosa_status prep_rows(const Shape &sh, const rosa_input *in, uint8_t *rows,
 
 }  // namespace
 
+namespace {
+
+// Query bits of the counterfactual branches: M for bf16 inputs, log2 K for
+// symbols when K is a power of two >= 2, else 0.
+int qk_cf_bits(const Shape &sh)
+{
+    if (sh.kind != ROSA_IN_SYMBOLS)
+        return sh.M;
+    int M = 0;
+    while ((1 << M) < sh.K)
+        ++M;
+    return (1 << M) == sh.K ? M : 0;
+}
+
+// Pointers of a query/key decode state and the launch's input geometry.
+QkdParams qkd_params(void *buf, int64_t S, int64_t K, int64_t Tcap,
+                     const Shape &sh, const rosa_input *q, const rosa_input *k,
+                     int rle, int cfbits)
+{
+    const QkdLayout l = qkd_layout(S, K, Tcap);
+    char *base = reinterpret_cast<char *>(buf);
+    QkdParams p;
+    memset(&p, 0, sizeof p);
+    p.flags = reinterpret_cast<int32_t *>(base + l.flags);
+    p.meta = reinterpret_cast<int4 *>(base + l.meta);
+    p.mst = reinterpret_cast<int4 *>(base + l.mst);
+    p.cfst = reinterpret_cast<int2 *>(base + l.cfst);
+    p.states = reinterpret_cast<int32_t *>(base + l.states);
+    p.start = reinterpret_cast<int32_t *>(base + l.start);
+    p.S = S;
+    p.Ncap = l.Ncap;
+    p.RSi = l.RS / 4;
+    p.Ucap = Tcap;
+    p.K = (int32_t)K;
+    p.M = cfbits;
+    p.rle = rle;
+    p.kind = sh.kind;
+    p.Min = sh.M;
+    p.q = q->data;
+    p.k = k->data;
+    p.ldq = q->ld;
+    p.ldk = k->ld;
+    p.R = sh.R;
+    p.Tin = sh.T;
+    return p;
+}
+
+void qkd_outputs(QkdParams &p, const rosa_qk_out *out)
+{
+    if (!out)
+        return;
+    p.tau = out->tau;
+    p.end = out->end;
+    p.len = out->len;
+    p.run_of = out->run_of;
+    p.run_start = out->run_start;
+    p.ridx = out->ridx;
+    p.cf_tau = out->cf_tau;
+    p.cf_ridx = out->cf_ridx;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t rosa_match_qk_workspace_bytes(int64_t S, int64_t T, int32_t K)
@@ -650,6 +716,8 @@ rosa_status rosa_step(rosa_state *h, const rosa_input *row, const uint16_t *V,
 {
     if (!handle_live(h))
         return ROSA_ERR_STATE;
+    if (h->qk)
+        return ROSA_ERR_ARG;
     Shape sh;
     rosa_status st = resolve(row, &sh, false);
     if (st != ROSA_OK)
@@ -672,6 +740,122 @@ rosa_status rosa_step(rosa_state *h, const rosa_input *row, const uint16_t *V,
                                    row->data, ld, h->R, h->M, V, ldv, ldv_b, end,
                                    sym, out_row, ldo_b, stream);
     if (e != hipSuccess)
+        return ROSA_ERR_HIP;
+    h->len += 1;
+    return ROSA_OK;
+}
+
+size_t rosa_qk_state_bytes(int64_t S, int32_t K, int64_t t_capacity)
+{
+    if (S < 1 || K < 1 || K > 256 || t_capacity < 1 || t_capacity >= kMaxT ||
+        S * t_capacity >= kMaxST)
+        return 0;
+    return qkd_layout(S, K, t_capacity).total;
+}
+
+rosa_status rosa_build_qk(const rosa_input *q, const rosa_input *k,
+                          int32_t flags, int64_t t_capacity, void *state_buf,
+                          size_t state_bytes, rosa_state **handle,
+                          const rosa_qk_out *out, hipStream_t stream)
+{
+    Shape sq, sk;
+    rosa_status st = resolve(q, &sq, true);
+    if (st != ROSA_OK)
+        return st;
+    st = resolve(k, &sk, true);
+    if (st != ROSA_OK)
+        return st;
+    if (sq.kind != sk.kind || sq.S != sk.S || sq.T != sk.T || sq.K != sk.K ||
+        sq.B != sk.B || sq.D != sk.D || sq.M != sk.M)
+        return ROSA_ERR_ARG;
+    if ((flags & ~ROSA_QK_RLE) != 0 || !handle || !state_buf ||
+        t_capacity < 1 || t_capacity < sq.T || t_capacity >= kMaxT ||
+        (reinterpret_cast<uintptr_t>(state_buf) & 255))
+        return ROSA_ERR_ARG;
+    const int cfbits = qk_cf_bits(sq);
+    if (out && ((sq.T > 0 && !out->tau) ||
+                ((out->cf_tau || out->cf_ridx) && cfbits < 1)))
+        return ROSA_ERR_ARG;
+    const size_t need = rosa_qk_state_bytes(sq.S, sq.K, t_capacity);
+    if (need == 0)
+        return ROSA_ERR_ARG;
+    if (state_bytes < need)
+        return ROSA_ERR_CAPACITY;
+    rosa_state *h = (rosa_state *)calloc(1, sizeof(rosa_state));
+    if (!h)
+        return ROSA_ERR_NOMEM;
+    if (!handle_add(h)) {
+        free(h);
+        return ROSA_ERR_NOMEM;
+    }
+    const int rle = (flags & ROSA_QK_RLE) ? 1 : 0;
+    QkdParams p = qkd_params(state_buf, sq.S, sq.K, t_capacity, sq, q, k, rle,
+                             cfbits);
+    p.init = 1;
+    p.t0 = 0;
+    p.n = sq.T;
+    p.ostride = sq.T;
+    qkd_outputs(p, out);
+    hipError_t e = launch_clear_flags(p.flags, stream);
+    if (e == hipSuccess)
+        e = launch_qkd(p, stream);
+    if (e != hipSuccess) {
+        handle_remove(h);
+        free(h);
+        return ROSA_ERR_HIP;
+    }
+    h->magic = kStateMagic;
+    h->buf = state_buf;
+    h->bytes = state_bytes;
+    h->S = sq.S;
+    h->K = sq.K;
+    h->Tcap = t_capacity;
+    h->len = sq.T;
+    h->kind = sq.kind;
+    h->M = sq.M;
+    h->B = sq.B;
+    h->D = sq.D;
+    h->R = sq.R;
+    h->qk = 1;
+    h->rle = rle;
+    h->cfbits = cfbits;
+    *handle = h;
+    return ROSA_OK;
+}
+
+rosa_status rosa_step_qk(rosa_state *h, const rosa_input *q_row,
+                         const rosa_input *k_row, const rosa_qk_out *out,
+                         hipStream_t stream)
+{
+    if (!handle_live(h))
+        return ROSA_ERR_STATE;
+    if (!h->qk)
+        return ROSA_ERR_ARG;
+    Shape sq, sk;
+    rosa_status st = resolve(q_row, &sq, false);
+    if (st != ROSA_OK)
+        return st;
+    st = resolve(k_row, &sk, false);
+    if (st != ROSA_OK)
+        return st;
+    for (const Shape *sh : {&sq, &sk})
+        if (sh->T != 1 || sh->kind != h->kind || sh->S != h->S || sh->K != h->K ||
+            (sh->kind == ROSA_IN_BF16 &&
+             (sh->B != h->B || sh->D != h->D || sh->M != h->M)))
+            return ROSA_ERR_ARG;
+    if (!out || !out->tau || out->run_start ||
+        ((out->cf_tau || out->cf_ridx) && h->cfbits < 1))
+        return ROSA_ERR_ARG;
+    if (h->len >= h->Tcap)
+        return ROSA_ERR_CAPACITY;
+    QkdParams p = qkd_params(h->buf, h->S, h->K, h->Tcap, sq, q_row, k_row,
+                             h->rle, h->cfbits);
+    p.init = 0;
+    p.t0 = h->len;
+    p.n = 1;
+    p.ostride = 1;
+    qkd_outputs(p, out);
+    if (launch_qkd(p, stream) != hipSuccess)
         return ROSA_ERR_HIP;
     h->len += 1;
     return ROSA_OK;

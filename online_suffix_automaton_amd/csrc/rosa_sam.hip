@@ -499,6 +499,168 @@ __global__ __launch_bounds__(64) void qk_kernel(QkParams p)
             p.run_start[s * T + v] = v <= u ? st[v] : -1;
 }
 
+// ------------------------------------------ query / key retrieval, decode
+//
+// The same automaton and matching state as qk_kernel, kept in a caller's
+// state buffer between calls: qkd_kernel loads a stream's state, runs time
+// steps t0 .. t0+n-1 and stores the state back.  rosa_build_qk runs it over
+// the prefix (init: empty automaton, no unit yet) and rosa_step_qk for one
+// time step, so build + steps give the batch call's outputs by
+// construction.  With run folding a step that continues the current key
+// run moves neither the automaton nor the matching state; its outputs come
+// from the unit's kept answers (E, L, destination, and each flipped query
+// bit's E and destination), with the destination kept only when it is
+// before t.  The flipped branches are computed at every unit whenever the
+// alphabet has query bits (K = 2^M), whether or not the call asks for them,
+// so a later step that asks finds them current.
+
+__device__ __forceinline__ int qkd_symbol(const QkdParams &p, const void *in,
+                                          int64_t ld, int64_t s, int64_t i)
+{
+    if (p.kind == 0) {
+        int c = reinterpret_cast<const uint8_t *>(in)[s * ld + i];
+        if (c >= p.K) {
+            atomicOr(&p.flags[0], 1);
+            c = p.K - 1;
+        }
+        return c;
+    }
+    const int64_t b = s / p.R, r = s % p.R;
+    const uint16_t *h = reinterpret_cast<const uint16_t *>(in) +
+                        (b * p.Tin + i) * ld + r * p.Min;
+    int c = 0;
+    for (int j = 0; j < p.Min; ++j)
+        c |= (int)bf16_pos_s(h[j]) << j;
+    return c;
+}
+
+// One wave per stream: lane 0 advances the matching state and appends the
+// key units, lanes 1..M make the flipped-bit updates from the same state;
+// a workgroup barrier (the workgroup is this one wave) orders lane 0's
+// writes before the next unit's reads by the other lanes.  The symbols of
+// 64 steps are loaded at once, one step per lane, and broadcast.
+__global__ __launch_bounds__(64) void qkd_kernel(QkdParams p)
+{
+    const int lane = threadIdx.x;
+    const int64_t s = blockIdx.x;
+    if (s >= p.S)
+        return;
+    const bool act = lane <= p.M;   // lane 0, and a lane per query bit
+    SamStream a;
+    int32_t *rec = p.states + s * p.Ncap * p.RSi;
+    a.nd = reinterpret_cast<int4 *>(rec);
+    a.nds = p.RSi / 4;
+    a.nx = rec + 4;
+    a.nxs = p.RSi;
+    a.K = p.K;
+    int32_t *st = p.start + s * p.Ucap;
+    int u, ms, ml, kprev, qc, ue, ul, dstart;
+    if (p.init) {
+        a.nst = 0;
+        if (lane == 0)
+            sam_new_state(a, 0);
+        a.nst = 1;
+        a.tail = 0;
+        a.tail_len = 0;
+        a.tail_link = -1;
+        u = -1; ms = 0; ml = 0; kprev = -1; qc = 0;
+        ue = -1; ul = 0; dstart = -1;
+    } else {
+        const int4 m = p.meta[s];
+        a.tail = m.x;
+        a.nst = m.y;
+        a.tail_len = m.z;
+        a.tail_link = m.w;
+        const int4 m1 = p.mst[2 * s], m2 = p.mst[2 * s + 1];
+        u = m1.x; ms = m1.y; ml = m1.z; kprev = m1.w; qc = m2.x;
+        ue = -1; ul = 0; dstart = -1;
+        if (lane == 0) {
+            ue = m2.y; ul = m2.z; dstart = m2.w;
+        } else if (act) {
+            const int2 c = p.cfst[s * kQkdMaxBits + lane - 1];
+            ue = c.x; dstart = c.y;
+        }
+    }
+    __syncthreads();   // the root record before any lane reads it
+    int kbuf = 0, qbuf = 0;
+    for (int64_t i = 0; i < p.n; ++i) {
+        const int64_t t = p.t0 + i;
+        if ((i & 63) == 0 && i + lane < p.n) {
+            kbuf = qkd_symbol(p, p.k, p.ldk, s, i + lane);
+            qbuf = qkd_symbol(p, p.q, p.ldq, s, i + lane);
+        }
+        const int kc = __shfl(kbuf, (int)(i & 63));
+        const int qcur = __shfl(qbuf, (int)(i & 63));
+        if (!p.rle || kc != kprev) {
+            ++u;
+            if (lane == 0)
+                st[u] = (int32_t)t;
+            qc = qcur;
+            __syncthreads();   // start of unit u visible to every lane
+            if (act) {
+                int s2 = ms, l2 = ml;
+                qk_advance(a, s2, l2, lane == 0 ? qc : (qc ^ (1 << (lane - 1))));
+                ue = l2 > 0 ? a.node(s2).z : -1;
+                ul = l2;
+                dstart = ue >= 0 ? st[ue + 1] : -1;
+                if (lane == 0) {
+                    ms = s2;
+                    ml = l2;
+                }
+            }
+            __syncthreads();   // every read of this unit before the append
+            if (lane == 0) {
+                const int cur = sam_extend(a, kc);
+                for (int w = cur; w != -1; w = a.node(w).y)
+                    a.node(w).z = u;
+            }
+            ms = __shfl(ms, 0);
+            ml = __shfl(ml, 0);
+            __syncthreads();   // this unit's appends before the next reads
+            kprev = kc;
+        }
+        const int64_t o = s * p.ostride + i;
+        const int tv = (ue >= 0 && dstart < t) ? dstart : -1;
+        const int rv = tv >= 0 ? ue + 1 : -1;
+        const int tt = __shfl(tv, 0), rt = __shfl(rv, 0);
+        if (lane == 0) {
+            if (p.tau)
+                p.tau[o] = tt;
+            if (p.end)
+                p.end[o] = ue;
+            if (p.len)
+                p.len[o] = ul;
+            if (p.run_of)
+                p.run_of[o] = u;
+            if (p.ridx)
+                p.ridx[o] = rt;
+        }
+        if (lane >= 1 && act) {
+            const int j = lane - 1;
+            const int b = (qc >> j) & 1;
+            const int64_t c0 = (o * p.M + j) * 2;
+            if (p.cf_tau) {
+                p.cf_tau[c0 + b] = tt;
+                p.cf_tau[c0 + 1 - b] = tv;
+            }
+            if (p.cf_ridx) {
+                p.cf_ridx[c0 + b] = rt;
+                p.cf_ridx[c0 + 1 - b] = rv;
+            }
+        }
+    }
+    if (lane == 0) {
+        p.meta[s] = make_int4(a.tail, a.nst, a.tail_len, a.tail_link);
+        p.mst[2 * s] = make_int4(u, ms, ml, kprev);
+        p.mst[2 * s + 1] = make_int4(qc, ue, ul, dstart);
+    } else if (act) {
+        p.cfst[s * kQkdMaxBits + lane - 1] = make_int2(ue, dstart);
+    }
+    if (p.run_start)
+        for (int64_t v = lane; v < p.n; v += 64)
+            p.run_start[s * p.ostride + v] = v <= u ? st[v] : -1;
+}
+
 // ---------------------------------- query / key retrieval, tables in LDS
 //
 // The same automaton and matching state as qk_kernel for streams of at most
@@ -848,6 +1010,28 @@ hipError_t launch_sam_step(void *buf, int64_t S, int64_t K, int64_t Tcap,
     hipLaunchKernelGGL(sam_step_kernel, grid, dim3(64), 0, st, v, S, t, spw,
                        kind, row, ld, R, M, V, ldv, ldv_b, end, sym, out_row,
                        ldo_b);
+    return hipGetLastError();
+}
+
+QkdLayout qkd_layout(int64_t S, int64_t K, int64_t Tcap)
+{
+    QkdLayout l;
+    l.Ncap = Tcap <= 1 ? 2 : 2 * Tcap - 1;
+    l.RS = (int64_t)align_up((size_t)(16 + 4 * K), 64);
+    size_t o = 0;
+    l.flags = o;  o += 256;
+    l.meta = o;   o = align_up(o + (size_t)S * 16, 256);
+    l.mst = o;    o = align_up(o + (size_t)S * 32, 256);
+    l.cfst = o;   o = align_up(o + (size_t)S * kQkdMaxBits * 8, 256);
+    l.states = o; o = align_up(o + (size_t)S * l.Ncap * l.RS, 256);
+    l.start = o;  o = align_up(o + (size_t)S * Tcap * 4, 256);
+    l.total = o;
+    return l;
+}
+
+hipError_t launch_qkd(const QkdParams &p, hipStream_t st)
+{
+    hipLaunchKernelGGL(qkd_kernel, dim3((unsigned)p.S), dim3(64), 0, st, p);
     return hipGetLastError();
 }
 

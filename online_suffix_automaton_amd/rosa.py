@@ -55,6 +55,7 @@ _SYMBOLS = ["rosa_match_workspace_bytes", "rosa_match", "rosa_match_timed",
             "rosa_match_qk", "rosa_scatter_grad_workspace_bytes",
             "rosa_scatter_grad",
             "rosa_gather", "rosa_state_bytes", "rosa_build", "rosa_step",
+            "rosa_qk_state_bytes", "rosa_build_qk", "rosa_step_qk",
             "rosa_state_length", "rosa_state_status", "rosa_free",
             "rosa_error_string"]
 
@@ -85,6 +86,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "rosa_state_bytes": ([I64, I32, I64], SZ),
         "rosa_build": ([P, I64, P, SZ, ctypes.POINTER(P), P, P], ctypes.c_int),
         "rosa_step": ([P, P, P, I64, I64, P, P, P, I64, P], ctypes.c_int),
+        "rosa_qk_state_bytes": ([I64, I32, I64], SZ),
+        "rosa_build_qk": ([P, P, I32, I64, P, SZ, ctypes.POINTER(P), P, P],
+                          ctypes.c_int),
+        "rosa_step_qk": ([P, P, P, P, P], ctypes.c_int),
         "rosa_state_length": ([P], I64),
         "rosa_state_status": ([P, P], ctypes.c_int),
         "rosa_free": ([P], None),
@@ -356,6 +361,34 @@ def rosa_step(state: RosaState, row: rosa_input, V, end, sym=None,
                                     _ptr(out_row), ldo_b,
                                     _stream(stream, end.device)),
            "rosa_step")
+
+
+def rosa_qk_state_bytes(S: int, K: int, t_capacity: int) -> int:
+    return int(load_library().rosa_qk_state_bytes(S, K, t_capacity))
+
+
+def rosa_build_qk(q: rosa_input, k: rosa_input, flags: int, t_capacity: int,
+                  state_buf: torch.Tensor, out: rosa_qk_out | None = None,
+                  stream=None) -> RosaState:
+    """Query/key decode state after the prefix q, k (T may be 0); `out`
+    receives the prefix's outputs as rosa_match_qk would."""
+    _require_device(state_buf)
+    h = ctypes.c_void_p()
+    _check(load_library().rosa_build_qk(
+        ctypes.byref(q), ctypes.byref(k), flags, t_capacity,
+        state_buf.data_ptr(), state_buf.numel() * state_buf.element_size(),
+        ctypes.byref(h), ctypes.byref(out) if out is not None else None,
+        _stream(stream)), "rosa_build_qk")
+    return RosaState(h, state_buf)
+
+
+def rosa_step_qk(state: RosaState, q_row: rosa_input, k_row: rosa_input,
+                 out: rosa_qk_out, stream=None) -> None:
+    """One query/key time step for every stream: q_row, k_row with T == 1;
+    out: make_qk_out over [S] arrays (cf tables [S, M, 2])."""
+    _check(load_library().rosa_step_qk(state.handle, ctypes.byref(q_row),
+                                       ctypes.byref(k_row), ctypes.byref(out),
+                                       _stream(stream)), "rosa_step_qk")
 
 
 def rosa_state_length(state: RosaState) -> int:

@@ -213,3 +213,45 @@ def test_scatter_grad_rejects_bad_arguments():
     assert f(None, 1, 10, 8, 8, 4, P, P, 8, ws, big, None) == rosa.ROSA_ERR_ARG
     assert f(P, 1, 10, 8, 8, 4, P, P, 8, 0x100010, big, None) == rosa.ROSA_ERR_ARG
     assert f(P, 1, 10, 8, 8, 4, P, P, 8, ws, 16, None) == rosa.ROSA_ERR_CAPACITY
+
+
+def test_qk_decode_api_rejects_bad_handles_and_args():
+    """The query/key decode entry points validate on the host: sizes,
+    unknown handles, mismatched inputs, flags, capacity below the prefix,
+    misaligned or short buffers, tables for an alphabet without query bits.
+    Nothing here reaches a kernel."""
+    lib = rosa.load_library()
+    assert lib.rosa_qk_state_bytes(0, 16, 10) == 0
+    assert lib.rosa_qk_state_bytes(4, 0, 10) == 0
+    assert lib.rosa_qk_state_bytes(4, 257, 10) == 0
+    assert lib.rosa_qk_state_bytes(4, 16, 0) == 0
+    assert lib.rosa_qk_state_bytes(4, 16, 1 << 26) == 0
+    # per stream: (2*Tcap-1) records of 16 + 4K bytes and a start time per step
+    assert lib.rosa_qk_state_bytes(8, 16, 1000) >= 8 * (1999 * 128 + 4 * 1000)
+    row = _inp(T=1, ld=1)
+    out = rosa.rosa_qk_out()
+    out.tau = FAKE.value
+    for h in (None, ctypes.c_void_p(0x10)):
+        assert lib.rosa_step_qk(h, ctypes.byref(row), ctypes.byref(row),
+                                ctypes.byref(out), None) == rosa.ROSA_ERR_STATE
+    h = ctypes.c_void_p()
+    q, k = _inp(), _inp()
+    ok_buf, big = 0x100000, 1 << 40
+
+    def build(qq=q, kk=k, flags=0, cap=200, buf=ok_buf, nb=big, o=None):
+        return lib.rosa_build_qk(ctypes.byref(qq), ctypes.byref(kk), flags, cap,
+                                 buf, nb, ctypes.byref(h),
+                                 ctypes.byref(o) if o is not None else None, None)
+    assert build(kk=_inp(T=99)) == rosa.ROSA_ERR_ARG          # shapes differ
+    assert build(kk=_inp(K=8)) == rosa.ROSA_ERR_ARG
+    assert build(flags=2) == rosa.ROSA_ERR_ARG                 # unknown flag
+    assert build(cap=50) == rosa.ROSA_ERR_ARG                  # capacity < T
+    assert build(buf=0x100010) == rosa.ROSA_ERR_ARG            # not 256-aligned
+    assert build(buf=None) == rosa.ROSA_ERR_ARG
+    assert build(nb=64) == rosa.ROSA_ERR_CAPACITY
+    noto = rosa.rosa_qk_out()                                   # tau missing
+    assert build(o=noto) == rosa.ROSA_ERR_ARG
+    cf = rosa.rosa_qk_out()
+    cf.tau, cf.cf_tau = FAKE.value, FAKE.value
+    assert build(qq=_inp(K=3), kk=_inp(K=3), o=cf) == rosa.ROSA_ERR_ARG
+    assert not h.value
