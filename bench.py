@@ -429,6 +429,160 @@ def run_decode(args):
     }
 
 
+# -------------------------------------------------------------- qk decode
+
+QKD_METRIC = ("query/key decode positions/sec (512 streams, 65,536-step "
+              "prefix, 1024 steps, one rosa_step_qk each)")
+
+
+def run_qk_decode(args):
+    """Query/key decode: query and key hidden states [1, 65536 + 1024, 2048]
+    bf16 (N(0,1), independent), M = 4: 512 streams.  rosa_build_qk over the
+    prefix, then 1024 rosa_step_qk calls (one time step of every stream
+    each), with --rle and --cf as for the qk workload."""
+    import torch
+    from online_suffix_automaton_amd import rosa, synth
+    dev = torch.device("cuda:0")
+    T0, n, D, M = 65536, 1024, 2048, 4
+    Tc = T0 + n
+    S, K = D // M, 1 << M
+    _log("workload qk_decode: generating")
+    Hq = synth.bf16_normal((1, Tc, D), 71)
+    Hk = synth.bf16_normal((1, Tc, D), 72)
+    hq = torch.from_numpy(Hq.view(np.int16)).to(dev)
+    hk = torch.from_numpy(Hk.view(np.int16)).to(dev)
+    flags = rosa.ROSA_QK_RLE if args.rle else 0
+    cfw = M if args.cf else 0
+    buf = torch.empty(rosa.rosa_qk_state_bytes(S, K, Tc), dtype=torch.uint8,
+                      device=dev)
+
+    def outs(rows):
+        o = {f: torch.empty((rows, S), dtype=torch.int32, device=dev)
+             for f in ("tau", "end", "len", "run_of", "ridx")}
+        if cfw:
+            for f in ("cf_tau", "cf_ridx"):
+                o[f] = torch.empty((rows, S, M, 2), dtype=torch.int32, device=dev)
+        return o
+
+    def step_out(o, i):
+        return rosa.make_qk_out(o["tau"][i], **{f: v[i] for f, v in o.items()
+                                                if f != "tau"})
+    # warm-up on a separate short state (same kernel, other buffer)
+    wbuf = torch.empty(rosa.rosa_qk_state_bytes(S, K, 64), dtype=torch.uint8,
+                       device=dev)
+    wo = outs(1)
+    wst = rosa.rosa_build_qk(rosa.bf16_input(hq[:, :32], M),
+                             rosa.bf16_input(hk[:, :32], M), flags, 64, wbuf)
+    for i in range(min(args.warmup, 32)):
+        rosa.rosa_step_qk(wst, rosa.bf16_input(hq[:, 32 + i:33 + i], M),
+                          rosa.bf16_input(hk[:, 32 + i:33 + i], M), step_out(wo, 0))
+    torch.cuda.synchronize()
+    del wst, wbuf
+    _log("build over the prefix")
+    qpre, kpre = rosa.bf16_input(hq[:, :T0], M), rosa.bf16_input(hk[:, :T0], M)
+    b0 = torch.cuda.Event(enable_timing=True)
+    b1 = torch.cuda.Event(enable_timing=True)
+    b0.record()
+    st = rosa.rosa_build_qk(qpre, kpre, flags, Tc, buf)
+    b1.record()
+    torch.cuda.synchronize()
+    build_ms = b0.elapsed_time(b1)
+    qrows = [rosa.bf16_input(hq[:, T0 + i:T0 + i + 1], M) for i in range(n)]
+    krows = [rosa.bf16_input(hk[:, T0 + i:T0 + i + 1], M) for i in range(n)]
+    o1 = outs(n)
+    so1 = [step_out(o1, i) for i in range(n)]
+    _log(f"timing {n} steps")
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record()
+    for i in range(n):
+        rosa.rosa_step_qk(st, qrows[i], krows[i], so1[i])
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = ev0.elapsed_time(ev1)
+    if rosa.rosa_state_status(st) != rosa.ROSA_OK:
+        raise SystemExit("symbol range flag raised")
+    _log("per-step latency pass")
+    del st
+    st = rosa.rosa_build_qk(qpre, kpre, flags, Tc, buf)
+    o2 = outs(n)
+    so2 = [step_out(o2, i) for i in range(n)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(n):
+        rosa.rosa_step_qk(st, qrows[i], krows[i], so2[i])
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    step_ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
+    for f in o1:
+        if not torch.equal(o1[f], o2[f]):
+            raise SystemExit("qk decode: the two passes disagree")
+    # compulsory bytes of one step for all streams: the query and key rows
+    # (2 x 2048 bf16) and the outputs (5 int32 per stream, 16 more with the
+    # tables at M = 4)
+    step_bytes = 2 * D * 2 + S * 4 * (5 + (4 * cfw if cfw else 0))
+    achieved = step_bytes / (total_ms / n / 1e3)
+    roof = {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK, "traffic": None}
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        _log("oracle over prefix + steps (parity + baseline)")
+        oracle._load()
+        threads = max(1, min(args.cpu_threads, os.cpu_count() or 1))
+        chunks = [c for c in np.array_split(np.arange(S), threads) if len(c)]
+
+        def work(c):
+            s0, s1 = int(c[0]), int(c[-1]) + 1
+            q = oracle.discretize_bf16(np.ascontiguousarray(Hq[:, :, s0 * M:s1 * M]), M)
+            k = oracle.discretize_bf16(np.ascontiguousarray(Hk[:, :, s0 * M:s1 * M]), M)
+            return s0, s1, oracle.match_qk(q, k, K, M, bool(args.rle), cf=bool(cfw))
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+            res = list(ex.map(work, chunks))
+        cwall = time.perf_counter() - t0
+        for f in o1:
+            got = o1[f].cpu().numpy()
+            for s0, s1, w in res:
+                want = np.moveaxis(w[f][:, T0:], 0, 1)
+                if not np.array_equal(got[:, s0:s1], want):
+                    raise SystemExit(f"parity failure: qk decode {f} differs")
+        _log(f"parity ok; oracle {cwall:.3f} s")
+        cpu = {"value": S * Tc / cwall, "unit": "positions/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{S} streams x {Tc} time steps (prefix + steps), "
+                         f"discretize + query/key automaton match"
+                         f"{' with run folding' if args.rle else ''}"
+                         f"{' and tables' if cfw else ''}, streams split over "
+                         f"{threads} threads"}
+    return {
+        "metric": QKD_METRIC, "value": S * n / (total_ms / 1e3),
+        "unit": "positions/s", "n_gpus": 1, "steps": n, "warmup": args.warmup,
+        "ms_per_step": total_ms / n, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u8",
+        "data": "synthetic",
+        "config": {"workload": "qk_decode: query and key hidden [1,T,2048] bf16, "
+                               "M=4 -> 512 streams, prefix 65536, 1024 steps"
+                               f"{', run folding' if args.rle else ''}"
+                               f"{', counterfactual tables' if cfw else ''}",
+                   "streams": S, "T": Tc, "K": K, "rle": bool(args.rle),
+                   "cf": bool(cfw), "parallelism": "single GPU"},
+        "roofline": roof,
+        "step_latency_us": {"median": float(np.median(step_ms)) * 1e3,
+                            "p99": float(np.percentile(step_ms, 99)) * 1e3,
+                            "host_wall_per_step": wall / n * 1e6,
+                            "note": "median/p99: intervals between events "
+                                    "recorded after every step (second pass); "
+                                    "host_wall_per_step: the timed pass"},
+        "build_ms": build_ms,
+        "cpu_baseline": cpu,
+    }
+
+
 # ---------------------------------------------------------------------- qk
 
 def run_qk(args):
@@ -626,11 +780,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long",
                     choices=["long", "batched", "repeat", "lowent", "decode",
-                             "qk", "scatter"])
+                             "qk", "qk_decode", "scatter"])
     ap.add_argument("--rle", action="store_true",
-                    help="qk workload: fold the key stream into runs")
+                    help="qk and qk_decode workloads: fold the key stream into runs")
     ap.add_argument("--cf", action="store_true",
-                    help="qk workload: also the per-bit counterfactual tables")
+                    help="qk and qk_decode workloads: also the per-bit "
+                         "counterfactual tables")
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the oracle baseline and parity check")
     ap.add_argument("--cpu-threads", type=int, default=16)
@@ -665,6 +820,9 @@ def main():
         return
     if args.workload == "qk":
         print(json.dumps(run_qk(args)), flush=True)
+        return
+    if args.workload == "qk_decode":
+        print(json.dumps(run_qk_decode(args)), flush=True)
         return
     if args.workload == "scatter":
         print(json.dumps(run_scatter(args)), flush=True)

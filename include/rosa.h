@@ -304,8 +304,13 @@ size_t rosa_qk_state_bytes(int64_t S, int32_t K, int64_t t_capacity);
  * ([S][T] arrays; tau required when T > 0; the counterfactual tables need
  * K = 2^M).  `flags`: 0 or ROSA_QK_RLE, fixed for the handle.  The handle
  * works with rosa_state_length, rosa_state_status and rosa_free, not with
- * rosa_step.  Cost: the prefix is walked in time order, one wave per
- * stream (latency-bound, like the pages' per-stream automaton). */
+ * rosa_step.  Cost: for prefixes of two steps or more and K <= 60, the
+ * batch query/key retrieval gives every step's answers, the automaton is
+ * built by appends without the last-unit walks (the last units filled in
+ * one pass afterwards), and only the last key run is walked in time order;
+ * otherwise the whole prefix is walked in time order, one wave per stream.
+ * During the build, the state buffer also holds the batch retrieval's
+ * workspace, which rosa_qk_state_bytes includes. */
 rosa_status rosa_build_qk(const rosa_input *q, const rosa_input *k,
                           int32_t flags, int64_t t_capacity, void *state_buf,
                           size_t state_bytes, rosa_state **handle,

@@ -403,6 +403,65 @@ int qk_cf_bits(const Shape &sh)
     return (1 << M) == sh.K ? M : 0;
 }
 
+// The query/key retrieval over shapes already checked (T > 0): symbol rows
+// into the workspace `ws` (layout qk_layout(S, T, K); a symbol >= K sets
+// *fl), then the kernels.  M: query bits of the counterfactual tables.
+rosa_status qk_impl(const Shape &sq, const Shape &sk, const rosa_input *q,
+                    const rosa_input *k, int rle, int M, const rosa_qk_out *out,
+                    void *ws, int32_t *fl, hipStream_t stream)
+{
+    const QkLayout l = qk_layout(sq.S, sq.T, sq.K);
+    char *base = reinterpret_cast<char *>(ws);
+    uint8_t *qrows = reinterpret_cast<uint8_t *>(base + l.qrows);
+    uint8_t *krows = reinterpret_cast<uint8_t *>(base + l.krows);
+    rosa_status st = prep_rows(sq, q, qrows, l.Tp, fl, stream);
+    if (st != ROSA_OK)
+        return st;
+    st = prep_rows(sk, k, krows, l.Tp, fl, stream);
+    if (st != ROSA_OK)
+        return st;
+    QkParams p;
+    memset(&p, 0, sizeof p);
+    p.q = qrows;
+    p.k = krows;
+    p.Tp = l.Tp;
+    p.S = sq.S;
+    p.T = sq.T;
+    p.Ncap = l.Ncap;
+    p.K = sq.K;
+    p.M = M;
+    p.rle = rle;
+    p.nodes = reinterpret_cast<int4 *>(base + l.nodes);
+    p.next = reinterpret_cast<int32_t *>(base + l.next);
+    p.start = reinterpret_cast<int32_t *>(base + l.start);
+    p.redo = reinterpret_cast<int32_t *>(base + l.redo);
+    p.qu = reinterpret_cast<uint8_t *>(base + l.qu);
+    p.ku = reinterpret_cast<uint8_t *>(base + l.ku);
+    p.nunit = reinterpret_cast<int32_t *>(base + l.nunit);
+    p.ucnt = reinterpret_cast<int32_t *>(base + l.ucnt);
+    p.hcnt = reinterpret_cast<int32_t *>(base + l.hcnt);
+    p.koff = reinterpret_cast<int32_t *>(base + l.koff);
+    p.klist = reinterpret_cast<int2 *>(base + l.klist);
+    p.ptab = reinterpret_cast<int32_t *>(base + l.ptab);
+    p.dfl = reinterpret_cast<uint32_t *>(base + l.dfl);
+    p.eo = reinterpret_cast<int4 *>(base + l.eo);
+    p.cfe = reinterpret_cast<int2 *>(base + l.cfe);
+    p.uof = reinterpret_cast<int32_t *>(base + l.uof);
+    p.dstream = reinterpret_cast<int32_t *>(base + l.dstream);
+    p.xl = reinterpret_cast<int2 *>(base + l.xl);
+    p.xn = reinterpret_cast<int32_t *>(base + l.xn);
+    p.tau = out->tau;
+    p.end = out->end;
+    p.len = out->len;
+    p.run_of = out->run_of;
+    p.run_start = out->run_start;
+    p.ridx = out->ridx;
+    p.cf_tau = out->cf_tau;
+    p.cf_ridx = out->cf_ridx;
+    ROSA_TRY(launch_qk(p, stream));
+    return ROSA_OK;
+}
+
 // Pointers of a query/key decode state and the launch's input geometry.
 QkdParams qkd_params(void *buf, int64_t S, int64_t K, int64_t Tcap,
                      const Shape &sh, const rosa_input *q, const rosa_input *k,
@@ -479,72 +538,18 @@ rosa_status rosa_match_qk(const rosa_input *q, const rosa_input *k,
     if ((flags & ~ROSA_QK_RLE) != 0 || !out || (!out->tau && sq.T > 0) || !ws ||
         (reinterpret_cast<uintptr_t>(ws) & 255) != 0)
         return ROSA_ERR_ARG;
-    int M = sq.M;
-    if (sq.kind == ROSA_IN_SYMBOLS) {
-        M = 0;
-        while ((1 << M) < sq.K)
-            ++M;
-        if ((1 << M) != sq.K)
-            M = 0;
-    }
+    const int M = qk_cf_bits(sq);
     if ((out->cf_tau || out->cf_ridx) && M < 1)
         return ROSA_ERR_ARG;
     const QkLayout l = qk_layout(sq.S, sq.T, sq.K);
     if (ws_bytes < l.total)
         return ROSA_ERR_CAPACITY;
-    char *base = reinterpret_cast<char *>(ws);
-    int32_t *fl = reinterpret_cast<int32_t *>(base + l.flags);
+    int32_t *fl = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(ws) + l.flags);
     ROSA_TRY(launch_clear_flags(fl, stream));
     if (sq.T == 0)
         return ROSA_OK;
-    uint8_t *qrows = reinterpret_cast<uint8_t *>(base + l.qrows);
-    uint8_t *krows = reinterpret_cast<uint8_t *>(base + l.krows);
-    st = prep_rows(sq, q, qrows, l.Tp, fl, stream);
-    if (st != ROSA_OK)
-        return st;
-    st = prep_rows(sk, k, krows, l.Tp, fl, stream);
-    if (st != ROSA_OK)
-        return st;
-    QkParams p;
-    memset(&p, 0, sizeof p);
-    p.q = qrows;
-    p.k = krows;
-    p.Tp = l.Tp;
-    p.S = sq.S;
-    p.T = sq.T;
-    p.Ncap = l.Ncap;
-    p.K = sq.K;
-    p.M = M;
-    p.rle = (flags & ROSA_QK_RLE) ? 1 : 0;
-    p.nodes = reinterpret_cast<int4 *>(base + l.nodes);
-    p.next = reinterpret_cast<int32_t *>(base + l.next);
-    p.start = reinterpret_cast<int32_t *>(base + l.start);
-    p.redo = reinterpret_cast<int32_t *>(base + l.redo);
-    p.qu = reinterpret_cast<uint8_t *>(base + l.qu);
-    p.ku = reinterpret_cast<uint8_t *>(base + l.ku);
-    p.nunit = reinterpret_cast<int32_t *>(base + l.nunit);
-    p.ucnt = reinterpret_cast<int32_t *>(base + l.ucnt);
-    p.hcnt = reinterpret_cast<int32_t *>(base + l.hcnt);
-    p.koff = reinterpret_cast<int32_t *>(base + l.koff);
-    p.klist = reinterpret_cast<int2 *>(base + l.klist);
-    p.ptab = reinterpret_cast<int32_t *>(base + l.ptab);
-    p.dfl = reinterpret_cast<uint32_t *>(base + l.dfl);
-    p.eo = reinterpret_cast<int4 *>(base + l.eo);
-    p.cfe = reinterpret_cast<int2 *>(base + l.cfe);
-    p.uof = reinterpret_cast<int32_t *>(base + l.uof);
-    p.dstream = reinterpret_cast<int32_t *>(base + l.dstream);
-    p.xl = reinterpret_cast<int2 *>(base + l.xl);
-    p.xn = reinterpret_cast<int32_t *>(base + l.xn);
-    p.tau = out->tau;
-    p.end = out->end;
-    p.len = out->len;
-    p.run_of = out->run_of;
-    p.run_start = out->run_start;
-    p.ridx = out->ridx;
-    p.cf_tau = out->cf_tau;
-    p.cf_ridx = out->cf_ridx;
-    ROSA_TRY(launch_qk(p, stream));
-    return ROSA_OK;
+    return qk_impl(sq, sk, q, k, (flags & ROSA_QK_RLE) ? 1 : 0, M, out, ws, fl,
+                   stream);
 }
 
 size_t rosa_scatter_grad_workspace_bytes(int64_t S, int64_t T)
@@ -797,12 +802,39 @@ rosa_status rosa_build_qk(const rosa_input *q, const rosa_input *k,
     p.ostride = sq.T;
     qkd_outputs(p, out);
     hipError_t e = launch_clear_flags(p.flags, stream);
-    if (e == hipSuccess)
+    rosa_status bs = ROSA_OK;
+    // Prefixes of two steps or more: the batch retrieval gives every time
+    // step's E and L (and the caller's outputs), the automaton is built by
+    // whole-wave appends, and only the last key run is walked in time order
+    // (qkd_prefix_kernel).  Otherwise, or for alphabets over 60 symbols, the
+    // whole prefix is walked in time order.
+    const QkdLayout l = qkd_layout(sq.S, sq.K, t_capacity);
+    const bool fast = sq.T >= 2 && sq.K <= 60 &&
+                      qk_layout(sq.S, sq.T, sq.K).total <= l.ws_bytes;
+    if (e == hipSuccess && fast) {
+        char *base = reinterpret_cast<char *>(state_buf);
+        int32_t *bscr = reinterpret_cast<int32_t *>(base + l.bscr);
+        rosa_qk_out o2;
+        memset(&o2, 0, sizeof o2);
+        if (out)
+            o2 = *out;
+        if (!o2.tau)
+            o2.tau = p.start;   // not read; the unit starts overwrite it
+        if (!o2.end)
+            o2.end = bscr;
+        if (!o2.len)
+            o2.len = bscr + sq.S * sq.T;
+        bs = qk_impl(sq, sk, q, k, rle, cfbits, &o2, base + l.states, p.flags,
+                     stream);
+        if (bs == ROSA_OK)
+            e = launch_qkd_prefix(p, o2.end, o2.len, sq.T, stream);
+    } else if (e == hipSuccess) {
         e = launch_qkd(p, stream);
-    if (e != hipSuccess) {
+    }
+    if (e != hipSuccess || bs != ROSA_OK) {
         handle_remove(h);
         free(h);
-        return ROSA_ERR_HIP;
+        return bs != ROSA_OK ? bs : ROSA_ERR_HIP;
     }
     h->magic = kStateMagic;
     h->buf = state_buf;

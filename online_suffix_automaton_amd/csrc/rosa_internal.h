@@ -153,10 +153,14 @@ struct QkParams {
 // unit, clone flag}, then the K-wide transition row), its registers, the
 // matching state and the current unit's answers, and the start time of
 // every unit.  Regions in QkdLayout, sizes for Ucap = t_capacity units.
+// During rosa_build_qk the records' region first holds the batch query/key
+// workspace (ws_bytes: room for t_capacity steps), and bscr the batch's E
+// and L per time step ([S][T] each) when the caller does not ask for them.
 constexpr int kQkdMaxBits = 8;   // counterfactual branches kept per stream
 
 struct QkdLayout {
-    size_t flags, meta, mst, cfst, states, start, total;
+    size_t flags, meta, mst, cfst, states, start, bscr, total;
+    size_t ws_bytes;
     int64_t Ncap, RS;
 };
 QkdLayout qkd_layout(int64_t S, int64_t K, int64_t Tcap);
@@ -182,6 +186,8 @@ struct QkdParams {
     int32_t *tau, *end, *len, *run_of, *run_start, *ridx, *cf_tau, *cf_ridx;
 };
 hipError_t launch_qkd(const QkdParams &p, hipStream_t st);
+hipError_t launch_qkd_prefix(const QkdParams &p, const int32_t *bend,
+                             const int32_t *blen, int64_t bld, hipStream_t st);
 
 // Output pieces per stream the grouped-key kernels may leave to their
 // expansion kernel: 64 time steps each, one per unit at most beyond the

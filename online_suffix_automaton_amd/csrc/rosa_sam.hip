@@ -534,18 +534,16 @@ __device__ __forceinline__ int qkd_symbol(const QkdParams &p, const void *in,
     return c;
 }
 
-// One wave per stream: lane 0 advances the matching state and appends the
-// key units, lanes 1..M make the flipped-bit updates from the same state;
-// a workgroup barrier (the workgroup is this one wave) orders lane 0's
-// writes before the next unit's reads by the other lanes.  The symbols of
-// 64 steps are loaded at once, one step per lane, and broadcast.
-__global__ __launch_bounds__(64) void qkd_kernel(QkdParams p)
+// A stream's decode registers between time steps: the current unit, the
+// matching state, the previous key symbol, the unit's query symbol and its
+// answers (lane 0: E, L, destination; lane j+1: E and destination with
+// query bit j flipped).
+struct QkdRegs {
+    int u, ms, ml, kprev, qc, ue, ul, dstart;
+};
+
+__device__ __forceinline__ SamStream qkd_stream(const QkdParams &p, int64_t s)
 {
-    const int lane = threadIdx.x;
-    const int64_t s = blockIdx.x;
-    if (s >= p.S)
-        return;
-    const bool act = lane <= p.M;   // lane 0, and a lane per query bit
     SamStream a;
     int32_t *rec = p.states + s * p.Ncap * p.RSi;
     a.nd = reinterpret_cast<int4 *>(rec);
@@ -553,44 +551,59 @@ __global__ __launch_bounds__(64) void qkd_kernel(QkdParams p)
     a.nx = rec + 4;
     a.nxs = p.RSi;
     a.K = p.K;
-    int32_t *st = p.start + s * p.Ucap;
-    int u, ms, ml, kprev, qc, ue, ul, dstart;
-    if (p.init) {
-        a.nst = 0;
-        if (lane == 0)
-            sam_new_state(a, 0);
-        a.nst = 1;
-        a.tail = 0;
-        a.tail_len = 0;
-        a.tail_link = -1;
-        u = -1; ms = 0; ml = 0; kprev = -1; qc = 0;
-        ue = -1; ul = 0; dstart = -1;
-    } else {
-        const int4 m = p.meta[s];
-        a.tail = m.x;
-        a.nst = m.y;
-        a.tail_len = m.z;
-        a.tail_link = m.w;
-        const int4 m1 = p.mst[2 * s], m2 = p.mst[2 * s + 1];
-        u = m1.x; ms = m1.y; ml = m1.z; kprev = m1.w; qc = m2.x;
-        ue = -1; ul = 0; dstart = -1;
-        if (lane == 0) {
-            ue = m2.y; ul = m2.z; dstart = m2.w;
-        } else if (act) {
-            const int2 c = p.cfst[s * kQkdMaxBits + lane - 1];
-            ue = c.x; dstart = c.y;
-        }
+    a.tail = 0;
+    a.nst = 0;
+    a.tail_len = 0;
+    a.tail_link = -1;
+    return a;
+}
+
+__device__ __forceinline__ QkdRegs qkd_fresh()
+{
+    QkdRegs r;
+    r.u = -1; r.ms = 0; r.ml = 0; r.kprev = -1; r.qc = 0;
+    r.ue = -1; r.ul = 0; r.dstart = -1;
+    return r;
+}
+
+__device__ __forceinline__ void qkd_save(const QkdParams &p, const SamStream &a, int64_t s,
+                         const QkdRegs &r)
+{
+    const int lane = threadIdx.x;
+    if (lane == 0) {
+        p.meta[s] = make_int4(a.tail, a.nst, a.tail_len, a.tail_link);
+        p.mst[2 * s] = make_int4(r.u, r.ms, r.ml, r.kprev);
+        p.mst[2 * s + 1] = make_int4(r.qc, r.ue, r.ul, r.dstart);
+    } else if (lane <= p.M) {
+        p.cfst[s * kQkdMaxBits + lane - 1] = make_int2(r.ue, r.dstart);
     }
-    __syncthreads();   // the root record before any lane reads it
+}
+
+// Time steps tb .. te-1 of stream s, in order, from the registers `r` (the
+// input and output index of time t is t - p.t0).  One wave: lane 0
+// advances the matching state and appends the key units, lanes 1..M make
+// the flipped-bit updates from the same state; a workgroup barrier (the
+// workgroup is this one wave) orders lane 0's writes before the next
+// unit's reads by the other lanes.  The symbols of 64 steps are loaded at
+// once, one step per lane, and broadcast.
+__device__ __forceinline__ void qkd_steps(const QkdParams &p, SamStream &a, int64_t s,
+                          int64_t tb, int64_t te, QkdRegs &r)
+{
+    const int lane = threadIdx.x;
+    const bool act = lane <= p.M;   // lane 0, and a lane per query bit
+    int32_t *st = p.start + s * p.Ucap;
+    // the registers as locals (kept out of memory), written back at the end
+    int u = r.u, ms = r.ms, ml = r.ml, kprev = r.kprev, qc = r.qc;
+    int ue = r.ue, ul = r.ul, dstart = r.dstart;
     int kbuf = 0, qbuf = 0;
-    for (int64_t i = 0; i < p.n; ++i) {
-        const int64_t t = p.t0 + i;
-        if ((i & 63) == 0 && i + lane < p.n) {
-            kbuf = qkd_symbol(p, p.k, p.ldk, s, i + lane);
-            qbuf = qkd_symbol(p, p.q, p.ldq, s, i + lane);
+    for (int64_t t = tb; t < te; ++t) {
+        const int64_t j = t - tb;
+        if ((j & 63) == 0 && t + lane < te) {
+            kbuf = qkd_symbol(p, p.k, p.ldk, s, t + lane - p.t0);
+            qbuf = qkd_symbol(p, p.q, p.ldq, s, t + lane - p.t0);
         }
-        const int kc = __shfl(kbuf, (int)(i & 63));
-        const int qcur = __shfl(qbuf, (int)(i & 63));
+        const int kc = __shfl(kbuf, (int)(j & 63));
+        const int qcur = __shfl(qbuf, (int)(j & 63));
         if (!p.rle || kc != kprev) {
             ++u;
             if (lane == 0)
@@ -619,7 +632,7 @@ __global__ __launch_bounds__(64) void qkd_kernel(QkdParams p)
             __syncthreads();   // this unit's appends before the next reads
             kprev = kc;
         }
-        const int64_t o = s * p.ostride + i;
+        const int64_t o = s * p.ostride + (t - p.t0);
         const int tv = (ue >= 0 && dstart < t) ? dstart : -1;
         const int rv = tv >= 0 ? ue + 1 : -1;
         const int tt = __shfl(tv, 0), rt = __shfl(rv, 0);
@@ -636,9 +649,9 @@ __global__ __launch_bounds__(64) void qkd_kernel(QkdParams p)
                 p.ridx[o] = rt;
         }
         if (lane >= 1 && act) {
-            const int j = lane - 1;
-            const int b = (qc >> j) & 1;
-            const int64_t c0 = (o * p.M + j) * 2;
+            const int jb = lane - 1;
+            const int b = (qc >> jb) & 1;
+            const int64_t c0 = (o * p.M + jb) * 2;
             if (p.cf_tau) {
                 p.cf_tau[c0 + b] = tt;
                 p.cf_tau[c0 + 1 - b] = tv;
@@ -649,16 +662,138 @@ __global__ __launch_bounds__(64) void qkd_kernel(QkdParams p)
             }
         }
     }
-    if (lane == 0) {
-        p.meta[s] = make_int4(a.tail, a.nst, a.tail_len, a.tail_link);
-        p.mst[2 * s] = make_int4(u, ms, ml, kprev);
-        p.mst[2 * s + 1] = make_int4(qc, ue, ul, dstart);
-    } else if (act) {
-        p.cfst[s * kQkdMaxBits + lane - 1] = make_int2(ue, dstart);
+    r.u = u; r.ms = ms; r.ml = ml; r.kprev = kprev; r.qc = qc;
+    r.ue = ue; r.ul = ul; r.dstart = dstart;
+}
+
+// Time steps t0 .. t0+n-1 for every stream, one wave each: from an empty
+// automaton (init) or the saved state, then the state saved back.
+__global__ __launch_bounds__(64) void qkd_kernel(QkdParams p)
+{
+    const int lane = threadIdx.x;
+    const int64_t s = blockIdx.x;
+    if (s >= p.S)
+        return;
+    SamStream a = qkd_stream(p, s);
+    QkdRegs r = qkd_fresh();
+    if (p.init) {
+        if (lane == 0)
+            sam_new_state(a, 0);
+        a.nst = 1;
+    } else {
+        const int4 m = p.meta[s];
+        a.tail = m.x;
+        a.nst = m.y;
+        a.tail_len = m.z;
+        a.tail_link = m.w;
+        const int4 m1 = p.mst[2 * s], m2 = p.mst[2 * s + 1];
+        r.u = m1.x; r.ms = m1.y; r.ml = m1.z; r.kprev = m1.w; r.qc = m2.x;
+        if (lane == 0) {
+            r.ue = m2.y; r.ul = m2.z; r.dstart = m2.w;
+        } else if (lane <= p.M) {
+            const int2 c = p.cfst[s * kQkdMaxBits + lane - 1];
+            r.ue = c.x; r.dstart = c.y;
+        }
     }
-    if (p.run_start)
+    __syncthreads();   // the root record before any lane reads it
+    qkd_steps(p, a, s, p.t0, p.t0 + p.n, r);
+    qkd_save(p, a, s, r);
+    if (p.run_start) {
+        const int32_t *st = p.start + s * p.Ucap;
         for (int64_t v = lane; v < p.n; v += 64)
-            p.run_start[s * p.ostride + v] = v <= u ? st[v] : -1;
+            p.run_start[s * p.ostride + v] = v <= r.u ? st[v] : -1;
+    }
+}
+
+// Build over a prefix of p.n steps (p.t0 = 0) whose E and L per time step
+// the batch retrieval has already written (bend, blen: [S][bld]).  With U
+// units in the prefix, the key units 0..U-2 are appended by the whole wave
+// without the last-unit walks and the last units filled afterwards (the
+// self-match build's method: a state's last unit is the newest unit among
+// the non-clone states of its link subtree, which is what the walks
+// compute).  The matching state after unit U-2 is the state of the string
+// of length L ending at unit E (unit U-2's answer): the state created at
+// unit E, up its suffix links while the link's length is at least L (the
+// suffix path of a string's state holds every suffix of it).  The steps of
+// the last unit then run through qkd_steps, which computes that unit's
+// answers and its flipped-bit branches and leaves the registers a later
+// step continues from.  The walk-free appends need K <= 60 (one int per
+// lane); qkd_kernel serves larger alphabets.
+__global__ __launch_bounds__(64) void qkd_prefix_kernel(QkdParams p,
+                                                        const int32_t *__restrict__ bend,
+                                                        const int32_t *__restrict__ blen,
+                                                        int64_t bld)
+{
+    const int lane = threadIdx.x;
+    const int64_t s = blockIdx.x;
+    if (s >= p.S)
+        return;
+    SamStream a = qkd_stream(p, s);
+    int32_t *st = p.start + s * p.Ucap;
+    const int64_t T = p.n;
+    // units: start times into st, 64 steps at a time
+    int U = 0, kp = -1;
+    for (int64_t t0 = 0; t0 < T; t0 += 64) {
+        const int64_t t = t0 + lane;
+        const int kc = t < T ? qkd_symbol(p, p.k, p.ldk, s, t) : -1;
+        const int prev = __shfl_up(kc, 1);
+        const int before = lane == 0 ? kp : prev;
+        const bool nu = t < T && (!p.rle || kc != before);
+        const uint64_t m = __ballot(nu);
+        if (nu)
+            st[U + __popcll(m & ((1ull << lane) - 1))] = (int32_t)t;
+        U += __popcll(m);
+        kp = __shfl(kc, 63);
+    }
+    __syncthreads();   // unit starts visible to every lane
+    QkdRegs r = qkd_fresh();
+    int64_t tl = 0;
+    if (lane < 4 + a.K)
+        sam_rec(a, 0)[lane] = lane == 0 ? 0 : lane == 3 ? 0 : -1;
+    a.nst = 1;
+    if (U >= 2) {
+        tl = st[U - 1];
+        const int e = bend[s * bld + tl - 1];
+        const int ml = blen[s * bld + tl - 1];
+        WaveSam ws = {-2, -1};
+        int se = 0;
+        int kc = 0;
+        for (int v0 = 0; v0 < U - 1; v0 += 64) {
+            // the key symbols of units v0 .. v0+63, one per lane
+            const int v = v0 + lane;
+            const int kv = v < U - 1 ? qkd_symbol(p, p.k, p.ldk, s, st[v]) : 0;
+            const int nv = min(64, U - 1 - v0);
+            for (int i = 0; i < nv; ++i) {
+                kc = __shfl(kv, i);
+                sam_extend_wave(a, ws, kc);
+                if (v0 + i == e)
+                    se = a.tail;
+            }
+        }
+        __syncthreads();   // the records visible to every lane
+        sam_fill_last_wave(a, a.nst);
+        // the fill's atomics are made in L2; invalidate this CU's L1 so that
+        // the plain loads below and in qkd_steps see them
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
+        __syncthreads();   // the last units before any read
+        int ms = 0;
+        if (ml > 0) {
+            ms = se;
+            for (;;) {
+                const int lk = a.node(ms).y;
+                if (lk < 0 || a.node(lk).x < ml)
+                    break;
+                ms = lk;
+            }
+        }
+        r.u = U - 2;
+        r.ms = ms;
+        r.ml = ml;
+        r.kprev = kc;
+    }
+    __syncthreads();   // the root record before any lane reads it
+    qkd_steps(p, a, s, tl, T, r);
+    qkd_save(p, a, s, r);
 }
 
 // ---------------------------------- query / key retrieval, tables in LDS
@@ -1023,8 +1158,12 @@ QkdLayout qkd_layout(int64_t S, int64_t K, int64_t Tcap)
     l.meta = o;   o = align_up(o + (size_t)S * 16, 256);
     l.mst = o;    o = align_up(o + (size_t)S * 32, 256);
     l.cfst = o;   o = align_up(o + (size_t)S * kQkdMaxBits * 8, 256);
-    l.states = o; o = align_up(o + (size_t)S * l.Ncap * l.RS, 256);
+    size_t rec = (size_t)S * l.Ncap * l.RS;
+    const size_t ws = qk_layout(S, Tcap, K).total;
+    l.ws_bytes = rec > ws ? rec : ws;
+    l.states = o; o = align_up(o + l.ws_bytes, 256);
     l.start = o;  o = align_up(o + (size_t)S * Tcap * 4, 256);
+    l.bscr = o;   o = align_up(o + (size_t)S * Tcap * 8, 256);
     l.total = o;
     return l;
 }
@@ -1032,6 +1171,14 @@ QkdLayout qkd_layout(int64_t S, int64_t K, int64_t Tcap)
 hipError_t launch_qkd(const QkdParams &p, hipStream_t st)
 {
     hipLaunchKernelGGL(qkd_kernel, dim3((unsigned)p.S), dim3(64), 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_qkd_prefix(const QkdParams &p, const int32_t *bend,
+                             const int32_t *blen, int64_t bld, hipStream_t st)
+{
+    hipLaunchKernelGGL(qkd_prefix_kernel, dim3((unsigned)p.S), dim3(64), 0, st, p,
+                       bend, blen, bld);
     return hipGetLastError();
 }
 

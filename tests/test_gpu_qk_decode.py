@@ -210,3 +210,27 @@ def test_qk_decode_errors():
                       rosa.make_qk_out(tau))
     assert rosa.rosa_state_status(h3) == rosa.ROSA_ERR_SYMBOL
     rosa.rosa_free(h3)
+
+
+@pytest.mark.parametrize("rle", [False, True])
+def test_qk_decode_build_paths(rle):
+    """The build's two paths: prefixes of two steps or more and alphabets of
+    at most 60 symbols take the batch retrieval plus whole-wave appends, the
+    rest walk the prefix in time order.  Edges: a prefix of nearly the whole
+    stream, the shortest such prefix, alphabets of 60 and 61 symbols, a
+    prefix of exactly two key runs, and a prefix that is a single run."""
+    S, T = 4, 480
+    for K, T0 in ((16, 470), (16, 2), (60, 300), (61, 300)):
+        q, k = _streams(900 + K + T0, S, T, K, "mixed")
+        _symbols_case(q, k, K, T0, rle, f"qk decode build K={K} T0={T0} rle={rle}")
+    K = 16
+    rng = np.random.default_rng(31)
+    q = rng.integers(0, K, (S, T)).astype(np.uint8)
+    k = rng.integers(0, K, (S, T)).astype(np.uint8)
+    k[0, :200] = 3
+    k[0, 200:260] = 5                      # two runs, the prefix ends in the second
+    k[1, :300] = 7                         # the prefix is one run
+    q[2] = k[2]                            # equal streams
+    k[3, 250:450] = k[3, 50:250]           # a long repeat across the prefix's end
+    q[3, 250:450] = k[3, 250:450]
+    _symbols_case(q, k, K, 240, rle, f"qk decode build runs rle={rle}")
