@@ -10,6 +10,7 @@
 
 #include "rosa.h"
 #include "rosa_internal.h"
+#include "rosa_qk_decode.h"
 
 namespace rosa {
 // rosa_stream_io.hip

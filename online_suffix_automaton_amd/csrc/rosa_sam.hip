@@ -42,6 +42,7 @@
 // One lane owns one stream, so every access to a stream's tables is ordered
 // by program order; lanes of a wave work on different streams.
 #include "rosa_internal.h"
+#include "rosa_qk_decode.h"
 #include "rosa_sam_core.h"
 
 namespace rosa {
