@@ -10,7 +10,8 @@
  * ---------------------------------------
  *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
  *    library never allocates device memory; scratch comes from a caller
- *    workspace (rosa_match) or a caller state buffer (rosa_build/rosa_step).
+ *    workspace (rosa_match, rosa_match_qk, rosa_scatter_grad) or a caller
+ *    state buffer (rosa_build/rosa_step, rosa_build_qk/rosa_step_qk).
  *    The one exception is the fixed device array behind rosa_match_noalloc,
  *    which the HIP runtime places on each device the library runs on.
  *  - Every call only enqueues work on the caller's `stream` and returns; no
