@@ -801,6 +801,10 @@ def main():
     ap.add_argument("--v-pad", type=int, default=64, metavar="ELEMS",
                     help="long workload: V rows stored at a pitch of D + ELEMS "
                          "bf16 (0: dense rows)")
+    ap.add_argument("--no-split", action="store_true",
+                    help="workloads with a gather: time unsplit steps one after "
+                         "another on one stream instead of the two pipelined "
+                         "stream halves")
     ap.add_argument("--no-dense", action="store_true",
                     help="long workload: skip the second timed pass with V's "
                          "rows at the dense pitch")
@@ -881,34 +885,106 @@ def main():
             if i is not None:
                 ge[i].record(stream)
 
-    def timed(V):
-        """Warm-up, then `steps` steps between two events on the stream (ms
-        per step), then the same steps again with events around the
-        retrieval and gather kernels (their mean durations; the events are
-        kept out of the first loop, where they would add to short steps)."""
+    # Pipelined steps (with a gather): the streams in two halves by channel
+    # (routes 0..R/2-1 and R/2..R-1 of H and V), each with its own workspace
+    # and HIP stream (default priority).  The second half's match starts when
+    # the first half's is done; the first half's gather waits for the event
+    # rosa_match_timed records just before the second half's retrieval
+    # kernel, so that gather (memory-bound, no LDS) runs beside that kernel
+    # (VALU-bound, one workgroup per CU with nearly all of its LDS).  Steps
+    # are not joined one by one: the next step's first half starts behind
+    # this step's first-half gather, beside its second-half gather.
+    split = (Vd is not None and w["kind"] == "bf16" and not args.no_split
+             and S % 2 == 0 and (w["H"].shape[2] // 2) % w["M"] == 0)
+    if split:
+        h, Dh = S // 2, w["H"].shape[2] // 2
+        inA = rosa.bf16_input(Hd[:, :, :Dh], w["M"])
+        inB = rosa.bf16_input(Hd[:, :, Dh:], w["M"])
+        wsA = torch.empty(rosa.rosa_match_workspace_bytes(h, T, K), dtype=torch.uint8,
+                          device=dev)
+        wsB = torch.empty_like(wsA)
+        oA, oB = rosa.make_out(E[:h], SYM[:h]), rosa.make_out(E[h:], SYM[h:])
+        s2 = torch.cuda.Stream(device=dev)
+        evA, evB0, evB1, evJ, evGA, evGB = (torch.cuda.Event() for _ in range(6))
+
+    def step_piped(V):
+        # one gather at a time (two at once share each XCD's L2 and thrash
+        # it at a row pitch that aliases), each beside a retrieval kernel
+        rosa.rosa_match(inA, oA, wsA, stream)
+        evA.record(stream)
+        s2.wait_event(evA)
+        rosa.rosa_match_timed(inB, oB, wsB, evB0, evB1, s2)
+        stream.wait_event(evB0)
+        stream.wait_event(evGB)    # the previous step's second-half gather
+        rosa.rosa_gather(V[:, :, :Dh], w["M"], E[:h], out[:, :, :Dh], stream)
+        evGA.record(stream)
+        s2.wait_event(evGA)
+        rosa.rosa_gather(V[:, :, Dh:], w["M"], E[h:], out[:, :, Dh:], s2)
+        evGB.record(s2)
+
+    def join():
+        evJ.record(s2)
+        stream.wait_event(evJ)
+
+    def loop_ms(V, piped):
+        """Warm-up, then `steps` steps between two events on the stream."""
+        run = step_piped if piped else step
         for _ in range(args.warmup):
-            step(V)
+            run(V)
+        if piped:
+            join()
         torch.cuda.synchronize()
         t_start = torch.cuda.Event(enable_timing=True)
         t_end = torch.cuda.Event(enable_timing=True)
         t_start.record(stream)
-        for i in range(args.steps):
-            step(V)
+        if piped:
+            s2.wait_event(t_start)
+        for _ in range(args.steps):
+            run(V)
+        if piped:
+            join()
         t_end.record(stream)
         torch.cuda.synchronize()
-        ms = t_start.elapsed_time(t_end) / args.steps
+        return t_start.elapsed_time(t_end) / args.steps
+
+    def piped_for(V):
+        """Pipeline the steps unless V's row pitch is a multiple of 2 KiB: there
+        the gather keeps a route group's lines in a few L2 sets, and a
+        retrieval kernel running beside it evicts them (measured on the long
+        workload at the dense pitch: 1.48 ms pipelined, 0.99 ms serial)."""
+        return split and (V.stride(1) * 2) % 2048 != 0
+
+    def timed(V):
+        """ms per step (pipelined when split and the pitch allows), then the
+        same steps again, serial and unsplit, with events around the
+        retrieval and gather kernels (their mean durations; the events are
+        kept out of the timed loop, where they would add to short steps)."""
+        piped = piped_for(V)
+        ms = loop_ms(V, piped)
+        piped_out = (E.clone(), SYM.clone(), out.clone()) if piped else None
         for i in range(args.steps):
             step(V, i)
         torch.cuda.synchronize()
+        if piped_out is not None and not (torch.equal(piped_out[0], E) and
+                                          torch.equal(piped_out[1], SYM) and
+                                          torch.equal(piped_out[2], out)):
+            raise SystemExit("pipelined steps differ from serial steps")
         k = float(np.mean([kb[i].elapsed_time(ke[i]) for i in range(n_ev)]))
         g = (float(np.mean([gb[i].elapsed_time(ge[i]) for i in range(n_ev)]))
              if V is not None else None)
         return ms, k, g
 
-    _log(f"warmup {args.warmup}, timing {args.steps} steps")
+    piped = Vd is not None and piped_for(Vd)
+    _log(f"warmup {args.warmup}, timing {args.steps} steps"
+         + (" (two stream halves, pipelined)" if piped else ""))
     ms_step, k_avg, g_avg = timed(Vd)
-    if rosa.rosa_match_status(ws) != rosa.ROSA_OK:
+    if rosa.rosa_match_status(ws) != rosa.ROSA_OK or (
+            split and (rosa.rosa_match_status(wsA) != rosa.ROSA_OK or
+                       rosa.rosa_match_status(wsB) != rosa.ROSA_OK)):
         raise SystemExit("symbol range flag raised")
+    # the same steps one after another on one stream, unsplit (reported beside
+    # the pipelined figure)
+    ms_serial = loop_ms(Vd, False) if piped else None
     if args.copy_reference > 0:
         # two plain copies of known size for scaling HBM byte counters: the
         # runtime's buffer copy, and an elementwise kernel (int32 x + 1) that
@@ -921,7 +997,8 @@ def main():
         del src, dst
     value = S * T / (ms_step / 1e3)
     _log(f"ms/step {ms_step:.4f}  retrieval kernel {k_avg:.4f} ms"
-         + (f"  gather {g_avg:.4f} ms" if g_avg is not None else ""))
+         + (f"  gather {g_avg:.4f} ms" if g_avg is not None else "")
+         + (f"  serial unsplit steps {ms_serial:.4f} ms" if piped else ""))
     dense = None
     if Vd is not None and args.v_pad != 0 and not args.no_dense:
         # the same steps with V's rows at the dense pitch (D elements); the
@@ -931,7 +1008,10 @@ def main():
         if not torch.equal(out, out_pad):
             raise SystemExit("dense-pitch gather differs from the padded one")
         dense = {"ms_per_step": ms_d, "retrieval_ms": k_d, "gather_ms": g_d,
-                 "v_row_pitch": int(Vdense.stride(1))}
+                 "v_row_pitch": int(Vdense.stride(1)),
+                 "schedule": "pipelined" if piped_for(Vdense) else "serial"}
+        if split and not piped_for(Vdense):
+            dense["ms_per_step_pipelined"] = loop_ms(Vdense, True)
         _log(f"dense V rows: ms/step {ms_d:.4f}  gather {g_d:.4f} ms")
 
     roof = kernel_roofline(S * T, k_avg, args.workload)
@@ -1004,7 +1084,13 @@ def main():
         "dtype": "u8", "data": "synthetic",
         "config": {"workload": w["desc"], "streams": S, "T": T, "K": K,
                    "parallelism": "single GPU",
-                   **({"v_row_pitch": int(Vd.stride(1))} if Vd is not None else {})},
+                   **({"v_row_pitch": int(Vd.stride(1))} if Vd is not None else {}),
+                   **({"pipeline": "streams in two halves by channel on two HIP "
+                                   "streams: the first half's gather beside the "
+                                   "second half's retrieval kernel, consecutive "
+                                   "steps overlapping (each step is the whole "
+                                   "path over all streams)"} if piped else {})},
+        **({"ms_per_step_serial": ms_serial} if piped else {}),
         "roofline": roof,
         "kernel_ms": {"retrieval": k_avg,
                       **({"gather": g_avg} if g_avg is not None else {})},

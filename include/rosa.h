@@ -99,6 +99,20 @@ typedef struct rosa_out {
     uint8_t *symbols;  /* [S][T] the packed input symbols, may be NULL        */
 } rosa_out;
 
+/* --------------------------------------------------------------- symbols */
+
+/* Sec. 3.2, Eq. (10)-(15): the symbols of a bf16 input alone, the first
+ * step of rosa_match (bit j = I[h > 0] of channel r*M + j, packed with
+ * weight 2^j): symbols[s*ld + t] for stream s = b*R + r and t < T.  `in`:
+ * kind ROSA_IN_BF16.  `symbols`: device bytes, rows of ld >= T.  Every
+ * symbol is < 2^M, so rosa_match over these rows (ROSA_IN_SYMBOLS, K = 2^M)
+ * gives the same outputs as over the bf16 input.  A caller that pipelines
+ * the path over parts of the streams (for instance one part's retrieval
+ * beside another part's gather, on two streams) can run this step apart
+ * from the retrieval. */
+rosa_status rosa_discretize(const rosa_input *in, uint8_t *symbols,
+                            int64_t ld, hipStream_t stream);
+
 /* ------------------------------------------------------------ batch match */
 
 /* Bytes of device workspace rosa_match needs for S streams of T positions

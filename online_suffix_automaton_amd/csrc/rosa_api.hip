@@ -234,6 +234,23 @@ const char *rosa_error_string(rosa_status st)
     return "unknown status";
 }
 
+rosa_status rosa_discretize(const rosa_input *in, uint8_t *symbols,
+                            int64_t ld, hipStream_t stream)
+{
+    Shape sh;
+    rosa_status st = resolve(in, &sh, true);
+    if (st != ROSA_OK)
+        return st;
+    if (sh.kind != ROSA_IN_BF16 || (sh.T > 0 && (!symbols || ld < sh.T)))
+        return ROSA_ERR_ARG;
+    if (sh.T == 0)
+        return ROSA_OK;
+    ROSA_TRY(launch_discretize(reinterpret_cast<const uint16_t *>(in->data), sh.B,
+                               sh.T, sh.D, sh.ld, sh.M, symbols, ld, 0, nullptr,
+                               stream));
+    return ROSA_OK;
+}
+
 size_t rosa_match_workspace_bytes(int64_t S, int64_t T, int32_t K)
 {
     if (S < 1 || T < 0 || T >= kMaxT || K < 1 || K > 256 ||

@@ -21,28 +21,70 @@ __device__ __forceinline__ uint32_t bf16_pos(uint32_t h)
 
 // Copies caller symbols [S][ld] into padded workspace rows (zero padding on
 // both sides), clamps values >= K to K-1 and raises the sticky flag for them.
+// A thread moves 16 bytes of a padded row; with 16-byte aligned caller rows
+// (vec) a chunk inside [0, T) is one vector load and store, its symbols
+// checked on whole words (for K a power of two: no bit at or above K's), and
+// only a chunk that holds a symbol >= K is clamped byte by byte.  Chunks at
+// the row's ends, and unaligned rows, go byte by byte.
 __global__ void prep_symbols_kernel(const uint8_t *__restrict__ in, int64_t ld,
                                     int64_t T, int32_t K,
                                     uint8_t *__restrict__ rows, int64_t Tp,
                                     uint8_t *__restrict__ copy_out,
-                                    int32_t *__restrict__ flags)
+                                    int32_t *__restrict__ flags, int vec)
 {
     const int64_t s = blockIdx.y;
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // 0..Tp-1
-    if (i >= Tp)
+    const int64_t i0 = 16 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+    if (i0 >= Tp)
         return;
-    const int64_t t = i - kPadFront;
-    uint8_t v = 0;
-    if (t >= 0 && t < T) {
-        v = in[s * ld + t];
-        if (v >= K) {
-            atomicOr(&flags[kFlagSymbol], 1);
-            v = (uint8_t)(K - 1);
+    const int64_t t0 = i0 - kPadFront;
+    uint8_t *dst = rows + s * Tp + i0;
+    if (vec && t0 >= 0 && t0 + 16 <= T) {
+        uint4 v = *reinterpret_cast<const uint4 *>(in + s * ld + t0);
+        bool bad;
+        if ((K & (K - 1)) == 0) {
+            const uint32_t m = (uint32_t)(~(K - 1) & 0xFF) * 0x01010101u;
+            bad = ((v.x | v.y | v.z | v.w) & m) != 0;
+        } else {
+            bad = false;
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                bad |= ((w[q >> 2] >> (8 * (q & 3))) & 0xFFu) >= (uint32_t)K;
         }
-        if (copy_out)
-            copy_out[s * T + t] = v;
+        if (bad) {
+            atomicOr(&flags[kFlagSymbol], 1);
+            uint8_t *b = reinterpret_cast<uint8_t *>(&v);
+            for (int q = 0; q < 16; ++q)
+                if (b[q] >= K)
+                    b[q] = (uint8_t)(K - 1);
+        }
+        *reinterpret_cast<uint4 *>(dst) = v;
+        if (copy_out) {
+            uint8_t *c = copy_out + s * T + t0;
+            if ((((uintptr_t)c) & 15) == 0) {
+                *reinterpret_cast<uint4 *>(c) = v;
+            } else {
+                const uint8_t *b = reinterpret_cast<const uint8_t *>(&v);
+                for (int q = 0; q < 16; ++q)
+                    c[q] = b[q];
+            }
+        }
+        return;
     }
-    rows[s * Tp + i] = v;
+    for (int q = 0; q < 16 && i0 + q < Tp; ++q) {
+        const int64_t t = t0 + q;
+        uint8_t v = 0;
+        if (t >= 0 && t < T) {
+            v = in[s * ld + t];
+            if (v >= K) {
+                atomicOr(&flags[kFlagSymbol], 1);
+                v = (uint8_t)(K - 1);
+            }
+            if (copy_out)
+                copy_out[s * T + t] = v;
+        }
+        dst[q] = v;
+    }
 }
 
 // Zeroes the 64-word headers at a and b (b may be null).
@@ -202,7 +244,7 @@ constexpr int kGatherWG = 32;   // workgroups of 4 waves per XCD
 typedef int32_t gather_v4i __attribute__((ext_vector_type(4)));
 
 template <int GPX>
-__global__ __launch_bounds__(256) void gather_wave_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void gather_wave_kernel(
     const uint16_t *__restrict__ V, int64_t T, int64_t R, int64_t ldv,
     const int32_t *__restrict__ E, uint16_t *__restrict__ out, int64_t ldo,
     int vec_e)
@@ -338,9 +380,11 @@ hipError_t launch_prep_symbols(const uint8_t *in, int64_t ld, int64_t S,
                                uint8_t *copy_out, int32_t *flags,
                                hipStream_t st)
 {
-    dim3 grid((unsigned)((Tp + 255) / 256), (unsigned)S);
+    const int vec = (ld % 16) == 0 && (((uintptr_t)in) & 15) == 0;
+    const int64_t chunks = (Tp + 15) / 16;
+    dim3 grid((unsigned)((chunks + 255) / 256), (unsigned)S);
     hipLaunchKernelGGL(prep_symbols_kernel, grid, dim3(256), 0, st, in, ld, T,
-                       K, rows, Tp, copy_out, flags);
+                       K, rows, Tp, copy_out, flags, vec);
     return hipGetLastError();
 }
 

@@ -50,7 +50,7 @@ class rosa_qk_out(ctypes.Structure):
 
 
 _lib = None
-_SYMBOLS = ["rosa_match_workspace_bytes", "rosa_match", "rosa_match_timed",
+_SYMBOLS = ["rosa_discretize", "rosa_match_workspace_bytes", "rosa_match", "rosa_match_timed",
             "rosa_match_status", "rosa_match_noalloc", "rosa_match_qk_workspace_bytes",
             "rosa_match_qk", "rosa_scatter_grad_workspace_bytes",
             "rosa_scatter_grad",
@@ -72,6 +72,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P, I32, I64, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                        ctypes.c_size_t)
     sig = {
+        "rosa_discretize": ([P, P, I64, P], ctypes.c_int),
         "rosa_match_workspace_bytes": ([I64, I64, I32], SZ),
         "rosa_match": ([P, P, P, SZ, P], ctypes.c_int),
         "rosa_match_timed": ([P, P, P, SZ, P, P, P], ctypes.c_int),
@@ -182,6 +183,18 @@ def make_out(end, sym=None, len=None, symbols=None) -> rosa_out:
 
 
 # ------------------------------------------------------ C-ABI functions
+
+def rosa_discretize(inp: rosa_input, symbols: torch.Tensor, stream=None) -> None:
+    """The symbols of a bf16 input alone: uint8 [S, T] rows (unit stride in
+    T, row stride >= T) for S = B*D/M streams."""
+    _require_device(symbols)
+    if symbols.dtype != torch.uint8 or symbols.dim() != 2 or symbols.stride(1) != 1 \
+            or tuple(symbols.shape) != (inp.B * (inp.D // max(inp.M, 1)), inp.T):
+        raise ValueError("symbols must be a uint8 [B*D/M, T] tensor, unit stride in T")
+    ld = symbols.stride(0) if symbols.shape[0] > 1 else max(inp.T, 1)
+    _check(load_library().rosa_discretize(ctypes.byref(inp), symbols.data_ptr(), ld,
+                                          _stream(stream)), "rosa_discretize")
+
 
 def rosa_match_workspace_bytes(S: int, T: int, K: int) -> int:
     return int(load_library().rosa_match_workspace_bytes(S, T, K))

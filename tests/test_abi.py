@@ -255,3 +255,14 @@ def test_qk_decode_api_rejects_bad_handles_and_args():
     cf.tau, cf.cf_tau = FAKE.value, FAKE.value
     assert build(qq=_inp(K=3), kk=_inp(K=3), o=cf) == rosa.ROSA_ERR_ARG
     assert not h.value
+
+
+def test_discretize_rejects_bad_arguments():
+    lib = rosa.load_library()
+    sym = _inp()                                   # a symbols input
+    assert lib.rosa_discretize(ctypes.byref(sym), FAKE.value, 100, None) == rosa.ROSA_ERR_ARG
+    bf = _inp(kind=1, M=4, B=1, D=8, ld=8, T=100)
+    assert lib.rosa_discretize(ctypes.byref(bf), None, 100, None) == rosa.ROSA_ERR_ARG
+    assert lib.rosa_discretize(ctypes.byref(bf), FAKE.value, 99, None) == rosa.ROSA_ERR_ARG
+    empty = _inp(kind=1, M=4, B=1, D=8, ld=8, T=0)
+    assert lib.rosa_discretize(ctypes.byref(empty), None, 0, None) == rosa.ROSA_OK

@@ -194,6 +194,53 @@ def test_streams_longer_than_lds_path():
         _run_symbols(sym, 16, f"T={T}")
 
 
+@pytest.mark.parametrize("K", [16, 10])
+def test_symbol_out_of_range_flag_wide_rows(K):
+    """The symbol check of the 16-byte copy into the workspace rows (rows of
+    a multiple of 16 bytes): a symbol >= K in the middle of a row (a whole
+    chunk: a mask test for K a power of two, byte compares otherwise) and at
+    its last position (the byte path) raise the flag; rows without one do
+    not, and then give the oracle's outputs."""
+    rng = np.random.default_rng(40 + K)
+    S, T = 3, 1000
+    base = rng.integers(0, K, size=(S, 1024), dtype=np.uint8)
+    x = _dev(base)[:, :T]
+    ws = torch.empty(rosa.rosa_match_workspace_bytes(S, T, K), dtype=torch.uint8,
+                     device=DEV)
+    E, SYM, L, _ = rosa.match(x, K=K, ws=ws)
+    assert rosa.rosa_match_status(ws) == rosa.ROSA_OK
+    Eo, SYMo, Lo = oracle.match(np.ascontiguousarray(base[:, :T]), K)
+    _check(E, SYM, L, Eo, SYMo, Lo, f"wide rows K={K}")
+    for where in (517, T - 1):
+        bad = base.copy()
+        bad[1, where] = K + 3
+        rosa.match(_dev(bad)[:, :T], K=K, ws=ws)
+        assert rosa.rosa_match_status(ws) == rosa.ROSA_ERR_SYMBOL, where
+
+
+@pytest.mark.parametrize("M,pad", [(4, 0), (4, 37), (3, 5), (8, 0), (1, 16)])
+def test_discretize_alone(M, pad):
+    """rosa_discretize: the symbols of a bf16 input into caller rows (row
+    stride T + pad), equal to the oracle's discretization on every bf16
+    pattern class (the hidden states include all 65,536 patterns), and
+    rosa_match over those rows equals rosa_match over the bf16 input."""
+    B, T, D = 2, 2048, 32 * M
+    H = synth.bf16_normal((B, T, D), 90 + M)
+    H.reshape(-1)[:65536] = np.arange(65536, dtype=np.uint16)
+    S = B * D // M
+    Hd = _dev(H.view(np.int16))
+    buf = torch.full((S, T + pad), 0xEE, dtype=torch.uint8, device=DEV)
+    syms = buf[:, :T]
+    rosa.rosa_discretize(rosa.bf16_input(Hd, M), syms)
+    want = oracle.discretize_bf16(H, M)
+    assert np.array_equal(syms.cpu().numpy(), want)
+    if pad:
+        assert bool((buf[:, T:] == 0xEE).all()), "bytes past T were written"
+    E1, SYM1, L1, _ = rosa.match(Hd, M=M)
+    E2, SYM2, L2, _ = rosa.match(syms, K=1 << M)
+    assert torch.equal(E1, E2) and torch.equal(SYM1, SYM2) and torch.equal(L1, L2)
+
+
 def test_strided_symbol_rows():
     rng = np.random.default_rng(8)
     base = rng.integers(0, 16, size=(6, 1500), dtype=np.uint8)
