@@ -887,40 +887,58 @@ def main():
 
     # Pipelined steps (with a gather): the streams in two halves by channel
     # (routes 0..R/2-1 and R/2..R-1 of H and V), each with its own workspace
-    # and HIP stream (default priority).  The second half's match starts when
-    # the first half's is done; the first half's gather waits for the event
-    # rosa_match_timed records just before the second half's retrieval
-    # kernel, so that gather (memory-bound, no LDS) runs beside that kernel
-    # (VALU-bound, one workgroup per CU with nearly all of its LDS).  Steps
-    # are not joined one by one: the next step's first half starts behind
-    # this step's first-half gather, beside its second-half gather.
+    # and HIP stream (default priority).  A retrieval kernel holds one
+    # workgroup per CU with nearly all of its LDS and is bound by VALU issue;
+    # the gather and the discretisation use no LDS and are bound by memory,
+    # so each runs beside the other half's retrieval kernel:
+    #  - the second half's match starts when the first half's is done, and
+    #    the first half's gather waits for the event rosa_match_timed records
+    #    just before the second half's retrieval kernel;
+    #  - each half's symbols are made by rosa_discretize one step ahead
+    #    (software pipelining: every timed step still discretises, matches
+    #    and gathers all streams once), after that half's gather, so they are
+    #    made beside the other half's retrieval; rosa_match then reads them
+    #    as 16-byte aligned symbol rows;
+    #  - the next step's first half waits for this step's second-half match
+    #    (whose last kernel needs a CU's LDS too), and its retrieval runs
+    #    beside this step's second-half gather.
     split = (Vd is not None and w["kind"] == "bf16" and not args.no_split
              and S % 2 == 0 and (w["H"].shape[2] // 2) % w["M"] == 0)
     if split:
         h, Dh = S // 2, w["H"].shape[2] // 2
         inA = rosa.bf16_input(Hd[:, :, :Dh], w["M"])
         inB = rosa.bf16_input(Hd[:, :, Dh:], w["M"])
+        symA = torch.empty((h, T), dtype=torch.uint8, device=dev)
+        symB = torch.empty_like(symA)
+        sinA, sinB = rosa.symbols_input(symA, K), rosa.symbols_input(symB, K)
         wsA = torch.empty(rosa.rosa_match_workspace_bytes(h, T, K), dtype=torch.uint8,
                           device=dev)
         wsB = torch.empty_like(wsA)
         oA, oB = rosa.make_out(E[:h], SYM[:h]), rosa.make_out(E[h:], SYM[h:])
         s2 = torch.cuda.Stream(device=dev)
-        evA, evB0, evB1, evJ, evGA, evGB = (torch.cuda.Event() for _ in range(6))
+        evA, evB0, evB1, evBE, evJ, evGA, evGB = (torch.cuda.Event() for _ in range(7))
+
+    def prologue():
+        """The first step's symbols of both halves."""
+        rosa.rosa_discretize(inA, symA, stream)
+        rosa.rosa_discretize(inB, symB, s2)
 
     def step_piped(V):
-        # one gather at a time (two at once share each XCD's L2 and thrash
-        # it at a row pitch that aliases), each beside a retrieval kernel
-        rosa.rosa_match(inA, oA, wsA, stream)
+        stream.wait_event(evBE)    # the previous step's second-half match
+        rosa.rosa_match(sinA, oA, wsA, stream)
         evA.record(stream)
         s2.wait_event(evA)
-        rosa.rosa_match_timed(inB, oB, wsB, evB0, evB1, s2)
+        rosa.rosa_match_timed(sinB, oB, wsB, evB0, evB1, s2)
+        evBE.record(s2)
         stream.wait_event(evB0)
         stream.wait_event(evGB)    # the previous step's second-half gather
         rosa.rosa_gather(V[:, :, :Dh], w["M"], E[:h], out[:, :, :Dh], stream)
         evGA.record(stream)
+        rosa.rosa_discretize(inA, symA, stream)   # next step's, beside this step's second retrieval
         s2.wait_event(evGA)
         rosa.rosa_gather(V[:, :, Dh:], w["M"], E[h:], out[:, :, Dh:], s2)
         evGB.record(s2)
+        rosa.rosa_discretize(inB, symB, s2)       # next step's, beside the next first retrieval
 
     def join():
         evJ.record(s2)
@@ -929,6 +947,8 @@ def main():
     def loop_ms(V, piped):
         """Warm-up, then `steps` steps between two events on the stream."""
         run = step_piped if piped else step
+        if piped:
+            prologue()
         for _ in range(args.warmup):
             run(V)
         if piped:
@@ -1086,10 +1106,12 @@ def main():
                    "parallelism": "single GPU",
                    **({"v_row_pitch": int(Vd.stride(1))} if Vd is not None else {}),
                    **({"pipeline": "streams in two halves by channel on two HIP "
-                                   "streams: the first half's gather beside the "
-                                   "second half's retrieval kernel, consecutive "
-                                   "steps overlapping (each step is the whole "
-                                   "path over all streams)"} if piped else {})},
+                                   "streams: each half's gather and its next "
+                                   "step's discretisation beside the other half's "
+                                   "retrieval kernel, consecutive steps "
+                                   "overlapping (each timed step discretises, "
+                                   "matches and gathers all streams once)"}
+                      if piped else {})},
         **({"ms_per_step_serial": ms_serial} if piped else {}),
         "roofline": roof,
         "kernel_ms": {"retrieval": k_avg,

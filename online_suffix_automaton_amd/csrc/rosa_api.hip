@@ -34,6 +34,7 @@ hipError_t launch_stream(const MatchParams &p, int64_t S, hipStream_t st);
 hipError_t launch_big(const MatchParams &p, int grid, hipStream_t st);
 hipError_t launch_unpermute(const MatchParams &p, int64_t S, hipStream_t st);
 bool stream_can_stage(int64_t T);
+bool stream_uses_records(int64_t T);
 // rosa_sam.hip
 size_t sam_total_bytes(int64_t S, int64_t K, int64_t Tcap);
 uint8_t *sam_hist_base(void *buf, int64_t S, int64_t K, int64_t Tcap,
@@ -283,7 +284,17 @@ static rosa_status match_impl(const rosa_input *in, const rosa_out *out,
     MatchParams p = match_params(sh, base, w, out);
     // the flags and the large-group counter start at zero; the bf16 path
     // clears them (and pads the rows) inside the discretisation launch
-    if (sh.kind == ROSA_IN_SYMBOLS) {
+    if (sh.kind == ROSA_IN_SYMBOLS && !out->symbols && stream_uses_records(sh.T) &&
+        sh.ld % 16 == 0 && (reinterpret_cast<uintptr_t>(in->data) & 15) == 0) {
+        // 16-byte aligned rows of a stream of the LDS plans: the stream
+        // kernel reads them itself (no copy into the workspace rows first)
+        ROSA_TRY(launch_clear_flags(flags, stream, p.big));
+        p.stage = 2;
+        p.symin = reinterpret_cast<const uint8_t *>(in->data);
+        p.symld = sh.ld;
+        p.sym_w = rows;
+        p.flags = flags;
+    } else if (sh.kind == ROSA_IN_SYMBOLS) {
         ROSA_TRY(launch_clear_flags(flags, stream, p.big));
         ROSA_TRY(launch_prep_symbols(reinterpret_cast<const uint8_t *>(in->data),
                                      sh.ld, sh.S, sh.T, sh.K, rows, w.Tp,

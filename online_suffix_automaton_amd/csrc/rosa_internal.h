@@ -67,12 +67,18 @@ struct MatchParams {
     int64_t Tp;
     int32_t T, K, d, NB, nbits, fl_total;
     int32_t fuse;               // the stream kernel runs the time-ordered pass itself
-    // stage: the stream kernel reads its symbols straight from bf16 hidden
+    // stage 1: the stream kernel reads its symbols straight from bf16 hidden
     // states H [B][T][Hld] (M = 4, route r of batch row b = stream b*R + r),
-    // writes the optional symbol copy and clears the flags itself
+    // writes the optional symbol copy and clears the flags itself.
+    // stage 2: it reads the caller's symbol rows symin [S][symld] (16-byte
+    // aligned), checks them against K and, unless it runs the time-ordered
+    // pass itself, writes its padded row to sym_w for the later kernel.
     int32_t stage, R;
     const uint16_t *H;
     int64_t Hld;
+    const uint8_t *symin;
+    int64_t symld;
+    uint8_t *sym_w;
     uint8_t *sym_copy;          // [S][T] or null
     int32_t *flags;
     int32_t pw[kMaxD + 1];      // K^i

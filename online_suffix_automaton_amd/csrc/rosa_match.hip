@@ -1287,7 +1287,7 @@ void stream_kernel_lds(MatchParams p)
     const int lane = tid & 63, wid = tid >> 6, nw = nt >> 6;
     const int T = p.T, K = p.K, d = DC > 0 ? DC : p.d, NB = p.NB;
     uint64_t *eqw = p.nbits <= 4 ? eqtab[wid] : nullptr;
-    if (p.stage) {
+    if (p.stage == 1) {
         // the padding, then the symbols straight from the bf16 rows: route
         // r packs channels 4r .. 4r+3 (one 8-byte load per position), bit j
         // = I[h > 0] of channel 4r+j (Sec. 3.2, Eq. (10)-(15)); eight loads
@@ -1321,6 +1321,50 @@ void stream_kernel_lds(MatchParams p)
                         p.sym_copy[(int64_t)s * T + t] = c;
                 }
             }
+        }
+    } else if (p.stage == 2) {
+        // the caller's row (16-byte aligned), 16 symbols per thread and
+        // step, with the zero padding around it; symbols >= K raise the flag
+        // and are clamped (as the copy into the workspace rows does).  The
+        // padded row also goes to the workspace for the later kernel that
+        // reads it, unless this kernel runs the time-ordered pass itself.
+        const uint8_t *src = p.symin + (int64_t)s * p.symld;
+        uint4 *dst = reinterpret_cast<uint4 *>(symrow);
+        uint4 *wdst = p.fuse ? nullptr : reinterpret_cast<uint4 *>(p.sym_w + (int64_t)s * p.Tp);
+        const bool pow2 = (K & (K - 1)) == 0;
+        const uint32_t hm = (uint32_t)(~(K - 1) & 0xFF) * 0x01010101u;
+        for (int i = tid; i < (int)(p.Tp >> 4); i += nt) {
+            const int t0 = 16 * i - kPadFront;
+            uint4 v;
+            if (t0 >= 0 && t0 + 16 <= T) {
+                v = *reinterpret_cast<const uint4 *>(src + t0);
+            } else {
+                uint32_t wv[4] = {0u, 0u, 0u, 0u};
+                for (int q = 0; q < 16; ++q)
+                    if (t0 + q >= 0 && t0 + q < T)
+                        wv[q >> 2] |= (uint32_t)src[t0 + q] << (8 * (q & 3));
+                v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+            }
+            bool bad;
+            if (pow2) {
+                bad = ((v.x | v.y | v.z | v.w) & hm) != 0;
+            } else {
+                bad = false;
+                const uint32_t wq[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    bad |= ((wq[q >> 2] >> (8 * (q & 3))) & 0xFFu) >= (uint32_t)K;
+            }
+            if (bad) {
+                atomicOr(&p.flags[kFlagSymbol], 1);
+                uint8_t *b = reinterpret_cast<uint8_t *>(&v);
+                for (int q = 0; q < 16; ++q)
+                    if (b[q] >= K)
+                        b[q] = (uint8_t)(K - 1);
+            }
+            dst[i] = v;
+            if (wdst)
+                wdst[i] = v;
         }
     } else {
         const uint4 *src = reinterpret_cast<const uint4 *>(p.sym + (int64_t)s * p.Tp);

@@ -1,7 +1,6 @@
 // rosa_stream_io.hip -- streaming kernels of librosa: symbol preparation,
 // bf16 discretisation and value gather.  All HBM-bound; each is laid out so
-// that global reads and writes are coalesced and the [B][T][D] <-> [S][T]
-// transposes happen in LDS.
+// that global reads are coalesced and writes go in 16-byte or larger pieces.
 //
 // Method: "ROSA-Tuning: Enhancing Long-Context Modeling via Suffix Matching"
 // (arXiv 2602.02499), Sec. 3.2 (Eq. 10-15: sign bits packed M per route) and
@@ -208,6 +207,85 @@ __global__ __launch_bounds__(256) void discretize_kernel(
     }
 }
 
+// The same 64-position x 64-route tiles with M = 4 and 16-byte aligned
+// rows (row stride and first symbol), without LDS: lane = route, wave w =
+// positions t0+16w .. t0+16w+15 (the same coalesced 512-byte row reads as
+// above), and the lane packs its 16 symbols into one 16-byte store of its
+// route's row.  The writes are the same 16-byte pieces the LDS kernel
+// stores (a workgroup covers 64 bytes of each of 64 rows), so memory sees
+// the same pattern; with no LDS and no barrier the kernel can run on a CU
+// beside a workgroup that holds all of that CU's LDS (the retrieval
+// kernel).  Padding, headers and copy_out as in discretize_kernel.
+__global__ __launch_bounds__(256) void discretize4_kernel(
+    const uint16_t *__restrict__ H, int64_t T, int64_t D, int64_t ld,
+    uint8_t *__restrict__ rows, int64_t row_stride, int64_t row_off,
+    uint8_t *__restrict__ copy_out, int64_t pad_end, int32_t *zero_a,
+    int32_t *zero_b)
+{
+    if ((blockIdx.x | blockIdx.y) == 0 && threadIdx.x < 64) {
+        if (zero_a)
+            zero_a[threadIdx.x] = 0;
+        if (zero_b)
+            zero_b[threadIdx.x] = 0;
+    }
+    const int64_t R = D / 4;
+    const int64_t b = blockIdx.y;
+    const int64_t nrt = (R + 63) / 64, ntt = (T + 63) / 64;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    for (int64_t tile_i = blockIdx.x; tile_i < nrt * ntt; tile_i += gridDim.x) {
+        const int64_t tt = tile_i / nrt;
+        const int64_t tc = tt * 64 + w * 16;   // this wave's first position
+        const int64_t r = (tile_i - tt * nrt) * 64 + lane;
+        uint2 v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int64_t t = tc + k;
+            v[k] = make_uint2(0u, 0u);
+            if (t < T && r < R)
+                v[k] = *reinterpret_cast<const uint2 *>(H + (b * T + t) * ld + r * 4);
+        }
+        if (r >= R)
+            continue;
+        uint32_t wv[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            wv[k >> 2] |= (bf16_pos(v[k].x & 0xFFFFu) | (bf16_pos(v[k].x >> 16) << 1) |
+                           (bf16_pos(v[k].y & 0xFFFFu) << 2) |
+                           (bf16_pos(v[k].y >> 16) << 3))
+                          << (8 * (k & 3));
+        const int64_t s = b * R + r;
+        uint8_t *row = rows + s * row_stride;
+        if (pad_end > 0) {
+            if (tt == 0 && w == 0)
+                for (int64_t i = 0; i < row_off; ++i)
+                    row[i] = 0;
+            if (tt == ntt - 1 && w == 3)
+                for (int64_t i = row_off + T; i < pad_end; ++i)
+                    row[i] = 0;
+        }
+        if (tc >= T)
+            continue;
+        const uint4 pk = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        uint8_t *dst = row + row_off + tc;
+        if (tc + 16 <= T) {
+            *reinterpret_cast<uint4 *>(dst) = pk;
+        } else {
+            for (int q = 0; q < T - tc; ++q)
+                dst[q] = (uint8_t)(wv[q >> 2] >> (8 * (q & 3)));
+        }
+        if (copy_out) {
+            uint8_t *c = copy_out + s * T + tc;
+            if (tc + 16 <= T && (((uintptr_t)c) & 15) == 0) {
+                *reinterpret_cast<uint4 *>(c) = pk;
+            } else {
+                for (int q = 0; q < 16 && tc + q < T; ++q)
+                    c[q] = (uint8_t)(wv[q >> 2] >> (8 * (q & 3)));
+            }
+        }
+    }
+}
+
 // ----------------------------------------------------------------- gather
 
 // XCDs of the chip (consecutive workgroups of a launch go to consecutive
@@ -405,7 +483,13 @@ hipError_t launch_discretize(const uint16_t *H, int64_t B, int64_t T,
     dim3 grid((unsigned)(ntiles < kTileGrid ? ntiles : kTileGrid), (unsigned)B);
     const bool vec4 = M == 4 && (ld % 4) == 0 &&
                       (((uintptr_t)H) & 7) == 0;
-    if (vec4)
+    const bool rows16 = (row_stride % 16) == 0 &&
+                        (((uintptr_t)(rows + row_off)) & 15) == 0;
+    if (vec4 && rows16)
+        hipLaunchKernelGGL(discretize4_kernel, grid, dim3(256), 0, st, H, T, D, ld,
+                           rows, row_stride, row_off, copy_out, pad_end, zero_a,
+                           zero_b);
+    else if (vec4)
         hipLaunchKernelGGL(discretize_kernel<4>, grid, dim3(256), 0, st, H, T,
                            D, ld, M, rows, row_stride, row_off, copy_out,
                            pad_end, zero_a, zero_b);

@@ -39,12 +39,28 @@ def _check(E, SYM, L, Eo, SYMo, Lo, what):
 
 
 def _run_symbols(sym, K, what):
+    """Symbol rows through rosa_match, checked against the oracle twice:
+    contiguous rows with the packed-symbol copy requested (the rows are first
+    copied into the workspace), and the same rows at a pitch of a multiple of
+    16 bytes (streams of at most 65536 positions: the retrieval kernel reads
+    them itself).  The bytes past T in the second hold 255, a symbol >= K for
+    every K < 256, so a read of them would raise the symbol flag."""
     x = _dev(sym)
     E, SYM, L, syms = rosa.match(x, K=K, want_symbols=True)
     torch.cuda.synchronize()
     Eo, SYMo, Lo = oracle.match(sym, K)
     _check(E, SYM, L, Eo, SYMo, Lo, what)
     assert np.array_equal(syms.cpu().numpy(), sym)
+    S, T = sym.shape
+    if S > 1 and T <= 65536:
+        ld = (T + 15) // 16 * 16 + 16
+        buf = torch.full((S, ld), 255, dtype=torch.uint8, device=DEV)
+        buf[:, :T] = x
+        ws = torch.empty(rosa.rosa_match_workspace_bytes(S, T, K), dtype=torch.uint8,
+                         device=DEV)
+        E2, SYM2, L2, _ = rosa.match(buf[:, :T], K=K, ws=ws)
+        assert rosa.rosa_match_status(ws) == rosa.ROSA_OK, what + " (aligned rows)"
+        _check(E2, SYM2, L2, Eo, SYMo, Lo, what + " (aligned rows)")
     return E
 
 
@@ -194,23 +210,28 @@ def test_streams_longer_than_lds_path():
         _run_symbols(sym, 16, f"T={T}")
 
 
-@pytest.mark.parametrize("K", [16, 10])
-def test_symbol_out_of_range_flag_wide_rows(K):
-    """The symbol check of the 16-byte copy into the workspace rows (rows of
-    a multiple of 16 bytes): a symbol >= K in the middle of a row (a whole
-    chunk: a mask test for K a power of two, byte compares otherwise) and at
-    its last position (the byte path) raise the flag; rows without one do
-    not, and then give the oracle's outputs."""
-    rng = np.random.default_rng(40 + K)
-    S, T = 3, 1000
-    base = rng.integers(0, K, size=(S, 1024), dtype=np.uint8)
+@pytest.mark.parametrize("K,T,ld", [(16, 1000, 1024), (10, 1000, 1024),
+                                    (16, 65536, 65536), (10, 50001, 50016)])
+def test_symbol_out_of_range_flag_wide_rows(K, T, ld):
+    """The symbol check where the retrieval kernel reads 16-byte aligned
+    caller rows itself (row pitch a multiple of 16 bytes; streams short
+    enough for that kernel to run the time-ordered pass too, and streams
+    long enough that it writes the padded rows out for the later kernel): a
+    symbol >= K in the middle of a row (a whole chunk: a mask test for K a
+    power of two, byte compares otherwise) and at its last position (the
+    byte path when T is not a multiple of 16) raise the flag; rows without
+    one do not, and then give the oracle's outputs."""
+    rng = np.random.default_rng(40 + K + T)
+    S = 3
+    base = rng.integers(0, K, size=(S, ld), dtype=np.uint8)
     x = _dev(base)[:, :T]
     ws = torch.empty(rosa.rosa_match_workspace_bytes(S, T, K), dtype=torch.uint8,
                      device=DEV)
+    _say(f"wide rows K={K} T={T} ld={ld}")
     E, SYM, L, _ = rosa.match(x, K=K, ws=ws)
     assert rosa.rosa_match_status(ws) == rosa.ROSA_OK
     Eo, SYMo, Lo = oracle.match(np.ascontiguousarray(base[:, :T]), K)
-    _check(E, SYM, L, Eo, SYMo, Lo, f"wide rows K={K}")
+    _check(E, SYM, L, Eo, SYMo, Lo, f"wide rows K={K} T={T}")
     for where in (517, T - 1):
         bad = base.copy()
         bad[1, where] = K + 3
@@ -353,6 +374,22 @@ def test_long_workload_with_gather():
     _check(E, SYM, L, Eo, SYMo, Lo, "long")
     oo = oracle.gather(V, Eo, 4)
     assert np.array_equal(out.cpu().numpy().view(np.uint16), oo)
+    # as the benchmark's pipelined steps run it: each half of the channels
+    # (a strided view of H) discretised alone into 16-byte aligned symbol
+    # rows, which the retrieval kernel reads itself
+    _say("halves through rosa_discretize")
+    S, T = so.shape
+    Dh = H.shape[2] // 2
+    for half, sl in ((0, slice(0, Dh)), (1, slice(Dh, 2 * Dh))):
+        sy = torch.empty((S // 2, T), dtype=torch.uint8, device=DEV)
+        rosa.rosa_discretize(rosa.bf16_input(Hd[:, :, sl], 4), sy)
+        ws = torch.empty(rosa.rosa_match_workspace_bytes(S // 2, T, 16),
+                         dtype=torch.uint8, device=DEV)
+        E2, SYM2, L2, _ = rosa.match(sy, K=16, ws=ws)
+        assert rosa.rosa_match_status(ws) == rosa.ROSA_OK
+        rows = slice(half * S // 2, (half + 1) * S // 2)
+        assert np.array_equal(sy.cpu().numpy(), so[rows])
+        _check(E2, SYM2, L2, Eo[rows], SYMo[rows], Lo[rows], f"long half {half}")
 
 
 def test_gather_random_destinations():
