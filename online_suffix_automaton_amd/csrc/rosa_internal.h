@@ -67,6 +67,7 @@ struct MatchParams {
     int64_t Tp;
     int32_t T, K, d, NB, nbits, fl_total;
     int32_t fuse;               // the stream kernel runs the time-ordered pass itself
+                                // (1: in its union, 2: over its whole LDS)
     // stage 1: the stream kernel reads its symbols straight from bf16 hidden
     // states H [B][T][Hld] (M = 4, route r of batch row b = stream b*R + r),
     // writes the optional symbol copy and clears the flags itself.

@@ -1233,6 +1233,22 @@ struct LdsCfg {
     static constexpr int kLposCap = (kUnion - kULpos) / 2;
     static constexpr int kPassCap = kLposCap - 64;
     static_assert(kSegTab > 0 && kLposCap > 64, "LDS plan");
+    // the workgroup's LDS, one buffer: padded symbol row | bucket offsets
+    // u16 [B+16] | first members' answers u16 [B] | misc int [32] | symbol
+    // split words u64 [waves][16] | union (every part 16-byte aligned)
+    static constexpr int kOffOff = kSymBytes;
+    static constexpr int kOffQres = kOffOff + (kBuckets + 16) * 2;
+    static constexpr int kOffMisc = kOffQres + kBuckets * 2;
+    static constexpr int kOffEq = kOffMisc + 128;
+    static constexpr int kOffU = kOffEq + (THREADS / 64) * 16 * 8;
+    static constexpr int kLdsBytes = kOffU + kUnion;
+    static_assert(kOffOff % 16 == 0 && kOffQres % 16 == 0 && kOffU % 16 == 0,
+                  "LDS plan alignment");
+    static_assert(kLdsBytes <= 163840, "LDS plan size");
+    // after the tasks the whole buffer can hold the time-ordered pass of a
+    // stream of TMAX positions over at most 16 symbols: the symbols as
+    // nibbles [TMAX/2] and the u16 destinations [TMAX]
+    static constexpr bool kNibPass = TMAX / 2 + 2 * TMAX <= kLdsBytes;
 };
 
 // Streams of up to 65536 positions, one 1024-thread workgroup per CU (the
@@ -1254,17 +1270,18 @@ __attribute__((amdgpu_waves_per_eu(Cfg::kThreads / 256 * Cfg::kMinBlocks)))
 void stream_kernel_lds(MatchParams p)
 {
     constexpr int kPassCap = Cfg::kPassCap;
-    __shared__ __align__(16) unsigned char symrow[Cfg::kSymBytes];
+    __shared__ __align__(16) unsigned char lds[Cfg::kLdsBytes];
+    unsigned char *symrow = lds;
     // bucket offsets fit 16 bits: off[NB] = T - d + 1 <= 65535
-    __shared__ uint16_t off[Cfg::kBuckets + 16];
+    uint16_t *off = reinterpret_cast<uint16_t *>(lds + Cfg::kOffOff);
     // E+1 of each bucket's first member (L < d, from phase D), written
     // with the bucket's task so all record stores stay coalesced
-    __shared__ uint16_t qres[Cfg::kBuckets];
-    __shared__ int32_t misc[32];
+    uint16_t *qres = reinterpret_cast<uint16_t *>(lds + Cfg::kOffQres);
+    int32_t *misc = reinterpret_cast<int32_t *>(lds + Cfg::kOffMisc);
     // per wave: 16 words for the symbol splits of alphabets of at most 16
     // symbols (wave_symbol_mask)
-    __shared__ uint64_t eqtab[Cfg::kThreads / 64][16];
-    __shared__ __align__(16) unsigned char U[Cfg::kUnion];
+    uint64_t(*eqtab)[16] = reinterpret_cast<uint64_t(*)[16]>(lds + Cfg::kOffEq);
+    unsigned char *U = lds + Cfg::kOffU;
     int32_t *cnt = reinterpret_cast<int32_t *>(U);
     int32_t *firstd = reinterpret_cast<int32_t *>(U + Cfg::kUFirstd);
     int32_t *firstl = reinterpret_cast<int32_t *>(U + Cfg::kUFirstl);
@@ -1330,7 +1347,8 @@ void stream_kernel_lds(MatchParams p)
         // reads it, unless this kernel runs the time-ordered pass itself.
         const uint8_t *src = p.symin + (int64_t)s * p.symld;
         uint4 *dst = reinterpret_cast<uint4 *>(symrow);
-        uint4 *wdst = p.fuse ? nullptr : reinterpret_cast<uint4 *>(p.sym_w + (int64_t)s * p.Tp);
+        uint4 *wdst = p.fuse == 1 ? nullptr
+                                  : reinterpret_cast<uint4 *>(p.sym_w + (int64_t)s * p.Tp);
         const bool pow2 = (K & (K - 1)) == 0;
         const uint32_t hm = (uint32_t)(~(K - 1) & 0xFF) * 0x01010101u;
         for (int i = tid; i < (int)(p.Tp >> 4); i += nt) {
@@ -1453,11 +1471,16 @@ void stream_kernel_lds(MatchParams p)
         // this range's tasks: [tlo, thi).  Wave w starts with task tlo + w,
         // then takes the next one from a counter (tasks inside long
         // recurrences cost many times the others); the next task's
-        // descriptor is loaded while this one is solved.  A task's records
-        // are stored at the start of the wave's next task, after the wait
-        // for that task's descriptor: vector loads and stores complete
-        // under one counter, so a wait for the descriptor right after the
-        // stores would wait for the stores too.
+        // descriptor is loaded while this one is solved, by a scalar load
+        // (the address is uniform).  A vector load would complete under the
+        // vector memory counter, in order with the record stores, so the
+        // wait for it would also wait for the stores issued before the wait,
+        // which take long when other kernels load memory; a scalar load
+        // waits on its own counter.  The lines are written by this
+        // workgroup's vector stores in phase B before a barrier (which waits
+        // for them), and no scalar load reads them earlier in the launch, so
+        // the scalar cache cannot hold an older copy of them.  A task's
+        // records are stored at the start of the wave's next task.
         const int tlo = tfirst, thi = tfirst + misc[kMiscPass + rg];
         tfirst = thi;
         int ti = tlo + wid;
@@ -1537,7 +1560,7 @@ void stream_kernel_lds(MatchParams p)
     // launcher): the time-ordered pass here, on this workgroup's records
     // (still in cache) and its LDS copy of the symbols, instead of a launch
     // of unpermute_kernel
-    if (p.fuse) {
+    if (p.fuse == 1) {
         // the records were stored by this workgroup's waves; the barrier
         // (a workgroup-scope fence) makes them visible to all of them
         __syncthreads();
@@ -1548,6 +1571,20 @@ void stream_kernel_lds(MatchParams p)
             unpermute_stream<true, false>(p, s, tau, nullptr, x);
         else
             unpermute_stream<false, false>(p, s, tau, nullptr, x);
+    }
+    if constexpr (Cfg::kNibPass && Cfg::kTMax > 8192) {
+        // longer streams over at most 16 symbols (fuse = 2, set by the
+        // launcher when the outputs allow 16-byte stores): once every wave
+        // is done with it, the whole LDS holds the time-ordered pass -- the
+        // symbols as nibbles, read back from the padded workspace row, then
+        // the u16 destinations -- as in a launch of unpermute_kernel, but
+        // with each workgroup's tail overlapping the other workgroups' tasks
+        if (p.fuse == 2) {
+            __syncthreads();
+            uint16_t *tau = reinterpret_cast<uint16_t *>(lds + Cfg::kTMax / 2);
+            unpermute_stream<true, true>(p, s, tau, lds,
+                                         p.sym + (int64_t)s * p.Tp + kPadFront);
+        }
     }
 }
 
@@ -1961,6 +1998,17 @@ bool stream_fuses_unpermute(int64_t T)
     return 2 * T <= uni;
 }
 
+// Whether the stream kernel runs the time-ordered pass itself over its whole
+// LDS (streams of the large plan too long for the union, at most 16
+// symbols, outputs that take 16-byte stores).
+bool stream_nib_pass(const MatchParams &p)
+{
+    return stream_uses_records(p.T) && !stream_fuses_unpermute(p.T) &&
+           p.T > CfgSmall::kTMax && CfgLarge::kNibPass && p.K <= 16 &&
+           (p.T & 3) == 0 && ((uintptr_t)p.E & 15) == 0 &&
+           ((uintptr_t)p.SYM & 7) == 0;
+}
+
 // Whether the stream kernel can read bf16 symbols itself (stage): streams
 // of the small LDS plan, which also runs the time-ordered pass itself (no
 // later kernel reads the padded symbol rows).
@@ -1972,7 +2020,7 @@ bool stream_can_stage(int64_t T)
 hipError_t launch_stream(const MatchParams &p_in, int64_t S, hipStream_t st)
 {
     MatchParams p = p_in;
-    p.fuse = stream_fuses_unpermute(p.T) ? 1 : 0;
+    p.fuse = stream_fuses_unpermute(p.T) ? 1 : stream_nib_pass(p) ? 2 : 0;
     if (stream_uses_records(p.T)) {
         const bool small = p.T <= CfgSmall::kTMax;
         const dim3 grid((unsigned)S);
@@ -2011,7 +2059,7 @@ hipError_t launch_big(const MatchParams &p, int grid, hipStream_t st)
 
 hipError_t launch_unpermute(const MatchParams &p, int64_t S, hipStream_t st)
 {
-    if (!stream_uses_records(p.T) || stream_fuses_unpermute(p.T))
+    if (!stream_uses_records(p.T) || stream_fuses_unpermute(p.T) || stream_nib_pass(p))
         return hipSuccess;
     const bool vec = (p.T & 3) == 0 && ((uintptr_t)p.E & 15) == 0 &&
                      ((uintptr_t)p.SYM & 7) == 0;

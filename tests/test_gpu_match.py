@@ -347,8 +347,12 @@ def test_long_repeats_deferred_answers():
     candidates than a deferred record holds), nested copies (where the
     extension from the previous position fails), a length that is not a
     multiple of 4 and an alphabet above 16 (the record kernel's other
-    variants)."""
-    for T, K in ((8192, 16), (5001, 16), (8192, 40), (5001, 200)):
+    variants).  Streams longer than the union of the large LDS plan holds
+    destinations for (T > 39728) take the pass over the retrieval kernel's
+    whole LDS when K <= 16 and T is a multiple of 4, else the separate
+    kernel."""
+    for T, K in ((8192, 16), (5001, 16), (8192, 40), (5001, 200), (65536, 16),
+                 (50000, 16), (50001, 16), (65536, 40)):
         rows = [_many_copies(T, K, 11), _many_copies(T, K, 12, block=200, copies=12),
                 synth.planted_copies(T, K, 13, gap_mean=50, len_lo=64, len_hi=400),
                 synth.planted_copies(T, K, 14, gap_mean=20, len_lo=20, len_hi=100)]
