@@ -1471,16 +1471,13 @@ void stream_kernel_lds(MatchParams p)
         // this range's tasks: [tlo, thi).  Wave w starts with task tlo + w,
         // then takes the next one from a counter (tasks inside long
         // recurrences cost many times the others); the next task's
-        // descriptor is loaded while this one is solved, by a scalar load
-        // (the address is uniform).  A vector load would complete under the
-        // vector memory counter, in order with the record stores, so the
-        // wait for it would also wait for the stores issued before the wait,
-        // which take long when other kernels load memory; a scalar load
-        // waits on its own counter.  The lines are written by this
-        // workgroup's vector stores in phase B before a barrier (which waits
-        // for them), and no scalar load reads them earlier in the launch, so
-        // the scalar cache cannot hold an older copy of them.  A task's
-        // records are stored at the start of the wave's next task.
+        // descriptor is loaded while this one is solved.  A task's records
+        // are stored at the start of the wave's next task, after the load of
+        // the descriptor after it.  (Loads and stores complete under one
+        // counter, so the wait for a descriptor also covers the stores
+        // issued before it.  Loading descriptors two ahead, or by scalar
+        // loads, which wait on the LDS counter instead, measured the same,
+        // also with the gather and the discretisation running beside.)
         const int tlo = tfirst, thi = tfirst + misc[kMiscPass + rg];
         tfirst = thi;
         int ti = tlo + wid;
