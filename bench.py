@@ -42,10 +42,14 @@ import numpy as np  # noqa: E402
 
 METRIC = "matched positions/sec (streams×T) at T=64K, 512 streams"
 HBM_PEAK = 8.0e12     # MI355X HBM3E, bytes/s
-# Algorithmic bytes per stream-position of the retrieval kernel (streams of
-# up to 65536 positions): the symbol read (1 B) and one 4-byte result record
-# (position, E+1) written; a separate kernel puts the records in time order.
-KERNEL_BYTES_PER_POS = 1 + 4
+# Algorithmic bytes per stream-position of the retrieval kernel on these
+# workloads (streams of up to 65536 positions over 16 symbols, where the
+# kernel also runs the time-ordered pass and writes E and SYM itself): the
+# symbol read (1 B; the batched workload reads its 4 bf16 channels, 8 B,
+# straight from the hidden rows) and E and SYM written (4 + 2 B).  The
+# result records the kernel writes and reads back are an intermediate.
+KERNEL_BYTES_PER_POS = {"batched": 8 + 6}
+KERNEL_BYTES_DEFAULT = 1 + 6
 # Compulsory bytes per stream-position of the whole step on the long
 # workload: 4 bf16 channels in (8 B), E and SYM out (4 + 2 B), the gathered
 # 4 bf16 values read (8 B) and written (8 B).
@@ -103,10 +107,11 @@ def kernel_roofline(npos, k_ms, workload):
     """Roofline of the retrieval kernel.  It is bound by vector instruction
     issue: `achieved` is its VALU wave instructions per launch (counters of
     the committed summary, same source) over the live event-timed duration,
-    against VALU_PEAK.  Its bytes (5 B per stream-position, symbol in and
-    result record out) against HBM peak are reported beside it; without a
-    current counter summary the bytes are the reported bound."""
-    kbytes = KERNEL_BYTES_PER_POS * npos
+    against VALU_PEAK.  Its bytes (7 B per stream-position, symbol in and
+    E and SYM out; 14 B when it reads bf16 rows) against HBM peak are
+    reported beside it; without a current counter summary the bytes are the
+    reported bound."""
+    kbytes = KERNEL_BYTES_PER_POS.get(workload, KERNEL_BYTES_DEFAULT) * npos
     hbm = kbytes / (k_ms / 1e3)
     traffic = measured_traffic() if workload == "long" else None
     valu = measured_valu() if workload == "long" else None
@@ -891,17 +896,20 @@ def main():
     # workgroup per CU with nearly all of its LDS and is bound by VALU issue;
     # the gather and the discretisation use no LDS and are bound by memory,
     # so each runs beside the other half's retrieval kernel:
-    #  - the second half's match starts when the first half's is done, and
-    #    the first half's gather waits for the event rosa_match_timed records
-    #    just before the second half's retrieval kernel;
+    #  - the first half's gather waits for the event rosa_match_timed records
+    #    just before the second half's retrieval kernel, and the second
+    #    half's gather for the first half's (one gather at a time);
     #  - each half's symbols are made by rosa_discretize one step ahead
     #    (software pipelining: every timed step still discretises, matches
     #    and gathers all streams once), after that half's gather, so they are
     #    made beside the other half's retrieval; rosa_match then reads them
     #    as 16-byte aligned symbol rows;
-    #  - the next step's first half waits for this step's second-half match
-    #    (whose last kernel needs a CU's LDS too), and its retrieval runs
-    #    beside this step's second-half gather.
+    #  - one half's match does not wait for the other's: the halves share
+    #    no buffer, each half's own order (symbols, match, gather, next
+    #    symbols) is that of its stream, and a retrieval kernel's workgroups
+    #    take the CUs that the other half's slowest workgroups leave idle
+    #    (measured: 0.69 ms per step when each match waited for the
+    #    other, 0.63 ms without).
     split = (Vd is not None and w["kind"] == "bf16" and not args.no_split
              and S % 2 == 0 and (w["H"].shape[2] // 2) % w["M"] == 0)
     if split:
@@ -916,7 +924,7 @@ def main():
         wsB = torch.empty_like(wsA)
         oA, oB = rosa.make_out(E[:h], SYM[:h]), rosa.make_out(E[h:], SYM[h:])
         s2 = torch.cuda.Stream(device=dev)
-        evA, evB0, evB1, evBE, evJ, evGA, evGB = (torch.cuda.Event() for _ in range(7))
+        evB0, evB1, evJ, evGA, evGB = (torch.cuda.Event() for _ in range(5))
 
     def prologue():
         """The first step's symbols of both halves."""
@@ -924,12 +932,8 @@ def main():
         rosa.rosa_discretize(inB, symB, s2)
 
     def step_piped(V):
-        stream.wait_event(evBE)    # the previous step's second-half match
         rosa.rosa_match(sinA, oA, wsA, stream)
-        evA.record(stream)
-        s2.wait_event(evA)
         rosa.rosa_match_timed(sinB, oB, wsB, evB0, evB1, s2)
-        evBE.record(s2)
         stream.wait_event(evB0)
         stream.wait_event(evGB)    # the previous step's second-half gather
         rosa.rosa_gather(V[:, :, :Dh], w["M"], E[:h], out[:, :, :Dh], stream)
