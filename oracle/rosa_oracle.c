@@ -330,7 +330,11 @@ int oracle_gather(const uint16_t *V, int64_t B, int64_t T, int64_t D, int M,
  * symbol exists, take it and add one, or fall to the root with l = 0; after
  * the key symbol of unit u is appended, move s up the suffix links while
  * the link's length is still >= l (a clone may have taken the matched
- * string).
+ * string).  That last move keeps (s, l) a valid pair but changes no output:
+ * until the next append a split state and its clone have the same
+ * transitions, and the next update leaves s through a transition (reaching
+ * the same state from either) or up the suffix links (from the split state
+ * the first link is the clone itself).
  *
  * Counterfactual (bit j < M, value v): the query symbol of unit u with bit j
  * forced to v, one matching update from the same state; tau^(v) as above.
