@@ -1403,7 +1403,7 @@ void stream_kernel_lds(MatchParams p)
     o.rec = p.rec + (int64_t)s * T;
 
     phase_hist<DC>(p, x, cnt, firstd, firstl);
-    phase_tasks(p, s, cnt, off, tasks, misc, kPassCap, true, Cfg::kTMax <= 8192 ? 128 : 256);
+    phase_tasks(p, s, cnt, off, tasks, misc, kPassCap, true, Cfg::kTMax <= 8192 ? 96 : 256);
 
     // D: records of the first d-1 positions go to the slots T-d+1.. (no
     // bucket holds them); the first occurrence of a d-gram in a singleton
