@@ -140,7 +140,11 @@ rosa_status rosa_match_timed(const rosa_input *in, const rosa_out *out,
                              hipEvent_t ev_begin, hipEvent_t ev_end);
 
 /* Synchronises `stream`, then returns ROSA_ERR_SYMBOL if the last rosa_match
- * that used `ws` saw a symbol >= K, else ROSA_OK (or ROSA_ERR_HIP). */
+ * that used `ws` saw a symbol >= K, else ROSA_OK (or ROSA_ERR_HIP, or
+ * ROSA_ERR_NOMEM if the host buffer for the per-stream status words cannot
+ * be allocated).  It reads the workspace's 256-byte header and, when the
+ * last call's retrieval kernel checked the symbols itself (16-byte aligned
+ * symbol rows), one status word per stream after it. */
 rosa_status rosa_match_status(const void *ws, hipStream_t stream);
 
 /* Size of the fixed device array rosa_match_noalloc works in. */

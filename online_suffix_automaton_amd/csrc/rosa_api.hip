@@ -288,12 +288,14 @@ static rosa_status match_impl(const rosa_input *in, const rosa_out *out,
         sh.ld % 16 == 0 && (reinterpret_cast<uintptr_t>(in->data) & 15) == 0) {
         // 16-byte aligned rows of a stream of the LDS plans: the stream
         // kernel reads them itself (no copy into the workspace rows first)
-        ROSA_TRY(launch_clear_flags(flags, stream, p.big));
+        // and reports bad symbols in per-stream slots, so nothing is
+        // cleared before it (the large-group counter is unused there)
         p.stage = 2;
         p.symin = reinterpret_cast<const uint8_t *>(in->data);
         p.symld = sh.ld;
         p.sym_w = rows;
         p.flags = flags;
+        p.sflag = reinterpret_cast<int32_t *>(base + w.sflag);
     } else if (sh.kind == ROSA_IN_SYMBOLS) {
         ROSA_TRY(launch_clear_flags(flags, stream, p.big));
         ROSA_TRY(launch_prep_symbols(reinterpret_cast<const uint8_t *>(in->data),
@@ -633,10 +635,31 @@ rosa_status rosa_match_status(const void *ws, hipStream_t stream)
         return ROSA_ERR_ARG;
     if (hipStreamSynchronize(stream) != hipSuccess)
         return ROSA_ERR_HIP;
-    int32_t f = 0;
-    if (hipMemcpy(&f, ws, sizeof f, hipMemcpyDeviceToHost) != hipSuccess)
+    // the header's symbol flag, and the per-stream slots right after the
+    // header when the last call's stream kernel marked them valid
+    int32_t h[3] = {0, 0, 0};
+    if (hipMemcpy(h, ws, sizeof h, hipMemcpyDeviceToHost) != hipSuccess)
         return ROSA_ERR_HIP;
-    return f ? ROSA_ERR_SYMBOL : ROSA_OK;
+    if (h[kFlagSymbol])
+        return ROSA_ERR_SYMBOL;
+    if (h[kFlagSlotMark] == kSlotMark && h[kFlagSlots] > 0 && h[kFlagSlots] <= (1 << 24)) {
+        const int32_t n = h[kFlagSlots];
+        int32_t *slots = static_cast<int32_t *>(malloc((size_t)n * sizeof(int32_t)));
+        if (!slots)
+            return ROSA_ERR_NOMEM;
+        const hipError_t e = hipMemcpy(slots, static_cast<const char *>(ws) + 256,
+                                       (size_t)n * sizeof(int32_t),
+                                       hipMemcpyDeviceToHost);
+        bool bad = false;
+        for (int32_t i = 0; i < n && e == hipSuccess; ++i)
+            bad = bad || slots[i] != 0;
+        free(slots);
+        if (e != hipSuccess)
+            return ROSA_ERR_HIP;
+        if (bad)
+            return ROSA_ERR_SYMBOL;
+    }
+    return ROSA_OK;
 }
 
 rosa_status rosa_gather(const uint16_t *V, int64_t B, int64_t T, int64_t D,

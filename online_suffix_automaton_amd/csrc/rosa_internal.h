@@ -27,12 +27,20 @@ constexpr size_t kNoAllocScratchBytes = (size_t)96 << 20;
 
 // Flags word layout in the match workspace (first 256 bytes).
 constexpr int kFlagSymbol = 0;       // int32: nonzero if a symbol >= K was seen
+// When the stream kernel reads the caller's symbol rows itself, each of its
+// workgroups stores its stream's symbol check into a slot (the int32 array
+// right after the 256 header bytes) and workgroup 0 stores the slot count
+// and kSlotMark into the header, so that no launch has to clear a flag
+// first; every other path clears the whole header before it runs.
+constexpr int kFlagSlots = 1;        // int32: number of per-stream slots
+constexpr int kFlagSlotMark = 2;     // int32: kSlotMark when the slots are valid
+constexpr int32_t kSlotMark = 0x534c4f54;
 
 // Words of the per-stream bitmap of deferred positions (record mode).
 inline __host__ __device__ int deep_words(int64_t T) { return (int)((T + 31) / 32); }
 
 struct WsLayout {
-    size_t flags, sym, pos, pos2, rec, big, stack, tasks, deep, dinfo, total;
+    size_t flags, sflag, sym, pos, pos2, rec, big, stack, tasks, deep, dinfo, total;
     int64_t Tp;          // bytes per padded symbol row
     int64_t big_cap;     // entries in the large-group list
 };
@@ -46,6 +54,7 @@ inline WsLayout ws_layout(int64_t S, int64_t T)
     w.big_cap = S * (T / 65 + 1);
     size_t o = 0;
     w.flags = o;  o += 256;
+    w.sflag = o;  o = align_up(o + (size_t)S * 4, 256);   // right after the header
     w.sym = o;    o = align_up(o + (size_t)S * w.Tp, 256);
     w.pos = o;    o = align_up(o + (size_t)S * T * 4, 256);
     w.pos2 = o;   o = align_up(o + (size_t)S * T * 4, 256);
@@ -82,6 +91,7 @@ struct MatchParams {
     uint8_t *sym_w;
     uint8_t *sym_copy;          // [S][T] or null
     int32_t *flags;
+    int32_t *sflag;             // [S] per-stream symbol check slots, or null
     int32_t pw[kMaxD + 1];      // K^i
     int32_t fl_off[kMaxD + 1];  // first-occurrence table offset of level l
     int32_t *pos;               // [S][T] bucket-ordered positions

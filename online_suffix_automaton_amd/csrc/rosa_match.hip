@@ -1341,16 +1341,19 @@ void stream_kernel_lds(MatchParams p)
         }
     } else if (p.stage == 2) {
         // the caller's row (16-byte aligned), 16 symbols per thread and
-        // step, with the zero padding around it; symbols >= K raise the flag
-        // and are clamped (as the copy into the workspace rows does).  The
-        // padded row also goes to the workspace for the later kernel that
-        // reads it, unless this kernel runs the time-ordered pass itself.
+        // step, with the zero padding around it; symbols >= K are clamped
+        // (as the copy into the workspace rows does) and reported in the
+        // stream's status slot (no launch clears a flag before this one).
+        // The padded row also goes to the workspace for the later kernel
+        // that reads it, unless this kernel runs the time-ordered pass
+        // itself.
         const uint8_t *src = p.symin + (int64_t)s * p.symld;
         uint4 *dst = reinterpret_cast<uint4 *>(symrow);
         uint4 *wdst = p.fuse == 1 ? nullptr
                                   : reinterpret_cast<uint4 *>(p.sym_w + (int64_t)s * p.Tp);
         const bool pow2 = (K & (K - 1)) == 0;
         const uint32_t hm = (uint32_t)(~(K - 1) & 0xFF) * 0x01010101u;
+        int anybad = 0;
         for (int i = tid; i < (int)(p.Tp >> 4); i += nt) {
             const int t0 = 16 * i - kPadFront;
             uint4 v;
@@ -1374,7 +1377,7 @@ void stream_kernel_lds(MatchParams p)
                     bad |= ((wq[q >> 2] >> (8 * (q & 3))) & 0xFFu) >= (uint32_t)K;
             }
             if (bad) {
-                atomicOr(&p.flags[kFlagSymbol], 1);
+                anybad = 1;
                 uint8_t *b = reinterpret_cast<uint8_t *>(&v);
                 for (int q = 0; q < 16; ++q)
                     if (b[q] >= K)
@@ -1383,6 +1386,22 @@ void stream_kernel_lds(MatchParams p)
             dst[i] = v;
             if (wdst)
                 wdst[i] = v;
+        }
+        // OR over the workgroup through the per-wave split words (unused
+        // until the tasks, which clear them before use)
+        const uint64_t wb = ballot(anybad != 0);
+        if (lane == 0)
+            eqtab[wid][0] = wb;
+        __syncthreads();
+        if (tid == 0) {
+            for (int w = 0; w < nw; ++w)
+                anybad |= eqtab[w][0] != 0 ? 1 : 0;
+            p.sflag[s] = anybad;
+            if (s == 0) {
+                p.flags[kFlagSymbol] = 0;
+                p.flags[kFlagSlots] = (int32_t)gridDim.x;   // one workgroup per stream
+                p.flags[kFlagSlotMark] = kSlotMark;
+            }
         }
     } else {
         const uint4 *src = reinterpret_cast<const uint4 *>(p.sym + (int64_t)s * p.Tp);

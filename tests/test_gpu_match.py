@@ -237,6 +237,26 @@ def test_symbol_out_of_range_flag_wide_rows(K, T, ld):
         bad[1, where] = K + 3
         rosa.match(_dev(bad)[:, :T], K=K, ws=ws)
         assert rosa.rosa_match_status(ws) == rosa.ROSA_ERR_SYMBOL, where
+    # the report belongs to the last call on the workspace, whichever path
+    # each call took: these rows are read by the retrieval kernel itself,
+    # which stores a status slot per stream and clears nothing first; with
+    # the packed-symbol copy requested the rows are copied into the
+    # workspace first, by a kernel that reports into the cleared header
+    x_bad = _dev(bad)[:, :T]
+    rosa.match(x, K=K, ws=ws)
+    assert rosa.rosa_match_status(ws) == rosa.ROSA_OK, "good after bad"
+    rosa.match(x_bad, K=K, ws=ws, want_symbols=True)
+    assert rosa.rosa_match_status(ws) == rosa.ROSA_ERR_SYMBOL, "copy path, bad"
+    rosa.match(x, K=K, ws=ws)
+    assert rosa.rosa_match_status(ws) == rosa.ROSA_OK, "own rows after copy path"
+    rosa.match(x_bad, K=K, ws=ws)
+    assert rosa.rosa_match_status(ws) == rosa.ROSA_ERR_SYMBOL, "own rows, bad"
+    rosa.match(x, K=K, ws=ws, want_symbols=True)
+    assert rosa.rosa_match_status(ws) == rosa.ROSA_OK, "copy path after own rows"
+    # fewer streams on the same workspace: only their slots count
+    rosa.match(x_bad, K=K, ws=ws)
+    rosa.match(x[:1], K=K, ws=ws)
+    assert rosa.rosa_match_status(ws) == rosa.ROSA_OK, "one stream after three"
 
 
 @pytest.mark.parametrize("M,pad", [(4, 0), (4, 37), (3, 5), (8, 0), (1, 16)])
