@@ -109,7 +109,9 @@ typedef struct rosa_out {
  * gives the same outputs as over the bf16 input.  A caller that pipelines
  * the path over parts of the streams (for instance one part's retrieval
  * beside another part's gather, on two streams) can run this step apart
- * from the retrieval. */
+ * from the retrieval.  With M = 4, rows whose pitch is a multiple of 16
+ * bytes at a 16-byte aligned address take a kernel that uses no LDS, so it
+ * can run on the same CUs as a retrieval kernel (which holds their LDS). */
 rosa_status rosa_discretize(const rosa_input *in, uint8_t *symbols,
                             int64_t ld, hipStream_t stream);
 
@@ -127,7 +129,11 @@ size_t rosa_match_workspace_bytes(int64_t S, int64_t T, int32_t K);
  * it must not be shared by calls in flight at the same time.  Limits:
  * 1 <= T < 2^26, S*T < 2^40.  A symbol >= K sets a sticky flag in `ws`
  * (read it with rosa_match_status); the outputs of that call are then
- * unspecified.  No device memory is read outside the given buffers. */
+ * unspecified.  No device memory is read outside the given buffers.
+ * Symbol rows with T <= 65536, a pitch that is a multiple of 16 bytes and a
+ * 16-byte aligned address (and no packed-symbol copy requested) are read by
+ * the retrieval kernel itself; other symbol rows are first copied into the
+ * workspace by a kernel of their own. */
 rosa_status rosa_match(const rosa_input *in, const rosa_out *out, void *ws,
                        size_t ws_bytes, hipStream_t stream);
 
