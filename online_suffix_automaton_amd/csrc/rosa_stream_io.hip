@@ -237,13 +237,24 @@ __global__ __launch_bounds__(256) void discretize4_kernel(
         const int64_t tt = tile_i / nrt;
         const int64_t tc = tt * 64 + w * 16;   // this wave's first position
         const int64_t r = (tile_i - tt * nrt) * 64 + lane;
+        // one pointer stepped by a row per load (the per-load 64-bit index
+        // products were most of this kernel's vector instructions, which
+        // take issue slots from a retrieval kernel on the same CU)
+        const int nk = (int)min<int64_t>(16, T - tc);
+        const uint16_t *hp = H + (b * T + tc) * ld + r * 4;
         uint2 v[16];
+        if (nk == 16 && r < R) {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int64_t t = tc + k;
-            v[k] = make_uint2(0u, 0u);
-            if (t < T && r < R)
-                v[k] = *reinterpret_cast<const uint2 *>(H + (b * T + t) * ld + r * 4);
+            for (int k = 0; k < 16; ++k)
+                v[k] = *reinterpret_cast<const uint2 *>(hp + k * ld);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                v[k] = make_uint2(0u, 0u);
+                if (k < nk && r < R)
+                    v[k] = *reinterpret_cast<const uint2 *>(hp);
+                hp += ld;
+            }
         }
         if (r >= R)
             continue;
@@ -321,7 +332,13 @@ constexpr int kGatherWG = 32;   // workgroups of 4 waves per XCD
 
 typedef int32_t gather_v4i __attribute__((ext_vector_type(4)));
 
-template <int GPX>
+// O32 (T, the row pitches in bytes below 2^24, one batch row of V and of
+// the output below 4 GiB): each row's byte offset is one 24-bit multiply-add
+// on a uniform base, and a lane without a hit reads row 0 and keeps zero by
+// a select, so a value load costs a few vector instructions instead of a
+// 64-bit index product and a branch (vector instructions here take issue
+// slots from a retrieval kernel on the same CU).
+template <int GPX, bool O32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void gather_wave_kernel(
     const uint16_t *__restrict__ V, int64_t T, int64_t R, int64_t ldv,
     const int32_t *__restrict__ E, uint16_t *__restrict__ out, int64_t ldo,
@@ -332,7 +349,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
     const int64_t ng = (R + 15) / 16, nch = (T + CH - 1) / CH;
     const int x = (int)(blockIdx.x % kXcds);
     const int lane = threadIdx.x & 63;
-    const int64_t wv = (int64_t)(blockIdx.x / kXcds) * 4 + (threadIdx.x >> 6);
+    // the chunk index is the wave's (scalar arithmetic)
+    const int64_t wv = __builtin_amdgcn_readfirstlane(
+        (int)(blockIdx.x / kXcds) * 4 + (int)(threadIdx.x >> 6));
     const int64_t Wv = (int64_t)(gridDim.x / kXcds) * 4;
     const int rl = lane & 15, q = lane >> 4;
     for (int64_t c = wv;; c += Wv) {
@@ -367,25 +386,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
                 }
         }
         uint64_t v[U][4];
+        if constexpr (O32) {
+            const unsigned char *vb = reinterpret_cast<const unsigned char *>(V + b * T * ldv);
+            const uint32_t lv = (uint32_t)ldv * 2u, col = (uint32_t)r * 8u;
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+            for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int32_t ee = e[u][i] > T - 2 ? (int32_t)(T - 2) : e[u][i];
-                v[u][i] = 0;
-                if (ee >= 0)
-                    v[u][i] = *reinterpret_cast<const uint64_t *>(
-                        V + (b * T + (ee + 1)) * ldv + r * 4);
-            }
+                for (int i = 0; i < 4; ++i) {
+                    const int32_t ee = min(e[u][i], (int32_t)T - 2);
+                    const uint32_t row = ee >= 0 ? (uint32_t)(ee + 1) : 0u;
+                    const uint64_t w = *reinterpret_cast<const uint64_t *>(
+                        vb + (__umul24(row, lv) + col));
+                    v[u][i] = ee >= 0 ? w : 0ull;
+                }
+        } else {
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+            for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t t = t0 + 16 * u + 4 * q + i;
-                if (t < T)
+                for (int i = 0; i < 4; ++i) {
+                    const int32_t ee = e[u][i] > T - 2 ? (int32_t)(T - 2) : e[u][i];
+                    v[u][i] = 0;
+                    if (ee >= 0)
+                        v[u][i] = *reinterpret_cast<const uint64_t *>(
+                            V + (b * T + (ee + 1)) * ldv + r * 4);
+                }
+        }
+        if (O32 && t0 + CH <= T) {
+            unsigned char *ob = reinterpret_cast<unsigned char *>(out + b * T * ldo);
+            const uint32_t lo = (uint32_t)ldo * 2u;
+            const uint32_t o0 = (__umul24((uint32_t)(t0 + 4 * q), lo) + (uint32_t)r * 8u);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
                     __builtin_nontemporal_store(
-                        v[u][i], reinterpret_cast<uint64_t *>(out + (b * T + t) * ldo + r * 4));
-            }
+                        v[u][i], reinterpret_cast<uint64_t *>(
+                                     ob + (o0 + (uint32_t)(16 * u + i) * lo)));
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t t = t0 + 16 * u + 4 * q + i;
+                    if (t < T)
+                        __builtin_nontemporal_store(
+                            v[u][i], reinterpret_cast<uint64_t *>(out + (b * T + t) * ldo + r * 4));
+                }
+        }
     }
 }
 
@@ -519,11 +566,20 @@ hipError_t launch_gather(const uint16_t *V, int64_t B, int64_t T, int64_t D,
         const int W = (int)(wgs < kGatherWG ? wgs : kGatherWG);
         const int vec_e = (T % 4) == 0 && (((uintptr_t)E) & 15) == 0;
         dim3 grid((unsigned)(kXcds * W), (unsigned)B);
-        if (aliased)
-            hipLaunchKernelGGL(gather_wave_kernel<2>, grid, dim3(256), 0, st, V, T,
+        const int64_t k24 = (int64_t)1 << 24, k32 = (int64_t)1 << 32;
+        const bool o32 = T < k24 && ldv * 2 < k24 && ldo * 2 < k24 && T * ldv * 2 < k32 &&
+                         T * ldo * 2 < k32;
+        if (aliased && o32)
+            hipLaunchKernelGGL((gather_wave_kernel<2, true>), grid, dim3(256), 0, st, V, T,
+                               R, ldv, E, out, ldo, vec_e);
+        else if (aliased)
+            hipLaunchKernelGGL((gather_wave_kernel<2, false>), grid, dim3(256), 0, st, V, T,
+                               R, ldv, E, out, ldo, vec_e);
+        else if (o32)
+            hipLaunchKernelGGL((gather_wave_kernel<1, true>), grid, dim3(256), 0, st, V, T,
                                R, ldv, E, out, ldo, vec_e);
         else
-            hipLaunchKernelGGL(gather_wave_kernel<1>, grid, dim3(256), 0, st, V, T,
+            hipLaunchKernelGGL((gather_wave_kernel<1, false>), grid, dim3(256), 0, st, V, T,
                                R, ldv, E, out, ldo, vec_e);
         return hipGetLastError();
     }
