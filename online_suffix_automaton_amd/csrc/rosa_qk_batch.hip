@@ -320,50 +320,44 @@ __global__ __launch_bounds__(kQtThreads) void qt_keys_scan_kernel(QkParams p, Qt
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int N = qt_units(p, s);
     if (blockIdx.x == 0) {
+        // rounds of kQtThreads consecutive groups, thread tid taking group
+        // r * kQtThreads + tid (so a segment's counts are read and written
+        // coalesced): each group's counts become exclusive running sums
+        // over the segments, and the groups' totals are scanned in group
+        // order, one block scan per round with the carry between rounds
         const int R = (sh.nb + kQtThreads - 1) / kQtThreads;   // <= 16
         const int nsegN = (N + kQbtSeg - 1) / kQbtSeg;
         int32_t *hc = p.hcnt + s * sh.nseg * sh.nb;
-        int run[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            run[r] = 0;
-            const int b = tid * R + r;
-            if (r < R && b < sh.nb) {
-                // eight segments' counts in flight at a time
+        int32_t *ko = p.koff + s * (sh.nb + 1);
+        int carry = 0;
+        for (int r = 0; r < R; ++r) {
+            const int b = r * kQtThreads + tid;
+            int acc = 0;
+            if (b < sh.nb) {
+                // sixteen segments' counts in flight at a time (all of a
+                // stream of 65536 units)
                 int32_t *col = hc + b;
-                int acc = 0;
-                for (int g0 = 0; g0 < nsegN; g0 += 8) {
-                    int h[8];
+                for (int g0 = 0; g0 < nsegN; g0 += 16) {
+                    int h[16];
 #pragma unroll
-                    for (int k = 0; k < 8; ++k)
+                    for (int k = 0; k < 16; ++k)
                         h[k] = g0 + k < nsegN ? col[(int64_t)(g0 + k) * sh.nb] : 0;
 #pragma unroll
-                    for (int k = 0; k < 8; ++k)
+                    for (int k = 0; k < 16; ++k)
                         if (g0 + k < nsegN) {
                             col[(int64_t)(g0 + k) * sh.nb] = acc;
                             acc += h[k];
                         }
                 }
-                run[r] = acc;
             }
-        }
-        int sum = 0;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            sum += run[r];
-        int total;
-        int base = qt_block_scan(sum, ws, &total);
-        int32_t *ko = p.koff + s * (sh.nb + 1);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int b = tid * R + r;
-            if (r < R && b < sh.nb) {
-                ko[b] = base;
-                base += run[r];
-            }
+            int total;
+            const int base = qt_block_scan(acc, ws, &total);
+            if (b < sh.nb)
+                ko[b] = carry + base;
+            carry += total;
         }
         if (tid == 0)
-            ko[sh.nb] = total;
+            ko[sh.nb] = carry;
         return;
     }
     const int slot = ((int)blockIdx.x - 1) * 16 + w;
