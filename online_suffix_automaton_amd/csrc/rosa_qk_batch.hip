@@ -309,8 +309,8 @@ __global__ __launch_bounds__(kQtThreads) void qt_keys_count_kernel(QkParams p, Q
 }
 
 // Workgroup 0 of a stream: group offsets (a running sum over the segments
-// per group, eight segments' counts in flight at a time, then a scan over
-// the groups).  Workgroups 1..: one wave per
+// per group, sixteen segments' counts in flight at a time, then a scan over
+// the groups, in rounds of 1024 groups).  Workgroups 1..: one wave per
 // short-table row, prefix maxima over its chunks: each lane takes 16
 // consecutive chunks, a wave scan joins the lanes, 1024 chunks per pass.
 __global__ __launch_bounds__(kQtThreads) void qt_keys_scan_kernel(QkParams p, QtShape sh)
