@@ -282,8 +282,11 @@ static rosa_status match_impl(const rosa_input *in, const rosa_out *out,
     }
     uint8_t *rows = reinterpret_cast<uint8_t *>(base + w.sym);
     MatchParams p = match_params(sh, base, w, out);
-    // the flags and the large-group counter start at zero; the bf16 path
-    // clears them (and pads the rows) inside the discretisation launch
+    // the flags and the large-group counter start at zero: cleared by a
+    // launch of their own before a copy of the symbol rows, inside the
+    // discretisation launch (bf16), or -- when the stream kernel reads the
+    // caller's rows itself -- replaced by per-stream status slots that the
+    // stream kernel always writes (no clear needed)
     if (sh.kind == ROSA_IN_SYMBOLS && !out->symbols && stream_uses_records(sh.T) &&
         sh.ld % 16 == 0 && (reinterpret_cast<uintptr_t>(in->data) & 15) == 0) {
         // 16-byte aligned rows of a stream of the LDS plans: the stream
