@@ -1038,13 +1038,31 @@ __device__ void solve_big_bucket(const MatchParams &p, const uint8_t *x, int s,
                 for (int u = 0; u < 4; ++u) {
                     const bool hs = tt[u] >= 0;
                     const uint64_t m = ballot(hs);
+                    const int t = tt[u];
                     if (hs) {
-                        const int t = tt[u];
                         o.rec[start + 1 + nrec + __popcll(m & below)] = (uint32_t)t << 16;
-                        atomicOr(&deepbits[t >> 5], 1u << (t & 31));
                         dinfo[t] = drec;
                     }
                     nrec += __popcll(m);
+                    // the bitmap bits, one atomic per word: members are in
+                    // time order, so the lanes of one word are adjacent (the
+                    // lanes without a member, at the end, each stand alone);
+                    // a segmented OR gathers each word's bits in its first
+                    // lane.  Per-lane atomics on one word are serialised at
+                    // the cache and made this loop the most expensive part
+                    // of a constant stream.
+                    const int wd = hs ? (t >> 5) : -1 - lane;
+                    uint32_t bits = hs ? 1u << (t & 31) : 0u;
+#pragma unroll
+                    for (int sh = 1; sh < 64; sh <<= 1) {
+                        const uint32_t ob = (uint32_t)__shfl_down((int)bits, sh);
+                        const int ow = __shfl_down(wd, sh);
+                        if (lane + sh < 64 && ow == wd)
+                            bits |= ob;
+                    }
+                    const int pw = __shfl_up(wd, 1);
+                    if (hs && (lane == 0 || pw != wd))
+                        atomicOr(&deepbits[wd], bits);
                 }
             }
         } else {
