@@ -908,7 +908,8 @@ constexpr int kBigDeferLevels = 8;
 // Whether the n members (positions X[0 .. n), in time order) of a group at
 // level ell agree for the next kBigDeferLevels (= 8) levels: member t's
 // symbols x[t-ell-7 .. t-ell] against the last member's (the longest
-// history), one 8-byte window per member, 256 members per round.  Symbols
+// history), one 8-byte window per member, 1024 members per round (16 position loads
+// of a lane in flight: the check is bound by their latency).  Symbols
 // before position 0 do not exist: a member compares only the symbols of its
 // own history, as a level step treats a member whose history has ended as
 // agreeing (such members are the group's first ones, which the level steps
@@ -919,16 +920,16 @@ __device__ bool big_group_uniform(const int32_t *X, int n, const uint8_t *x, int
     static_assert(kBigDeferLevels == 8, "one 8-symbol window per member");
     const int lane = __lane_id();
     const uint64_t ref = load8_end(x, X[n - 1] - ell);
-    for (int i0 = 0; i0 < n; i0 += 256) {
-        int tt[4];
+    for (int i0 = 0; i0 < n; i0 += 64 * 16) {
+        int tt[16];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 16; ++u) {
             const int i = i0 + 64 * u + lane;
             tt[u] = i < n ? X[i] : -1;
         }
         bool bad = false;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 16; ++u) {
             const int v = tt[u] - ell + 1;   // symbols of the member's history in the window
             if (tt[u] >= 0 && v > 0) {
                 const uint64_t m = v >= 8 ? ~0ull : ~0ull << (8 * (8 - v));
@@ -1026,16 +1027,16 @@ __device__ void solve_big_bucket(const MatchParams &p, const uint8_t *x, int s,
             const uint4 drec = make_uint4((uint32_t)ga,
                                           (uint32_t)gn | ((uint32_t)cur.buf << 31),
                                           0u, (lb << 3) << 16);
-            // 256 members per round, a lane's four position loads in flight
-            for (int i0 = 1; i0 < gn; i0 += 256) {
-                int tt[4];
+            // 512 members per round, a lane's eight position loads in flight
+            for (int i0 = 1; i0 < gn; i0 += 64 * 8) {
+                int tt[8];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
+                for (int u = 0; u < 8; ++u) {
                     const int i = i0 + 64 * u + lane;
                     tt[u] = i < gn ? X[ga + i] : -1;
                 }
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
+                for (int u = 0; u < 8; ++u) {
                     const bool hs = tt[u] >= 0;
                     const uint64_t m = ballot(hs);
                     const int t = tt[u];
