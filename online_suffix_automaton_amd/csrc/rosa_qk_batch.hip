@@ -893,19 +893,33 @@ __global__ __launch_bounds__(64) void qt_defer_kernel(QkParams p, QtShape sh)
     const bool want_cf = p.cf_tau || p.cf_ridx;
     const int V = want_cf ? 1 + p.M : 1;
     int Ep = -1, Lp = 0;   // own answer of the unit before the chunk
+    // a chunk's flags, kept answers and query symbols are loaded while the
+    // chunk before it is answered (one wave per stream: the walk is bound by
+    // memory latency, and a load issued after the chunk's stores would wait
+    // for them too)
+    uint32_t dfn = lane < N ? p.dfl[s * T + lane] : 0u;
+    int4 eon = lane < N ? p.eo[s * T + lane] : make_int4(-1, 0, -1, 0);
+    int qn = lane < N ? (int)Q[lane] : 0;
     for (int c0 = 0; c0 < N; c0 += 64) {
         const int u = c0 + lane;
         const bool act = u < N;
         const int n = min(64, N - c0);
-        const uint32_t df = act ? p.dfl[s * T + u] : 0u;
-        const int4 eoa = act ? p.eo[s * T + u] : make_int4(-1, 0, -1, 0);
+        const uint32_t df = dfn;
+        const int4 eoa = eon;
+        const int qraw = qn;
+        {
+            const int un = u + 64;
+            dfn = un < N ? p.dfl[s * T + un] : 0u;
+            eon = un < N ? p.eo[s * T + un] : make_int4(-1, 0, -1, 0);
+            qn = un < N ? (int)Q[un] : 0;
+        }
         if (!qt_ballot(df != 0u)) {
             Ep = __shfl(eoa.x, n - 1);
             Lp = __shfl(eoa.y, n - 1);
             continue;
         }
         const int Ein = Ep, Lin = Lp;
-        const int qs = act ? min((int)Q[u], K - 1) : 0;
+        const int qs = act ? min(qraw, K - 1) : 0;
         int myE = eoa.x, myL = eoa.y;
         const uint64_t dm0 = qt_ballot(df & 1u);
         // own symbols in time order: runs by the extension rule
